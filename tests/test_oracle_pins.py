@@ -1,0 +1,372 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself.
+
+Each test states what it pins and the basis: a closed form, an identity the
+pages state, a worked example printed on the pages (``tests/golden``), or a
+textbook property.  A plausible slip in the oracle (dropped scale, wrong sign,
+swapped K/V, wrong GQA head map, causal off-by-one, wrong rotary pairing or
+frequency) fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand(rng, *shape):
+    return rng.standard_normal(size=shape)
+
+
+# ---------------------------------------------------------------------------
+# Attention: closed forms
+# ---------------------------------------------------------------------------
+def test_two_key_closed_form():
+    """Two keys: weights are a logistic of the scaled score gap (pins scale,
+    sign, K vs V roles).  softmax([a, b]) = [1/(1+e^(b-a)), 1/(1+e^(a-b))]."""
+    rng = np.random.default_rng(11)
+    D = 8
+    q = rand(rng, 1, 1, 1, D)
+    k = rand(rng, 1, 2, 1, D)
+    v = rand(rng, 1, 2, 1, D)
+    scale = 0.37
+    a = scale * float(q[0, 0, 0] @ k[0, 0, 0])
+    b = scale * float(q[0, 0, 0] @ k[0, 1, 0])
+    w0 = 1.0 / (1.0 + math.exp(b - a))
+    w1 = 1.0 / (1.0 + math.exp(a - b))
+    want = w0 * v[0, 0, 0] + w1 * v[0, 1, 0]
+    out, lse = oracle.attention(q, k, v, scale)
+    np.testing.assert_allclose(out[0, 0, 0], want, rtol=0, atol=1e-14)
+    assert abs(lse[0, 0, 0] - (max(a, b) + math.log(math.exp(a - max(a, b)) + math.exp(b - max(a, b))))) < 1e-14
+
+
+def test_uniform_scores_give_mean_of_v():
+    """q = 0 makes every score 0, so the output is the mean of V and
+    LSE = ln(n) (definition of softmax, §18.3)."""
+    rng = np.random.default_rng(12)
+    n, D = 37, 16
+    q = np.zeros((1, 3, 2, D))
+    k = rand(rng, 1, n, 2, D)
+    v = rand(rng, 1, n, 2, D)
+    out, lse = oracle.attention(q, k, v, 0.25)
+    for h in range(2):
+        np.testing.assert_allclose(out[0, :, h], np.broadcast_to(v[0, :, h].mean(0), (3, D)), atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(n), atol=1e-14)
+
+
+def test_single_key_returns_v():
+    """One visible key: output is that key's V and LSE is its scaled score."""
+    rng = np.random.default_rng(13)
+    D = 32
+    q = rand(rng, 2, 1, 4, D)
+    k = rand(rng, 2, 1, 1, D)
+    v = rand(rng, 2, 1, 1, D)
+    out, lse = oracle.attention(q, k, v, 0.5)
+    for b in range(2):
+        for h in range(4):
+            np.testing.assert_allclose(out[b, 0, h], v[b, 0, 0], atol=0)
+            assert abs(lse[b, h, 0] - 0.5 * float(q[b, 0, h] @ k[b, 0, 0])) < 1e-13
+
+
+def test_causal_row0_and_row1():
+    """Causal row 0 sees only key 0 (returns V[0]); row 1 sees exactly keys 0
+    and 1 (two-key closed form) — pins the j <= i convention."""
+    rng = np.random.default_rng(14)
+    S, D = 9, 8
+    q = rand(rng, 1, S, 1, D)
+    k = rand(rng, 1, S, 1, D)
+    v = rand(rng, 1, S, 1, D)
+    scale = 0.3
+    out, _ = oracle.attention(q, k, v, scale, causal=True)
+    np.testing.assert_allclose(out[0, 0, 0], v[0, 0, 0], atol=0)
+    a = scale * float(q[0, 1, 0] @ k[0, 0, 0])
+    b = scale * float(q[0, 1, 0] @ k[0, 1, 0])
+    w0 = 1.0 / (1.0 + math.exp(b - a))
+    np.testing.assert_allclose(out[0, 1, 0], w0 * v[0, 0, 0] + (1 - w0) * v[0, 1, 0], atol=1e-14)
+
+
+def test_shift_invariance_and_needle():
+    """Adding a constant to every score of a row leaves softmax unchanged;
+    a key with an overwhelming score returns its value (needle)."""
+    rng = np.random.default_rng(15)
+    n, D = 50, 16
+    q = rand(rng, 1, 1, 1, D)
+    k = rand(rng, 1, n, 1, D)
+    v = rand(rng, 1, n, 1, D)
+    # shift: append a coordinate with q = 1 and identical k -> every score += c*scale
+    q2 = np.concatenate([q, np.ones((1, 1, 1, 1))], axis=-1)
+    k2 = np.concatenate([k, np.full((1, n, 1, 1), 5.0)], axis=-1)
+    v2 = np.concatenate([v, np.zeros((1, n, 1, 1))], axis=-1)
+    o1, _ = oracle.attention(q, k, v, 0.2)
+    o2, _ = oracle.attention(q2, k2, v2, 0.2)
+    np.testing.assert_allclose(o2[0, 0, 0, :D], o1[0, 0, 0], atol=1e-14)
+    kn = k.copy()
+    kn[0, 17, 0] = 400.0 * q[0, 0, 0] / np.linalg.norm(q[0, 0, 0])
+    o3, _ = oracle.attention(q, kn, v, 1.0)
+    np.testing.assert_allclose(o3[0, 0, 0], v[0, 17, 0], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Attention: identities and independent formulations
+# ---------------------------------------------------------------------------
+def online_softmax_attention(qv, K, V, scale):
+    """Streaming form of §18.3, element by element: running max m and
+    denominator l with rescaling of the output accumulator, divided once at
+    the end.  Written here independently of the oracle."""
+    m, l = -math.inf, 0.0
+    acc = np.zeros(V.shape[-1])
+    for j in range(K.shape[0]):
+        x = scale * float(qv @ K[j])
+        m_new = max(m, x)
+        corr = math.exp(m - m_new) if m != -math.inf else 0.0
+        l = l * corr + math.exp(x - m_new)
+        acc = acc * corr + math.exp(x - m_new) * V[j]
+        m = m_new
+    return acc / l, m + math.log(l)
+
+
+def test_three_pass_equals_online_recurrence():
+    """The three-pass oracle equals the online recurrence (the pages state the
+    two are mathematically identical)."""
+    rng = np.random.default_rng(16)
+    S, D = 60, 24
+    q = rand(rng, 1, S, 2, D)
+    k = rand(rng, 1, S, 1, D) * 3.0
+    v = rand(rng, 1, S, 1, D)
+    out, lse = oracle.attention(q, k, v, 0.2, causal=True)
+    for i in [0, 1, 7, 31, 59]:
+        for h in range(2):
+            o_ref, l_ref = online_softmax_attention(q[0, i, h], k[0, :i + 1, 0], v[0, :i + 1, 0], 0.2)
+            np.testing.assert_allclose(out[0, i, h], o_ref, rtol=1e-12, atol=1e-13)
+            assert abs(lse[0, h, i] - l_ref) < 1e-12
+
+
+def test_bruteforce_matrix_form_small():
+    """Full-matrix softmax(Q K^T * scale) V in numpy (the naive form of §18.2)
+    agrees with the row-wise oracle for N <= 64, causal and not."""
+    rng = np.random.default_rng(17)
+    for S, D, causal in [(1, 4, False), (16, 8, True), (64, 64, False), (64, 32, True)]:
+        q = rand(rng, 1, S, 1, D)
+        k = rand(rng, 1, S, 1, D)
+        v = rand(rng, 1, S, 1, D)
+        s = (q[0, :, 0] @ k[0, :, 0].T) * 0.125
+        if causal:
+            s = np.where(np.tril(np.ones((S, S), bool)), s, -np.inf)
+        a = np.exp(s - s.max(1, keepdims=True))
+        a /= a.sum(1, keepdims=True)
+        out, _ = oracle.attention(q, k, v, 0.125, causal=causal)
+        np.testing.assert_allclose(out[0, :, 0], a @ v[0, :, 0], rtol=1e-12, atol=1e-13)
+
+
+def test_pure_python_fsum_tiny():
+    """Pure-Python loops with math.fsum for N <= 16 (independent of numpy)."""
+    rng = np.random.default_rng(18)
+    S, D = 16, 5
+    q = rand(rng, 1, S, 1, D)
+    k = rand(rng, 1, S, 1, D)
+    v = rand(rng, 1, S, 1, D)
+    out, _ = oracle.attention(q, k, v, 0.7, causal=True)
+    for i in range(S):
+        sc = [0.7 * math.fsum(q[0, i, 0, d] * k[0, j, 0, d] for d in range(D)) for j in range(i + 1)]
+        mx = max(sc)
+        e = [math.exp(x - mx) for x in sc]
+        z = math.fsum(e)
+        for d in range(D):
+            want = math.fsum(e[j] / z * v[0, j, 0, d] for j in range(i + 1))
+            assert abs(out[0, i, 0, d] - want) < 1e-13
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    """Query head h reads KV head h // (Hq/Hkv): GQA equals MHA with each KV
+    head repeated group-size times (pins the head map)."""
+    rng = np.random.default_rng(19)
+    S, Hq, Hkv, D = 12, 8, 2, 16
+    q = rand(rng, 1, S, Hq, D)
+    k = rand(rng, 1, S, Hkv, D)
+    v = rand(rng, 1, S, Hkv, D)
+    out, lse = oracle.attention(q, k, v, 0.3, causal=True)
+    kr = np.repeat(k, Hq // Hkv, axis=2)
+    vr = np.repeat(v, Hq // Hkv, axis=2)
+    out2, lse2 = oracle.attention(q, kr, vr, 0.3, causal=True)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+    # and differs from the wrong (modulo) mapping
+    kw = np.tile(k, (1, 1, Hq // Hkv, 1))
+    vw = np.tile(v, (1, 1, Hq // Hkv, 1))
+    out3, _ = oracle.attention(q, kw, vw, 0.3, causal=True)
+    assert np.abs(out3 - out).max() > 1e-3
+
+
+def test_split_merge_equals_unsplit():
+    """Partials over key ranges merged by the rescale identity of §18.3 equal
+    the unsplit three-pass result, including an empty range."""
+    rng = np.random.default_rng(20)
+    n, D = 300, 16
+    q = rand(rng, 1, 1, 1, D)
+    k = rand(rng, 1, n, 1, D) * 2
+    v = rand(rng, 1, n, 1, D)
+    out, lse = oracle.attention(q, k, v, 0.25)
+    cuts = [0, 64, 64, 130, 257, 300]
+    parts = [oracle.partial_attention(q[0, 0, 0], k[0, a:b, 0], v[0, a:b, 0], 0.25)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    o, l = oracle.lse_merge(parts)
+    np.testing.assert_allclose(o, out[0, 0, 0], rtol=1e-12, atol=1e-14)
+    assert abs(l - lse[0, 0, 0]) < 1e-12
+
+
+def test_chunked_rows_equal_causal_rows():
+    """A chunk row i at cache offset c sees keys 0..c+i, i.e. exactly causal
+    row c+i of the concatenated sequence (chunked prefill, multi-GPU
+    partitioning article §2.2)."""
+    rng = np.random.default_rng(21)
+    S, C, D = 40, 8, 8
+    q = rand(rng, 1, S, 2, D)
+    k = rand(rng, 1, S, 1, D)
+    v = rand(rng, 1, S, 1, D)
+    full, _ = oracle.attention(q, k, v, 0.4, causal=True)
+    for c0 in range(0, S, C):
+        rows = np.arange(C)
+        lim = (c0 + rows + 1)[None, :]
+        o, _ = oracle.attention_rows(q[:, c0:c0 + C], k, v, lim, 0.4)
+        np.testing.assert_array_equal(o, full[:, c0:c0 + C])
+
+
+def test_empty_row_is_nan_with_minus_inf_lse():
+    q = np.ones((1, 1, 1, 4))
+    k = np.ones((1, 3, 1, 4))
+    out, lse = oracle.attention_rows(q, k, k, np.zeros((1, 1), np.int64), 1.0)
+    assert np.isnan(out).all() and lse[0, 0, 0] == -np.inf
+
+
+def test_bf16_inputs_widen_exactly():
+    """bf16 bit patterns are widened exactly (no re-rounding) on the way in."""
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((1, 20, 1, 8)).astype(np.float32)
+    xb = synth.f32_to_bf16_bits(x)
+    xf = synth.bf16_bits_to_f32(xb).astype(np.float64)
+    o1, l1 = oracle.attention(xb, xb, xb, 0.3, causal=True)
+    o2, l2 = oracle.attention(xf, xf, xf, 0.3, causal=True)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# Rotary embedding
+# ---------------------------------------------------------------------------
+def test_rope_closed_form_d2_and_d4():
+    """D=2: theta_0 = 1, so position p rotates (x0, x1) by p radians
+    counter-clockwise.  D=4, base 10000: pairs (0,2) at theta 1 and (1,3) at
+    theta 10000^(-1/2) = 0.01 (the rotate-half reading)."""
+    x = np.array([[[0.3, -1.2]]])
+    for p in [0, 1, 5, 1000]:
+        got = oracle.rope(x, [p])
+        c, s = math.cos(p), math.sin(p)
+        np.testing.assert_allclose(got[0, 0], [0.3 * c + 1.2 * s, -1.2 * c + 0.3 * s], atol=1e-15)
+    x4 = np.array([[[1.0, 2.0, 3.0, 4.0]]])
+    p = 7
+    got = oracle.rope(x4, [p])
+    c0, s0 = math.cos(7.0), math.sin(7.0)
+    c1, s1 = math.cos(0.07), math.sin(0.07)
+    want = [1 * c0 - 3 * s0, 2 * c1 - 4 * s1, 3 * c0 + 1 * s0, 4 * c1 + 2 * s1]
+    np.testing.assert_allclose(got[0, 0], want, atol=1e-14)
+
+
+def test_rope_identity_norm_and_relative_position():
+    """R(0) = I; rotations keep the norm; <R(p)q, R(p')k> depends only on
+    p - p' (textbook RoPE properties; shifts up to 2^17)."""
+    rng = np.random.default_rng(23)
+    D = 128
+    x = rng.standard_normal((3, 2, D))
+    np.testing.assert_array_equal(oracle.rope(x, [0, 0, 0]), x)
+    r = oracle.rope(x, [5, 70000, 131071])
+    np.testing.assert_allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    q = rng.standard_normal((1, 1, D))
+    k = rng.standard_normal((1, 1, D))
+    for p, pk, t in [(10, 3, 1000), (65535, 0, 65536), (100, 90000, 31)]:
+        a = float(oracle.rope(q, [p])[0, 0] @ oracle.rope(k, [pk])[0, 0])
+        b = float(oracle.rope(q, [p + t])[0, 0] @ oracle.rope(k, [pk + t])[0, 0])
+        assert abs(a - b) < 1e-9 * np.linalg.norm(q) * np.linalg.norm(k)
+
+
+# ---------------------------------------------------------------------------
+# Relayout
+# ---------------------------------------------------------------------------
+def _read_golden(name):
+    spec = {}
+    heads = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            if parts[0] == "rank":
+                heads[int(parts[1])] = [int(x) for x in parts[3:]]
+            else:
+                spec[parts[0]] = int(parts[1])
+    return spec, heads
+
+
+def test_permute_worked_example():
+    """The article's worked example: SP=4, 16-token shards, 8 heads; after the
+    exchange rank r holds heads 2r, 2r+1 for all 64 tokens in global order."""
+    spec, heads = _read_golden("ulysses_relayout_example.txt")
+    SP, S_loc, H, D = spec["SP"], spec["S_loc"], spec["H_tot"], 3
+    code = np.zeros((SP, S_loc, H, D), dtype=np.int64)
+    for k_ in range(SP):
+        for s in range(S_loc):
+            for h in range(H):
+                for d in range(D):
+                    code[k_, s, h, d] = ((k_ * 100 + s) * 100 + h) * 100 + d
+    for r in range(SP):
+        out = oracle.permute(code, r)
+        assert out.shape == (spec["tokens_after"], spec["heads_after"], D)
+        for t in range(spec["tokens_after"]):
+            for hl, hg in enumerate(heads[r]):
+                for d in range(D):
+                    assert out[t, hl, d] == ((t // S_loc * 100 + t % S_loc) * 100 + hg) * 100 + d
+
+
+def test_permute_all_ranks_is_a_bijection():
+    rng = np.random.default_rng(24)
+    SP, S_loc, H, D = 4, 5, 8, 6
+    x = rng.integers(0, 2**16, size=(SP, S_loc, H, D), dtype=np.uint16)
+    outs = [oracle.permute(x, r) for r in range(SP)]
+    # stack heads back: rank r's heads are global heads r*H/SP .. (r+1)*H/SP - 1
+    full = np.concatenate(outs, axis=1)          # [SP*S_loc][H][D]
+    np.testing.assert_array_equal(full.reshape(SP, S_loc, H, D), x)
+
+
+# ---------------------------------------------------------------------------
+# Paged cache read-back
+# ---------------------------------------------------------------------------
+def test_paged_gather_hand_example():
+    """Two requests, one KV head, 64-token blocks placed at hand-chosen
+    physical ids; V blocks are dimension-major."""
+    D = 2
+    k_pool = np.zeros((3, 64, D), np.uint16)
+    v_pool = np.zeros((3, D, 64), np.uint16)
+    k_pool[2, 5] = [7, 8]
+    v_pool[2, :, 5] = [9, 10]
+    k_pool[0, 1] = [1, 2]
+    v_pool[0, :, 1] = [3, 4]
+    table = np.array([[[1, 2]], [[0, -1]]], np.int32)     # b0: blocks 1,2 ; b1: block 0
+    ko, vo = oracle.paged_gather(k_pool, v_pool, table, [70, 2], 70)
+    assert list(ko[0, 64 + 5, 0]) == [7, 8] and list(vo[0, 69, 0]) == [9, 10]
+    assert list(ko[1, 1, 0]) == [1, 2] and list(vo[1, 1, 0]) == [3, 4]
+
+
+def test_paged_gather_roundtrip_decode_cache():
+    c = synth.decode_cache(seed=5, B=3, ctx_lens=[1, 64, 200], Hq=4, Hkv=2, D=16)
+    ko, vo = oracle.paged_gather(c["k_pool"], c["v_pool"], c["block_table"], c["ctx_len"])
+    for b, n in enumerate(c["ctx_len"]):
+        np.testing.assert_array_equal(ko[b, :n], c["k_seq"][b])
+        np.testing.assert_array_equal(vo[b, :n], c["v_seq"][b])
+    bad = c["block_table"].copy()
+    bad[0, 0, 0] = 10**6
+    with pytest.raises(RuntimeError):
+        oracle.paged_gather(c["k_pool"], c["v_pool"], bad, c["ctx_len"])
