@@ -1,0 +1,174 @@
+/*
+ * libattn — exact long-context attention for AMD MI355X (gfx950), C ABI.
+ *
+ * Sources for what each call computes (pages cited by title and section):
+ *  [FA18]    "Flash Attention and distributed inference: memory hierarchy and
+ *            multi-GPU" (Transformer anatomy, chapter 18): §18.2 naive
+ *            attention, §18.3 tiling with the online softmax (running max m,
+ *            denominator l, rescaled output accumulator), §18.4 deferred
+ *            normalisation and the Q-outer loop order.
+ *  [ULY]     Ulysses sequence parallelism moved into long-context inference
+ *            (kwkr.cn article): §2.2 sequence-shard -> head-shard relayout,
+ *            §2.3 head-sharded KV cache in per-head blocks tagged with a
+ *            global head index, §3.2 RoPE at absolute token positions,
+ *            §3.5 1e-3 numeric alignment, §5.3 full-sequence causal mask.
+ *  [MGP]     "LLM推理中的多卡切分" (multi-GPU partitioning in LLM inference):
+ *            §2.1 request-token -> KV-slot allocation, §2.2 chunked prefill.
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates or frees device memory and keeps no mutable state, so
+ *    calls are thread-safe.  `stream` is a hipStream_t passed as void*
+ *    (NULL = the default stream).  Every call only enqueues work on `stream`
+ *    and returns without synchronising.  Grid sizes come from host arguments
+ *    only; device arrays (ctx_before, ctx_len, tables) are read on the device.
+ *  - Return value: ATTN_OK (0) or a synchronous error code below.  Argument
+ *    errors are detected before anything is enqueued.  A failed launch is
+ *    reported as ATTN_ERR_HIP.
+ *  - Device-detected errors (a block tag that is not the expected global KV
+ *    head, a block id outside [0, n_blocks)) store a non-zero ATTN_DEV_* code
+ *    into *dev_status (if dev_status is not NULL); the caller reads it after
+ *    synchronising.  Output rows touched by such a block are undefined.
+ *  - bf16 is IEEE bfloat16 (1-8-7); fp32 is IEEE binary32.  Head dimension D
+ *    is 128 for every bf16 path.  Tensors are dense, row-major, innermost
+ *    index last, with 16-byte aligned base pointers.
+ *  - Paged KV cache (per [ULY] §2.3): a pool of n_blocks blocks of 64 tokens,
+ *    each block holding ONE KV head:
+ *        k_pool [n_blocks][64][D]   token-major  (row = one token)
+ *        v_pool [n_blocks][D][64]   dimension-major (row = one channel)
+ *        block_head  [n_blocks]           int32 global KV-head tag per block
+ *        block_table [B][Hkv][max_blocks] int32 physical block of logical
+ *                    block j (tokens 64j..64j+63) of request b, local KV head g
+ *    Local KV head g of this GPU is global head kv_head_base + g; every block
+ *    read or written for (b, g) must carry that tag.
+ */
+#ifndef LCAT_ATTN_H
+#define LCAT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* negative size, Hq % Hkv != 0, H_tot % SP != 0, rank out of range */
+  ATTN_ERR_DTYPE = 3,       /* unknown dtype / element size */
+  ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  ATTN_ERR_UNSUPPORTED = 5, /* valid but not implemented (e.g. D != 128 on a bf16 path) */
+  ATTN_ERR_WORKSPACE = 6,   /* decode workspace missing or too small */
+  ATTN_ERR_HIP = 7          /* the HIP runtime rejected a launch */
+};
+
+enum attn_dtype { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 };
+
+enum attn_dev_status { ATTN_DEV_OK = 0, ATTN_DEV_BAD_TAG = 1, ATTN_DEV_BAD_BLOCK = 2 };
+
+/*
+ * attn_prefill — exact softmax attention over dense Q/K/V ([FA18] §18.2 for
+ * the result, §18.3-§18.4 for the tiled online-softmax evaluation).
+ *   q   [B][S][Hq][D]      o [B][S][Hq][D] (same dtype as q)
+ *   k,v [B][S][Hkv][D]     lse [B][Hq][S] fp32, natural log, or NULL
+ * out[b,i,h,:] = sum_j softmax_j(scale * q_i . k_j) v_j over keys j of KV
+ * head h / (Hq/Hkv); with causal != 0 only keys j <= i are visible (global
+ * token indices, [ULY] §5.3).  lse[b,h,i] = log sum_j exp(scale * q_i . k_j).
+ *   dtype ATTN_DTYPE_BF16: D must be 128, Hq/Hkv must divide 8 or be a
+ *         multiple of 8; bf16 MFMA products with fp32 accumulation.
+ *   dtype ATTN_DTYPE_F32 : D must be 64 or 128; fp32 arithmetic throughout.
+ * S = 0 or B = 0 is a no-op.
+ */
+int attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int B, int S,
+                 int Hq, int Hkv, int D, int dtype, int causal, float scale, void *stream);
+
+/*
+ * attn_kv_append — write T new tokens per request into the paged cache
+ * ([ULY] §2.3 layout; slots follow the request-token -> KV-slot map of
+ * [MGP] §2.1).  For request b, local KV head g and t in [0, T):
+ *   pos  = start_pos[b] + t,  blk = block_table[b][g][pos / 64]
+ *   k_pool[blk][pos % 64][:] = k_new[b][t][g][:]
+ *   v_pool[blk][:][pos % 64] = v_new[b][t][g][:]
+ *   k_new, v_new [B][T][Hkv][D] bf16; start_pos [B] int32 (device).
+ * Blocks must already be assigned in block_table and tagged in block_head;
+ * a wrong tag or an out-of-range id sets *dev_status and skips that block.
+ */
+int attn_kv_append(const void *k_new, const void *v_new, void *k_pool, void *v_pool, int n_blocks,
+                   const int32_t *block_head, const int32_t *block_table, int max_blocks,
+                   const int32_t *start_pos, int T, int B, int Hkv, int D, int kv_head_base,
+                   int32_t *dev_status, void *stream);
+
+/*
+ * attn_chunked_prefill — one chunk of C new tokens per request attending to
+ * all previously cached tokens plus, causally, to the chunk itself ([MGP]
+ * §2.2).  First appends the chunk's K/V (exactly attn_kv_append with
+ * start_pos = ctx_before, T = C), then, in stream order, for chunk row i
+ * (global position ctx_before[b] + i) attends keys at positions
+ * 0 .. ctx_before[b] + i read from the paged cache.
+ *   q [B][C][Hq][D] bf16, k_new/v_new [B][C][Hkv][D] bf16,
+ *   o [B][C][Hq][D] bf16, lse [B][Hq][C] fp32 or NULL,
+ *   ctx_before [B] int32 (device): tokens already cached per request.
+ * D must be 128.  C = 0 or B = 0 is a no-op.
+ */
+int attn_chunked_prefill(const void *q, const void *k_new, const void *v_new, void *k_pool,
+                         void *v_pool, int n_blocks, const int32_t *block_head,
+                         const int32_t *block_table, int max_blocks, const int32_t *ctx_before,
+                         int C, void *o, float *lse, int B, int Hq, int Hkv, int D,
+                         int kv_head_base, float scale, int32_t *dev_status, void *stream);
+
+/*
+ * attn_decode — one new query token per request over its whole cached
+ * context, split over key ranges whose partial (max, denominator, output)
+ * triples are merged with the log-sum-exp rescale of [FA18] §18.3.
+ *   q [B][Hq][D] bf16, o [B][Hq][D] bf16, lse [B][Hq] fp32 or NULL,
+ *   ctx_len [B] int32 (device): cached tokens INCLUDING the new one; every
+ *   key 0 .. ctx_len-1 is visible.  Slots past ctx_len are never used in
+ *   arithmetic (they may hold NaN).
+ *   split_tokens: keys per split, a positive multiple of 64, or 0 = automatic.
+ *   workspace: caller-owned device scratch of at least
+ *   attn_decode_workspace_bytes(B, Hq, D, max_blocks, split_tokens) bytes.
+ * D must be 128 and Hq/Hkv at most 16.  ctx_len[b] = 0 gives o = 0 and
+ * lse = -inf for that request.
+ */
+int attn_decode(const void *q, const void *k_pool, const void *v_pool, int n_blocks,
+                const int32_t *block_head, const int32_t *block_table, int max_blocks,
+                const int32_t *ctx_len, void *o, float *lse, int B, int Hq, int Hkv, int D,
+                int kv_head_base, float scale, int split_tokens, void *workspace,
+                size_t workspace_bytes, int32_t *dev_status, void *stream);
+
+/* Workspace bytes attn_decode needs (0 on invalid arguments). */
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_blocks, int split_tokens);
+
+/*
+ * rope_apply — rotary position embedding at absolute token positions, in
+ * place ([ULY] §3.2 global token index table, §5.3).
+ *   x [S][H][D] bf16, positions [S] int32 (device).
+ * For i < D/2, theta_i = base^(-2i/D) and a = positions[t] * theta_i:
+ *   x'[i]     = x[i] cos a - x[i + D/2] sin a
+ *   x'[i+D/2] = x[i + D/2] cos a + x[i] sin a
+ * The angle is formed and range-reduced in fp64, sin/cos and the rotation
+ * run in fp32, results are rounded to bf16 (nearest-even).
+ * D must be even and at most 256; S = 0 is a no-op.
+ */
+int rope_apply(void *x, const int32_t *positions, int S, int H, int D, float base, void *stream);
+
+/*
+ * seq_to_head_permute — the local half of the Ulysses exchange ([ULY] §2.2):
+ * gather this rank's heads from every sequence shard into global token order.
+ *   in  [SP][S_loc][H_tot][D], out [SP*S_loc][H_tot/SP][D], elements of
+ *   elem_bytes bytes (1, 2, 4 or 8), copied bit for bit:
+ *   out[k*S_loc + s][h][:] = in[k][s][rank*(H_tot/SP) + h][:]
+ * in and out must not overlap.
+ */
+int seq_to_head_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
+                        int elem_bytes, void *stream);
+
+/* Static, human-readable text for an attn_status value. */
+const char *attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCAT_ATTN_H */

@@ -1,0 +1,231 @@
+"""Exact long-context attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libattn.so`` (``include/attn.h``).
+Each function has the name of the C entry point it calls and does argument
+marshalling only: it checks tensor dtypes/devices/shapes, allocates outputs
+with PyTorch when the caller does not pass them, and enqueues the HIP kernels
+on the current PyTorch stream.  Every step of the computation runs in the
+library's kernels; there is no fallback.
+
+Layouts (all tensors contiguous, on the GPU):
+
+* ``attn_prefill``: q ``[B][S][Hq][128]``, k/v ``[B][S][Hkv][128]`` (bf16), or
+  fp32 with head_dim 64/128.
+* paged cache: ``k_pool [n_blocks][64][128]``, ``v_pool [n_blocks][128][64]``,
+  ``block_head [n_blocks]`` int32, ``block_table [B][Hkv][max_blocks]`` int32.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import (ATTN_DEV_BAD_BLOCK, ATTN_DEV_BAD_TAG, ATTN_DEV_OK, ATTN_DTYPE_BF16,
+                   ATTN_DTYPE_F32, AttnError)
+
+__all__ = [
+    "attn_prefill", "attn_chunked_prefill", "attn_kv_append", "attn_decode",
+    "attn_decode_workspace_bytes", "rope_apply", "seq_to_head_permute", "attn_status_string",
+    "AttnError", "ATTN_DEV_OK", "ATTN_DEV_BAD_TAG", "ATTN_DEV_BAD_BLOCK", "load_library",
+]
+
+HEAD_DIM = 128
+BLOCK_TOKENS = 64
+
+
+def load_library():
+    return _lib.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def attn_status_string(status: int) -> str:
+    return _lib.load().attn_status_string(int(status)).decode()
+
+
+def attn_prefill(q, k, v, causal=True, scale=None, o=None, lse=None, stream=None):
+    """Exact attention over dense tensors; returns ``(o, lse)``.
+
+    q ``[B][S][Hq][D]``, k/v ``[B][S][Hkv][D]``; ``lse`` is ``[B][Hq][S]`` fp32
+    (natural log).  bf16 needs D = 128; fp32 accepts D in {64, 128}.
+    """
+    torch = _torch()
+    _need(q, "q")
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    dt = q.dtype
+    if dt == torch.bfloat16:
+        code = ATTN_DTYPE_BF16
+    elif dt == torch.float32:
+        code = ATTN_DTYPE_F32
+    else:
+        raise TypeError("q must be bf16 or fp32")
+    _need(k, "k", dt, (B, S, Hkv, D))
+    _need(v, "v", dt, (B, S, Hkv, D))
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", dt, q.shape)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, (B, Hq, S))
+    scale = float(D ** -0.5) if scale is None else float(scale)
+    st = _lib.load().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, S, Hq, Hkv, D,
+                                  code, int(bool(causal)), scale, _stream(stream))
+    _lib.check("attn_prefill", st)
+    return o, lse
+
+
+def attn_kv_append(k_new, v_new, k_pool, v_pool, block_head, block_table, start_pos,
+                   kv_head_base=0, dev_status=None, stream=None):
+    """Write ``k_new/v_new [B][T][Hkv][128]`` at positions ``start_pos[b] + t``."""
+    torch = _torch()
+    _need(k_new, "k_new", torch.bfloat16)
+    B, T, Hkv, D = k_new.shape
+    _need(v_new, "v_new", torch.bfloat16, k_new.shape)
+    n_blocks = k_pool.shape[0]
+    _need(k_pool, "k_pool", torch.bfloat16, (n_blocks, BLOCK_TOKENS, D))
+    _need(v_pool, "v_pool", torch.bfloat16, (n_blocks, D, BLOCK_TOKENS))
+    _need(block_head, "block_head", torch.int32, (n_blocks,))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.shape[:2] != (B, Hkv):
+        raise ValueError("block_table must be [B][Hkv][max_blocks]")
+    _need(start_pos, "start_pos", torch.int32, (B,))
+    st = _lib.load().attn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), n_blocks,
+                                    _ptr(block_head), _ptr(block_table), block_table.shape[2],
+                                    _ptr(start_pos), T, B, Hkv, D, int(kv_head_base),
+                                    _ptr(dev_status), _stream(stream))
+    _lib.check("attn_kv_append", st)
+
+
+def attn_chunked_prefill(q, k_new, v_new, k_pool, v_pool, block_head, block_table, ctx_before,
+                         kv_head_base=0, scale=None, o=None, lse=None, dev_status=None,
+                         stream=None):
+    """Append a chunk's K/V to the paged cache, then attend; returns ``(o, lse)``.
+
+    q ``[B][C][Hq][128]``, k_new/v_new ``[B][C][Hkv][128]``; chunk row i sits
+    at position ``ctx_before[b] + i`` and sees every cached key up to it.
+    """
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    B, C, Hq, D = q.shape
+    Hkv = k_new.shape[2]
+    _need(k_new, "k_new", torch.bfloat16, (B, C, Hkv, D))
+    _need(v_new, "v_new", torch.bfloat16, (B, C, Hkv, D))
+    n_blocks = k_pool.shape[0]
+    _need(k_pool, "k_pool", torch.bfloat16, (n_blocks, BLOCK_TOKENS, D))
+    _need(v_pool, "v_pool", torch.bfloat16, (n_blocks, D, BLOCK_TOKENS))
+    _need(block_head, "block_head", torch.int32, (n_blocks,))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.shape[:2] != (B, Hkv):
+        raise ValueError("block_table must be [B][Hkv][max_blocks]")
+    _need(ctx_before, "ctx_before", torch.int32, (B,))
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, q.shape)
+    if lse is None:
+        lse = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, (B, Hq, C))
+    scale = float(D ** -0.5) if scale is None else float(scale)
+    st = _lib.load().attn_chunked_prefill(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), n_blocks, _ptr(block_head),
+        _ptr(block_table), block_table.shape[2], _ptr(ctx_before), C, _ptr(o), _ptr(lse), B, Hq,
+        Hkv, D, int(kv_head_base), scale, _ptr(dev_status), _stream(stream))
+    _lib.check("attn_chunked_prefill", st)
+    return o, lse
+
+
+def attn_decode_workspace_bytes(B, Hq, max_blocks, split_tokens=0, D=HEAD_DIM) -> int:
+    return int(_lib.load().attn_decode_workspace_bytes(B, Hq, D, max_blocks, split_tokens))
+
+
+def attn_decode(q, k_pool, v_pool, block_head, block_table, ctx_len, kv_head_base=0, scale=None,
+                split_tokens=0, workspace=None, o=None, lse=None, dev_status=None, stream=None):
+    """One query token per request over its paged context; returns ``(o, lse)``.
+
+    q ``[B][Hq][128]``; ``ctx_len[b]`` counts the cached tokens including the
+    new one.  ``workspace`` (uint8 tensor) is allocated if not given.
+    """
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    B, Hq, D = q.shape
+    n_blocks = k_pool.shape[0]
+    _need(k_pool, "k_pool", torch.bfloat16, (n_blocks, BLOCK_TOKENS, D))
+    _need(v_pool, "v_pool", torch.bfloat16, (n_blocks, D, BLOCK_TOKENS))
+    _need(block_head, "block_head", torch.int32, (n_blocks,))
+    _need(block_table, "block_table", torch.int32)
+    Hkv, max_blocks = block_table.shape[1], block_table.shape[2]
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][Hkv][max_blocks]")
+    _need(ctx_len, "ctx_len", torch.int32, (B,))
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, q.shape)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, (B, Hq))
+    need = attn_decode_workspace_bytes(B, Hq, max_blocks, split_tokens, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace")
+    scale = float(D ** -0.5) if scale is None else float(scale)
+    st = _lib.load().attn_decode(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), n_blocks, _ptr(block_head), _ptr(block_table),
+        max_blocks, _ptr(ctx_len), _ptr(o), _ptr(lse), B, Hq, Hkv, D, int(kv_head_base), scale,
+        int(split_tokens), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(dev_status), _stream(stream))
+    _lib.check("attn_decode", st)
+    return o, lse
+
+
+def rope_apply(x, positions, base=10000.0, stream=None):
+    """Rotate ``x [S][H][D]`` (bf16) in place at absolute ``positions [S]`` (int32)."""
+    torch = _torch()
+    _need(x, "x", torch.bfloat16)
+    S, H, D = x.shape
+    _need(positions, "positions", torch.int32, (S,))
+    st = _lib.load().rope_apply(_ptr(x), _ptr(positions), S, H, D, float(base), _stream(stream))
+    _lib.check("rope_apply", st)
+    return x
+
+
+def seq_to_head_permute(x, rank, out=None, stream=None):
+    """``x [SP][S_loc][H_tot][D]`` -> ``out [SP*S_loc][H_tot/SP][D]`` for ``rank``."""
+    torch = _torch()
+    _need(x, "x")
+    SP, S_loc, H_tot, D = x.shape
+    if H_tot % SP:
+        raise ValueError("H_tot must be divisible by SP")
+    if out is None:
+        out = torch.empty((SP * S_loc, H_tot // SP, D), dtype=x.dtype, device=x.device)
+    _need(out, "out", x.dtype, (SP * S_loc, H_tot // SP, D))
+    st = _lib.load().seq_to_head_permute(_ptr(x), _ptr(out), SP, S_loc, H_tot, D, int(rank),
+                                         x.element_size(), _stream(stream))
+    _lib.check("seq_to_head_permute", st)
+    return out

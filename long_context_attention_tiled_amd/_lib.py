@@ -1,0 +1,69 @@
+"""ctypes loader for ``libattn.so`` with the C signatures of ``include/attn.h``."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn.so")
+
+# enum attn_status / attn_dtype / attn_dev_status
+ATTN_OK = 0
+ATTN_DTYPE_F32 = 0
+ATTN_DTYPE_BF16 = 1
+ATTN_DEV_OK = 0
+ATTN_DEV_BAD_TAG = 1
+ATTN_DEV_BAD_BLOCK = 2
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+SIGNATURES = {
+    "attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
+    "attn_kv_append": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _vp,
+                            _vp]),
+    "attn_chunked_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _vp,
+                                  _i, _i, _i, _i, _i, _f, _vp, _vp]),
+    "attn_decode": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                         _i, _vp, _sz, _vp, _vp]),
+    "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "rope_apply": (_i, [_vp, _vp, _i, _i, _i, _f, _vp]),
+    "seq_to_head_permute": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "attn_status_string": (ctypes.c_char_p, [_i]),
+}
+
+
+class AttnError(RuntimeError):
+    """A libattn call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library; fails loudly when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP extension first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != ATTN_OK:
+        text = load().attn_status_string(status).decode()
+        raise AttnError(fn, status, text)

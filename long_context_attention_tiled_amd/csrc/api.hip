@@ -1,0 +1,192 @@
+// C-ABI entry points of libattn: argument validation, launch planning and
+// dispatch.  Every check happens before the first HIP call, so an invalid
+// call enqueues nothing.  The semantics of each entry point are documented
+// in include/attn.h.
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlockTokens = 64;
+constexpr int kDecodeRecord = 132;          // floats per decode split record
+constexpr int kDefaultSplitTokens = 1024;   // keys per decode split when 0 is passed
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+// GQA group sizes the bf16 kernels handle: divisors of 8 or multiples of 8.
+inline bool group_ok(int Hq, int Hkv) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return false;
+  const int g = Hq / Hkv;
+  return (g <= 8 && 8 % g == 0) || (g % 8 == 0);
+}
+
+inline int decode_split_tokens(int split_tokens) {
+  return split_tokens == 0 ? kDefaultSplitTokens : split_tokens;
+}
+
+inline long long decode_n_split(int max_blocks, int split_tokens) {
+  const long long keys = (long long)max_blocks * kBlockTokens;
+  return (keys + split_tokens - 1) / split_tokens;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape or rank";
+    case ATTN_ERR_DTYPE: return "unsupported dtype or element size";
+    case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case ATTN_ERR_UNSUPPORTED: return "configuration not supported";
+    case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int B, int S,
+                 int Hq, int Hkv, int D, int dtype, int causal, float scale, void *stream) {
+  if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (B == 0 || S == 0) return ATTN_OK;
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_DTYPE_F32) {
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+    return hip_status(lcat::launch_attn_f32(static_cast<const float *>(q),
+                                            static_cast<const float *>(k),
+                                            static_cast<const float *>(v), static_cast<float *>(o),
+                                            lse, B, S, Hq, Hkv, D, causal, scale, st));
+  }
+  if (D != kHeadDim || !group_ok(Hq, Hkv)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+  lcat::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.Sq = S; p.Sk = S; p.Hq = Hq; p.Hkv = Hkv;
+  p.causal = causal != 0;
+  p.scale = scale;
+  return hip_status(lcat::launch_prefill_bf16(p, false, st));
+}
+
+int attn_kv_append(const void *k_new, const void *v_new, void *k_pool, void *v_pool, int n_blocks,
+                   const int32_t *block_head, const int32_t *block_table, int max_blocks,
+                   const int32_t *start_pos, int T, int B, int Hkv, int D, int kv_head_base,
+                   int32_t *dev_status, void *stream) {
+  if (T < 0 || B < 0 || Hkv <= 0 || n_blocks < 0 || max_blocks <= 0) return ATTN_ERR_SHAPE;
+  if (D != kHeadDim) return ATTN_ERR_UNSUPPORTED;
+  if (T == 0 || B == 0) return ATTN_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_head || !block_table || !start_pos)
+    return ATTN_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return ATTN_ERR_ALIGN;
+  return hip_status(lcat::launch_kv_append(k_new, v_new, k_pool, v_pool, n_blocks, block_head,
+                                           block_table, max_blocks, start_pos, T, B, Hkv,
+                                           kv_head_base, dev_status,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int attn_chunked_prefill(const void *q, const void *k_new, const void *v_new, void *k_pool,
+                         void *v_pool, int n_blocks, const int32_t *block_head,
+                         const int32_t *block_table, int max_blocks, const int32_t *ctx_before,
+                         int C, void *o, float *lse, int B, int Hq, int Hkv, int D,
+                         int kv_head_base, float scale, int32_t *dev_status, void *stream) {
+  if (C < 0 || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n_blocks < 0 || max_blocks <= 0)
+    return ATTN_ERR_SHAPE;
+  if (D != kHeadDim || !group_ok(Hq, Hkv)) return ATTN_ERR_UNSUPPORTED;
+  if (C == 0 || B == 0) return ATTN_OK;
+  if (!q || !k_new || !v_new || !k_pool || !v_pool || !block_head || !block_table || !ctx_before ||
+      !o)
+    return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) ||
+      !aligned16(v_pool) || !aligned16(o))
+    return ATTN_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int rc = hip_status(lcat::launch_kv_append(k_new, v_new, k_pool, v_pool, n_blocks, block_head,
+                                             block_table, max_blocks, ctx_before, C, B, Hkv,
+                                             kv_head_base, dev_status, st));
+  if (rc != ATTN_OK) return rc;
+  lcat::PrefillParams p{};
+  p.q = q; p.k = k_pool; p.v = v_pool; p.o = o; p.lse = lse;
+  p.block_table = block_table; p.block_head = block_head; p.ctx_before = ctx_before;
+  p.dev_status = dev_status;
+  p.B = B; p.Sq = C; p.Sk = 0; p.Hq = Hq; p.Hkv = Hkv;
+  p.max_blocks = max_blocks; p.n_blocks = n_blocks; p.kv_head_base = kv_head_base;
+  p.causal = 1;
+  p.scale = scale;
+  return hip_status(lcat::launch_prefill_bf16(p, true, st));
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_blocks, int split_tokens) {
+  if (B < 0 || Hq <= 0 || D != kHeadDim || max_blocks <= 0 || split_tokens < 0 ||
+      split_tokens % kBlockTokens)
+    return 0;
+  const int st = decode_split_tokens(split_tokens);
+  return (size_t)B * Hq * decode_n_split(max_blocks, st) * kDecodeRecord * sizeof(float);
+}
+
+int attn_decode(const void *q, const void *k_pool, const void *v_pool, int n_blocks,
+                const int32_t *block_head, const int32_t *block_table, int max_blocks,
+                const int32_t *ctx_len, void *o, float *lse, int B, int Hq, int Hkv, int D,
+                int kv_head_base, float scale, int split_tokens, void *workspace,
+                size_t workspace_bytes, int32_t *dev_status, void *stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n_blocks < 0 || max_blocks <= 0)
+    return ATTN_ERR_SHAPE;
+  if (split_tokens < 0 || split_tokens % kBlockTokens) return ATTN_ERR_SHAPE;
+  if (D != kHeadDim || Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0) return ATTN_OK;
+  if (!q || !k_pool || !v_pool || !block_head || !block_table || !ctx_len || !o)
+    return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return ATTN_ERR_ALIGN;
+  const int st = decode_split_tokens(split_tokens);
+  const size_t need = attn_decode_workspace_bytes(B, Hq, D, max_blocks, st);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  const long long n_split = decode_n_split(max_blocks, st);
+  if (n_split > 0x7FFFFFFFLL) return ATTN_ERR_UNSUPPORTED;
+  lcat::DecodeParams p{};
+  p.q = q; p.k_pool = k_pool; p.v_pool = v_pool;
+  p.block_head = block_head; p.block_table = block_table; p.ctx_len = ctx_len;
+  p.o = o; p.lse = lse; p.ws = static_cast<float *>(workspace); p.dev_status = dev_status;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_blocks = max_blocks; p.n_blocks = n_blocks;
+  p.kv_head_base = kv_head_base; p.split_tokens = st; p.n_split = (int)n_split;
+  p.scale = scale;
+  return hip_status(lcat::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int rope_apply(void *x, const int32_t *positions, int S, int H, int D, float base, void *stream) {
+  if (S < 0 || H <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+  if (D % 16 || D > 256) return ATTN_ERR_UNSUPPORTED;
+  if (!(base > 0.f)) return ATTN_ERR_SHAPE;
+  if (S == 0) return ATTN_OK;
+  if (!x || !positions) return ATTN_ERR_NULL;
+  if (!aligned16(x)) return ATTN_ERR_ALIGN;
+  return hip_status(lcat::launch_rope(x, positions, S, H, D, base, static_cast<hipStream_t>(stream)));
+}
+
+int seq_to_head_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
+                        int elem_bytes, void *stream) {
+  if (SP <= 0 || S_loc < 0 || H_tot <= 0 || D <= 0 || H_tot % SP) return ATTN_ERR_SHAPE;
+  if (rank < 0 || rank >= SP) return ATTN_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return ATTN_ERR_DTYPE;
+  if (S_loc == 0) return ATTN_OK;
+  if (!in || !out) return ATTN_ERR_NULL;
+  const char *a = static_cast<const char *>(in);
+  char *c = static_cast<char *>(out);
+  const long long out_bytes = (long long)SP * S_loc * (H_tot / SP) * D * elem_bytes;
+  const long long in_bytes = (long long)SP * S_loc * H_tot * D * elem_bytes;
+  if (!(c + out_bytes <= a || a + in_bytes <= c)) return ATTN_ERR_SHAPE;   // overlap
+  return hip_status(lcat::launch_permute(in, out, SP, S_loc, H_tot, D, rank, elem_bytes,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lcat {
+
+// Causal / non-causal tiled attention with bf16 MFMA, head_dim 128.
+// Dense mode: K/V are [B][Sk][Hkv][128].  Paged mode: K/V come from the
+// block pool through block_table, query row i sits at position
+// ctx_before[b] + i and the key count is ctx_before[b] + Sq.
+struct PrefillParams {
+  const void *q;            // [B][Sq][Hq][128] bf16
+  const void *k;            // dense K or k_pool
+  const void *v;            // dense V or v_pool
+  void *o;                  // [B][Sq][Hq][128] bf16
+  float *lse;               // [B][Hq][Sq] or null
+  const int32_t *block_table;
+  const int32_t *block_head;
+  const int32_t *ctx_before;
+  int32_t *dev_status;
+  int B, Sq, Sk, Hq, Hkv;
+  int max_blocks, n_blocks, kv_head_base;
+  int causal;
+  float scale;
+};
+
+hipError_t launch_prefill_bf16(const PrefillParams &p, bool paged, hipStream_t stream);
+
+hipError_t launch_attn_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+                           int B, int S, int Hq, int Hkv, int D, int causal, float scale,
+                           hipStream_t stream);
+
+hipError_t launch_kv_append(const void *k_new, const void *v_new, void *k_pool, void *v_pool,
+                            int n_blocks, const int32_t *block_head, const int32_t *block_table,
+                            int max_blocks, const int32_t *start_pos, int T, int B, int Hkv,
+                            int kv_head_base, int32_t *dev_status, hipStream_t stream);
+
+struct DecodeParams {
+  const void *q;            // [B][Hq][128]
+  const void *k_pool;       // [n_blocks][64][128]
+  const void *v_pool;       // [n_blocks][128][64]
+  const int32_t *block_head;
+  const int32_t *block_table;
+  const int32_t *ctx_len;
+  void *o;                  // [B][Hq][128]
+  float *lse;               // [B][Hq] or null
+  float *ws;                // [B][Hq][n_split][130]
+  int32_t *dev_status;
+  int B, Hq, Hkv, max_blocks, n_blocks, kv_head_base;
+  int split_tokens, n_split;
+  float scale;
+};
+
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+
+hipError_t launch_rope(void *x, const int32_t *positions, int S, int H, int D, float base,
+                       hipStream_t stream);
+
+hipError_t launch_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
+                          int elem_bytes, hipStream_t stream);
+
+}  // namespace lcat

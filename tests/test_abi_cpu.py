@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads on a machine without a GPU (only the HIP runtime library
+is needed), exports every function ``include/attn.h`` declares, and rejects
+invalid arguments with the documented status codes before touching HIP.
+Every call here fails validation (or is an empty no-op), so no fake pointer
+ever reaches a launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_attention_tiled_amd as lcat
+from long_context_attention_tiled_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, HIP = range(8)
+P = ctypes.c_void_p
+A16 = P(0x10000)      # aligned, never dereferenced (every call below fails first)
+MIS = P(0x10001)      # misaligned
+NUL = P(0)
+S0 = P(0)             # stream
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libattn.so not built")
+    return lcat.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["attn_prefill", "attn_chunked_prefill", "attn_decode", "attn_decode_workspace_bytes",
+              "attn_kv_append", "rope_apply", "seq_to_head_permute", "attn_status_string"]:
+        assert n in names
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lcat.attn_status_string(code)
+        assert s and s != "unknown status"
+    assert lcat.attn_status_string(99) == "unknown status"
+
+
+def test_prefill_validation(lib):
+    f = lib.attn_prefill
+    # shape: Hq not a multiple of Hkv
+    assert f(A16, A16, A16, A16, NUL, 1, 64, 3, 2, 128, 1, 1, 0.1, S0) == SHAPE
+    assert f(A16, A16, A16, A16, NUL, -1, 64, 2, 2, 128, 1, 1, 0.1, S0) == SHAPE
+    # dtype
+    assert f(A16, A16, A16, A16, NUL, 1, 64, 2, 2, 128, 7, 1, 0.1, S0) == DTYPE
+    # empty input is a no-op
+    assert f(NUL, NUL, NUL, NUL, NUL, 1, 0, 2, 2, 128, 1, 1, 0.1, S0) == OK
+    assert f(NUL, NUL, NUL, NUL, NUL, 0, 10, 2, 2, 128, 1, 1, 0.1, S0) == OK
+    # nulls
+    assert f(NUL, A16, A16, A16, NUL, 1, 64, 2, 2, 128, 1, 1, 0.1, S0) == NULL
+    assert f(A16, A16, A16, NUL, NUL, 1, 64, 2, 2, 128, 1, 1, 0.1, S0) == NULL
+    # unsupported head dim / group
+    assert f(A16, A16, A16, A16, NUL, 1, 64, 2, 2, 64, 1, 1, 0.1, S0) == UNSUP
+    assert f(A16, A16, A16, A16, NUL, 1, 64, 12, 1, 128, 1, 1, 0.1, S0) == UNSUP
+    assert f(A16, A16, A16, A16, NUL, 1, 64, 2, 2, 96, 0, 1, 0.1, S0) == UNSUP
+    # alignment
+    assert f(MIS, A16, A16, A16, NUL, 1, 64, 2, 2, 128, 1, 1, 0.1, S0) == ALIGN
+    assert f(A16, A16, A16, MIS, NUL, 1, 64, 2, 2, 64, 0, 1, 0.1, S0) == ALIGN
+
+
+def test_chunked_and_append_validation(lib):
+    f = lib.attn_chunked_prefill
+    args = dict(q=A16, kn=A16, vn=A16, kp=A16, vp=A16, nb=10, bh=A16, bt=A16, mb=4, cb=A16, C=64,
+                o=A16, lse=NUL, B=1, Hq=16, Hkv=2, D=128, base=0, scale=0.1, st=NUL, s=S0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+
+    assert call(Hq=15) == SHAPE
+    assert call(mb=0) == SHAPE
+    assert call(D=64) == UNSUP
+    assert call(C=0, q=NUL) == OK
+    assert call(bt=NUL) == NULL
+    assert call(cb=NUL) == NULL
+    assert call(vp=MIS) == ALIGN
+    g = lib.attn_kv_append
+    assert g(A16, A16, A16, A16, 10, A16, A16, 4, A16, 8, 1, 2, 64, 0, NUL, S0) == UNSUP
+    assert g(A16, A16, A16, A16, 10, A16, A16, 0, A16, 8, 1, 2, 128, 0, NUL, S0) == SHAPE
+    assert g(A16, A16, A16, A16, 10, NUL, A16, 4, A16, 8, 1, 2, 128, 0, NUL, S0) == NULL
+    assert g(NUL, NUL, NUL, NUL, 10, NUL, NUL, 4, NUL, 0, 1, 2, 128, 0, NUL, S0) == OK
+
+
+def test_decode_validation(lib):
+    f = lib.attn_decode
+    need = lib.attn_decode_workspace_bytes(32, 16, 128, 2048, 1024)
+    assert need == 32 * 16 * 128 * 132 * 4
+    assert lib.attn_decode_workspace_bytes(32, 16, 128, 2048, 0) == need   # 0 = default 1024
+    assert lib.attn_decode_workspace_bytes(32, 16, 128, 2048, 100) == 0    # not a multiple of 64
+    assert lib.attn_decode_workspace_bytes(32, 16, 64, 2048, 0) == 0
+
+    def call(ws=A16, wsb=need, split=1024, Hq=16, Hkv=2, D=128, q=A16):
+        return f(q, A16, A16, 100, A16, A16, 2048, A16, A16, NUL, 32, Hq, Hkv, D, 0, 0.1, split,
+                 ws, wsb, NUL, S0)
+
+    assert call(split=100) == SHAPE
+    assert call(Hq=15) == SHAPE
+    assert call(Hq=64, Hkv=2) == UNSUP      # group of 32 > 16
+    assert call(D=64) == UNSUP
+    assert call(q=NUL) == NULL
+    assert call(ws=NUL) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(ws=MIS) == ALIGN
+
+
+def test_rope_and_permute_validation(lib):
+    r = lib.rope_apply
+    assert r(A16, A16, 10, 2, 100, 10000.0, S0) == UNSUP
+    assert r(A16, A16, 10, 2, 128, -1.0, S0) == SHAPE
+    assert r(NUL, NUL, 0, 2, 128, 10000.0, S0) == OK
+    assert r(NUL, A16, 10, 2, 128, 10000.0, S0) == NULL
+    assert r(MIS, A16, 10, 2, 128, 10000.0, S0) == ALIGN
+    p = lib.seq_to_head_permute
+    assert p(A16, P(0x90000000), 4, 16, 6, 128, 0, 2, S0) == SHAPE     # 6 % 4
+    assert p(A16, P(0x90000000), 4, 16, 8, 128, 4, 2, S0) == SHAPE     # rank out of range
+    assert p(A16, P(0x90000000), 4, 16, 8, 128, 0, 3, S0) == DTYPE
+    assert p(A16, NUL, 4, 16, 8, 128, 0, 2, S0) == NULL
+    assert p(NUL, NUL, 4, 0, 8, 128, 0, 2, S0) == OK
+    assert p(A16, P(0x10000 + 64), 4, 16, 8, 128, 0, 2, S0) == SHAPE   # overlapping buffers
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()
