@@ -1,0 +1,352 @@
+"""Throughput of the exact-attention hot path on one MI355X.
+
+Step (the timed unit): one pass of the causal GQA prefill workload —
+RoPE at absolute positions on Q and K, then causal attention — for batch 1,
+sequence 32768, 16 query heads / 2 KV heads, head_dim 128, bf16 inputs.
+``value`` is the algorithmic attention FLOP rate of that step (QK^T and PV
+over the unmasked causal pairs only: 4*D*Hq*S*(S+1)/2 FLOP).
+
+The same JSON line also carries, each measured in this run:
+  roofline        the prefill kernel's average duration from HIP events on
+                  its stream, against the bf16 dense MFMA peak;
+  decode          split-K paged decode, 32 requests with contexts uniform in
+                  [8192, 131072], KV bytes per second against 8 TB/s;
+  relayout        sequence-shard -> head-shard relayout of one rank's share of
+                  [4][16384][64|8][128] bf16 Q/K/V, bytes per second;
+  prefill_64k     the relayout + RoPE + causal prefill pipeline at 65536;
+  chunked_prefill 4 requests x 131072 tokens in 8192-token chunks;
+  cpu_baseline    the fp64 CPU oracle timed on a bounded sample of query rows
+                  of the step workload, on this host's cores.
+
+Inputs are seeded synthetic N(0,1) data resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn prefill TFLOP/s (% MFMA peak) + decode KV GB/s (% HBM peak), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+D = 128
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def causal_flops(B, S, Hq, D=D, ctx_before=0):
+    """QK^T + PV FLOPs over visible pairs: row i sees ctx_before + i + 1 keys."""
+    pairs = S * ctx_before + S * (S + 1) // 2
+    return 4.0 * D * Hq * B * pairs
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_attention_tiled_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
+    by a copy-kernel calibration) if recorded for the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel, {}).get(workload)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+class EventTimer:
+    """Average duration of one launch site, from HIP events on the stream the
+    kernels are enqueued on (the current torch stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        self.s = self.torch.cuda.Event(enable_timing=True)
+        self.e = self.torch.cuda.Event(enable_timing=True)
+        self.s.record()
+        return self
+
+    def __exit__(self, *a):
+        self.e.record()
+        self.pairs.append((self.s, self.e))
+
+    def mean_ms(self):
+        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
+
+
+def dev_tensor(torch, a):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.cuda()
+
+
+def seeded_normal_bf16(torch, shape, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------------------
+def bench_step(torch, lcat, synth, steps, warmup):
+    S, Hq, Hkv = 32768, 16, 2
+    d = synth.causal_gqa(seed=2, S=S, Hq=Hq, Hkv=Hkv)
+    q, k, v = dev_tensor(torch, d["q"]), dev_tensor(torch, d["k"]), dev_tensor(torch, d["v"])
+    pos = dev_tensor(torch, d["positions"])
+    o = torch.empty_like(q)
+    lse = torch.empty((1, Hq, S), dtype=torch.float32, device="cuda")
+    timer = EventTimer(torch)
+
+    def step(time_kernel):
+        lcat.rope_apply(q[0], pos)
+        lcat.rope_apply(k[0], pos)
+        if time_kernel:
+            with timer:
+                lcat.attn_prefill(q, k, v, causal=True, o=o, lse=lse)
+        else:
+            lcat.attn_prefill(q, k, v, causal=True, o=o, lse=lse)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flops = causal_flops(1, S, Hq)
+    ms_step = wall * 1e3 / steps
+    k_ms = timer.mean_ms()
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    traffic = load_traffic("prefill_kernel", "causal_gqa_32k")
+    return d, dict(
+        value=flops / (wall / steps) / 1e12, ms_per_step=ms_step,
+        roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
+                      unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
+                      traffic=traffic, kernel="prefill_kernel<dense,causal>",
+                      kernel_ms=round(k_ms, 4), flop_per_launch=flops))
+
+
+def bench_decode(torch, lcat, synth, iters=20):
+    c = synth.decode_cache(seed=4, B=32, with_content=False)
+    n_blocks = c["n_blocks"]
+    k_pool = seeded_normal_bf16(torch, (n_blocks, 64, D), 41)
+    v_pool = seeded_normal_bf16(torch, (n_blocks, D, 64), 42)
+    args = [dev_tensor(torch, c["q"]), k_pool, v_pool, dev_tensor(torch, c["block_head"]),
+            dev_tensor(torch, c["block_table"]), dev_tensor(torch, c["ctx_len"])]
+    B, Hq = c["q"].shape[:2]
+    ws = torch.empty(lcat.attn_decode_workspace_bytes(B, Hq, c["max_blocks"]), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        lcat.attn_decode(*args, workspace=ws, o=o, lse=lse)
+    timer = EventTimer(torch)
+    torch.cuda.synchronize()
+    for _ in range(iters):
+        with timer:
+            lcat.attn_decode(*args, workspace=ws, o=o, lse=lse)
+    torch.cuda.synchronize()
+    ms = timer.mean_ms()
+    ctx_total = int(c["ctx_len"].sum())
+    nbytes = ctx_total * c["Hkv"] * D * 2 * 2 + 2 * B * Hq * D * 2 + B * Hq * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(ms=round(ms, 4), GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
+                bytes=nbytes, context_tokens=ctx_total, requests=B,
+                workload="32 requests, ctx U[8192,131072], 16 Q / 2 KV heads, paged 64-token blocks")
+
+
+def bench_relayout_and_prefill_64k(torch, lcat, iters=10):
+    SP, S_loc, Hq_tot, Hkv_tot = 4, 16384, 64, 8
+    S = SP * S_loc
+    qin = seeded_normal_bf16(torch, (SP, S_loc, Hq_tot, D), 31)
+    kin = seeded_normal_bf16(torch, (SP, S_loc, Hkv_tot, D), 32)
+    vin = seeded_normal_bf16(torch, (SP, S_loc, Hkv_tot, D), 33)
+    qo = torch.empty((S, Hq_tot // SP, D), dtype=torch.bfloat16, device="cuda")
+    ko = torch.empty((S, Hkv_tot // SP, D), dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+
+    def relayout():
+        lcat.seq_to_head_permute(qin, 0, out=qo)
+        lcat.seq_to_head_permute(kin, 0, out=ko)
+        lcat.seq_to_head_permute(vin, 0, out=vo)
+
+    for _ in range(3):
+        relayout()
+    timer = EventTimer(torch)
+    torch.cuda.synchronize()
+    for _ in range(iters):
+        with timer:
+            relayout()
+    torch.cuda.synchronize()
+    ms = timer.mean_ms()
+    nbytes = 2 * (qo.numel() + ko.numel() + vo.numel()) * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    relay = dict(ms=round(ms, 4), GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
+                 bytes=nbytes, workload="rank 0 of [4][16384][64|8][128] bf16 Q/K/V")
+
+    pos = torch.arange(S, dtype=torch.int32, device="cuda")
+    o = torch.empty((1, S, Hq_tot // SP, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, Hq_tot // SP, S), dtype=torch.float32, device="cuda")
+    ptimer, ktimer = EventTimer(torch), EventTimer(torch)
+    for it in range(4):
+        with ptimer:
+            relayout()
+            lcat.rope_apply(qo, pos)
+            lcat.rope_apply(ko, pos)
+            with ktimer:
+                lcat.attn_prefill(qo[None], ko[None], vo[None], causal=True, o=o, lse=lse)
+        if it == 0:
+            torch.cuda.synchronize()
+            ptimer.pairs.clear()
+            ktimer.pairs.clear()
+    torch.cuda.synchronize()
+    flops = causal_flops(1, S, Hq_tot // SP)
+    kms = ktimer.mean_ms()
+    pre = dict(pipeline_ms=round(ptimer.mean_ms(), 3), kernel_ms=round(kms, 3),
+               TFLOPs=round(flops / (kms * 1e-3) / 1e12, 1),
+               frac_mfma=round(flops / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               workload="relayout + RoPE + causal prefill, seq 65536, 16 Q / 2 KV heads")
+    return relay, pre
+
+
+def bench_chunked(torch, lcat, synth):
+    B, S, C, Hq, Hkv = 4, 131072, 8192, 16, 2
+    table, tags, n_blocks = synth.chunked_block_table(B, S, C, Hkv)
+    q = seeded_normal_bf16(torch, (B, S, Hq, D), 51)
+    k = seeded_normal_bf16(torch, (B, S, Hkv, D), 52)
+    v = seeded_normal_bf16(torch, (B, S, Hkv, D), 53)
+    k_pool = torch.empty((n_blocks, 64, D), dtype=torch.bfloat16, device="cuda")
+    v_pool = torch.empty((n_blocks, D, 64), dtype=torch.bfloat16, device="cuda")
+    tags_d, table_d = dev_tensor(torch, tags), dev_tensor(torch, table)
+    qs = [q[:, c0:c0 + C].contiguous() for c0 in range(0, S, C)]
+    ks = [k[:, c0:c0 + C].contiguous() for c0 in range(0, S, C)]
+    vs = [v[:, c0:c0 + C].contiguous() for c0 in range(0, S, C)]
+    cbs = [torch.full((B,), c0, dtype=torch.int32, device="cuda") for c0 in range(0, S, C)]
+    o = torch.empty((B, C, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, C), dtype=torch.float32, device="cuda")
+    timer = EventTimer(torch)
+    for rep in range(2):
+        with timer:
+            for i in range(len(qs)):
+                lcat.attn_chunked_prefill(qs[i], ks[i], vs[i], k_pool, v_pool, tags_d, table_d,
+                                          cbs[i], o=o, lse=lse)
+        if rep == 0:
+            torch.cuda.synchronize()
+            timer.pairs.clear()
+    torch.cuda.synchronize()
+    ms = timer.mean_ms()
+    flops = causal_flops(B, S, Hq)
+    tf = flops / (ms * 1e-3) / 1e12
+    return dict(ms_per_pass=round(ms, 2), TFLOPs=round(tf, 1),
+                frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4), chunks=S // C,
+                workload="4 requests x 131072 tokens, 8192-token chunks, 16 Q / 2 KV heads")
+
+
+def cpu_baseline(d, target_rows=1024):
+    """fp64 oracle on a seeded sample of query rows of the step workload
+    (RoPE of those rows and of all keys, then causal attention)."""
+    import oracle
+    import synth
+    S, Hq = d["q"].shape[1], d["q"].shape[2]
+    rows = synth.sample_rows(77, S, target_rows)
+    pos = d["positions"].astype(np.int64)
+    t0 = time.perf_counter()
+    qr = oracle.rope(d["q"][0, rows], pos[rows])[None]
+    kr = oracle.rope(d["k"][0], pos)[None]
+    oracle.attention_rows(qr, kr, oracle.widen(d["v"]), (rows + 1)[None], d["scale"])
+    dt = time.perf_counter() - t0
+    flops = 4.0 * D * Hq * float(np.sum(rows + 1))
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=oracle.num_threads(),
+                kind="oracle", seconds=round(dt, 2),
+                sample=f"{rows.size} seeded query rows x {Hq} heads of the seq-32768 causal "
+                       f"workload ({flops:.3g} algorithmic FLOP), fp64, incl. RoPE of those rows "
+                       f"and all keys")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="time only the step workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["step", "decode", "relayout", "chunked"],
+                    help="run a single leg (for profiling); prints its own JSON object")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (the sequence-parallel exchange across GPUs is not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_attention_tiled_amd as lcat
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    lcat.load_library()
+    if args.only and args.only != "step":
+        log(f"bench: only {args.only}")
+        if args.only == "decode":
+            res = bench_decode(torch, lcat, synth)
+        elif args.only == "relayout":
+            res = bench_relayout_and_prefill_64k(torch, lcat)[0]
+        else:
+            res = bench_chunked(torch, lcat, synth)
+        print(json.dumps({args.only: res}), flush=True)
+        return
+    log("bench: causal GQA prefill step (seq 32768)")
+    d, step = bench_step(torch, lcat, synth, args.steps, args.warmup)
+    out = {
+        "metric": METRIC, "value": round(step["value"], 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16, resident in HBM",
+        "config": {"workload": "causal GQA prefill with RoPE at absolute positions: batch 1, "
+                               "seq 32768, 16 Q / 2 KV heads, head_dim 128",
+                   "global_batch": 1, "seq_len": 32768, "parallelism": "single GPU"},
+        "roofline": step["roofline"],
+    }
+    if not args.no_extra and not args.only:
+        log("bench: decode")
+        out["decode"] = bench_decode(torch, lcat, synth)
+        log("bench: relayout + prefill 64k")
+        out["relayout"], out["prefill_64k"] = bench_relayout_and_prefill_64k(torch, lcat)
+        log("bench: chunked prefill")
+        out["chunked_prefill"] = bench_chunked(torch, lcat, synth)
+    if not args.no_cpu_baseline and not args.only:
+        log("bench: cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -81,7 +81,7 @@ int attn_kv_append(const void *k_new, const void *v_new, void *k_pool, void *v_p
                    const int32_t *block_head, const int32_t *block_table, int max_blocks,
                    const int32_t *start_pos, int T, int B, int Hkv, int D, int kv_head_base,
                    int32_t *dev_status, void *stream) {
-  if (T < 0 || B < 0 || Hkv <= 0 || n_blocks < 0 || max_blocks <= 0) return ATTN_ERR_SHAPE;
+  if (T < 0 || B < 0 || Hkv <= 0 || n_blocks <= 0 || max_blocks <= 0) return ATTN_ERR_SHAPE;
   if (D != kHeadDim) return ATTN_ERR_UNSUPPORTED;
   if (T == 0 || B == 0) return ATTN_OK;
   if (!k_new || !v_new || !k_pool || !v_pool || !block_head || !block_table || !start_pos)
@@ -99,7 +99,7 @@ int attn_chunked_prefill(const void *q, const void *k_new, const void *v_new, vo
                          const int32_t *block_table, int max_blocks, const int32_t *ctx_before,
                          int C, void *o, float *lse, int B, int Hq, int Hkv, int D,
                          int kv_head_base, float scale, int32_t *dev_status, void *stream) {
-  if (C < 0 || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n_blocks < 0 || max_blocks <= 0)
+  if (C < 0 || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n_blocks <= 0 || max_blocks <= 0)
     return ATTN_ERR_SHAPE;
   if (D != kHeadDim || !group_ok(Hq, Hkv)) return ATTN_ERR_UNSUPPORTED;
   if (C == 0 || B == 0) return ATTN_OK;
@@ -138,7 +138,7 @@ int attn_decode(const void *q, const void *k_pool, const void *v_pool, int n_blo
                 const int32_t *ctx_len, void *o, float *lse, int B, int Hq, int Hkv, int D,
                 int kv_head_base, float scale, int split_tokens, void *workspace,
                 size_t workspace_bytes, int32_t *dev_status, void *stream) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n_blocks < 0 || max_blocks <= 0)
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n_blocks <= 0 || max_blocks <= 0)
     return ATTN_ERR_SHAPE;
   if (split_tokens < 0 || split_tokens % kBlockTokens) return ATTN_ERR_SHAPE;
   if (D != kHeadDim || Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;

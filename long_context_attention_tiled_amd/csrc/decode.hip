@@ -30,7 +30,20 @@ constexpr int HD = 128;
 constexpr int BT = 64;
 constexpr int REC = 132;   // floats per workspace record: O[128], m (log2 units), l, pad
 
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
+
+struct BlockRegs {
+  u32x4 k[4][4];   // K rows of the four 16-key sub-tiles, four 32-wide d slices
+  u32x4 v[2][8];   // V^T: two 32-key halves x eight 16-row d tiles
+};
+
+constexpr int BLOCK_BYTES = BT * HD * 2;   // 16 KiB: one K block or one V block
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_split_kernel(
+    DecodeParams p) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   int ctx = p.ctx_len[b];
@@ -41,66 +54,94 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int t_begin = split * p.split_tokens;
   if (t_begin >= ctx) return;
   const int t_end = min(ctx, t_begin + p.split_tokens);
+  const int j_begin = t_begin / BT;
+  const int nblk = (t_end - t_begin + BT - 1) / BT;
+  const int tail = t_end - t_begin - (nblk - 1) * BT;   // keys in the last block (1..64)
   const int group = p.Hq / p.Hkv;
   const int qi = lane & 15;   // query (head within the group) owned by this lane
   const int g4 = lane >> 4;   // 8-wide K slice of the MFMA operands
 
   const bf16 *kp = static_cast<const bf16 *>(p.k_pool);
   const bf16 *vp = static_cast<const bf16 *>(p.v_pool);
-  const u32x4 zero = {0u, 0u, 0u, 0u};
 
   bf16x8 qf[4];
   {
-    const bool qv = qi < group;
-    const bf16 *src = static_cast<const bf16 *>(p.q) + ((size_t)b * p.Hq + g * group + (qv ? qi : 0)) * HD + 8 * g4;
+    const int qh = g * group + min(qi, group - 1);   // padding lanes reuse a real head
+    const bf16 *src = static_cast<const bf16 *>(p.q) + ((size_t)b * p.Hq + qh) * HD + 8 * g4;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(qv ? ld_global_16(src + 32 * s) : zero);
+    for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(ld_global_16(src + 32 * s));
   }
+
+  // Physical ids of this split's blocks, 64 per vector register (lane i holds
+  // block i of the chunk); tags are checked for the whole chunk at once.  An
+  // invalid id is reported and replaced by block 0 (rows undefined, no
+  // out-of-range access).
+  const int32_t *table = p.block_table + ((size_t)b * p.Hkv + g) * p.max_blocks;
+  const int want = p.kv_head_base + g;
+  auto load_ids = [&](int base) -> int {
+    const bool in = base + lane < nblk;
+    const int id = in ? table[j_begin + base + lane] : 0;
+    const bool ok = id >= 0 && id < p.n_blocks;
+    const int tag = ok ? p.block_head[id] : want;
+    const unsigned long long bad_block = __ballot(in && !ok);
+    const unsigned long long bad_tag = __ballot(in && ok && tag != want);
+    if (p.dev_status && lane == 0 && (bad_block | bad_tag)) p.dev_status[0] = bad_block ? 2 : 1;
+    return ok ? id : 0;
+  };
+  int ids = load_ids(0);
+  int ids_base = 0;
+  auto block_id = [&](int i) -> int {
+    if (i - ids_base >= 64) {   // next chunk of 64 ids (only for splits over 4096 keys)
+      ids_base += 64;
+      ids = load_ids(ids_base);
+    }
+    return __builtin_amdgcn_readlane(ids, i - ids_base);
+  };
 
   // K row (within a block) read by this lane for sub-tile t = 2w + e:
   //   32w + 8*(qi>>2) + 4e + (qi&3); its score then lands in register r of
-  //   the lane group 4*g4+r order used as the B operand of P V.
-  const int krow_base = 8 * (qi >> 2) + (qi & 3);
+  //   lane group g4 exactly where the B operand of P V expects key
+  //   32w + 8*g4 + 4e + r.
+  const int k_voff = (8 * (qi >> 2) + (qi & 3)) * (HD * 2) + 16 * g4;
+  const int v_voff = qi * (BT * 2) + 16 * g4;
+  auto load_k = [&](BlockRegs &R, int blk) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(kp + (size_t)blk * BT * HD, BLOCK_BYTES);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        R.k[t][s] = buf_load_16(r, k_voff + 64 * s + 1024 * (t & 1), 8192 * (t >> 1));
+  };
+  auto load_v = [&](BlockRegs &R, int blk) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(vp + (size_t)blk * HD * BT, BLOCK_BYTES);
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) R.v[w][dt] = buf_load_16(r, v_voff + 64 * w, 2048 * dt);
+  };
+
   const float c2 = p.scale * kLog2e;
   f32x4 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{};
   float m_run = -INFINITY, l_run = 0.f;
-  const int32_t *table = p.block_table + ((size_t)b * p.Hkv + g) * p.max_blocks;
 
-  for (int t0 = t_begin; t0 < t_end; t0 += BT) {
-    const int blk = table[t0 / BT];
-    const bool ok = blk >= 0 && blk < p.n_blocks;
-    if (!ok || p.block_head[blk] != p.kv_head_base + g) {
-      if (lane == 0 && p.dev_status) p.dev_status[0] = ok ? 1 : 2;
-      if (!ok) continue;
-    }
-    const int nv = min(BT, ctx - t0);
-    const bf16 *kb = kp + (size_t)blk * BT * HD;
-    const bf16 *vb = vp + (size_t)blk * HD * BT;
-
-    u32x4 kr[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int row = 32 * (t >> 1) + 4 * (t & 1) + krow_base;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kr[t][s] = ld_global_16(kb + row * HD + 32 * s + 8 * g4);
-    }
-    u32x4 vr[2][8];
-#pragma unroll
-    for (int w = 0; w < 2; ++w)
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) vr[w][dt] = ld_global_16(vb + (16 * dt + qi) * BT + 32 * w + 8 * g4);
-
-    // S^T = K Q^T, four 16-key sub-tiles
+  // One 64-key block: S^T = K Q^T, online softmax, O^T += V^T P^T.  The
+  // next block's K is requested as soon as this block's K registers are
+  // consumed, its V as soon as the V registers are, so a full block of
+  // loads is always in flight.  MASKED handles the final partial block.
+  BlockRegs R;
+  auto step = [&](auto masked_tag, int blk_next, bool has_next, int nv) {
+    constexpr bool MASKED = decltype(masked_tag)::value != 0;
     f32x4 s[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       s[t] = f32x4{};
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) s[t] = mfma_16x16x32(as_bf16x8(kr[t][ds]), qf[ds], s[t]);
+      for (int ds = 0; ds < 4; ++ds) s[t] = mfma_16x16x32(as_bf16x8(R.k[t][ds]), qf[ds], s[t]);
     }
-    if (nv < BT) {
+    if (has_next) load_k(R, blk_next);
+    if constexpr (MASKED) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -113,7 +154,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
           const int k0 = 32 * w + 8 * g4 + 2 * e;
           const uint32_t keep = (k0 >= nv ? 0u : 0xFFFFu) | (k0 + 1 >= nv ? 0u : 0xFFFF0000u);
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) vr[w][dt][e] &= keep;
+          for (int dt = 0; dt < 8; ++dt) R.v[w][dt][e] &= keep;
         }
       }
     }
@@ -136,7 +177,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pv = fast_exp2(s[t][r] * c2 - msc);
+        const float pv = fast_exp2(fmaf(s[t][r], c2, -msc));
         psum += pv;
         pb[t >> 1][4 * (t & 1) + r] = to_bf16(pv);
       }
@@ -145,9 +186,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
     for (int dt = 0; dt < 8; ++dt) {
       acc[dt] *= alpha;
 #pragma unroll
-      for (int w = 0; w < 2; ++w) acc[dt] = mfma_16x16x32(as_bf16x8(vr[w][dt]), pb[w], acc[dt]);
+      for (int w = 0; w < 2; ++w) acc[dt] = mfma_16x16x32(as_bf16x8(R.v[w][dt]), pb[w], acc[dt]);
     }
+    if (has_next) load_v(R, blk_next);
+  };
+
+  int blk = block_id(0);
+  load_k(R, blk);
+  load_v(R, blk);
+  for (int i = 0; i + 1 < nblk; ++i) {
+    const int blk_next = block_id(i + 1);
+    step(Int<0>{}, blk_next, true, BT);
   }
+  if (tail == BT)
+    step(Int<0>{}, 0, false, BT);
+  else
+    step(Int<1>{}, 0, false, tail);
 
   l_run += wave_shfl_xor(l_run, 16);
   l_run += wave_shfl_xor(l_run, 32);
@@ -162,33 +216,64 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   }
 }
 
-// One workgroup per (request, query head); thread d owns output channel d.
-__global__ __launch_bounds__(HD) void decode_merge_kernel(DecodeParams p) {
+// One workgroup (4 waves) per (request, query head).  Wave w folds splits
+// w, w+4, ... with lane l owning output channels 2l and 2l+1, then the four
+// partial sums are combined through LDS.
+constexpr int MERGE_WAVES = 4;
+
+__global__ __launch_bounds__(64 * MERGE_WAVES) void decode_merge_kernel(DecodeParams p) {
+  __shared__ float part[MERGE_WAVES][HD + 2];
+  __shared__ float wmax[MERGE_WAVES];
   const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ctx = min(p.ctx_len[b], p.max_blocks * BT);
   bf16 *o = static_cast<bf16 *>(p.o) + ((size_t)b * p.Hq + h) * HD;
   if (ctx <= 0) {
-    o[d] = to_bf16(0.f);
-    if (p.lse && d == 0) p.lse[(size_t)b * p.Hq + h] = -INFINITY;
+    if (tid < HD) o[tid] = to_bf16(0.f);
+    if (p.lse && tid == 0) p.lse[(size_t)b * p.Hq + h] = -INFINITY;
     return;
   }
   const int ns = (ctx + p.split_tokens - 1) / p.split_tokens;
   const float *rec = p.ws + ((size_t)b * p.Hq + h) * p.n_split * REC;
+
+  // global max of the split maxima
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[s * REC + HD]);
-  float num = 0.f, den = 0.f;
+  for (int s = tid; s < ns; s += 64 * MERGE_WAVES) M = fmaxf(M, rec[(size_t)s * REC + HD]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, wave_shfl_xor(M, off));
+  if (lane == 0) wmax[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+
+  float n0 = 0.f, n1 = 0.f, den = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < ns; ++s) {
-      const float ms = rec[s * REC + HD];
-      if (ms == -INFINITY) continue;
-      const float w = fast_exp2(ms - M);
-      num = fmaf(w, rec[s * REC + d], num);
-      den = fmaf(w, rec[s * REC + HD + 1], den);
+#pragma unroll 4
+    for (int s = wave; s < ns; s += MERGE_WAVES) {
+      const float *r = rec + (size_t)s * REC;
+      const float ms = r[HD];
+      const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+      const float2 ov = *reinterpret_cast<const float2 *>(r + 2 * lane);
+      n0 = fmaf(w, ov.x, n0);
+      n1 = fmaf(w, ov.y, n1);
+      den = fmaf(w, r[HD + 1], den);
     }
   }
-  o[d] = to_bf16(den > 0.f ? num / den : 0.f);
-  if (p.lse && d == 0) p.lse[(size_t)b * p.Hq + h] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+  part[wave][2 * lane] = n0;
+  part[wave][2 * lane + 1] = n1;
+  if (lane == 0) part[wave][HD] = den;
+  __syncthreads();
+  if (tid < HD) {
+    float num = 0.f, dsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < MERGE_WAVES; ++w) {
+      num += part[w][tid];
+      dsum += part[w][HD];
+    }
+    o[tid] = to_bf16(dsum > 0.f ? num / dsum : 0.f);
+    if (p.lse && tid == 0)
+      p.lse[(size_t)b * p.Hq + h] = dsum > 0.f ? (M + __log2f(dsum)) * kLn2 : -INFINITY;
+  }
 }
 
 }  // namespace
@@ -199,7 +284,7 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
   hipLaunchKernelGGL(decode_split_kernel, g1, b1, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g2(p.B * p.Hq), b2(HD);
+  dim3 g2(p.B * p.Hq), b2(64 * MERGE_WAVES);
   hipLaunchKernelGGL(decode_merge_kernel, g2, b2, 0, stream, p);
   return hipGetLastError();
 }

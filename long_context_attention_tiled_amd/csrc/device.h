@@ -55,4 +55,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t bits) {
 
 __device__ __forceinline__ float wave_shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Raw buffer descriptor over `bytes` bytes at `base` (gfx9-family word 3).
+// Reads outside [0, bytes) return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// 16-byte buffer load at voffset (per lane) + soffset (wave-uniform) bytes.
+__device__ __forceinline__ u32x4 buf_load_16(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0));
+}
+
 }  // namespace lcat

@@ -50,8 +50,23 @@ __device__ __forceinline__ int vt_lds_off(int d, int chunk) {
   return K_BYTES + d * 128 + ((chunk ^ (((d >> 1) ^ (d >> 3)) & 7)) << 4);
 }
 
+// Online-softmax rescale threshold in log2 units.  The running maximum m is
+// only raised when a tile's maximum exceeds it by more than this, so most
+// tiles skip the O/l rescale.  Exponentials are then bounded by 2^8, which
+// fp32 (accumulators) and bf16 (P) hold without loss of relative precision;
+// the result is unchanged because O and l always share the same m.
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
+
 struct TileRegs {
   u32x4 r[4];
+  int ok;    // paged: block id was in range
+  int nv;    // paged: valid keys in this block
+  int tag;   // paged: global KV-head tag read from the block
 };
 
 // Gather the 16-bit lane `i` (0..7) of four 8 x bf16 vectors into 4 x bf16.
@@ -68,84 +83,88 @@ __device__ __forceinline__ u32x2 column4(const TileRegs &t, int i) {
   return out;
 }
 
+// Global -> register -> LDS movement of one 64-key tile.  Waves 0-3 move V,
+// waves 4-7 move K; `wave` is wave-uniform so the split is a scalar branch.
+// load() only issues memory reads (nothing consumes them until store(), which
+// runs after the current tile's math), so the fetch overlaps the compute.
+// Dense keys past the end are clamped to the last key (finite data whose
+// scores are masked to -inf, so their P is exactly 0); paged slots past the
+// end are zeroed before they reach LDS because they may hold anything,
+// including NaN.
 template <bool PAGED>
 struct TileIO {
-  // Issue the global loads of key tile `tile` into registers.
-  //   threads   0..255 fetch V, threads 256..511 fetch K.
-  // Keys at or past n_keys are never used in arithmetic: K rows there are
-  // masked to -inf later, V entries are replaced by zeros here.
   static __device__ __forceinline__ void load(const PrefillParams &p, int b, int g, int tile,
-                                              int n_keys, int tid, TileRegs &t) {
+                                              int blk, int n_keys, int tid, int wave,
+                                              TileRegs &t) {
     const int key0 = tile * BN;
     const bf16 *kb = static_cast<const bf16 *>(p.k);
     const bf16 *vb = static_cast<const bf16 *>(p.v);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
     if constexpr (PAGED) {
-      const int blk = tile < p.max_blocks
-                          ? p.block_table[((size_t)b * p.Hkv + g) * p.max_blocks + tile]
-                          : -1;
-      const bool ok = blk >= 0 && blk < p.n_blocks;
-      if (tid == 0 && p.dev_status) {
-        if (!ok)
-          p.dev_status[0] = 2;
-        else if (p.block_head[blk] != p.kv_head_base + g)
-          p.dev_status[0] = 1;
-      }
-      const int nv = n_keys - key0;   // valid keys in this block (>= 1)
-      if (tid < 256) {
-        const int u = tid;
+      t.ok = blk >= 0 && blk < p.n_blocks;
+      const int sblk = t.ok ? blk : 0;
+      t.nv = n_keys - key0;
+      t.tag = p.block_head[sblk];
+      if (wave < 4) {
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-          const int d = 32 * pp + (u >> 3), c = u & 7;
-          u32x4 x = ok ? ld_global_16(vb + ((size_t)blk * HD + d) * BN + 8 * c) : zero;
-          if (nv < BN) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int k0 = 8 * c + 2 * e;
-              uint32_t w = x[e];
-              if (k0 >= nv) w &= 0xFFFF0000u;
-              if (k0 + 1 >= nv) w &= 0x0000FFFFu;
-              x[e] = w;
-            }
-          }
-          t.r[pp] = x;
+          const int d = 32 * pp + (tid >> 3), c = tid & 7;
+          t.r[pp] = ld_global_16(vb + ((size_t)sblk * HD + d) * BN + 8 * c);
         }
       } else {
         const int u = tid - 256;
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
           const int row = 16 * pp + (u >> 4), c = u & 15;
-          t.r[pp] = ok ? ld_global_16(kb + ((size_t)blk * BN + row) * HD + 8 * c) : zero;
+          t.r[pp] = ld_global_16(kb + ((size_t)sblk * BN + row) * HD + 8 * c);
         }
       }
     } else {
-      if (tid < 256) {
+      const int last = n_keys - 1;
+      if (wave < 4) {
         const int kq = tid >> 4, dc = tid & 15;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int key = key0 + 4 * kq + e;
-          t.r[e] = key < n_keys
-                       ? ld_global_16(vb + (((size_t)b * p.Sk + key) * p.Hkv + g) * HD + 8 * dc)
-                       : zero;
+          const int key = min(key0 + 4 * kq + e, last);
+          t.r[e] = ld_global_16(vb + (((size_t)b * p.Sk + key) * p.Hkv + g) * HD + 8 * dc);
         }
       } else {
         const int u = tid - 256;
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-          const int row = 16 * pp + (u >> 4), c = u & 15;
-          const int key = key0 + row;
-          t.r[pp] = key < n_keys
-                        ? ld_global_16(kb + (((size_t)b * p.Sk + key) * p.Hkv + g) * HD + 8 * c)
-                        : zero;
+          const int key = min(key0 + 16 * pp + (u >> 4), last);
+          t.r[pp] = ld_global_16(kb + (((size_t)b * p.Sk + key) * p.Hkv + g) * HD + 8 * (u & 15));
         }
       }
     }
   }
 
-  // Write the fetched tile into one LDS stage (V transposed for dense input).
-  static __device__ __forceinline__ void store(char *stage, int tid, const TileRegs &t) {
-    if (tid < 256) {
+  static __device__ __forceinline__ void store(const PrefillParams &p, int g, char *stage,
+                                               int tid, int wave, TileRegs &t) {
+    if constexpr (PAGED) {
+      if (tid == 0 && p.dev_status) {
+        if (!t.ok)
+          p.dev_status[0] = 2;
+        else if (t.tag != p.kv_head_base + g)
+          p.dev_status[0] = 1;
+      }
+      if (!t.ok) {
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) t.r[pp] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (wave < 4) {
       if constexpr (PAGED) {
+        if (t.nv < BN) {
+          const int c = tid & 7;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int k0 = 8 * c + 2 * e;
+            const uint32_t keep =
+                (k0 >= t.nv ? 0u : 0xFFFFu) | (k0 + 1 >= t.nv ? 0u : 0xFFFF0000u);
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) t.r[pp][e] &= keep;
+          }
+        }
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
           const int d = 32 * pp + (tid >> 3), c = tid & 7;
@@ -177,7 +196,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31;   // query column of this lane within the wave's 32 rows
   const int gq = lane >> 5;   // which 8-wide half of each 16-long K slice
 
@@ -212,103 +231,153 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   const int wave_tiles = (wave_keys + BN - 1) / BN;
 
   // ---- this wave's 32 query rows, held as the B operand of S^T = K Q^T ----
-  const bf16 *qp = static_cast<const bf16 *>(p.q);
+  // Rows past the end read the last row (finite data) and are never stored.
   const int qrow = row0 + lr;
   bf16x8 qf[8];
   {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const bf16 *src = qp + (((size_t)b * p.Sq + qrow) * p.Hq + h) * HD + 8 * gq;
+    const int qr = min(qrow, p.Sq - 1);
+    const bf16 *src =
+        static_cast<const bf16 *>(p.q) + (((size_t)b * p.Sq + qr) * p.Hq + h) * HD + 8 * gq;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(qrow < p.Sq ? ld_global_16(src + 16 * s) : zero);
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(ld_global_16(src + 16 * s));
+    // Consume Q here so its loads are complete before the tile loop; the
+    // loop then never waits on the memory counter before its QK^T MFMAs.
+#pragma unroll
+    for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(as_u32x4(qf[s])));
   }
 
-  // K row read by this lane for S^T rows 0..31 (bits 2 and 3 swapped) so that
-  // the score registers land directly in the B-operand order of P V.
+  // LDS operand addresses (stage 0).  K rows are read in a fixed permuted
+  // order (bits 2 and 3 of the row swapped) so that the score registers land
+  // directly in the B-operand order of P V; rows 32..63 sit 8 KiB further.
+  // V^T rows 32*db + lr: the swizzle of row d+32 is that of row d with chunk
+  // bit 2 flipped, so one address per chunk pair serves all four d blocks.
   const int krow = (lr & ~12) | ((lr & 4) << 1) | ((lr & 8) >> 1);
-  const float c2 = p.scale * kLog2e;
+  int ka[8], va[4];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) ka[s] = k_lds_off(krow, 2 * s + gq);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) va[u] = vt_lds_off(lr, 2 * u + gq);
+
+  const float c2 = p.scale * kLog2e;   // scores -> log2 units
   const int qpos = qoff + qrow;
 
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m2 = -INFINITY;   // running max of this lane's row, log2 units
+  float l_run = 0.f;      // lane-partial denominator (keys of this lane)
 
-  TileRegs tr;
-  if (n_tiles > 0) {
-    TileIO<PAGED>::load(p, b, g, 0, n_keys, tid, tr);
-    TileIO<PAGED>::store(smem, tid, tr);
-  }
-  __syncthreads();
+  auto compute = [&](auto stage_tag, int j) {
+    constexpr int SOFF = decltype(stage_tag)::value * STAGE;
+    // ---- S^T = K Q^T over the 64-key tile (two 32-key halves) ------------
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(smem + SOFF + ka[s]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(smem + SOFF + 8192 + ka[s]);
+      s0 = mfma_32x32x16(a0, qf[s], s0);
+      s1 = mfma_32x32x16(a1, qf[s], s1);
+    }
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const char *cur = smem + (j & 1) * STAGE;
-    if (j + 1 < n_tiles) TileIO<PAGED>::load(p, b, g, j + 1, n_keys, tid, tr);
-
-    if (j < wave_tiles) {
-      // ---- S^T = K Q^T over the 64-key tile (two 32-key halves) ----------
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+    // ---- mask: keys past the end, and (causal) keys after the query ------
+    const int key0 = j * BN;
+    const bool need_mask = (key0 + BN > n_keys) || (CAUSAL && key0 + BN - 1 > qoff + row0);
+    if (need_mask) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(cur + k_lds_off(krow, 2 * s + gq));
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(cur + k_lds_off(krow + 32, 2 * s + gq));
-        s0 = mfma_32x32x16(a0, qf[s], s0);
-        s1 = mfma_32x32x16(a1, qf[s], s1);
-      }
-
-      // ---- mask: keys past the end, and (causal) keys after the query ----
-      const int key0 = j * BN;
-      const bool need_mask = (key0 + BN > n_keys) || (CAUSAL && key0 + BN - 1 > qoff + row0);
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = key0 + 16 * (r >> 3) + 8 * gq + (r & 7);
-          if (kk >= n_keys || (CAUSAL && kk > qpos)) s0[r] = -INFINITY;
-          if (kk + 32 >= n_keys || (CAUSAL && kk + 32 > qpos)) s1[r] = -INFINITY;
-        }
-      }
-
-      // ---- online softmax statistics (lane-local + one exchange) ---------
-      float mx = s0[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-      mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float msc = (m_new == -INFINITY) ? 0.f : m_new * c2;
-      const float alpha = fast_exp2(m_run * c2 - msc);
-      m_run = m_new;
-
-      bf16x8 pb[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p0 = fast_exp2(s0[8 * u + e] * c2 - msc);
-          const float p1 = fast_exp2(s1[8 * u + e] * c2 - msc);
-          psum += p0 + p1;
-          pb[u][e] = to_bf16(p0);
-          pb[2 + u][e] = to_bf16(p1);
-        }
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
-
-      // ---- O^T += V^T P^T ------------------------------------------------
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(cur + vt_lds_off(32 * db + lr, 2 * u + gq));
-          acc[db] = mfma_32x32x16(a, pb[u], acc[db]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int kk = key0 + 16 * (r >> 3) + 8 * gq + (r & 7);
+        if (kk >= n_keys || (CAUSAL && kk > qpos)) s0[r] = -INFINITY;
+        if (kk + 32 >= n_keys || (CAUSAL && kk + 32 > qpos)) s1[r] = -INFINITY;
       }
     }
 
-    if (j + 1 < n_tiles) TileIO<PAGED>::store(smem + ((j + 1) & 1) * STAGE, tid, tr);
+    // ---- online softmax statistics (lane-local + one exchange) -----------
+    float mx = fmaxf(s0[0], s0[1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    const float mx2 = mx * c2;
+    const bool grow = mx2 > m2 + kRescaleLog2;
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx2 : m2;
+      const float alpha = grow ? fast_exp2(m2 - m_new) : 1.f;
+      m2 = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+    }
+    const float msc = (m2 == -INFINITY) ? 0.f : m2;
+
+    bf16x8 pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p0 = fast_exp2(fmaf(s0[8 * u + e], c2, -msc));
+        const float p1 = fast_exp2(fmaf(s1[8 * u + e], c2, -msc));
+        psum += p0 + p1;
+        pb[u][e] = to_bf16(p0);
+        pb[2 + u][e] = to_bf16(p1);
+      }
+    }
+    l_run += psum;
+
+    // ---- O^T += V^T P^T --------------------------------------------------
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(smem + SOFF + 4096 * db +
+                                                           va[u ^ (2 * (db & 1))]);
+        acc[db] = mfma_32x32x16(a, pb[u], acc[db]);
+      }
+    }
+  };
+
+  // Paged: physical block of a tile, read one tile ahead of its data so the
+  // table lookup never stalls the data fetch.
+  const int32_t *table = PAGED ? p.block_table + ((size_t)b * p.Hkv + g) * p.max_blocks : nullptr;
+  auto block_of = [&](int tile) -> int {
+    if constexpr (PAGED) return tile < p.max_blocks ? table[tile] : -1;
+    return 0;
+  };
+
+  // The looked-up id stays in a vector register until the fetch that needs
+  // it (one tile later); only then is it made wave-uniform, so the lookup's
+  // latency is never waited on right after it is issued.
+  auto uniform_block = [&](int v) -> int {
+    asm volatile("" : "+v"(v));
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+
+  TileRegs tr;
+  int blk_next = block_of(0);
+  if (n_tiles > 0) {
+    TileIO<PAGED>::load(p, b, g, 0, uniform_block(blk_next), n_keys, tid, wave, tr);
+    blk_next = block_of(1);
+    TileIO<PAGED>::store(p, g, smem, tid, wave, tr);
+  }
+  __syncthreads();
+
+  // Two tiles per trip so each LDS stage offset is a compile-time constant.
+  for (int j = 0; j < n_tiles; j += 2) {
+    if (j + 1 < n_tiles) {
+      TileIO<PAGED>::load(p, b, g, j + 1, uniform_block(blk_next), n_keys, tid, wave, tr);
+      blk_next = block_of(j + 2);
+    }
+    if (j < wave_tiles) compute(Int<0>{}, j);
+    if (j + 1 < n_tiles) TileIO<PAGED>::store(p, g, smem + STAGE, tid, wave, tr);
+    __syncthreads();
+    if (j + 1 >= n_tiles) break;
+    if (j + 2 < n_tiles) {
+      TileIO<PAGED>::load(p, b, g, j + 2, uniform_block(blk_next), n_keys, tid, wave, tr);
+      blk_next = block_of(j + 3);
+    }
+    if (j + 1 < wave_tiles) compute(Int<1>{}, j + 1);
+    if (j + 2 < n_tiles) TileIO<PAGED>::store(p, g, smem, tid, wave, tr);
     __syncthreads();
   }
 
@@ -329,7 +398,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     }
     if (p.lse && gq == 0)
       p.lse[((size_t)b * p.Hq + h) * p.Sq + qrow] =
-          l_tot > 0.f ? (m_run * c2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+          l_tot > 0.f ? (m2 + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 

@@ -56,8 +56,8 @@ def _load():
             build()
         lib = ctypes.CDLL(_LIB_PATH)
         vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
-        lib.oracle_attention_rows.argtypes = [vp, i32, vp, vp, i32, i64, i64, i64, i64, i64, i64,
-                                              vp, dbl, vp, vp]
+        lib.oracle_attention_rows.argtypes = [vp, i32, vp, i32, vp, i32, i64, i64, i64, i64, i64,
+                                              i64, vp, dbl, vp, vp]
         lib.oracle_attention_rows.restype = i32
         lib.oracle_rope.argtypes = [vp, i32, vp, i64, i64, i64, dbl, vp]
         lib.oracle_rope.restype = i32
@@ -110,8 +110,6 @@ def attention_rows(q_rows, k, v, key_limit, scale):
     q_rows = np.ascontiguousarray(q_rows)
     k = np.ascontiguousarray(k)
     v = np.ascontiguousarray(v)
-    if k.dtype != v.dtype:
-        raise TypeError("oracle: k and v must share a dtype")
     B, R, Hq, D = q_rows.shape
     Bk, Sk, Hkv, Dk = k.shape
     if Bk != B or Dk != D or v.shape != k.shape:
@@ -119,8 +117,8 @@ def attention_rows(q_rows, k, v, key_limit, scale):
     lim = np.ascontiguousarray(np.broadcast_to(np.asarray(key_limit, dtype=np.int64), (B, R)))
     out = np.empty((B, R, Hq, D), dtype=np.float64)
     lse = np.empty((B, Hq, R), dtype=np.float64)
-    rc = _load().oracle_attention_rows(_ptr(q_rows), _dtype_code(q_rows), _ptr(k), _ptr(v),
-                                       _dtype_code(k), B, R, Sk, Hq, Hkv, D, _ptr(lim),
+    rc = _load().oracle_attention_rows(_ptr(q_rows), _dtype_code(q_rows), _ptr(k), _dtype_code(k),
+                                       _ptr(v), _dtype_code(v), B, R, Sk, Hq, Hkv, D, _ptr(lim),
                                        float(scale), _ptr(out), _ptr(lse))
     if rc != 0:
         raise RuntimeError(f"oracle_attention_rows failed ({rc})")

@@ -41,7 +41,7 @@ static double widen(const void *base, int dtype, int64_t idx) {
 /*
  * Attention for selected query rows.
  *   q_rows : [B][R][Hq][D]   the query vectors of the R selected rows
- *   k, v   : [B][Sk][Hkv][D] keys and values
+ *   k, v   : [B][Sk][Hkv][D] keys and values (each with its own dtype code)
  *   key_limit : [B][R]       row r of batch b may attend keys 0 .. key_limit-1
  *                            (this single rule expresses non-causal, causal,
  *                            chunked and decode masks; the caller computes it)
@@ -51,8 +51,8 @@ static double widen(const void *base, int dtype, int64_t idx) {
  * A row with no allowed key gets out = NaN and lse = -inf.
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
-int oracle_attention_rows(const void *q_rows, int q_dtype, const void *k, const void *v,
-                          int kv_dtype, int64_t B, int64_t R, int64_t Sk, int64_t Hq,
+int oracle_attention_rows(const void *q_rows, int q_dtype, const void *k, int k_dtype,
+                          const void *v, int v_dtype, int64_t B, int64_t R, int64_t Sk, int64_t Hq,
                           int64_t Hkv, int64_t D, const int64_t *key_limit, double scale,
                           double *out, double *lse) {
   if (!q_rows || !k || !v || !key_limit || !out || !lse) return -1;
@@ -87,7 +87,7 @@ int oracle_attention_rows(const void *q_rows, int q_dtype, const void *k, const 
       for (int64_t j = 0; j < lim; ++j) {
         const int64_t k_off = ((b * Sk + j) * Hkv + g) * D;
         double acc = 0.0;
-        for (int64_t d = 0; d < D; ++d) acc += widen(q_rows, q_dtype, q_off + d) * widen(k, kv_dtype, k_off + d);
+        for (int64_t d = 0; d < D; ++d) acc += widen(q_rows, q_dtype, q_off + d) * widen(k, k_dtype, k_off + d);
         s[j] = scale * acc;
       }
       /* pass 1: maximum */
@@ -102,7 +102,7 @@ int oracle_attention_rows(const void *q_rows, int q_dtype, const void *k, const 
       for (int64_t j = 0; j < lim; ++j) {
         const double a = exp(s[j] - m) / z;
         const int64_t v_off = ((b * Sk + j) * Hkv + g) * D;
-        for (int64_t d = 0; d < D; ++d) o[d] += a * widen(v, kv_dtype, v_off + d);
+        for (int64_t d = 0; d < D; ++d) o[d] += a * widen(v, v_dtype, v_off + d);
       }
       lse[(b * Hq + h) * R + r] = m + log(z);
     }

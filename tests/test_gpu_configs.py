@@ -1,0 +1,159 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times.
+
+* causal GQA prefill with RoPE, 1 x 32768 tokens, 16 Q / 2 KV heads, D=128;
+* sequence-shard input [4][16384][64 heads][128] relayed out to one rank's
+  [65536][16][128] (bit-exact against the oracle relayout), RoPE at global
+  positions 0..65535, causal prefill;
+* split-K decode of 32 requests with contexts uniform in [8192, 131072] over
+  a shuffled, NaN-poisoned paged cache (every output row checked);
+* chunked prefill of 4 x 131072 tokens in 8192-token chunks against the
+  growing paged cache.
+
+Large outputs are compared on a seeded sample of >= 512 query rows per head
+plus forced rows (first/last, tile edges, shard and chunk boundaries); the
+fp64 oracle evaluates exactly those rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_helpers import assert_attention_close, bits, log, to_dev, to_np64
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+torch = pytest.importorskip("torch")
+lcat = pytest.importorskip("long_context_attention_tiled_amd")
+
+N_SAMPLE = 512
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lcat.load_library()
+
+
+def prefill_reference(q, k, v, positions, rows, scale, base=10000.0):
+    """Oracle rows of causal attention after fp64 RoPE of the raw bf16 inputs."""
+    qr = oracle.rope(q[0, rows], positions[rows], base)[None]      # [1][R][Hq][D]
+    kr = oracle.rope(k[0], positions, base)[None]                    # [1][S][Hkv][D]
+    lim = (rows + 1)[None, :]
+    return oracle.attention_rows(qr, kr, oracle.widen(v), lim, scale)
+
+
+def forced_rows(S, extra=()):
+    base = [0, 1, 31, 32, 63, 64, 65, 127, 128, 255, 256, S // 2, S - 2, S - 1]
+    return [r for r in list(base) + list(extra) if 0 <= r < S]
+
+
+def test_causal_gqa_prefill_32k():
+    S = 32768
+    log("C2: generating inputs")
+    d = synth.causal_gqa(seed=2, S=S)
+    q, k, v = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
+    pos = to_dev(d["positions"])
+    log("C2: rope + prefill")
+    lcat.rope_apply(q[0], pos)
+    lcat.rope_apply(k[0], pos)
+    o, lse = lcat.attn_prefill(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(22, S, N_SAMPLE, forced_rows(S))
+    log(f"C2: oracle on {rows.size} rows x 16 heads")
+    ref, ref_lse = prefill_reference(d["q"], d["k"], d["v"], d["positions"].astype(np.int64),
+                                     rows, d["scale"])
+    got = to_np64(o[:, torch.from_numpy(rows).cuda()])
+    got_lse = lse[:, :, torch.from_numpy(rows).cuda()].cpu().numpy()
+    e, r = assert_attention_close(got, ref, got_lse, ref_lse, what="C2")
+    log(f"C2: max abs {e:.3g} rel-L2 {r:.3g}")
+
+
+def test_ulysses_relayout_rope_prefill_64k():
+    SP, S_loc = 4, 16384
+    S = SP * S_loc
+    log("C3: generating shard inputs")
+    d = synth.ulysses_shards(seed=3, SP=SP, S_loc=S_loc)
+    rank = 0
+    qd = lcat.seq_to_head_permute(to_dev(d["q"]), rank)
+    kd = lcat.seq_to_head_permute(to_dev(d["k"]), rank)
+    vd = lcat.seq_to_head_permute(to_dev(d["v"]), rank)
+    torch.cuda.synchronize()
+    log("C3: relayout bit-exact check")
+    q_p = oracle.permute(d["q"], rank)
+    k_p = oracle.permute(d["k"], rank)
+    v_p = oracle.permute(d["v"], rank)
+    assert np.array_equal(bits(qd), q_p)
+    assert np.array_equal(bits(kd), k_p)
+    assert np.array_equal(bits(vd), v_p)
+    gpos = d["shard_positions"].reshape(-1)          # global position of relayed token t
+    assert np.array_equal(gpos, np.arange(S))
+    log("C3: rope + prefill")
+    posd = to_dev(gpos.astype(np.int32))
+    lcat.rope_apply(qd, posd)
+    lcat.rope_apply(kd, posd)
+    o, lse = lcat.attn_prefill(qd[None], kd[None], vd[None], causal=True)
+    torch.cuda.synchronize()
+    boundaries = [S_loc * i + j for i in range(1, SP) for j in (-1, 0, 1)]
+    rows = synth.sample_rows(33, S, N_SAMPLE, forced_rows(S, boundaries))
+    log(f"C3: oracle on {rows.size} rows x 16 heads")
+    ref, ref_lse = prefill_reference(q_p[None], k_p[None], v_p[None], gpos.astype(np.int64), rows,
+                                     d["scale"])
+    idx = torch.from_numpy(rows).cuda()
+    e, r = assert_attention_close(to_np64(o[:, idx]), ref, lse[:, :, idx].cpu().numpy(), ref_lse,
+                                  what="C3")
+    log(f"C3: max abs {e:.3g} rel-L2 {r:.3g}")
+
+
+def test_decode_paged_32_requests():
+    log("C4: generating cache")
+    c = synth.decode_cache(seed=4, B=32)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    args = [to_dev(c[k_]) for k_ in ("q", "k_pool", "v_pool", "block_head", "block_table", "ctx_len")]
+    log(f"C4: decode, total context {int(c['ctx_len'].sum())} tokens")
+    o, lse = lcat.attn_decode(*args, dev_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    ref, ref_lse = oracle.decode_attention(c["q"], c["k_seq"], c["v_seq"], c["ctx_len"], c["scale"])
+    e, r = assert_attention_close(to_np64(o), ref, lse.cpu().numpy(), ref_lse, what="C4")
+    log(f"C4: max abs {e:.3g} rel-L2 {r:.3g}")
+
+
+def test_chunked_prefill_4x131072():
+    B, S, C = 4, 131072, 8192
+    log("C5: generating inputs")
+    d = synth.chunked_prefill(seed=5, B=B, S=S, C=C)
+    q, k, v = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
+    n_blocks = d["n_blocks"]
+    k_pool = torch.full((n_blocks, 64, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    v_pool = torch.full((n_blocks, 128, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    tags, table = to_dev(d["block_head"]), to_dev(d["block_table"])
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, 16, S), dtype=torch.float32, device="cuda")
+    log("C5: 16 chunk steps")
+    for c0 in range(0, S, C):
+        cb = torch.full((B,), c0, dtype=torch.int32, device="cuda")
+        oc, lc = lcat.attn_chunked_prefill(q[:, c0:c0 + C].contiguous(), k[:, c0:c0 + C].contiguous(),
+                                           v[:, c0:c0 + C].contiguous(), k_pool, v_pool, tags, table,
+                                           cb, dev_status=st)
+        o[:, c0:c0 + C] = oc
+        lse[:, :, c0:c0 + C] = lc
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    # >= 512 sampled rows per head across the 4 requests (128 seeded rows per
+    # request), plus every chunk boundary 8192c-1 / 8192c spread over requests
+    boundaries = [C * i + j for i in range(1, S // C) for j in (-1, 0)]
+    for b in range(B):
+        rows = synth.sample_rows(55 + b, S, 128, forced_rows(S, boundaries[b::B]))
+        idx = torch.from_numpy(rows).cuda()
+        log(f"C5: oracle request {b}: {rows.size} rows x 16 heads")
+        ref, ref_lse = oracle.attention(d["q"][b:b + 1], d["k"][b:b + 1], d["v"][b:b + 1],
+                                        d["scale"], causal=True, rows=rows)
+        e, r = assert_attention_close(to_np64(o[b:b + 1, idx]), ref,
+                                      lse[b:b + 1, :, idx].cpu().numpy(), ref_lse, what=f"C5[{b}]")
+        log(f"C5[{b}]: max abs {e:.3g} rel-L2 {r:.3g}")
+    log("C5: cache read-back for request 0")
+    kg, vg = oracle.paged_gather(bits(k_pool), bits(v_pool), d["block_table"][:1], [S])
+    assert np.array_equal(kg[0], d["k"][0]) and np.array_equal(vg[0], d["v"][0])

@@ -51,11 +51,13 @@ def test_permute_bit_exact(SP, S_loc, H, D, dtype):
 # RoPE
 # ---------------------------------------------------------------------------
 def _rope_ref_bits_close(got_bits, ref):
-    """GPU bf16 vs fp64 reference: within one bf16 ulp everywhere, and the
-    correctly rounded value for (almost) every element."""
+    """GPU bf16 vs fp64 reference: within one bf16 ulp plus the fp32 rotation
+    error (about 1e-7 absolute, which dominates only where the two rotation
+    terms cancel), and the correctly rounded value for (almost) every element."""
     got = synth.bf16_bits_to_f32(got_bits).astype(np.float64)
-    ulp = np.maximum(np.abs(ref), 1e-30) * 2.0 ** -7
-    assert np.all(np.abs(got - ref) <= ulp), f"max rel err {np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30))}"
+    err = np.abs(got - ref)
+    bound = np.abs(ref) * 2.0 ** -7 + 1e-6
+    assert np.all(err <= bound), f"max excess {np.max(err - bound):.3g}"
     exact = synth.f32_to_bf16_bits(ref.astype(np.float32))
     frac = np.mean(got_bits == exact)
     assert frac > 0.99, f"only {frac:.4f} correctly rounded"
@@ -64,8 +66,7 @@ def _rope_ref_bits_close(got_bits, ref):
 def test_rope_matches_oracle_large_positions():
     S, H, D = 1000, 16, 128
     log("rope S=1000 H=16 positions up to 131k")
-    rng = np.random.default_rng(200)
-    x = synth.normal_bf16(rng, (S, H, D))
+    x = synth.normal_bf16(200, (S, H, D))
     pos = (np.arange(S, dtype=np.int64) * 131).astype(np.int32)
     xd = to_dev(x)
     lcat.rope_apply(xd, to_dev(pos))
@@ -77,8 +78,7 @@ def test_rope_local_positions_fail_negative_control():
     """Local positions (0..S_loc-1 on every shard) must NOT reproduce the
     global-position result beyond the first shard (the article's §5.3 bug)."""
     S_loc, H, D = 64, 2, 128
-    rng = np.random.default_rng(201)
-    x = synth.normal_bf16(rng, (2 * S_loc, H, D))
+    x = synth.normal_bf16(201, (2 * S_loc, H, D))
     glob = np.arange(2 * S_loc, dtype=np.int32)
     loc = np.concatenate([np.arange(S_loc), np.arange(S_loc)]).astype(np.int32)
     a, b = to_dev(x), to_dev(x)
@@ -93,8 +93,7 @@ def test_rope_commutes_with_relayout():
     """RoPE on each shard with its global positions, then the relayout, equals
     the relayout then RoPE at positions 0..S-1 (bit for bit)."""
     SP, S_loc, H, D = 4, 48, 16, 128
-    rng = np.random.default_rng(202)
-    x = synth.normal_bf16(rng, (SP, S_loc, H, D))
+    x = synth.normal_bf16(202, (SP, S_loc, H, D))
     shard_pos = (np.arange(SP)[:, None] * S_loc + np.arange(S_loc)[None]).astype(np.int32)
     for r in range(SP):
         a = to_dev(x)
@@ -168,7 +167,7 @@ def test_prefill_needle():
     k = rng.standard_normal((1, S, Hkv, 128)).astype(np.float32) * 0.1
     v = rng.standard_normal((1, S, Hkv, 128)).astype(np.float32)
     rows = np.arange(100, S)
-    needle = rows // 2
+    needle = rows - 60                  # one distinct earlier key per row
     for g in range(Hkv):
         k[0, needle, g] = 4.0 * q[0, rows, 0]
     qb, kb, vb = (synth.f32_to_bf16_bits(a) for a in (q, k, v))
