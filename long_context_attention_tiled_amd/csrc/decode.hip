@@ -30,11 +30,6 @@ constexpr int HD = 128;
 constexpr int BT = 64;
 constexpr int REC = 132;   // floats per workspace record: O[128], m (log2 units), l, pad
 
-template <int N>
-struct Int {
-  static constexpr int value = N;
-};
-
 struct BlockRegs {
   u32x4 k[4][4];   // K rows of the four 16-key sub-tiles, four 32-wide d slices
   u32x4 v[2][8];   // V^T: two 32-key halves x eight 16-row d tiles
@@ -78,7 +73,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   // out-of-range access).
   const int32_t *table = p.block_table + ((size_t)b * p.Hkv + g) * p.max_blocks;
   const int want = p.kv_head_base + g;
-  auto load_ids = [&](int base) -> int {
+  auto load_ids = [&](int base) __attribute__((always_inline)) -> int {
     const bool in = base + lane < nblk;
     const int id = in ? table[j_begin + base + lane] : 0;
     const bool ok = id >= 0 && id < p.n_blocks;
@@ -90,7 +85,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   };
   int ids = load_ids(0);
   int ids_base = 0;
-  auto block_id = [&](int i) -> int {
+  auto block_id = [&](int i) __attribute__((always_inline)) -> int {
     if (i - ids_base >= 64) {   // next chunk of 64 ids (only for splits over 4096 keys)
       ids_base += 64;
       ids = load_ids(ids_base);
@@ -104,7 +99,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   //   32w + 8*g4 + 4e + r.
   const int k_voff = (8 * (qi >> 2) + (qi & 3)) * (HD * 2) + 16 * g4;
   const int v_voff = qi * (BT * 2) + 16 * g4;
-  auto load_k = [&](BlockRegs &R, int blk) {
+  auto load_k = [&](BlockRegs &R, int blk) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(kp + (size_t)blk * BT * HD, BLOCK_BYTES);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -112,7 +107,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       for (int s = 0; s < 4; ++s)
         R.k[t][s] = buf_load_16(r, k_voff + 64 * s + 1024 * (t & 1), 8192 * (t >> 1));
   };
-  auto load_v = [&](BlockRegs &R, int blk) {
+  auto load_v = [&](BlockRegs &R, int blk) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(vp + (size_t)blk * HD * BT, BLOCK_BYTES);
 #pragma unroll
     for (int w = 0; w < 2; ++w)
@@ -131,7 +126,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   // consumed, its V as soon as the V registers are, so a full block of
   // loads is always in flight.  MASKED handles the final partial block.
   BlockRegs R;
-  auto step = [&](auto masked_tag, int blk_next, bool has_next, int nv) {
+  auto step = [&](auto masked_tag, int blk_next, bool has_next, int nv) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value != 0;
     f32x4 s[4];
 #pragma unroll

@@ -15,6 +15,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Compile-time integer tag (selects a specialisation of a generic lambda).
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
 constexpr float kLn2 = 0.6931471805599453f;
 
 // 32x32 output tile, K = 16 per instruction.  Operand lane layout (wave64):
@@ -54,6 +60,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t bits) {
 }
 
 __device__ __forceinline__ float wave_shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Returns v unchanged but hides its value from the optimiser, so address
+// arithmetic derived from it is recomputed where it is used (1-2 VALU ops)
+// instead of being hoisted out of a loop and kept in registers.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 // Raw buffer descriptor over `bytes` bytes at `base` (gfx9-family word 3).
 // Reads outside [0, bytes) return zeros instead of touching memory.

@@ -38,17 +38,35 @@ constexpr int HD = 128;                 // head dimension
 constexpr int BN = 64;                  // keys per tile (= KV block)
 constexpr int NW = 8;                   // waves per workgroup
 constexpr int NT = NW * 64;             // threads per workgroup
-constexpr int K_BYTES = BN * HD * 2;    // K tile   [64][128] bf16
-constexpr int V_BYTES = HD * BN * 2;    // V^T tile [128][64] bf16
-constexpr int STAGE = K_BYTES + V_BYTES;
+constexpr int TILE = BN * HD * 2;       // bytes of one K tile [64][128] or V^T tile [128][64]
 
+// LDS: K slots 0/1 at [0, 2*TILE), V^T slots 0/1 at [2*TILE, 4*TILE).
+// Rows are XOR-swizzled on 16-byte chunks so that MFMA operand reads (8
+// rows, same chunk) and tile writes hit distinct banks.
 __device__ __forceinline__ int k_lds_off(int row, int chunk) {
   return row * 256 + ((chunk ^ (row & 15)) << 4);
 }
 
 __device__ __forceinline__ int vt_lds_off(int d, int chunk) {
-  return K_BYTES + d * 128 + ((chunk ^ (((d >> 1) ^ (d >> 3)) & 7)) << 4);
+  return 2 * TILE + d * 128 + ((chunk ^ (((d >> 1) ^ (d >> 3)) & 7)) << 4);
 }
+
+// Scheduling shape of a GEMM phase (NREADS LDS operand reads feeding 16
+// MFMAs): keep a few reads in flight ahead of the MFMA that consumes them
+// instead of hoisting all of them, which would cost many extra registers.
+template <int NREADS>
+__device__ __forceinline__ void interleave_reads_with_mfma() {
+  constexpr int per = NREADS / 16;   // reads issued per MFMA in steady state
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 * per, 0);
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, per, 0);   // next DS read(s)
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+constexpr int QROWS_BYTES = 32 * HD * 2;   // one wave's 32 query rows in LDS
 
 // Online-softmax rescale threshold in log2 units.  The running maximum m is
 // only raised when a tile's maximum exceeds it by more than this, so most
@@ -56,11 +74,6 @@ __device__ __forceinline__ int vt_lds_off(int d, int chunk) {
 // fp32 (accumulators) and bf16 (P) hold without loss of relative precision;
 // the result is unchanged because O and l always share the same m.
 constexpr float kRescaleLog2 = 8.0f;
-
-template <int N>
-struct Int {
-  static constexpr int value = N;
-};
 
 struct TileRegs {
   u32x4 r[4];
@@ -83,65 +96,91 @@ __device__ __forceinline__ u32x2 column4(const TileRegs &t, int i) {
   return out;
 }
 
-// Global -> register -> LDS movement of one 64-key tile.  Waves 0-3 move V,
-// waves 4-7 move K; `wave` is wave-uniform so the split is a scalar branch.
-// load() only issues memory reads (nothing consumes them until store(), which
-// runs after the current tile's math), so the fetch overlaps the compute.
-// Dense keys past the end are clamped to the last key (finite data whose
-// scores are masked to -inf, so their P is exactly 0); paged slots past the
-// end are zeroed before they reach LDS because they may hold anything,
-// including NaN.
+// Global -> register -> LDS movement of one 64-key tile by one group of four
+// waves (`gt` = thread index within the group, 0..255).  fetch_*() only issues
+// memory reads; store_*() runs a half-step later, so the fetch overlaps
+// compute.  Reads go through a buffer descriptor whose base is the tile's
+// first row (wave-uniform) and whose extent stops at the end of the tensor,
+// with per-lane byte offsets that are the same for every tile: rows past the
+// end of the tensor read as zero, rows past the key count belong to other
+// positions (finite data whose scores are masked to -inf, so their P is
+// exactly 0).  Paged slots past the key count are zeroed before they reach
+// LDS because they may hold anything, including NaN.
+struct TileOffsets {
+  int k[4];   // byte offsets of this thread's four K chunks within a tile
+  int v[4];   // byte offsets of this thread's four V chunks within a tile
+};
+
 template <bool PAGED>
 struct TileIO {
-  static __device__ __forceinline__ void load(const PrefillParams &p, int b, int g, int tile,
-                                              int blk, int n_keys, int tid, int wave,
-                                              TileRegs &t) {
-    const int key0 = tile * BN;
-    const bf16 *kb = static_cast<const bf16 *>(p.k);
-    const bf16 *vb = static_cast<const bf16 *>(p.v);
+  static __device__ __forceinline__ TileOffsets offsets(const PrefillParams &p, int gt) {
+    TileOffsets o;
     if constexpr (PAGED) {
-      t.ok = blk >= 0 && blk < p.n_blocks;
-      const int sblk = t.ok ? blk : 0;
-      t.nv = n_keys - key0;
-      t.tag = p.block_head[sblk];
-      if (wave < 4) {
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const int d = 32 * pp + (tid >> 3), c = tid & 7;
-          t.r[pp] = ld_global_16(vb + ((size_t)sblk * HD + d) * BN + 8 * c);
-        }
-      } else {
-        const int u = tid - 256;
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const int row = 16 * pp + (u >> 4), c = u & 15;
-          t.r[pp] = ld_global_16(kb + ((size_t)sblk * BN + row) * HD + 8 * c);
-        }
+      for (int pp = 0; pp < 4; ++pp) {
+        o.k[pp] = (16 * pp + (gt >> 4)) * (HD * 2) + 16 * (gt & 15);   // [64][128] block
+        o.v[pp] = (32 * pp + (gt >> 3)) * (BN * 2) + 16 * (gt & 7);    // [128][64] block
       }
     } else {
-      const int last = n_keys - 1;
-      if (wave < 4) {
-        const int kq = tid >> 4, dc = tid & 15;
+      const int rs = p.Hkv * HD * 2;   // bytes between consecutive keys
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = min(key0 + 4 * kq + e, last);
-          t.r[e] = ld_global_16(vb + (((size_t)b * p.Sk + key) * p.Hkv + g) * HD + 8 * dc);
-        }
-      } else {
-        const int u = tid - 256;
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const int key = min(key0 + 16 * pp + (u >> 4), last);
-          t.r[pp] = ld_global_16(kb + (((size_t)b * p.Sk + key) * p.Hkv + g) * HD + 8 * (u & 15));
-        }
+      for (int pp = 0; pp < 4; ++pp) {
+        o.k[pp] = (16 * pp + (gt >> 4)) * rs + 16 * (gt & 15);
+        o.v[pp] = (4 * (gt >> 4) + pp) * rs + 16 * (gt & 15);
       }
+    }
+    return o;
+  }
+
+  // Descriptor over the tile starting at key tile*64 of (b, g) (dense), or
+  // over one 16 KiB block (paged).
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const PrefillParams &p,
+                                                                     const void *base, int b,
+                                                                     int g, int tile, int blk) {
+    if constexpr (PAGED) {
+      return make_rsrc(static_cast<const bf16 *>(base) + (size_t)blk * TILE / 2, TILE);
+    } else {
+      const size_t first = (((size_t)b * p.Sk + (size_t)tile * BN) * p.Hkv + g) * HD;
+      const size_t total = (size_t)p.B * p.Sk * p.Hkv * HD;
+      const size_t bytes = (total - first) * 2;
+      return make_rsrc(static_cast<const bf16 *>(base) + first,
+                       bytes > 0x7FFFFFFFu ? 0x7FFFFFFF : (int)bytes);
     }
   }
 
-  static __device__ __forceinline__ void store(const PrefillParams &p, int g, char *stage,
-                                               int tid, int wave, TileRegs &t) {
+  static __device__ __forceinline__ void fetch_k(const PrefillParams &p, const TileOffsets &o,
+                                                 int b, int g, int tile, int blk, int gt,
+                                                 TileRegs &t) {
+    int sblk = 0;
     if constexpr (PAGED) {
-      if (tid == 0 && p.dev_status) {
+      t.ok = blk >= 0 && blk < p.n_blocks;
+      sblk = t.ok ? blk : 0;
+      t.tag = p.block_head[sblk];
+    }
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(p, p.k, b, g, tile, sblk);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) t.r[pp] = buf_load_16(r, o.k[pp], 0);
+  }
+
+  static __device__ __forceinline__ void fetch_v(const PrefillParams &p, const TileOffsets &o,
+                                                 int b, int g, int tile, int blk, int n_keys,
+                                                 int gt, TileRegs &t) {
+    int sblk = 0;
+    if constexpr (PAGED) {
+      t.ok = blk >= 0 && blk < p.n_blocks;
+      sblk = t.ok ? blk : 0;
+      t.nv = n_keys - tile * BN;
+    }
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(p, p.v, b, g, tile, sblk);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) t.r[pp] = buf_load_16(r, o.v[pp], 0);
+  }
+
+  static __device__ __forceinline__ void store_k(const PrefillParams &p, int g, char *slot, int gt_,
+                                                 TileRegs &t) {
+    const int gt = opaque(gt_);
+    if constexpr (PAGED) {
+      if (gt == 0 && p.dev_status) {
         if (!t.ok)
           p.dev_status[0] = 2;
         else if (t.tag != p.kv_head_base + g)
@@ -152,51 +191,70 @@ struct TileIO {
         for (int pp = 0; pp < 4; ++pp) t.r[pp] = u32x4{0u, 0u, 0u, 0u};
       }
     }
-    if (wave < 4) {
-      if constexpr (PAGED) {
-        if (t.nv < BN) {
-          const int c = tid & 7;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k0 = 8 * c + 2 * e;
-            const uint32_t keep =
-                (k0 >= t.nv ? 0u : 0xFFFFu) | (k0 + 1 >= t.nv ? 0u : 0xFFFF0000u);
+    for (int pp = 0; pp < 4; ++pp) {
+      const int row = 16 * pp + (gt >> 4), c = gt & 15;
+      *reinterpret_cast<u32x4 *>(slot + k_lds_off(row, c)) = t.r[pp];
+    }
+  }
+
+  // V^T slot: paged blocks are already dimension-major; dense tiles are
+  // transposed here (4 keys x 8 channels per thread -> 8 rows of 4 keys).
+  static __device__ __forceinline__ void store_v(char *slot_base, int gt_, TileRegs &t) {
+    const int gt = opaque(gt_);
+    if constexpr (PAGED) {
+      if (!t.ok) {
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) t.r[pp][e] &= keep;
-          }
-        }
+        for (int pp = 0; pp < 4; ++pp) t.r[pp] = u32x4{0u, 0u, 0u, 0u};
+      }
+      if (t.nv < BN) {
+        const int c = gt & 7;
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const int d = 32 * pp + (tid >> 3), c = tid & 7;
-          *reinterpret_cast<u32x4 *>(stage + vt_lds_off(d, c)) = t.r[pp];
-        }
-      } else {
-        const int kq = tid >> 4, dc = tid & 15;
+        for (int e = 0; e < 4; ++e) {
+          const int k0 = 8 * c + 2 * e;
+          const uint32_t keep = (k0 >= t.nv ? 0u : 0xFFFFu) | (k0 + 1 >= t.nv ? 0u : 0xFFFF0000u);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int d = 8 * dc + i;
-          *reinterpret_cast<u32x2 *>(stage + vt_lds_off(d, kq >> 1) + 8 * (kq & 1)) = column4(t, i);
+          for (int pp = 0; pp < 4; ++pp) t.r[pp][e] &= keep;
         }
       }
-    } else {
-      const int u = tid - 256;
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
-        const int row = 16 * pp + (u >> 4), c = u & 15;
-        *reinterpret_cast<u32x4 *>(stage + k_lds_off(row, c)) = t.r[pp];
+        const int d = 32 * pp + (gt >> 3), c = gt & 7;
+        *reinterpret_cast<u32x4 *>(slot_base + vt_lds_off(d, c)) = t.r[pp];
+      }
+    } else {
+      const int kq = gt >> 4, dc = gt & 15;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int d = 8 * dc + i;
+        *reinterpret_cast<u32x2 *>(slot_base + vt_lds_off(d, kq >> 1) + 8 * (kq & 1)) = column4(t, i);
       }
     }
   }
 };
 
+// Schedule ("ping-pong").  Waves 0-3 form group A and fetch K tiles, waves
+// 4-7 form group B and fetch V tiles; each SIMD runs one wave of each group.
+// A wave alternates two kinds of half-step, separated by workgroup barriers:
+//   GEMM(j):    O^T += V_{j-1}^T P_{j-1}^T   and   S_j^T = K_j Q^T    (MFMA)
+//   SOFTMAX(j): mask, running max, exponentials P_j, denominator      (VALU)
+// Group B runs half a step behind group A, so in every half-step one wave
+// of each SIMD feeds the matrix core while the other runs the softmax.
+// Half-step 2j:   A: fetch K_{j+1}; GEMM(j)   B: store V_j; SOFTMAX(j-1)
+// Half-step 2j+1: A: SOFTMAX(j); store K_{j+1} B: fetch V_{j+1}; GEMM(j)
+// K_j lives in K slot j%2 and V_j in V slot j%2; every store lands in a
+// slot whose previous tile was last read at least one barrier earlier.
 template <bool PAGED, bool CAUSAL>
 __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_per_wg,
                                                      int head_slices, int n_qblk) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  // K slots, V^T slots, then each wave's 32 query rows (8 KiB per wave).
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE + NW * QROWS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grp_a = wave < 4;
+  const int gt = tid & 255;   // thread index within its group
   const int lr = lane & 31;   // query column of this lane within the wave's 32 rows
   const int gq = lane >> 5;   // which 8-wide half of each 16-long K slice
 
@@ -230,31 +288,35 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   const int n_tiles = (wg_keys + BN - 1) / BN;
   const int wave_tiles = (wave_keys + BN - 1) / BN;
 
-  // ---- this wave's 32 query rows, held as the B operand of S^T = K Q^T ----
-  // Rows past the end read the last row (finite data) and are never stored.
+  // ---- this wave's 32 query rows, staged in its own LDS region ----------
+  // (swizzled like K) and read as the B operand of S^T = K Q^T during each
+  // GEMM half-step.  Rows past the end copy the last row (finite data) and
+  // are never stored.
   const int qrow = row0 + lr;
-  bf16x8 qf[8];
+  char *const qs = smem + 4 * TILE + wave * QROWS_BYTES;
   {
-    const int qr = min(qrow, p.Sq - 1);
-    const bf16 *src =
-        static_cast<const bf16 *>(p.q) + (((size_t)b * p.Sq + qr) * p.Hq + h) * HD + 8 * gq;
+    const int c = lane & 15;
+    const bf16 *qp = static_cast<const bf16 *>(p.q);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(ld_global_16(src + 16 * s));
-    // Consume Q here so its loads are complete before the tile loop; the
-    // loop then never waits on the memory counter before its QK^T MFMAs.
-#pragma unroll
-    for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(as_u32x4(qf[s])));
+    for (int i = 0; i < 8; ++i) {
+      const int r = (lane >> 4) + 4 * i;
+      const int qr = min(row0 + r, p.Sq - 1);
+      const u32x4 x = ld_global_16(qp + (((size_t)b * p.Sq + qr) * p.Hq + h) * HD + 8 * c);
+      *reinterpret_cast<u32x4 *>(qs + k_lds_off(r, c)) = x;
+    }
   }
+  const int qbase = (int)(qs - smem) + lr * 256;
+  const int qx = gq ^ (lr & 15);     // chunk 2s+gq of row lr sits at (2s ^ (qx & 14)) | (qx & 1)
 
-  // LDS operand addresses (stage 0).  K rows are read in a fixed permuted
+  // LDS operand addresses (slot 0).  K rows are read in a fixed permuted
   // order (bits 2 and 3 of the row swapped) so that the score registers land
   // directly in the B-operand order of P V; rows 32..63 sit 8 KiB further.
   // V^T rows 32*db + lr: the swizzle of row d+32 is that of row d with chunk
   // bit 2 flipped, so one address per chunk pair serves all four d blocks.
   const int krow = (lr & ~12) | ((lr & 4) << 1) | ((lr & 8) >> 1);
-  int ka[8], va[4];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) ka[s] = k_lds_off(krow, 2 * s + gq);
+  const int kbase = krow * 256;
+  const int kx = gq ^ (krow & 15);   // chunk 2s+gq lands at (2s ^ (kx & 14)) | (kx & 1)
+  int va[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) va[u] = vt_lds_off(lr, 2 * u + gq);
 
@@ -264,22 +326,54 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  bf16x8 pb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) pb[u] = bf16x8{};
   float m2 = -INFINITY;   // running max of this lane's row, log2 units
   float l_run = 0.f;      // lane-partial denominator (keys of this lane)
 
-  auto compute = [&](auto stage_tag, int j) {
-    constexpr int SOFF = decltype(stage_tag)::value * STAGE;
-    // ---- S^T = K Q^T over the 64-key tile (two 32-key halves) ------------
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+  // GEMM(j): P_{j-1} V_{j-1} into O, then S_j = K_j Q^T.
+  auto gemm = [&](int j) __attribute__((always_inline)) {
+    if (j >= 1 && j - 1 < wave_tiles) {
+      const int vso = ((j - 1) & 1) * TILE;
+      int vr[4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(smem + SOFF + ka[s]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(smem + SOFF + 8192 + ka[s]);
-      s0 = mfma_32x32x16(a0, qf[s], s0);
-      s1 = mfma_32x32x16(a1, qf[s], s1);
+      for (int u = 0; u < 4; ++u) vr[u] = opaque(va[u]) + vso;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(smem + 4096 * db +
+                                                             vr[u ^ (2 * (db & 1))]);
+          acc[db] = mfma_32x32x16(a, pb[u], acc[db]);
+        }
+      }
+      interleave_reads_with_mfma<16>();
     }
+    __builtin_amdgcn_sched_barrier(0);   // P is dead before S is produced
+    if (j < n_tiles && j < wave_tiles) {
+      const int kso = (j & 1) * TILE;
+      const int kb0 = opaque(kbase) + kso, kx0 = opaque(kx);
+      const int qb0 = opaque(qbase), qx0 = opaque(qx);
+      s0 = f32x16{};
+      s1 = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int ka = kb0 + ((2 * s) ^ kx0) * 16;
+        const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(smem + qb0 + ((2 * s) ^ qx0) * 16);
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(smem + ka);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(smem + 8192 + ka);
+        s0 = mfma_32x32x16(a0, qf, s0);
+        s1 = mfma_32x32x16(a1, qf, s1);
+      }
+      interleave_reads_with_mfma<24>();
+    }
+  };
 
-    // ---- mask: keys past the end, and (causal) keys after the query ------
+  // SOFTMAX(j): mask S_j, update the running max (lazily), P_j and l.
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    if (j >= wave_tiles) return;
     const int key0 = j * BN;
     const bool need_mask = (key0 + BN > n_keys) || (CAUSAL && key0 + BN - 1 > qoff + row0);
     if (need_mask) {
@@ -290,8 +384,6 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
         if (kk + 32 >= n_keys || (CAUSAL && kk + 32 > qpos)) s1[r] = -INFINITY;
       }
     }
-
-    // ---- online softmax statistics (lane-local + one exchange) -----------
     float mx = fmaxf(s0[0], s0[1]);
 #pragma unroll
     for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s0[r]);
@@ -309,8 +401,6 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
       for (int i = 0; i < 4; ++i) acc[i] *= alpha;
     }
     const float msc = (m2 == -INFINITY) ? 0.f : m2;
-
-    bf16x8 pb[4];
     float psum = 0.f;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -324,62 +414,75 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
       }
     }
     l_run += psum;
-
-    // ---- O^T += V^T P^T --------------------------------------------------
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(smem + SOFF + 4096 * db +
-                                                           va[u ^ (2 * (db & 1))]);
-        acc[db] = mfma_32x32x16(a, pb[u], acc[db]);
-      }
-    }
   };
 
-  // Paged: physical block of a tile, read one tile ahead of its data so the
-  // table lookup never stalls the data fetch.
-  const int32_t *table = PAGED ? p.block_table + ((size_t)b * p.Hkv + g) * p.max_blocks : nullptr;
-  auto block_of = [&](int tile) -> int {
+  // Paged: physical block of a tile, read one tile ahead of its data.  The
+  // id stays in a vector register until the fetch that needs it; only then is
+  // it made wave-uniform, so the lookup latency is never waited on early.
+  const int32_t *table =
+      PAGED ? p.block_table + ((size_t)b * p.Hkv + g) * p.max_blocks : nullptr;
+  auto block_of = [&](int tile) __attribute__((always_inline)) -> int {
     if constexpr (PAGED) return tile < p.max_blocks ? table[tile] : -1;
     return 0;
   };
-
-  // The looked-up id stays in a vector register until the fetch that needs
-  // it (one tile later); only then is it made wave-uniform, so the lookup's
-  // latency is never waited on right after it is issued.
-  auto uniform_block = [&](int v) -> int {
+  auto uniform_block = [&](int v) __attribute__((always_inline)) -> int {
     asm volatile("" : "+v"(v));
     return __builtin_amdgcn_readfirstlane(v);
   };
 
-  TileRegs tr;
-  int blk_next = block_of(0);
-  if (n_tiles > 0) {
-    TileIO<PAGED>::load(p, b, g, 0, uniform_block(blk_next), n_keys, tid, wave, tr);
-    blk_next = block_of(1);
-    TileIO<PAGED>::store(p, g, smem, tid, wave, tr);
-  }
-  __syncthreads();
-
-  // Two tiles per trip so each LDS stage offset is a compile-time constant.
-  for (int j = 0; j < n_tiles; j += 2) {
-    if (j + 1 < n_tiles) {
-      TileIO<PAGED>::load(p, b, g, j + 1, uniform_block(blk_next), n_keys, tid, wave, tr);
-      blk_next = block_of(j + 2);
+  // Each group runs its own copy of the loop (so each keeps only its own
+  // loop-invariant addresses live).  One trip is GEMM(j) then SOFTMAX(j), so
+  // S and the prefetched tile never cross the loop back-edge.  Group B starts
+  // one half-step later (storing V_0), and both groups execute exactly
+  // 2*n_tiles + 3 barriers, so the workgroup stays in step.
+  auto run_group = [&](auto is_a_tag) __attribute__((always_inline)) {
+    constexpr bool IS_A = decltype(is_a_tag)::value != 0;
+    TileRegs tr;
+    const TileOffsets to = TileIO<PAGED>::offsets(p, gt);
+    int blk_next = block_of(0);
+    if (n_tiles > 0) {
+      if constexpr (IS_A) {
+        TileIO<PAGED>::fetch_k(p, to, b, g, 0, uniform_block(blk_next), gt, tr);
+        TileIO<PAGED>::store_k(p, g, smem, gt, tr);
+      } else {
+        TileIO<PAGED>::fetch_v(p, to, b, g, 0, uniform_block(blk_next), n_keys, gt, tr);
+      }
+      blk_next = block_of(1);
     }
-    if (j < wave_tiles) compute(Int<0>{}, j);
-    if (j + 1 < n_tiles) TileIO<PAGED>::store(p, g, smem + STAGE, tid, wave, tr);
     __syncthreads();
-    if (j + 1 >= n_tiles) break;
-    if (j + 2 < n_tiles) {
-      TileIO<PAGED>::load(p, b, g, j + 2, uniform_block(blk_next), n_keys, tid, wave, tr);
-      blk_next = block_of(j + 3);
+    if constexpr (!IS_A) {
+      if (n_tiles > 0) TileIO<PAGED>::store_v(smem, gt, tr);   // V slot 0
+      __syncthreads();
     }
-    if (j + 1 < wave_tiles) compute(Int<1>{}, j + 1);
-    if (j + 2 < n_tiles) TileIO<PAGED>::store(p, g, smem, tid, wave, tr);
-    __syncthreads();
-  }
+#pragma clang loop unroll(disable)
+    for (int j = 0; j <= n_tiles; ++j) {
+      // GEMM half-step: issue the next tile's fetch, then P_{j-1}V_{j-1}, S_j.
+      if (j + 1 < n_tiles) {
+        if constexpr (IS_A)
+          TileIO<PAGED>::fetch_k(p, to, b, g, j + 1, uniform_block(blk_next), gt, tr);
+        else
+          TileIO<PAGED>::fetch_v(p, to, b, g, j + 1, uniform_block(blk_next), n_keys, gt, tr);
+        blk_next = block_of(j + 2);
+      }
+      gemm(j);
+      __syncthreads();
+      if (IS_A || j < n_tiles) {
+        // SOFTMAX half-step: P_j from S_j, then publish the fetched tile.
+        if (j < n_tiles) softmax(j);
+        if (j + 1 < n_tiles) {
+          if constexpr (IS_A)
+            TileIO<PAGED>::store_k(p, g, smem + ((j + 1) & 1) * TILE, gt, tr);
+          else
+            TileIO<PAGED>::store_v(smem + ((j + 1) & 1) * TILE, gt, tr);
+        }
+        __syncthreads();
+      }
+    }
+  };
+  if (grp_a)
+    run_group(Int<1>{});
+  else
+    run_group(Int<0>{});
 
   // ---- epilogue: divide by l once, store O (bf16) and LSE ----------------
   const float l_tot = l_run + wave_shfl_xor(l_run, 32);
