@@ -80,4 +80,72 @@ __device__ __forceinline__ u32x4 buf_load_16(__amdgpu_buffer_rsrc_t r, int voffs
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0));
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor as four words (for inline assembly operands).
+__device__ __forceinline__ u32x4 rsrc_words(const void *base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)bytes, 0x00020000u};
+}
+
+// Global -> LDS copy without registers: lane l's 16 bytes at buffer offset
+// `voffset` land at LDS address `lds_dst + 16 * l` (lds_dst wave-uniform).
+// Lanes whose range check fails write zeros.  Completion is tracked by the
+// wave's vector-memory counter only: a reader must wait_vmcnt() and then
+// pass a barrier before using the data.  Issued from inline assembly so
+// that the compiler does not also make every later LDS read wait for it.
+__device__ __forceinline__ void dma_to_lds_16(u32x4 rsrc, char *lds_dst, int voffset) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void *)lds_dst;
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %2, 0 offen lds"
+      :
+      : "v"(voffset), "s"(m0), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that neither waits for outstanding memory operations nor
+// lets the compiler move memory operations across it.  LDS written by the
+// DMA above is published by wait_vmcnt() + this barrier; LDS reads may stay
+// in flight across it.
+__device__ __forceinline__ void barrier_no_wait() { asm volatile("s_barrier" ::: "memory"); }
+
+// Transposing LDS read (16-bit elements).  Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte rows addressed by lanes
+// i/4, 4 + i/4, 8 + i/4 and 12 + i/4, in that order.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) i16x4 *)p));
+}
+
+// max / sum of x over the lane pair (l, l ^ 32).
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// acc + a.x + a.y for a pair of bf16 packed in one register (fp32 accumulate).
+__device__ __forceinline__ float add_bf16_pair(uint32_t a, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), one, acc, false);
+}
+
 }  // namespace lcat

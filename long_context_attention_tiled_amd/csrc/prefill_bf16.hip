@@ -14,6 +14,7 @@
 //    8 query heads each wave owns one query head and the same 32 query rows,
 //    so one K/V tile in LDS feeds 8 x 32 query rows.  Smaller groups stack
 //    query-row blocks instead; larger groups split over several workgroups.
+//    Each wave keeps its 32 query rows in registers for the whole kernel.
 //  * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on
 //    the M axis, its 32 queries on N).  In that layout a lane owns one query
 //    and 32 keys of a 64-key tile, so the row max and row sum are lane-local
@@ -22,12 +23,15 @@
 //  * O^T = V^T P^T is the second MFMA: the exponentiated scores are already
 //    in the B-operand layout once the K rows are read in a fixed permuted
 //    order (bits 2 and 3 of the row swapped), so P never goes through LDS.
-//    V is kept transposed in LDS (dimension-major) so its A-operand reads
-//    are 16-byte vectors.
-//  * The next K/V tile is fetched from HBM into registers while the current
-//    tile is computed, then written to the other half of a double buffer.
-//  * LDS rows are XOR-swizzled on 16-byte chunks so the MFMA operand reads
-//    and the tile writes avoid bank conflicts.
+//    The V^T operand is read from a key-major V tile with the transposing LDS
+//    read (ds_read_b64_tr_b16); paged V blocks are stored dimension-major
+//    and read directly.
+//  * K and V tiles move from HBM to LDS by buffer loads that write LDS
+//    directly (no register staging), into a ring of four slots per tensor,
+//    two tiles ahead of the tile being computed.
+//  * LDS rows are XOR-swizzled on 16-byte chunks so that MFMA operand reads
+//    hit distinct banks; the swizzle is applied by choosing which global
+//    chunk each lane of a DMA fetches.
 #include "device.h"
 #include "kernels.h"
 
@@ -38,35 +42,24 @@ constexpr int HD = 128;                 // head dimension
 constexpr int BN = 64;                  // keys per tile (= KV block)
 constexpr int NW = 8;                   // waves per workgroup
 constexpr int NT = NW * 64;             // threads per workgroup
-constexpr int TILE = BN * HD * 2;       // bytes of one K tile [64][128] or V^T tile [128][64]
+constexpr int TILE = BN * HD * 2;       // bytes of one K tile [64][128] or V tile
+constexpr int NSLOT = 4;                // ring slots per tensor
+constexpr int AHEAD = 2;                // tiles in flight ahead of the one computed
+constexpr int VBASE = NSLOT * TILE;     // V slots follow the K slots
+constexpr int DMA_PER_TILE = TILE / 1024 / 4;   // 1 KiB DMA instructions per wave per tile
+constexpr int NPRE = 8;                 // P V operands read before the barrier
+static_assert(AHEAD + 2 <= NSLOT, "a slot is refilled only after both groups finished with it");
+static_assert(DMA_PER_TILE == 4, "vmcnt waits below assume 4 DMA instructions per tile");
 
-// LDS: K slots 0/1 at [0, 2*TILE), V^T slots 0/1 at [2*TILE, 4*TILE).
-// Rows are XOR-swizzled on 16-byte chunks so that MFMA operand reads (8
-// rows, same chunk) and tile writes hit distinct banks.
-__device__ __forceinline__ int k_lds_off(int row, int chunk) {
-  return row * 256 + ((chunk ^ (row & 15)) << 4);
-}
-
-__device__ __forceinline__ int vt_lds_off(int d, int chunk) {
-  return 2 * TILE + d * 128 + ((chunk ^ (((d >> 1) ^ (d >> 3)) & 7)) << 4);
-}
-
-// Scheduling shape of a GEMM phase (NREADS LDS operand reads feeding 16
-// MFMAs): keep a few reads in flight ahead of the MFMA that consumes them
-// instead of hoisting all of them, which would cost many extra registers.
-template <int NREADS>
-__device__ __forceinline__ void interleave_reads_with_mfma() {
-  constexpr int per = NREADS / 16;   // reads issued per MFMA in steady state
-  __builtin_amdgcn_sched_group_barrier(0x100, 4 * per, 0);
-#pragma unroll
-  for (int i = 0; i < 12; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, per, 0);   // next DS read(s)
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-}
-
-constexpr int QROWS_BYTES = 32 * HD * 2;   // one wave's 32 query rows in LDS
+// K tile (and dense V tile): 64 key rows x 16 chunks of 8 dims (256 B rows).
+// Chunk c of K row r sits at position c ^ (r & 15): the 16 rows read by one
+// quarter-wave in the S = K Q^T operand read fall on distinct banks.
+__device__ __forceinline__ int k_pos(int row, int c) { return c ^ (row & 15); }
+// Dense V rows: chunk c of row r at c ^ 4*(r & 3).  A transposing read takes
+// 4 consecutive rows x 64 bytes per half-wave; this spreads them over all banks.
+__device__ __forceinline__ int vd_pos(int row, int c) { return c ^ ((row & 3) << 2); }
+// Paged V^T tile (dimension-major, 128 rows x 8 chunks of 8 keys, 128 B rows).
+__device__ __forceinline__ int vp_pos(int d, int c) { return c ^ (((d >> 1) ^ (d >> 3)) & 7); }
 
 // Online-softmax rescale threshold in log2 units.  The running maximum m is
 // only raised when a tile's maximum exceeds it by more than this, so most
@@ -75,163 +68,20 @@ constexpr int QROWS_BYTES = 32 * HD * 2;   // one wave's 32 query rows in LDS
 // the result is unchanged because O and l always share the same m.
 constexpr float kRescaleLog2 = 8.0f;
 
-struct TileRegs {
-  u32x4 r[4];
-  int ok;    // paged: block id was in range
-  int nv;    // paged: valid keys in this block
-  int tag;   // paged: global KV-head tag read from the block
-};
+typedef __attribute__((address_space(4))) const int32_t const_i32;
 
-// Gather the 16-bit lane `i` (0..7) of four 8 x bf16 vectors into 4 x bf16.
-__device__ __forceinline__ u32x2 column4(const TileRegs &t, int i) {
-  const int w = i >> 1;
-  u32x2 out;
-  if (i & 1) {
-    out.x = (t.r[0][w] >> 16) | (t.r[1][w] & 0xFFFF0000u);
-    out.y = (t.r[2][w] >> 16) | (t.r[3][w] & 0xFFFF0000u);
-  } else {
-    out.x = (t.r[0][w] & 0xFFFFu) | (t.r[1][w] << 16);
-    out.y = (t.r[2][w] & 0xFFFFu) | (t.r[3][w] << 16);
+// Zero the elements of an 8-key operand whose key index (key_first + e) is at
+// or past nv.  Used only on the last tile of a paged sequence, whose slots
+// past the key count may hold anything, including NaN.
+__device__ __forceinline__ bf16x8 mask_keys(bf16x8 a, int key_first, int nv) {
+  u32x4 w = as_u32x4(a);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int k = key_first + 2 * e;
+    w[e] &= (k < nv ? 0x0000FFFFu : 0u) | (k + 1 < nv ? 0xFFFF0000u : 0u);
   }
-  return out;
+  return as_bf16x8(w);
 }
-
-// Global -> register -> LDS movement of one 64-key tile by one group of four
-// waves (`gt` = thread index within the group, 0..255).  fetch_*() only issues
-// memory reads; store_*() runs a half-step later, so the fetch overlaps
-// compute.  Reads go through a buffer descriptor whose base is the tile's
-// first row (wave-uniform) and whose extent stops at the end of the tensor,
-// with per-lane byte offsets that are the same for every tile: rows past the
-// end of the tensor read as zero, rows past the key count belong to other
-// positions (finite data whose scores are masked to -inf, so their P is
-// exactly 0).  Paged slots past the key count are zeroed before they reach
-// LDS because they may hold anything, including NaN.
-struct TileOffsets {
-  int k[4];   // byte offsets of this thread's four K chunks within a tile
-  int v[4];   // byte offsets of this thread's four V chunks within a tile
-};
-
-template <bool PAGED>
-struct TileIO {
-  static __device__ __forceinline__ TileOffsets offsets(const PrefillParams &p, int gt) {
-    TileOffsets o;
-    if constexpr (PAGED) {
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        o.k[pp] = (16 * pp + (gt >> 4)) * (HD * 2) + 16 * (gt & 15);   // [64][128] block
-        o.v[pp] = (32 * pp + (gt >> 3)) * (BN * 2) + 16 * (gt & 7);    // [128][64] block
-      }
-    } else {
-      const int rs = p.Hkv * HD * 2;   // bytes between consecutive keys
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        o.k[pp] = (16 * pp + (gt >> 4)) * rs + 16 * (gt & 15);
-        o.v[pp] = (4 * (gt >> 4) + pp) * rs + 16 * (gt & 15);
-      }
-    }
-    return o;
-  }
-
-  // Descriptor over the tile starting at key tile*64 of (b, g) (dense), or
-  // over one 16 KiB block (paged).
-  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const PrefillParams &p,
-                                                                     const void *base, int b,
-                                                                     int g, int tile, int blk) {
-    if constexpr (PAGED) {
-      return make_rsrc(static_cast<const bf16 *>(base) + (size_t)blk * TILE / 2, TILE);
-    } else {
-      const size_t first = (((size_t)b * p.Sk + (size_t)tile * BN) * p.Hkv + g) * HD;
-      const size_t total = (size_t)p.B * p.Sk * p.Hkv * HD;
-      const size_t bytes = (total - first) * 2;
-      return make_rsrc(static_cast<const bf16 *>(base) + first,
-                       bytes > 0x7FFFFFFFu ? 0x7FFFFFFF : (int)bytes);
-    }
-  }
-
-  static __device__ __forceinline__ void fetch_k(const PrefillParams &p, const TileOffsets &o,
-                                                 int b, int g, int tile, int blk, int gt,
-                                                 TileRegs &t) {
-    int sblk = 0;
-    if constexpr (PAGED) {
-      t.ok = blk >= 0 && blk < p.n_blocks;
-      sblk = t.ok ? blk : 0;
-      t.tag = p.block_head[sblk];
-    }
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(p, p.k, b, g, tile, sblk);
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) t.r[pp] = buf_load_16(r, o.k[pp], 0);
-  }
-
-  static __device__ __forceinline__ void fetch_v(const PrefillParams &p, const TileOffsets &o,
-                                                 int b, int g, int tile, int blk, int n_keys,
-                                                 int gt, TileRegs &t) {
-    int sblk = 0;
-    if constexpr (PAGED) {
-      t.ok = blk >= 0 && blk < p.n_blocks;
-      sblk = t.ok ? blk : 0;
-      t.nv = n_keys - tile * BN;
-    }
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(p, p.v, b, g, tile, sblk);
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) t.r[pp] = buf_load_16(r, o.v[pp], 0);
-  }
-
-  static __device__ __forceinline__ void store_k(const PrefillParams &p, int g, char *slot, int gt_,
-                                                 TileRegs &t) {
-    const int gt = opaque(gt_);
-    if constexpr (PAGED) {
-      if (gt == 0 && p.dev_status) {
-        if (!t.ok)
-          p.dev_status[0] = 2;
-        else if (t.tag != p.kv_head_base + g)
-          p.dev_status[0] = 1;
-      }
-      if (!t.ok) {
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) t.r[pp] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const int row = 16 * pp + (gt >> 4), c = gt & 15;
-      *reinterpret_cast<u32x4 *>(slot + k_lds_off(row, c)) = t.r[pp];
-    }
-  }
-
-  // V^T slot: paged blocks are already dimension-major; dense tiles are
-  // transposed here (4 keys x 8 channels per thread -> 8 rows of 4 keys).
-  static __device__ __forceinline__ void store_v(char *slot_base, int gt_, TileRegs &t) {
-    const int gt = opaque(gt_);
-    if constexpr (PAGED) {
-      if (!t.ok) {
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) t.r[pp] = u32x4{0u, 0u, 0u, 0u};
-      }
-      if (t.nv < BN) {
-        const int c = gt & 7;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k0 = 8 * c + 2 * e;
-          const uint32_t keep = (k0 >= t.nv ? 0u : 0xFFFFu) | (k0 + 1 >= t.nv ? 0u : 0xFFFF0000u);
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) t.r[pp][e] &= keep;
-        }
-      }
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int d = 32 * pp + (gt >> 3), c = gt & 7;
-        *reinterpret_cast<u32x4 *>(slot_base + vt_lds_off(d, c)) = t.r[pp];
-      }
-    } else {
-      const int kq = gt >> 4, dc = gt & 15;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int d = 8 * dc + i;
-        *reinterpret_cast<u32x2 *>(slot_base + vt_lds_off(d, kq >> 1) + 8 * (kq & 1)) = column4(t, i);
-      }
-    }
-  }
-};
 
 // Schedule ("ping-pong").  Waves 0-3 form group A and fetch K tiles, waves
 // 4-7 form group B and fetch V tiles; each SIMD runs one wave of each group.
@@ -240,21 +90,23 @@ struct TileIO {
 //   SOFTMAX(j): mask, running max, exponentials P_j, denominator      (VALU)
 // Group B runs half a step behind group A, so in every half-step one wave
 // of each SIMD feeds the matrix core while the other runs the softmax.
-// Half-step 2j:   A: fetch K_{j+1}; GEMM(j)   B: store V_j; SOFTMAX(j-1)
-// Half-step 2j+1: A: SOFTMAX(j); store K_{j+1} B: fetch V_{j+1}; GEMM(j)
-// K_j lives in K slot j%2 and V_j in V slot j%2; every store lands in a
-// slot whose previous tile was last read at least one barrier earlier.
+//   half-step 2j:   A: fetch K_{j+2}; GEMM(j)     B: SOFTMAX(j-1); V_j ready
+//   half-step 2j+1: A: SOFTMAX(j); K_{j+1} ready  B: fetch V_{j+2}; GEMM(j)
+// "ready" = the fetching waves wait for their DMA and the next barrier
+// publishes the tile.  Tile t lives in slot t % 4 of its ring; a slot is
+// refilled two half-steps after its last reader finished.  At the end of
+// SOFTMAX(j) a wave already reads the first half of the V_j operands it
+// needs in GEMM(j+1), so they arrive while it waits at the barrier.
 template <bool PAGED, bool CAUSAL>
 __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_per_wg,
                                                      int head_slices, int n_qblk) {
-  // K slots, V^T slots, then each wave's 32 query rows (8 KiB per wave).
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE + NW * QROWS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool grp_a = wave < 4;
-  const int gt = tid & 255;   // thread index within its group
+  const int w4 = wave & 3;    // wave index within its group
   const int lr = lane & 31;   // query column of this lane within the wave's 32 rows
   const int gq = lane >> 5;   // which 8-wide half of each 16-long K slice
 
@@ -288,37 +140,49 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   const int n_tiles = (wg_keys + BN - 1) / BN;
   const int wave_tiles = (wave_keys + BN - 1) / BN;
 
-  // ---- this wave's 32 query rows, staged in its own LDS region ----------
-  // (swizzled like K) and read as the B operand of S^T = K Q^T during each
-  // GEMM half-step.  Rows past the end copy the last row (finite data) and
-  // are never stored.
+  // ---- this wave's 32 query rows -> registers (B operand of S^T = K Q^T) --
+  // qf[s] = dims 16s + 8gq .. +7 of query row row0 + lr.  Rows past the end
+  // repeat the last row (finite data) and are never stored.
   const int qrow = row0 + lr;
-  char *const qs = smem + 4 * TILE + wave * QROWS_BYTES;
+  bf16x8 qf[8];
   {
-    const int c = lane & 15;
-    const bf16 *qp = static_cast<const bf16 *>(p.q);
+    const int qr = min(qrow, p.Sq - 1);
+    const bf16 *qp = static_cast<const bf16 *>(p.q) + (((size_t)b * p.Sq + qr) * p.Hq + h) * HD;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (lane >> 4) + 4 * i;
-      const int qr = min(row0 + r, p.Sq - 1);
-      const u32x4 x = ld_global_16(qp + (((size_t)b * p.Sq + qr) * p.Hq + h) * HD + 8 * c);
-      *reinterpret_cast<u32x4 *>(qs + k_lds_off(r, c)) = x;
-    }
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(ld_global_16(qp + 16 * s + 8 * gq));
+#pragma unroll
+    for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(qf[s]));   // wait for Q here, not in the loop
   }
-  const int qbase = (int)(qs - smem) + lr * 256;
-  const int qx = gq ^ (lr & 15);     // chunk 2s+gq of row lr sits at (2s ^ (qx & 14)) | (qx & 1)
 
-  // LDS operand addresses (slot 0).  K rows are read in a fixed permuted
-  // order (bits 2 and 3 of the row swapped) so that the score registers land
-  // directly in the B-operand order of P V; rows 32..63 sit 8 KiB further.
-  // V^T rows 32*db + lr: the swizzle of row d+32 is that of row d with chunk
-  // bit 2 flipped, so one address per chunk pair serves all four d blocks.
+  // LDS operand addresses.  K rows are read in a fixed permuted order (bits
+  // 2 and 3 of the row swapped) so that the score registers land directly in
+  // the B-operand order of P V; rows 32..63 sit 8 KiB further.
   const int krow = (lr & ~12) | ((lr & 4) << 1) | ((lr & 8) >> 1);
   const int kbase = krow * 256;
   const int kx = gq ^ (krow & 15);   // chunk 2s+gq lands at (2s ^ (kx & 14)) | (kx & 1)
+  // V^T operand for (key step u, dim block db): dense tiles via transposing
+  // reads (two 8-byte reads per operand, at +4096u and +4096u+1024), paged
+  // V^T tiles via one 16-byte read of row 32db+lr.
   int va[4];
+  if constexpr (PAGED) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) va[u] = vt_lds_off(lr, 2 * u + gq);
+    for (int u = 0; u < 4; ++u) va[u] = lr * 128 + ((vp_pos(lr, 2 * u + gq)) << 4);
+  } else {
+    const int q4 = (lane >> 2) & 3;
+    const int r0 = 8 * (lane >> 5) + q4;
+    const int c0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) va[db] = r0 * 256 + 16 * (4 * (db ^ q4) + c0) + 8 * (lane & 1);
+  }
+  auto read_v = [&](int vslot, int u, int db) __attribute__((always_inline)) -> bf16x8 {
+    if constexpr (PAGED) {
+      return *reinterpret_cast<const bf16x8 *>(smem + vslot + va[u ^ (2 * (db & 1))] + 4096 * db);
+    } else {
+      const char *a = smem + vslot + va[db] + 4096 * u;
+      const u32x2 lo = lds_read_tr16(a), hi = lds_read_tr16(a + 1024);
+      return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+    }
+  };
 
   const float c2 = p.scale * kLog2e;   // scores -> log2 units
   const int qpos = qoff + qrow;
@@ -330,58 +194,55 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   bf16x8 pb[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) pb[u] = bf16x8{};
+  bf16x8 vpre[NPRE];
+#pragma unroll
+  for (int i = 0; i < NPRE; ++i) vpre[i] = bf16x8{};
   float m2 = -INFINITY;   // running max of this lane's row, log2 units
   float l_run = 0.f;      // lane-partial denominator (keys of this lane)
 
   // GEMM(j): P_{j-1} V_{j-1} into O, then S_j = K_j Q^T.
   auto gemm = [&](int j) __attribute__((always_inline)) {
     if (j >= 1 && j - 1 < wave_tiles) {
-      const int vso = ((j - 1) & 1) * TILE;
-      int vr[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) vr[u] = opaque(va[u]) + vso;
+      const int vslot = VBASE + ((j - 1) % NSLOT) * TILE;
+      const int nv = n_keys - (j - 1) * BN;   // valid keys in this tile
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(smem + 4096 * db +
-                                                             vr[u ^ (2 * (db & 1))]);
+          const int i = 4 * u + db;
+          bf16x8 a = i < NPRE ? vpre[i < NPRE ? i : 0] : read_v(vslot, u, db);
+          if (PAGED && nv < BN) a = mask_keys(a, 16 * u + 8 * gq, nv);
           acc[db] = mfma_32x32x16(a, pb[u], acc[db]);
         }
       }
-      interleave_reads_with_mfma<16>();
     }
     __builtin_amdgcn_sched_barrier(0);   // P is dead before S is produced
     if (j < n_tiles && j < wave_tiles) {
-      const int kso = (j & 1) * TILE;
-      const int kb0 = opaque(kbase) + kso, kx0 = opaque(kx);
-      const int qb0 = opaque(qbase), qx0 = opaque(qx);
+      const int kb0 = opaque(kbase) + (j % NSLOT) * TILE, kx0 = opaque(kx);
       s0 = f32x16{};
       s1 = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int ka = kb0 + ((2 * s) ^ kx0) * 16;
-        const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(smem + qb0 + ((2 * s) ^ qx0) * 16);
         const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(smem + ka);
         const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(smem + 8192 + ka);
-        s0 = mfma_32x32x16(a0, qf, s0);
-        s1 = mfma_32x32x16(a1, qf, s1);
+        s0 = mfma_32x32x16(a0, qf[s], s0);
+        s1 = mfma_32x32x16(a1, qf[s], s1);
       }
-      interleave_reads_with_mfma<24>();
     }
   };
 
   // SOFTMAX(j): mask S_j, update the running max (lazily), P_j and l.
   auto softmax = [&](int j) __attribute__((always_inline)) {
-    if (j >= wave_tiles) return;
     const int key0 = j * BN;
     const bool need_mask = (key0 + BN > n_keys) || (CAUSAL && key0 + BN - 1 > qoff + row0);
     if (need_mask) {
+      const int lim = CAUSAL ? min(n_keys - 1, qpos) : n_keys - 1;   // last visible key
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = key0 + 16 * (r >> 3) + 8 * gq + (r & 7);
-        if (kk >= n_keys || (CAUSAL && kk > qpos)) s0[r] = -INFINITY;
-        if (kk + 32 >= n_keys || (CAUSAL && kk + 32 > qpos)) s1[r] = -INFINITY;
+        if (kk > lim) s0[r] = -INFINITY;
+        if (kk + 32 > lim) s1[r] = -INFINITY;
       }
     }
     float mx = fmaxf(s0[0], s0[1]);
@@ -389,7 +250,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s0[r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    mx = pair_max32(mx);
     const float mx2 = mx * c2;
     const bool grow = mx2 > m2 + kRescaleLog2;
     if (__ballot(grow)) {
@@ -401,81 +262,120 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
       for (int i = 0; i < 4; ++i) acc[i] *= alpha;
     }
     const float msc = (m2 == -INFINITY) ? 0.f : m2;
-    float psum = 0.f;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p0 = fast_exp2(fmaf(s0[8 * u + e], c2, -msc));
-        const float p1 = fast_exp2(fmaf(s1[8 * u + e], c2, -msc));
-        psum += p0 + p1;
-        pb[u][e] = to_bf16(p0);
-        pb[2 + u][e] = to_bf16(p1);
+        pb[u][e] = to_bf16(fast_exp2(fmaf(s0[8 * u + e], c2, -msc)));
+        pb[2 + u][e] = to_bf16(fast_exp2(fmaf(s1[8 * u + e], c2, -msc)));
       }
     }
-    l_run += psum;
+    // l accumulates the bf16-rounded P, i.e. exactly the weights P V uses.
+    float psum = l_run;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 w = as_u32x4(pb[u]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) psum = add_bf16_pair(w[e], psum);
+    }
+    l_run = psum;
   };
 
-  // Paged: physical block of a tile, read one tile ahead of its data.  The
-  // id stays in a vector register until the fetch that needs it; only then is
-  // it made wave-uniform, so the lookup latency is never waited on early.
+  // First NPRE operands of P_j V_j, read while the wave waits at the barrier.
+  auto prefetch_v = [&](int j) __attribute__((always_inline)) {
+    const int vslot = VBASE + (j % NSLOT) * TILE;
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) vpre[i] = read_v(vslot, i / 4, i % 4);
+  };
+
+  // ---- tile fetch: this group's tensor, 4 DMA instructions per wave -------
+  // Instruction i of wave w4 fills LDS bytes [(4*w4 + i) KiB, +1 KiB) of the
+  // slot: key rows 16*w4 + 4i .. +3 (K, dense V) or dimension rows
+  // 32*w4 + 8i .. +7 (paged V^T).  Each lane picks the global chunk whose
+  // swizzled position is its own LDS position.
   const int32_t *table =
       PAGED ? p.block_table + ((size_t)b * p.Hkv + g) * p.max_blocks : nullptr;
   auto block_of = [&](int tile) __attribute__((always_inline)) -> int {
-    if constexpr (PAGED) return tile < p.max_blocks ? table[tile] : -1;
+    if constexpr (PAGED) return tile < p.max_blocks ? ((const const_i32 *)table)[tile] : -1;
     return 0;
   };
-  auto uniform_block = [&](int v) __attribute__((always_inline)) -> int {
-    asm volatile("" : "+v"(v));
-    return __builtin_amdgcn_readfirstlane(v);
-  };
 
-  // Each group runs its own copy of the loop (so each keeps only its own
-  // loop-invariant addresses live).  One trip is GEMM(j) then SOFTMAX(j), so
-  // S and the prefetched tile never cross the loop back-edge.  Group B starts
-  // one half-step later (storing V_0), and both groups execute exactly
-  // 2*n_tiles + 3 barriers, so the workgroup stays in step.
   auto run_group = [&](auto is_a_tag) __attribute__((always_inline)) {
     constexpr bool IS_A = decltype(is_a_tag)::value != 0;
-    TileRegs tr;
-    const TileOffsets to = TileIO<PAGED>::offsets(p, gt);
-    int blk_next = block_of(0);
-    if (n_tiles > 0) {
-      if constexpr (IS_A) {
-        TileIO<PAGED>::fetch_k(p, to, b, g, 0, uniform_block(blk_next), gt, tr);
-        TileIO<PAGED>::store_k(p, g, smem, gt, tr);
+    constexpr bool KEY_MAJOR = IS_A || !PAGED;
+    const int rs = PAGED ? HD * 2 : p.Hkv * HD * 2;   // bytes between key rows
+    int voff[DMA_PER_TILE];
+#pragma unroll
+    for (int i = 0; i < DMA_PER_TILE; ++i) {
+      if constexpr (KEY_MAJOR) {
+        const int r = 16 * w4 + 4 * i + (lane >> 4), pos = lane & 15;
+        voff[i] = r * rs + 16 * (IS_A ? k_pos(r, pos) : vd_pos(r, pos));
       } else {
-        TileIO<PAGED>::fetch_v(p, to, b, g, 0, uniform_block(blk_next), n_keys, gt, tr);
+        const int d = 32 * w4 + 8 * i + (lane >> 3), pos = lane & 7;
+        voff[i] = d * (BN * 2) + 16 * vp_pos(d, pos);
       }
-      blk_next = block_of(1);
     }
-    __syncthreads();
-    if constexpr (!IS_A) {
-      if (n_tiles > 0) TileIO<PAGED>::store_v(smem, gt, tr);   // V slot 0
-      __syncthreads();
+    char *const ring = smem + (IS_A ? 0 : VBASE) + w4 * 4096;
+    const bf16 *const src = static_cast<const bf16 *>(IS_A ? p.k : p.v);
+
+    auto issue = [&](int tile, int blk) __attribute__((always_inline)) {
+      u32x4 r;
+      if constexpr (PAGED) {
+        const bool ok = blk >= 0 && blk < p.n_blocks;
+        r = rsrc_words(src + (size_t)(ok ? blk : 0) * (TILE / 2), ok ? TILE : 0);
+        if (IS_A && w4 == 0 && lane == 0 && p.dev_status) {
+          if (!ok)
+            p.dev_status[0] = 2;
+          else if (((const const_i32 *)p.block_head)[blk] != p.kv_head_base + g)
+            p.dev_status[0] = 1;
+        }
+      } else {
+        // the range ends at key row Sk of this batch: later rows read as zero
+        const size_t first = (((size_t)b * p.Sk + (size_t)tile * BN) * p.Hkv + g) * HD;
+        const long long bytes = ((long long)(p.Sk - tile * BN) * p.Hkv - g) * HD * 2;
+        r = rsrc_words(src + first, bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes);
+      }
+      char *const dst = ring + (tile % NSLOT) * TILE;
+#pragma unroll
+      for (int i = 0; i < DMA_PER_TILE; ++i) dma_to_lds_16(r, dst + i * 1024, voff[i]);
+    };
+    // wait until tile t's DMA from this wave has landed (tiles issued later
+    // may stay in flight)
+    auto wait_tile = [&](int t) __attribute__((always_inline)) {
+      if (t + 1 < n_tiles)
+        wait_vmcnt<DMA_PER_TILE>();
+      else
+        wait_vmcnt<0>();
+    };
+
+    int blk_next = 0;
+    if (n_tiles > 0) {
+      issue(0, block_of(0));
+      if (n_tiles > 1) issue(1, block_of(1));
+      blk_next = block_of(AHEAD);
+      wait_tile(0);
     }
+    barrier_no_wait();
+    if constexpr (!IS_A) barrier_no_wait();   // half-step 0: nothing to do yet
 #pragma clang loop unroll(disable)
     for (int j = 0; j <= n_tiles; ++j) {
-      // GEMM half-step: issue the next tile's fetch, then P_{j-1}V_{j-1}, S_j.
-      if (j + 1 < n_tiles) {
-        if constexpr (IS_A)
-          TileIO<PAGED>::fetch_k(p, to, b, g, j + 1, uniform_block(blk_next), gt, tr);
-        else
-          TileIO<PAGED>::fetch_v(p, to, b, g, j + 1, uniform_block(blk_next), n_keys, gt, tr);
-        blk_next = block_of(j + 2);
+      // GEMM half-step
+      if (j + AHEAD < n_tiles) {
+        issue(j + AHEAD, blk_next);
+        blk_next = block_of(j + AHEAD + 1);
       }
       gemm(j);
-      __syncthreads();
+      barrier_no_wait();
       if (IS_A || j < n_tiles) {
-        // SOFTMAX half-step: P_j from S_j, then publish the fetched tile.
-        if (j < n_tiles) softmax(j);
-        if (j + 1 < n_tiles) {
-          if constexpr (IS_A)
-            TileIO<PAGED>::store_k(p, g, smem + ((j + 1) & 1) * TILE, gt, tr);
-          else
-            TileIO<PAGED>::store_v(smem + ((j + 1) & 1) * TILE, gt, tr);
+        // SOFTMAX half-step; then make the next tile ready and pre-read the
+        // first P V operands of this tile
+        if (j < n_tiles) {
+          if (j < wave_tiles) softmax(j);
+          if (PAGED) asm volatile("" ::"s"(blk_next));   // block id lands here, not later
+          wait_tile(j + 1);
+          if (NPRE > 0 && j < wave_tiles) prefetch_v(j);
         }
-        __syncthreads();
+        barrier_no_wait();
       }
     }
   };
@@ -485,7 +385,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     run_group(Int<0>{});
 
   // ---- epilogue: divide by l once, store O (bf16) and LSE ----------------
-  const float l_tot = l_run + wave_shfl_xor(l_run, 32);
+  const float l_tot = pair_sum32(l_run);
   if (qrow < p.Sq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     bf16 *op = static_cast<bf16 *>(p.o) + (((size_t)b * p.Sq + qrow) * p.Hq + h) * HD;
