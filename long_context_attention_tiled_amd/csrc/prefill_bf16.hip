@@ -43,13 +43,17 @@ constexpr int BN = 64;                  // keys per tile (= KV block)
 constexpr int NW = 8;                   // waves per workgroup
 constexpr int NT = NW * 64;             // threads per workgroup
 constexpr int TILE = BN * HD * 2;       // bytes of one K tile [64][128] or V tile
-constexpr int NSLOT = 4;                // ring slots per tensor
-constexpr int AHEAD = 2;                // tiles in flight ahead of the one computed
-constexpr int VBASE = NSLOT * TILE;     // V slots follow the K slots
-constexpr int DMA_PER_TILE = TILE / 1024 / 4;   // 1 KiB DMA instructions per wave per tile
-constexpr int NPRE = 8;                 // P V operands read before the barrier
-static_assert(AHEAD + 2 <= NSLOT, "a slot is refilled only after both groups finished with it");
-static_assert(DMA_PER_TILE == 4, "vmcnt waits below assume 4 DMA instructions per tile");
+constexpr int NKS = 4;                  // K ring slots
+constexpr int NVS = 4;                  // V ring slots (after the K slots)
+constexpr int KA = 4;                   // iteration j fetches K_{j+KA}
+constexpr int VA = 2;                   // iteration j fetches V_{j+VA}
+constexpr int NPV = 4;                  // P V operands read before the barrier
+constexpr int NPK = 4;                  // K Q^T operands read before the barrier
+// K_t is read (operands) from the end of iteration t-2 to iteration t-1 and
+// refilled by K_{t+NKS} in iteration t+NKS-KA; V_t is read from the end of
+// iteration t to iteration t+1 and refilled in iteration t+NVS-VA.
+static_assert(NKS - KA >= 0 && NVS - VA >= 2, "a slot is refilled only after its last reader");
+static_assert(TILE / 1024 == 2 * NW, "each wave moves two 1 KiB pieces of a tile");
 
 // K tile (and dense V tile): 64 key rows x 16 chunks of 8 dims (256 B rows).
 // Chunk c of K row r sits at position c ^ (r & 15): the 16 rows read by one
@@ -83,30 +87,31 @@ __device__ __forceinline__ bf16x8 mask_keys(bf16x8 a, int key_first, int nv) {
   return as_bf16x8(w);
 }
 
-// Schedule ("ping-pong").  Waves 0-3 form group A and fetch K tiles, waves
-// 4-7 form group B and fetch V tiles; each SIMD runs one wave of each group.
-// A wave alternates two kinds of half-step, separated by workgroup barriers:
-//   GEMM(j):    O^T += V_{j-1}^T P_{j-1}^T   and   S_j^T = K_j Q^T    (MFMA)
-//   SOFTMAX(j): mask, running max, exponentials P_j, denominator      (VALU)
-// Group B runs half a step behind group A, so in every half-step one wave
-// of each SIMD feeds the matrix core while the other runs the softmax.
-//   half-step 2j:   A: fetch K_{j+2}; GEMM(j)     B: SOFTMAX(j-1); V_j ready
-//   half-step 2j+1: A: SOFTMAX(j); K_{j+1} ready  B: fetch V_{j+2}; GEMM(j)
-// "ready" = the fetching waves wait for their DMA and the next barrier
-// publishes the tile.  Tile t lives in slot t % 4 of its ring; a slot is
-// refilled two half-steps after its last reader finished.  At the end of
-// SOFTMAX(j) a wave already reads the first half of the V_j operands it
-// needs in GEMM(j+1), so they arrive while it waits at the barrier.
+// Schedule (software pipelined within each wave).  Iteration j of a wave
+// interleaves three independent pieces of work in one instruction stream:
+//   O^T += V_{j-1}^T P_{j-1}^T      (16 MFMA, operands from the V ring)
+//   softmax of S_j -> P_j, m, l     (VALU: max, exp2, bf16 pack, row sum)
+//   S_{j+1}^T = K_{j+1} Q^T         (16 MFMA, operands from the K ring)
+// so the matrix core and the vector ALU of a SIMD are busy at the same time
+// in each wave (a wave can issue about four VALU instructions between two
+// back-to-back MFMAs for free).  All 8 waves run the same schedule and meet
+// at one barrier per iteration.
+// Tile movement: iteration j fetches K_{j+4} and V_{j+2} (each wave moves
+// 2 KiB of each tile); at its end every wave waits for the DMAs it issued in
+// iteration j-1, so after the barrier K_{j+3} and V_{j+1} are complete.
+// Each ring has four slots; a slot is refilled one iteration after its last
+// reader.  Before the barrier a wave already reads the first operands of
+// the next iteration (V_j for P_j V_j and K_{j+2} for S_{j+2}).
+// Tiles that need the causal/length mask, and the first and last
+// iterations, take a plain sequential path instead of the interleaved one.
 template <bool PAGED, bool CAUSAL>
 __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_per_wg,
                                                      int head_slices, int n_qblk) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TILE];
+  __shared__ __attribute__((aligned(1024))) char smem[(NKS + NVS) * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool grp_a = wave < 4;
-  const int w4 = wave & 3;    // wave index within its group
   const int lr = lane & 31;   // query column of this lane within the wave's 32 rows
   const int gq = lane >> 5;   // which 8-wide half of each 16-long K slice
 
@@ -154,12 +159,15 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(qf[s]));   // wait for Q here, not in the loop
   }
 
-  // LDS operand addresses.  K rows are read in a fixed permuted order (bits
-  // 2 and 3 of the row swapped) so that the score registers land directly in
-  // the B-operand order of P V; rows 32..63 sit 8 KiB further.
+  // ---- LDS operand addresses (within a slot) ------------------------------
+  // K rows are read in a fixed permuted order (bits 2 and 3 of the row
+  // swapped) so that the score registers land directly in the B-operand
+  // order of P V; rows 32..63 sit 8 KiB further.  K operand s (s = 0..7,
+  // dims 16s .. 16s+15) of half hf is at kaddr[s] + 8192 hf.
   const int krow = (lr & ~12) | ((lr & 4) << 1) | ((lr & 8) >> 1);
-  const int kbase = krow * 256;
-  const int kx = gq ^ (krow & 15);   // chunk 2s+gq lands at (2s ^ (kx & 14)) | (kx & 1)
+  int kaddr[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kaddr[s] = krow * 256 + (k_pos(krow, 2 * s + gq) << 4);
   // V^T operand for (key step u, dim block db): dense tiles via transposing
   // reads (two 8-byte reads per operand, at +4096u and +4096u+1024), paged
   // V^T tiles via one 16-byte read of row 32db+lr.
@@ -174,15 +182,23 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
 #pragma unroll
     for (int db = 0; db < 4; ++db) va[db] = r0 * 256 + 16 * (4 * (db ^ q4) + c0) + 8 * (lane & 1);
   }
-  auto read_v = [&](int vslot, int u, int db) __attribute__((always_inline)) -> bf16x8 {
+  // operand i = 4u + db of P V for the V tile in LDS slot `vs` (byte offset)
+  auto read_v = [&](int vs, int i) __attribute__((always_inline)) -> bf16x8 {
+    const int u = i >> 2, db = i & 3;
     if constexpr (PAGED) {
-      return *reinterpret_cast<const bf16x8 *>(smem + vslot + va[u ^ (2 * (db & 1))] + 4096 * db);
+      return *reinterpret_cast<const bf16x8 *>(smem + vs + va[u ^ (2 * (db & 1))] + 4096 * db);
     } else {
-      const char *a = smem + vslot + va[db] + 4096 * u;
+      const char *a = smem + vs + va[db] + 4096 * u;
       const u32x2 lo = lds_read_tr16(a), hi = lds_read_tr16(a + 1024);
       return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
     }
   };
+  // operand i = 2s + hf of S = K Q^T for the K tile in LDS slot `ks`
+  auto read_k = [&](int ks, int i) __attribute__((always_inline)) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8 *>(smem + ks + kaddr[i >> 1] + 8192 * (i & 1));
+  };
+  auto kslot = [](int t) { return (t % NKS) * TILE; };
+  auto vslot = [](int t) { return (NKS + t % NVS) * TILE; };
 
   const float c2 = p.scale * kLog2e;   // scores -> log2 units
   const int qpos = qoff + qrow;
@@ -190,68 +206,82 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
-  bf16x8 pb[4];
+  f32x16 S[2][2];        // S[parity][half]: scores of tile j in S[j & 1]
+  bf16x8 P[2][4];        // P[parity][u]:    probabilities of tile j in P[j & 1]
 #pragma unroll
-  for (int u = 0; u < 4; ++u) pb[u] = bf16x8{};
-  bf16x8 vpre[NPRE];
+  for (int a = 0; a < 2; ++a) {
+    S[a][0] = S[a][1] = f32x16{};
 #pragma unroll
-  for (int i = 0; i < NPRE; ++i) vpre[i] = bf16x8{};
+    for (int u = 0; u < 4; ++u) P[a][u] = bf16x8{};
+  }
+  bf16x8 vpre[NPV], kpre[NPK];   // operands read before the barrier
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) vpre[i] = bf16x8{};
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) kpre[i] = bf16x8{};
   float m2 = -INFINITY;   // running max of this lane's row, log2 units
   float l_run = 0.f;      // lane-partial denominator (keys of this lane)
 
-  // GEMM(j): P_{j-1} V_{j-1} into O, then S_j = K_j Q^T.
-  auto gemm = [&](int j) __attribute__((always_inline)) {
-    if (j >= 1 && j - 1 < wave_tiles) {
-      const int vslot = VBASE + ((j - 1) % NSLOT) * TILE;
-      const int nv = n_keys - (j - 1) * BN;   // valid keys in this tile
+  // ---- plain (sequential) pieces, used for edge iterations ----------------
+  auto pv_plain = [&](int t, const bf16x8 (&pp)[4]) __attribute__((always_inline)) {
+    const int vs = vslot(t);
+    const int nv = n_keys - t * BN;   // valid keys in this tile
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int i = 4 * u + db;
-          bf16x8 a = i < NPRE ? vpre[i < NPRE ? i : 0] : read_v(vslot, u, db);
-          if (PAGED && nv < BN) a = mask_keys(a, 16 * u + 8 * gq, nv);
-          acc[db] = mfma_32x32x16(a, pb[u], acc[db]);
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);   // P is dead before S is produced
-    if (j < n_tiles && j < wave_tiles) {
-      const int kb0 = opaque(kbase) + (j % NSLOT) * TILE, kx0 = opaque(kx);
-      s0 = f32x16{};
-      s1 = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int ka = kb0 + ((2 * s) ^ kx0) * 16;
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(smem + ka);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(smem + 8192 + ka);
-        s0 = mfma_32x32x16(a0, qf[s], s0);
-        s1 = mfma_32x32x16(a1, qf[s], s1);
-      }
+    for (int i = 0; i < 16; ++i) {
+      bf16x8 a = i < NPV ? vpre[i < NPV ? i : 0] : read_v(vs, i);
+      if (PAGED && nv < BN) a = mask_keys(a, 16 * (i >> 2) + 8 * gq, nv);
+      acc[i & 3] = mfma_32x32x16(a, pp[i >> 2], acc[i & 3]);
     }
   };
-
-  // SOFTMAX(j): mask S_j, update the running max (lazily), P_j and l.
-  auto softmax = [&](int j) __attribute__((always_inline)) {
-    const int key0 = j * BN;
+  auto s_plain = [&](int t, f32x16 (&sn)[2], bool use_pre) __attribute__((always_inline)) {
+    const int ks = kslot(t);
+    sn[0] = sn[1] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bf16x8 a = (i < NPK && use_pre) ? kpre[i < NPK ? i : 0] : read_k(ks, i);
+      sn[i & 1] = mfma_32x32x16(a, qf[i >> 1], sn[i & 1]);
+    }
+  };
+  // Row max of a score tile (tree of max3) and the lazily raised running max.
+  auto tile_max = [&](const f32x16 (&sc)[2]) __attribute__((always_inline)) -> float {
+    float t[11];
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      const int a = 3 * i, b2 = 3 * i + 1, c = 3 * i + 2;
+      t[i] = fmaxf(fmaxf(sc[a >> 4][a & 15], sc[b2 >> 4][b2 & 15]), sc[c >> 4][c & 15]);
+    }
+    t[10] = fmaxf(sc[1][14], sc[1][15]);
+    const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
+    const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(t[9], t[10]);
+    return pair_max32(fmaxf(fmaxf(u0, u1), fmaxf(u2, u3)));
+  };
+  // exp2 of half hf of the scores into P (bf16), returning the partial row sum
+  auto exp_half = [&](const f32x16 (&sc)[2], bf16x8 (&pc)[4], int hf, float msc,
+                      float psum) __attribute__((always_inline)) -> float {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pc[2 * hf + u][e] = to_bf16(fast_exp2(fmaf(sc[hf][8 * u + e], c2, -msc)));
+      const u32x4 w = as_u32x4(pc[2 * hf + u]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) psum = add_bf16_pair(w[e], psum);
+    }
+    return psum;
+  };
+  auto softmax_plain = [&](int t, f32x16 (&sc)[2], bf16x8 (&pc)[4]) __attribute__((always_inline)) {
+    const int key0 = t * BN;
     const bool need_mask = (key0 + BN > n_keys) || (CAUSAL && key0 + BN - 1 > qoff + row0);
     if (need_mask) {
       const int lim = CAUSAL ? min(n_keys - 1, qpos) : n_keys - 1;   // last visible key
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = key0 + 16 * (r >> 3) + 8 * gq + (r & 7);
-        if (kk > lim) s0[r] = -INFINITY;
-        if (kk + 32 > lim) s1[r] = -INFINITY;
+        if (kk > lim) sc[0][r] = -INFINITY;
+        if (kk + 32 > lim) sc[1][r] = -INFINITY;
       }
     }
-    float mx = fmaxf(s0[0], s0[1]);
-#pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s0[r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-    mx = pair_max32(mx);
-    const float mx2 = mx * c2;
+    const float mx2 = tile_max(sc) * c2;
     const bool grow = mx2 > m2 + kRescaleLog2;
     if (__ballot(grow)) {
       const float m_new = grow ? mx2 : m2;
@@ -262,127 +292,215 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
       for (int i = 0; i < 4; ++i) acc[i] *= alpha;
     }
     const float msc = (m2 == -INFINITY) ? 0.f : m2;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[u][e] = to_bf16(fast_exp2(fmaf(s0[8 * u + e], c2, -msc)));
-        pb[2 + u][e] = to_bf16(fast_exp2(fmaf(s1[8 * u + e], c2, -msc)));
-      }
-    }
-    // l accumulates the bf16-rounded P, i.e. exactly the weights P V uses.
-    float psum = l_run;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x4 w = as_u32x4(pb[u]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) psum = add_bf16_pair(w[e], psum);
-    }
-    l_run = psum;
+    l_run = exp_half(sc, pc, 1, msc, exp_half(sc, pc, 0, msc, l_run));
   };
 
-  // First NPRE operands of P_j V_j, read while the wave waits at the barrier.
-  auto prefetch_v = [&](int j) __attribute__((always_inline)) {
-    const int vslot = VBASE + (j % NSLOT) * TILE;
-#pragma unroll
-    for (int i = 0; i < NPRE; ++i) vpre[i] = read_v(vslot, i / 4, i % 4);
-  };
-
-  // ---- tile fetch: this group's tensor, 4 DMA instructions per wave -------
-  // Instruction i of wave w4 fills LDS bytes [(4*w4 + i) KiB, +1 KiB) of the
-  // slot: key rows 16*w4 + 4i .. +3 (K, dense V) or dimension rows
-  // 32*w4 + 8i .. +7 (paged V^T).  Each lane picks the global chunk whose
+  // ---- tile fetch: every wave moves 2 KiB of each K and V tile ------------
+  // DMA instruction i (0..1) of wave w fills LDS bytes [(2w + i) KiB, +1 KiB)
+  // of the slot: key rows 8w + 4i .. +3 (K, dense V) or dimension rows
+  // 16w + 8i .. +7 (paged V^T).  Each lane picks the global chunk whose
   // swizzled position is its own LDS position.
+  const int rs = PAGED ? HD * 2 : p.Hkv * HD * 2;   // bytes between key rows
+  int koff[2], voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * wave + 4 * i + (lane >> 4), pos = lane & 15;
+    koff[i] = r * rs + 16 * k_pos(r, pos);
+    if constexpr (PAGED) {
+      const int d = 16 * wave + 8 * i + (lane >> 3), pv = lane & 7;
+      voff[i] = d * (BN * 2) + 16 * vp_pos(d, pv);
+    } else {
+      voff[i] = r * rs + 16 * vd_pos(r, pos);
+    }
+  }
   const int32_t *table =
       PAGED ? p.block_table + ((size_t)b * p.Hkv + g) * p.max_blocks : nullptr;
   auto block_of = [&](int tile) __attribute__((always_inline)) -> int {
     if constexpr (PAGED) return tile < p.max_blocks ? ((const const_i32 *)table)[tile] : -1;
     return 0;
   };
-
-  auto run_group = [&](auto is_a_tag) __attribute__((always_inline)) {
-    constexpr bool IS_A = decltype(is_a_tag)::value != 0;
-    constexpr bool KEY_MAJOR = IS_A || !PAGED;
-    const int rs = PAGED ? HD * 2 : p.Hkv * HD * 2;   // bytes between key rows
-    int voff[DMA_PER_TILE];
-#pragma unroll
-    for (int i = 0; i < DMA_PER_TILE; ++i) {
-      if constexpr (KEY_MAJOR) {
-        const int r = 16 * w4 + 4 * i + (lane >> 4), pos = lane & 15;
-        voff[i] = r * rs + 16 * (IS_A ? k_pos(r, pos) : vd_pos(r, pos));
-      } else {
-        const int d = 32 * w4 + 8 * i + (lane >> 3), pos = lane & 7;
-        voff[i] = d * (BN * 2) + 16 * vp_pos(d, pos);
+  auto tile_rsrc = [&](const void *base, int tile, int blk, bool check) __attribute__((always_inline)) -> u32x4 {
+    const bf16 *src = static_cast<const bf16 *>(base);
+    if constexpr (PAGED) {
+      const bool ok = blk >= 0 && blk < p.n_blocks;
+      if (check && wave == 0 && lane == 0 && p.dev_status) {
+        if (!ok)
+          p.dev_status[0] = 2;
+        else if (((const const_i32 *)p.block_head)[blk] != p.kv_head_base + g)
+          p.dev_status[0] = 1;
       }
-    }
-    char *const ring = smem + (IS_A ? 0 : VBASE) + w4 * 4096;
-    const bf16 *const src = static_cast<const bf16 *>(IS_A ? p.k : p.v);
-
-    auto issue = [&](int tile, int blk) __attribute__((always_inline)) {
-      u32x4 r;
-      if constexpr (PAGED) {
-        const bool ok = blk >= 0 && blk < p.n_blocks;
-        r = rsrc_words(src + (size_t)(ok ? blk : 0) * (TILE / 2), ok ? TILE : 0);
-        if (IS_A && w4 == 0 && lane == 0 && p.dev_status) {
-          if (!ok)
-            p.dev_status[0] = 2;
-          else if (((const const_i32 *)p.block_head)[blk] != p.kv_head_base + g)
-            p.dev_status[0] = 1;
-        }
-      } else {
-        // the range ends at key row Sk of this batch: later rows read as zero
-        const size_t first = (((size_t)b * p.Sk + (size_t)tile * BN) * p.Hkv + g) * HD;
-        const long long bytes = ((long long)(p.Sk - tile * BN) * p.Hkv - g) * HD * 2;
-        r = rsrc_words(src + first, bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes);
-      }
-      char *const dst = ring + (tile % NSLOT) * TILE;
-#pragma unroll
-      for (int i = 0; i < DMA_PER_TILE; ++i) dma_to_lds_16(r, dst + i * 1024, voff[i]);
-    };
-    // wait until tile t's DMA from this wave has landed (tiles issued later
-    // may stay in flight)
-    auto wait_tile = [&](int t) __attribute__((always_inline)) {
-      if (t + 1 < n_tiles)
-        wait_vmcnt<DMA_PER_TILE>();
-      else
-        wait_vmcnt<0>();
-    };
-
-    int blk_next = 0;
-    if (n_tiles > 0) {
-      issue(0, block_of(0));
-      if (n_tiles > 1) issue(1, block_of(1));
-      blk_next = block_of(AHEAD);
-      wait_tile(0);
-    }
-    barrier_no_wait();
-    if constexpr (!IS_A) barrier_no_wait();   // half-step 0: nothing to do yet
-#pragma clang loop unroll(disable)
-    for (int j = 0; j <= n_tiles; ++j) {
-      // GEMM half-step
-      if (j + AHEAD < n_tiles) {
-        issue(j + AHEAD, blk_next);
-        blk_next = block_of(j + AHEAD + 1);
-      }
-      gemm(j);
-      barrier_no_wait();
-      if (IS_A || j < n_tiles) {
-        // SOFTMAX half-step; then make the next tile ready and pre-read the
-        // first P V operands of this tile
-        if (j < n_tiles) {
-          if (j < wave_tiles) softmax(j);
-          if (PAGED) asm volatile("" ::"s"(blk_next));   // block id lands here, not later
-          wait_tile(j + 1);
-          if (NPRE > 0 && j < wave_tiles) prefetch_v(j);
-        }
-        barrier_no_wait();
-      }
+      return rsrc_words(src + (size_t)(ok ? blk : 0) * (TILE / 2), ok ? TILE : 0);
+    } else {
+      // the range ends at key row Sk of this batch: later rows read as zero
+      const size_t first = (((size_t)b * p.Sk + (size_t)tile * BN) * p.Hkv + g) * HD;
+      const long long bytes = ((long long)(p.Sk - tile * BN) * p.Hkv - g) * HD * 2;
+      return rsrc_words(src + first, bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes);
     }
   };
-  if (grp_a)
-    run_group(Int<1>{});
-  else
-    run_group(Int<0>{});
+  auto issue_k = [&](int t, int blk) __attribute__((always_inline)) {
+    const u32x4 r = tile_rsrc(p.k, t, blk, true);
+    char *dst = smem + kslot(t) + wave * 2048;
+    dma_to_lds_16(r, dst, koff[0]);
+    dma_to_lds_16(r, dst + 1024, koff[1]);
+  };
+  auto issue_v = [&](int t, int blk) __attribute__((always_inline)) {
+    const u32x4 r = tile_rsrc(p.v, t, blk, false);
+    char *dst = smem + vslot(t) + wave * 2048;
+    dma_to_lds_16(r, dst, voff[0]);
+    dma_to_lds_16(r, dst + 1024, voff[1]);
+  };
+
+  // ---- prologue: K_0..K_3, V_0, V_1 in flight, S_0 -------------------------
+  for (int t = 0; t < KA && t < n_tiles; ++t) issue_k(t, block_of(t));
+  for (int t = 0; t < VA && t < n_tiles; ++t) issue_v(t, block_of(t));
+  int blk_k = block_of(KA), blk_v = block_of(VA);
+  wait_vmcnt<0>();
+  barrier_no_wait();
+  if (wave_tiles > 0) s_plain(0, S[0], false);
+  if (1 < wave_tiles) {
+#pragma unroll
+    for (int i = 0; i < NPK; ++i) kpre[i] = read_k(kslot(1), i);
+  }
+  // every wave is done with K_0 before iteration 0 refills its slot with K_KA
+  barrier_no_wait();
+
+  // Per-iteration tile fetch and the wait that publishes the previous
+  // iteration's tiles at this iteration's barrier.
+  auto fetch = [&](int j) __attribute__((always_inline)) -> int {
+    const bool fk = j + KA < n_tiles, fv = j + VA < n_tiles;
+    if (fk) issue_k(j + KA, blk_k);
+    if (fv) issue_v(j + VA, blk_v);
+    if (fk) blk_k = block_of(j + KA + 1);
+    if (fv) blk_v = block_of(j + VA + 1);
+    return 2 * (int)fk + 2 * (int)fv;   // DMA instructions issued by this wave
+  };
+  auto finish = [&](int j, int issued) __attribute__((always_inline)) {
+    // DMAs of iteration j-1 have landed (this iteration's may still fly)
+    if (issued == 4)
+      wait_vmcnt<4>();
+    else if (issued == 2)
+      wait_vmcnt<2>();
+    else
+      wait_vmcnt<0>();
+    if (PAGED) asm volatile("" ::"s"(blk_k), "s"(blk_v));   // block ids land here
+    // first operands of the next iteration, read while waiting at the barrier
+    if (j < wave_tiles) {
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) vpre[i] = read_v(vslot(j), i);
+    }
+    if (j + 2 < wave_tiles) {
+#pragma unroll
+      for (int i = 0; i < NPK; ++i) kpre[i] = read_k(kslot(j + 2), i);
+    }
+    barrier_no_wait();
+  };
+
+  // Interleaved iteration j (needs j >= 1, j + 1 < wave_tiles, no mask):
+  // P_{j-1} V_{j-1}, softmax(S_j) and S_{j+1} in one instruction stream.
+  auto fused = [&](int j, auto par_tag) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par_tag)::value;
+    f32x16 (&sc)[2] = S[PAR];
+    f32x16 (&sn)[2] = S[PAR ^ 1];
+    bf16x8 (&pc)[4] = P[PAR];
+    const bf16x8 (&pp)[4] = P[PAR ^ 1];
+    const int issued = fetch(j);
+    const int vs = vslot(j - 1), ks = kslot(j + 1);
+    // The iteration is written as 32 MFMA slots, each fenced off from the
+    // next: slot i issues MFMA i (16 of P V, then 16 of K Q^T), the LDS read
+    // of the operand used four slots later, and a fixed share of the
+    // softmax VALU work (the row max in slots 0-4, then the 16 bf16 pairs of
+    // P with their exp2, pack and row-sum steps spread over slots 5-30).
+    bf16x8 op[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      op[i] = vpre[i];
+      op[16 + i] = kpre[i];
+    }
+    float t[11], mxv = 0.f, alpha = 1.f, psum = 0.f;
+    bool grow = false;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int nx = i + 4;   // operand read in this slot
+      if (nx < 16)
+        op[nx] = read_v(vs, nx);
+      else if (nx >= 20 && nx < 32)
+        op[nx] = read_k(ks, nx - 16);
+      if (i == 16) sn[0] = sn[1] = f32x16{};
+      if (i < 16)
+        acc[i & 3] = mfma_32x32x16(op[i], pp[i >> 2], acc[i & 3]);
+      else
+        sn[i & 1] = mfma_32x32x16(op[i], qf[(i - 16) >> 1], sn[i & 1]);
+      // -- VALU share of slot i --
+      if (i < 3) {   // 11 partial maxima of three (two for the last) scores
+#pragma unroll
+        for (int q = 4 * i; q < 4 * i + 4 && q < 11; ++q) {
+          const int a = 3 * q, b2 = 3 * q + 1, c = 3 * q + 2;
+          t[q] = q < 10 ? fmaxf(fmaxf(sc[a >> 4][a & 15], sc[b2 >> 4][b2 & 15]), sc[c >> 4][c & 15])
+                        : fmaxf(sc[1][14], sc[1][15]);
+        }
+      } else if (i == 3) {
+        mxv = fmaxf(fmaxf(fmaxf(fmaxf(t[0], t[1]), t[2]), fmaxf(fmaxf(t[3], t[4]), t[5])),
+                    fmaxf(fmaxf(fmaxf(t[6], t[7]), t[8]), fmaxf(t[9], t[10])));
+      } else if (i == 4) {
+        const float mx2 = pair_max32(mxv) * c2;
+        grow = mx2 > m2 + kRescaleLog2;
+        const float m_new = grow ? mx2 : m2;
+        alpha = fast_exp2(m2 - m_new);   // 1 where the max did not move
+        m2 = m_new;
+        psum = l_run * alpha;
+      } else {
+#pragma unroll
+        for (int pr = 0; pr < 16; ++pr) {
+          if (i != 5 + (pr * 27) / 16) continue;
+          // pair pr = scores 2pr, 2pr+1 -> word (pr & 3) of P operand pr >> 2
+          const int hf = pr >> 3, r = 2 * (pr & 7), u = pr >> 2;
+          const float p0 = fast_exp2(fmaf(sc[hf][r], c2, -m2));
+          const float p1 = fast_exp2(fmaf(sc[hf][r + 1], c2, -m2));
+          pc[u][2 * (pr & 3)] = to_bf16(p0);
+          pc[u][2 * (pr & 3) + 1] = to_bf16(p1);
+          psum = add_bf16_pair(as_u32x4(pc[u])[pr & 3], psum);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run = psum;
+    // P_j and l are produced in this iteration, not sunk into the next one
+#pragma unroll
+    for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(pc[u]));
+    asm volatile("" ::"v"(l_run));
+    if (__ballot(grow)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= alpha;   // after P_{j-1} V_{j-1}
+    }
+    finish(j, issued);
+  };
+
+  // Plain iteration j: whatever of P_{j-1} V_{j-1}, softmax(S_j), S_{j+1}
+  // this wave still has, one after the other.
+  auto plain = [&](int j, auto par_tag) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par_tag)::value;
+    const int issued = fetch(j);
+    if (j >= 1 && j - 1 < wave_tiles) pv_plain(j - 1, P[PAR ^ 1]);
+    if (j < wave_tiles) softmax_plain(j, S[PAR], P[PAR]);
+    if (j + 1 < wave_tiles) s_plain(j + 1, S[PAR ^ 1], true);
+    finish(j, issued);
+  };
+
+  // Iterations 1 .. fused_end-1 need no mask and have all three parts.
+  int fused_end = min(n_keys / BN, wave_tiles - 1);
+  if (CAUSAL) fused_end = min(fused_end, (qoff + row0 + 1) / BN);
+  plain(0, Int<0>{});
+  int j = 1;
+#pragma clang loop unroll(disable)
+  for (; j + 1 < fused_end; j += 2) {
+    fused(j, Int<1>{});
+    fused(j + 1, Int<0>{});
+  }
+#pragma clang loop unroll(disable)
+  for (; j <= n_tiles; j += 2) {
+    plain(j, Int<1>{});
+    if (j + 1 <= n_tiles) plain(j + 1, Int<0>{});
+  }
 
   // ---- epilogue: divide by l once, store O (bf16) and LSE ----------------
   const float l_tot = pair_sum32(l_run);
