@@ -141,6 +141,27 @@ __device__ __forceinline__ float pair_sum32(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// max(a, b, c) / max(a, b) as single instructions.  fmaxf() first quiets
+// possible signalling NaNs in its inputs (one extra instruction per input
+// that comes straight from an MFMA); these skip that step and are meant for
+// finite scores.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float d;
+  asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+// max of x over the lane pair (l, l ^ 32), inputs assumed finite.
+__device__ __forceinline__ float pair_max32_raw(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return max_raw(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // acc + a.x + a.y for a pair of bf16 packed in one register (fp32 accumulate).
 __device__ __forceinline__ float add_bf16_pair(uint32_t a, float acc) {

@@ -43,16 +43,23 @@ constexpr int BN = 64;                  // keys per tile (= KV block)
 constexpr int NW = 8;                   // waves per workgroup
 constexpr int NT = NW * 64;             // threads per workgroup
 constexpr int TILE = BN * HD * 2;       // bytes of one K tile [64][128] or V tile
-constexpr int NKS = 4;                  // K ring slots
-constexpr int NVS = 4;                  // V ring slots (after the K slots)
-constexpr int KA = 4;                   // iteration j fetches K_{j+KA}
-constexpr int VA = 2;                   // iteration j fetches V_{j+VA}
+constexpr int WD = 1;                   // DMAs are waited for WD iterations after issue
+constexpr int KA = WD + 3;              // iteration j fetches K_{j+KA}
+constexpr int VA = WD + 1;              // iteration j fetches V_{j+VA}
+constexpr int NKS = KA;                 // K ring slots
+constexpr int NVS = VA + 2;             // V ring slots (after the K slots)
+constexpr int VBASE = NKS * TILE;       // LDS byte offset of the V ring
 constexpr int NPV = 4;                  // P V operands read before the barrier
 constexpr int NPK = 4;                  // K Q^T operands read before the barrier
-// K_t is read (operands) from the end of iteration t-2 to iteration t-1 and
-// refilled by K_{t+NKS} in iteration t+NKS-KA; V_t is read from the end of
-// iteration t to iteration t+1 and refilled in iteration t+NVS-VA.
-static_assert(NKS - KA >= 0 && NVS - VA >= 2, "a slot is refilled only after its last reader");
+// Every iteration issues 4 DMA instructions per wave; iteration j ends by
+// waiting for those issued in iteration j-WD and earlier, and the barrier
+// then publishes them.  K_t is read from the end of iteration t-2
+// (first operands) to iteration t-1, V_t from the end of iteration t to
+// iteration t+1; a slot is refilled (K_{t+NKS} in iteration t+NKS-KA,
+// V_{t+NVS} in iteration t+NVS-VA) only after its last reader's barrier.
+static_assert(KA >= WD + 3 && VA >= WD + 1, "tiles are published before their first read");
+static_assert(NKS >= KA && NVS >= VA + 2, "a slot is refilled only after its last reader");
+static_assert((NKS + NVS) * 16384 <= 160 * 1024, "LDS");
 static_assert(TILE / 1024 == 2 * NW, "each wave moves two 1 KiB pieces of a tile");
 
 // K tile (and dense V tile): 64 key rows x 16 chunks of 8 dims (256 B rows).
@@ -96,12 +103,12 @@ __device__ __forceinline__ bf16x8 mask_keys(bf16x8 a, int key_first, int nv) {
 // in each wave (a wave can issue about four VALU instructions between two
 // back-to-back MFMAs for free).  All 8 waves run the same schedule and meet
 // at one barrier per iteration.
-// Tile movement: iteration j fetches K_{j+4} and V_{j+2} (each wave moves
-// 2 KiB of each tile); at its end every wave waits for the DMAs it issued in
-// iteration j-1, so after the barrier K_{j+3} and V_{j+1} are complete.
-// Each ring has four slots; a slot is refilled one iteration after its last
-// reader.  Before the barrier a wave already reads the first operands of
-// the next iteration (V_j for P_j V_j and K_{j+2} for S_{j+2}).
+// Tile movement: iteration j fetches K_{j+KA} and V_{j+VA} (each wave moves
+// 2 KiB of each tile) and ends by waiting for the DMAs it issued WD
+// iterations earlier, so a tile has WD iterations to arrive.  A ring slot is
+// refilled one iteration after its last reader.  Before the barrier a wave
+// already reads the first operands of the next iteration (V_j for P_j V_j
+// and K_{j+2} for S_{j+2}).
 // Tiles that need the causal/length mask, and the first and last
 // iterations, take a plain sequential path instead of the interleaved one.
 template <bool PAGED, bool CAUSAL>
@@ -182,13 +189,19 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
 #pragma unroll
     for (int db = 0; db < 4; ++db) va[db] = r0 * 256 + 16 * (4 * (db ^ q4) + c0) + 8 * (lane & 1);
   }
-  // operand i = 4u + db of P V for the V tile in LDS slot `vs` (byte offset)
+  // The V ring starts at byte VBASE; keeping VBASE in the per-lane base
+  // registers leaves slot + operand offsets below 64 KiB, so every V read
+  // below is base register + immediate offset.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) va[i] = opaque(va[i] + VBASE);
+  // operand i = 4u + db of P V for the V tile in LDS slot `vs` (byte offset
+  // of the slot from the start of LDS)
   auto read_v = [&](int vs, int i) __attribute__((always_inline)) -> bf16x8 {
     const int u = i >> 2, db = i & 3;
     if constexpr (PAGED) {
-      return *reinterpret_cast<const bf16x8 *>(smem + vs + va[u ^ (2 * (db & 1))] + 4096 * db);
+      return *reinterpret_cast<const bf16x8 *>(smem + (vs - VBASE) + va[u ^ (2 * (db & 1))] + 4096 * db);
     } else {
-      const char *a = smem + vs + va[db] + 4096 * u;
+      const char *a = smem + (vs - VBASE) + va[db] + 4096 * u;
       const u32x2 lo = lds_read_tr16(a), hi = lds_read_tr16(a + 1024);
       return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
     }
@@ -197,8 +210,9 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   auto read_k = [&](int ks, int i) __attribute__((always_inline)) -> bf16x8 {
     return *reinterpret_cast<const bf16x8 *>(smem + ks + kaddr[i >> 1] + 8192 * (i & 1));
   };
-  auto kslot = [](int t) { return (t % NKS) * TILE; };
-  auto vslot = [](int t) { return (NKS + t % NVS) * TILE; };
+  // Ring slot byte offsets advance by one slot per iteration (no division).
+  auto next_k = [](int x) { return x + TILE == NKS * TILE ? 0 : x + TILE; };
+  auto next_v = [](int x) { return x + TILE == (NKS + NVS) * TILE ? NKS * TILE : x + TILE; };
 
   const float c2 = p.scale * kLog2e;   // scores -> log2 units
   const int qpos = qoff + qrow;
@@ -223,8 +237,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   float l_run = 0.f;      // lane-partial denominator (keys of this lane)
 
   // ---- plain (sequential) pieces, used for edge iterations ----------------
-  auto pv_plain = [&](int t, const bf16x8 (&pp)[4]) __attribute__((always_inline)) {
-    const int vs = vslot(t);
+  auto pv_plain = [&](int t, int vs, const bf16x8 (&pp)[4]) __attribute__((always_inline)) {
     const int nv = n_keys - t * BN;   // valid keys in this tile
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -233,8 +246,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
       acc[i & 3] = mfma_32x32x16(a, pp[i >> 2], acc[i & 3]);
     }
   };
-  auto s_plain = [&](int t, f32x16 (&sn)[2], bool use_pre) __attribute__((always_inline)) {
-    const int ks = kslot(t);
+  auto s_plain = [&](int ks, f32x16 (&sn)[2], bool use_pre) __attribute__((always_inline)) {
     sn[0] = sn[1] = f32x16{};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -319,92 +331,108 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     if constexpr (PAGED) return tile < p.max_blocks ? ((const const_i32 *)table)[tile] : -1;
     return 0;
   };
-  auto tile_rsrc = [&](const void *base, int tile, int blk, bool check) __attribute__((always_inline)) -> u32x4 {
-    const bf16 *src = static_cast<const bf16 *>(base);
+  // Tile sources.  Dense: a running descriptor per tensor whose range ends at
+  // key row Sk of this batch (later rows read as zero).  Paged: one block.
+  // Tiles at or past n_tiles get an empty range: their DMA reads nothing and
+  // writes zeros into a slot that is free anyway, so every iteration issues
+  // the same number of DMA instructions.
+  struct Stream {
+    const char *base;   // first byte of the next tile to fetch
+    int rows_left;      // key rows of this batch from there on (Sk - 64 tile)
+  };
+  const long long tstride = (long long)BN * p.Hkv * HD * 2;   // bytes per dense tile
+  auto dense_stream = [&](const void *t0) __attribute__((always_inline)) -> Stream {
+    const size_t first = (((size_t)b * p.Sk) * p.Hkv + g) * HD;
+    return Stream{static_cast<const char *>(t0) + first * 2, p.Sk};
+  };
+  Stream ks_stream = dense_stream(p.k), vs_stream = dense_stream(p.v);
+  auto issue = [&](Stream &st, int tile, int blk, int slot_off, const int (&off)[2],
+                   bool is_k) __attribute__((always_inline)) {
+    u32x4 r;
     if constexpr (PAGED) {
+      const bf16 *src = static_cast<const bf16 *>(is_k ? p.k : p.v);
       const bool ok = blk >= 0 && blk < p.n_blocks;
-      if (check && wave == 0 && lane == 0 && p.dev_status) {
+      if (is_k && tile < n_tiles && wave == 0 && lane == 0 && p.dev_status) {
         if (!ok)
           p.dev_status[0] = 2;
         else if (((const const_i32 *)p.block_head)[blk] != p.kv_head_base + g)
           p.dev_status[0] = 1;
       }
-      return rsrc_words(src + (size_t)(ok ? blk : 0) * (TILE / 2), ok ? TILE : 0);
+      r = rsrc_words(src + (size_t)(ok ? blk : 0) * (TILE / 2), ok && tile < n_tiles ? TILE : 0);
     } else {
-      // the range ends at key row Sk of this batch: later rows read as zero
-      const size_t first = (((size_t)b * p.Sk + (size_t)tile * BN) * p.Hkv + g) * HD;
-      const long long bytes = ((long long)(p.Sk - tile * BN) * p.Hkv - g) * HD * 2;
-      return rsrc_words(src + first, bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes);
+      // the range ends at key row Sk of this batch (later rows read as zero)
+      // or after the tile, whichever comes first
+      const int nb = tile < n_tiles ? (min(st.rows_left, BN) * p.Hkv - g) * (HD * 2) : 0;
+      r = rsrc_words(st.base, nb);
+      st.base += tstride;
+      st.rows_left -= BN;
     }
-  };
-  auto issue_k = [&](int t, int blk) __attribute__((always_inline)) {
-    const u32x4 r = tile_rsrc(p.k, t, blk, true);
-    char *dst = smem + kslot(t) + wave * 2048;
-    dma_to_lds_16(r, dst, koff[0]);
-    dma_to_lds_16(r, dst + 1024, koff[1]);
-  };
-  auto issue_v = [&](int t, int blk) __attribute__((always_inline)) {
-    const u32x4 r = tile_rsrc(p.v, t, blk, false);
-    char *dst = smem + vslot(t) + wave * 2048;
-    dma_to_lds_16(r, dst, voff[0]);
-    dma_to_lds_16(r, dst + 1024, voff[1]);
+    char *dst = smem + slot_off + wave * 2048;
+    dma_to_lds_16(r, dst, off[0]);
+    dma_to_lds_16(r, dst + 1024, off[1]);
   };
 
-  // ---- prologue: K_0..K_3, V_0, V_1 in flight, S_0 -------------------------
-  for (int t = 0; t < KA && t < n_tiles; ++t) issue_k(t, block_of(t));
-  for (int t = 0; t < VA && t < n_tiles; ++t) issue_v(t, block_of(t));
+  // ---- prologue: K_0..K_{KA-1}, V_0..V_{VA-1} in flight, then S_0 --------
+#pragma unroll
+  for (int t = 0; t < KA; ++t) issue(ks_stream, t, block_of(t), t * TILE, koff, true);
+#pragma unroll
+  for (int t = 0; t < VA; ++t) issue(vs_stream, t, block_of(t), (NKS + t) * TILE, voff, false);
   int blk_k = block_of(KA), blk_v = block_of(VA);
   wait_vmcnt<0>();
   barrier_no_wait();
-  if (wave_tiles > 0) s_plain(0, S[0], false);
+  if (wave_tiles > 0) s_plain(0, S[0], false);   // K_0 in slot 0
   if (1 < wave_tiles) {
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) kpre[i] = read_k(kslot(1), i);
+    for (int i = 0; i < NPK; ++i) kpre[i] = read_k(TILE, i);
   }
   // every wave is done with K_0 before iteration 0 refills its slot with K_KA
   barrier_no_wait();
 
-  // Per-iteration tile fetch and the wait that publishes the previous
-  // iteration's tiles at this iteration's barrier.
-  auto fetch = [&](int j) __attribute__((always_inline)) -> int {
-    const bool fk = j + KA < n_tiles, fv = j + VA < n_tiles;
-    if (fk) issue_k(j + KA, blk_k);
-    if (fv) issue_v(j + VA, blk_v);
-    if (fk) blk_k = block_of(j + KA + 1);
-    if (fv) blk_v = block_of(j + VA + 1);
-    return 2 * (int)fk + 2 * (int)fv;   // DMA instructions issued by this wave
+  // kc: K slot of tile j (= slot of K_{j+KA}, refilled in iteration j);
+  // vc: V slot of tile j-2 (= slot of V_{j+VA}, refilled in iteration j).
+  // The interleaved loop below uses the same positions as constants.
+  int kc = 0, vc = (NKS + NVS - 2) * TILE;
+  static_assert(NKS == KA && NVS == VA + 2, "slot bookkeeping below");
+  static_assert(NKS == 4 && NVS == 4, "the interleaved loop is unrolled over a 4-slot ring");
+
+  // Per-iteration tile fetch (4 DMA instructions per wave, always) into the
+  // given K and V slots, and the wait that publishes the tiles fetched WD
+  // iterations earlier, followed by the first operand reads of the next
+  // iteration (V_j and K_{j+2}, from the given slots).
+  auto fetch = [&](int j, int kdst, int vdst) __attribute__((always_inline)) {
+    issue(ks_stream, j + KA, blk_k, kdst, koff, true);
+    issue(vs_stream, j + VA, blk_v, vdst, voff, false);
+    blk_k = block_of(j + KA + 1);
+    blk_v = block_of(j + VA + 1);
   };
-  auto finish = [&](int j, int issued) __attribute__((always_inline)) {
-    // DMAs of iteration j-1 have landed (this iteration's may still fly)
-    if (issued == 4)
-      wait_vmcnt<4>();
-    else if (issued == 2)
-      wait_vmcnt<2>();
-    else
-      wait_vmcnt<0>();
+  auto finish = [&](int j, int v_next, int k_next2) __attribute__((always_inline)) {
+    wait_vmcnt<4 * WD>();   // DMAs of iterations j-WD+1 .. j may still fly
     if (PAGED) asm volatile("" ::"s"(blk_k), "s"(blk_v));   // block ids land here
-    // first operands of the next iteration, read while waiting at the barrier
     if (j < wave_tiles) {
 #pragma unroll
-      for (int i = 0; i < NPV; ++i) vpre[i] = read_v(vslot(j), i);
+      for (int i = 0; i < NPV; ++i) vpre[i] = read_v(v_next, i);
     }
     if (j + 2 < wave_tiles) {
 #pragma unroll
-      for (int i = 0; i < NPK; ++i) kpre[i] = read_k(kslot(j + 2), i);
+      for (int i = 0; i < NPK; ++i) kpre[i] = read_k(k_next2, i);
     }
     barrier_no_wait();
   };
 
   // Interleaved iteration j (needs j >= 1, j + 1 < wave_tiles, no mask):
   // P_{j-1} V_{j-1}, softmax(S_j) and S_{j+1} in one instruction stream.
-  auto fused = [&](int j, auto par_tag) __attribute__((always_inline)) {
+  // R = j % 4 is the ring position, so every LDS offset is a constant.
+  auto fused = [&](int j, auto par_tag, auto ring_tag) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
+    constexpr int R = decltype(ring_tag)::value;
     f32x16 (&sc)[2] = S[PAR];
     f32x16 (&sn)[2] = S[PAR ^ 1];
     bf16x8 (&pc)[4] = P[PAR];
     const bf16x8 (&pp)[4] = P[PAR ^ 1];
-    const int issued = fetch(j);
-    const int vs = vslot(j - 1), ks = kslot(j + 1);
+    constexpr int kdma = R * TILE, ks = ((R + 1) % NKS) * TILE, kpre_s = ((R + 2) % NKS) * TILE;
+    constexpr int vdma = (NKS + (R + VA) % NVS) * TILE, vs = (NKS + (R + NVS - 1) % NVS) * TILE,
+                  vpre_s = (NKS + R) * TILE;
+    fetch(j, kdma, vdma);
     // The iteration is written as 32 MFMA slots, each fenced off from the
     // next: slot i issues MFMA i (16 of P V, then 16 of K Q^T), the LDS read
     // of the operand used four slots later, and a fixed share of the
@@ -435,14 +463,14 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
 #pragma unroll
         for (int q = 4 * i; q < 4 * i + 4 && q < 11; ++q) {
           const int a = 3 * q, b2 = 3 * q + 1, c = 3 * q + 2;
-          t[q] = q < 10 ? fmaxf(fmaxf(sc[a >> 4][a & 15], sc[b2 >> 4][b2 & 15]), sc[c >> 4][c & 15])
-                        : fmaxf(sc[1][14], sc[1][15]);
+          t[q] = q < 10 ? max3_raw(sc[a >> 4][a & 15], sc[b2 >> 4][b2 & 15], sc[c >> 4][c & 15])
+                        : max_raw(sc[1][14], sc[1][15]);
         }
       } else if (i == 3) {
-        mxv = fmaxf(fmaxf(fmaxf(fmaxf(t[0], t[1]), t[2]), fmaxf(fmaxf(t[3], t[4]), t[5])),
-                    fmaxf(fmaxf(fmaxf(t[6], t[7]), t[8]), fmaxf(t[9], t[10])));
+        mxv = max3_raw(max3_raw(t[0], t[1], t[2]), max3_raw(t[3], t[4], t[5]),
+                       max3_raw(max3_raw(t[6], t[7], t[8]), t[9], t[10]));
       } else if (i == 4) {
-        const float mx2 = pair_max32(mxv) * c2;
+        const float mx2 = pair_max32_raw(mxv) * c2;
         grow = mx2 > m2 + kRescaleLog2;
         const float m_new = grow ? mx2 : m2;
         alpha = fast_exp2(m2 - m_new);   // 1 where the max did not move
@@ -472,30 +500,39 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] *= alpha;   // after P_{j-1} V_{j-1}
     }
-    finish(j, issued);
+    finish(j, vpre_s, kpre_s);
   };
 
   // Plain iteration j: whatever of P_{j-1} V_{j-1}, softmax(S_j), S_{j+1}
-  // this wave still has, one after the other.
+  // this wave still has, one after the other (ring positions at run time).
   auto plain = [&](int j, auto par_tag) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
-    const int issued = fetch(j);
-    if (j >= 1 && j - 1 < wave_tiles) pv_plain(j - 1, P[PAR ^ 1]);
+    const int vs = next_v(vc), ks = next_k(kc);   // V_{j-1}, K_{j+1}
+    fetch(j, kc, vc);
+    if (j >= 1 && j - 1 < wave_tiles) pv_plain(j - 1, vs, P[PAR ^ 1]);
     if (j < wave_tiles) softmax_plain(j, S[PAR], P[PAR]);
-    if (j + 1 < wave_tiles) s_plain(j + 1, S[PAR ^ 1], true);
-    finish(j, issued);
+    if (j + 1 < wave_tiles) s_plain(ks, S[PAR ^ 1], true);
+    finish(j, next_v(vs), next_k(ks));
+    kc = next_k(kc);
+    vc = next_v(vc);
   };
 
-  // Iterations 1 .. fused_end-1 need no mask and have all three parts.
+  // Iterations 1 .. fused_end-1 need no mask and have all three parts; the
+  // interleaved loop takes them four at a time (ring positions 1, 2, 3, 0).
   int fused_end = min(n_keys / BN, wave_tiles - 1);
   if (CAUSAL) fused_end = min(fused_end, (qoff + row0 + 1) / BN);
   plain(0, Int<0>{});
   int j = 1;
 #pragma clang loop unroll(disable)
-  for (; j + 1 < fused_end; j += 2) {
-    fused(j, Int<1>{});
-    fused(j + 1, Int<0>{});
+  for (; j + 3 < fused_end; j += 4) {
+    fused(j, Int<1>{}, Int<1>{});
+    fused(j + 1, Int<0>{}, Int<2>{});
+    fused(j + 2, Int<1>{}, Int<3>{});
+    fused(j + 3, Int<0>{}, Int<0>{});
   }
+  // back to run-time ring positions for the remaining iterations
+  kc = (j % NKS) * TILE;
+  vc = (NKS + (j + NVS - 2) % NVS) * TILE;
 #pragma clang loop unroll(disable)
   for (; j <= n_tiles; j += 2) {
     plain(j, Int<1>{});
