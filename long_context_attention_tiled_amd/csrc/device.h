@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace lcat {
 
 typedef __bf16 bf16;
@@ -21,6 +23,17 @@ template <int N>
 struct Int {
   static constexpr int value = N;
 };
+
+// f(Int<0>{}), f(Int<1>{}), ..., f(Int<N-1>{}): a loop whose index is a
+// constant expression in every step, independent of unrolling heuristics.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(Int<I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 constexpr float kLn2 = 0.6931471805599453f;
 
 // 32x32 output tile, K = 16 per instruction.  Operand lane layout (wave64):
@@ -95,6 +108,9 @@ __device__ __forceinline__ u32x4 rsrc_words(const void *base, int bytes) {
 // wave's vector-memory counter only: a reader must wait_vmcnt() and then
 // pass a barrier before using the data.  Issued from inline assembly so
 // that the compiler does not also make every later LDS read wait for it.
+// The statement declares no memory effects: it stays ordered with the other
+// volatile statements (the barrier, the counter waits), and callers only
+// target LDS that no wave reads before the next barrier.
 __device__ __forceinline__ void dma_to_lds_16(u32x4 rsrc, char *lds_dst, int voffset) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void *)lds_dst;
   asm volatile(
@@ -103,7 +119,7 @@ __device__ __forceinline__ void dma_to_lds_16(u32x4 rsrc, char *lds_dst, int vof
       "buffer_load_dwordx4 %0, %2, 0 offen lds"
       :
       : "v"(voffset), "s"(m0), "s"(rsrc)
-      : "memory", "m0");
+      : "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight

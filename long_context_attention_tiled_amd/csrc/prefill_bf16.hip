@@ -444,53 +444,72 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
       op[i] = vpre[i];
       op[16 + i] = kpre[i];
     }
-    float t[11], mxv = 0.f, alpha = 1.f, psum = 0.f;
+    float t[11], mxv = 0.f, alpha = 1.f, psum = 0.f, m_old = 0.f;
+    float xs[4][2];   // pairs in flight between the scale, exp2 and pack steps
     bool grow = false;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int nx = i + 4;   // operand read in this slot
-      if (nx < 16)
+    // pair pr of P (scores 2pr, 2pr+1 -> word pr & 3 of operand pr >> 2) is
+    // scaled and shifted in slot pair_slot(pr), exponentiated one slot later
+    // and packed and summed one slot after that, so that no step waits for
+    // the one before it inside a slot.
+    constexpr auto pair_at = [](int slot) constexpr -> int {   // pair whose first step is here
+      if (slot < 7) return -1;
+      const int k = slot - 7;
+      return k % 3 == 2 ? -1 : 2 * (k / 3) + (k % 3);
+    };
+    static_for<32>([&](auto slot_tag) __attribute__((always_inline)) {
+      constexpr int i = decltype(slot_tag)::value;
+      constexpr int nx = i + 4;   // operand read in this slot
+      if constexpr (nx < 16)
         op[nx] = read_v(vs, nx);
-      else if (nx >= 20 && nx < 32)
+      else if constexpr (nx >= 20 && nx < 32)
         op[nx] = read_k(ks, nx - 16);
-      if (i == 16) sn[0] = sn[1] = f32x16{};
-      if (i < 16)
+      if constexpr (i == 16) sn[0] = sn[1] = f32x16{};
+      if constexpr (i < 16)
         acc[i & 3] = mfma_32x32x16(op[i], pp[i >> 2], acc[i & 3]);
       else
         sn[i & 1] = mfma_32x32x16(op[i], qf[(i - 16) >> 1], sn[i & 1]);
       // -- VALU share of slot i --
-      if (i < 3) {   // 11 partial maxima of three (two for the last) scores
-#pragma unroll
-        for (int q = 4 * i; q < 4 * i + 4 && q < 11; ++q) {
-          const int a = 3 * q, b2 = 3 * q + 1, c = 3 * q + 2;
-          t[q] = q < 10 ? max3_raw(sc[a >> 4][a & 15], sc[b2 >> 4][b2 & 15], sc[c >> 4][c & 15])
-                        : max_raw(sc[1][14], sc[1][15]);
-        }
-      } else if (i == 3) {
+      if constexpr (i < 3) {   // 11 partial maxima of three (two for the last) scores
+        static_for<4>([&](auto q_tag) __attribute__((always_inline)) {
+          constexpr int q = 4 * i + decltype(q_tag)::value;
+          constexpr int a = 3 * q, b2 = 3 * q + 1, c = 3 * q + 2;
+          if constexpr (q < 10)
+            t[q] = max3_raw(sc[a >> 4][a & 15], sc[b2 >> 4][b2 & 15], sc[c >> 4][c & 15]);
+          else if constexpr (q == 10)
+            t[q] = max_raw(sc[1][14], sc[1][15]);
+        });
+      } else if constexpr (i == 3) {
         mxv = max3_raw(max3_raw(t[0], t[1], t[2]), max3_raw(t[3], t[4], t[5]),
                        max3_raw(max3_raw(t[6], t[7], t[8]), t[9], t[10]));
-      } else if (i == 4) {
+      } else if constexpr (i == 4) {
         const float mx2 = pair_max32_raw(mxv) * c2;
         grow = mx2 > m2 + kRescaleLog2;
-        const float m_new = grow ? mx2 : m2;
-        alpha = fast_exp2(m2 - m_new);   // 1 where the max did not move
-        m2 = m_new;
+        m_old = m2;
+        m2 = grow ? mx2 : m2;
+      } else if constexpr (i == 5) {
+        alpha = fast_exp2(m_old - m2);   // 1 where the max did not move
+      } else if constexpr (i == 6) {
         psum = l_run * alpha;
-      } else {
-#pragma unroll
-        for (int pr = 0; pr < 16; ++pr) {
-          if (i != 5 + (pr * 27) / 16) continue;
-          // pair pr = scores 2pr, 2pr+1 -> word (pr & 3) of P operand pr >> 2
-          const int hf = pr >> 3, r = 2 * (pr & 7), u = pr >> 2;
-          const float p0 = fast_exp2(fmaf(sc[hf][r], c2, -m2));
-          const float p1 = fast_exp2(fmaf(sc[hf][r + 1], c2, -m2));
-          pc[u][2 * (pr & 3)] = to_bf16(p0);
-          pc[u][2 * (pr & 3) + 1] = to_bf16(p1);
-          psum = add_bf16_pair(as_u32x4(pc[u])[pr & 3], psum);
-        }
+      }
+      constexpr int pa = pair_at(i), pb = pair_at(i - 1), pcx = pair_at(i - 2);
+      if constexpr (pa >= 0) {
+        constexpr int hf = pa >> 3, r = 2 * (pa & 7);
+        xs[pa & 3][0] = fmaf(sc[hf][r], c2, -m2);
+        xs[pa & 3][1] = fmaf(sc[hf][r + 1], c2, -m2);
+      }
+      if constexpr (pb >= 0) {
+        xs[pb & 3][0] = fast_exp2(xs[pb & 3][0]);
+        xs[pb & 3][1] = fast_exp2(xs[pb & 3][1]);
+      }
+      if constexpr (pcx >= 0) {
+        constexpr int u = pcx >> 2;
+        pc[u][2 * (pcx & 3)] = to_bf16(xs[pcx & 3][0]);
+        pc[u][2 * (pcx & 3) + 1] = to_bf16(xs[pcx & 3][1]);
+        psum = add_bf16_pair(as_u32x4(pc[u])[pcx & 3], psum);
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
+    static_assert(pair_at(7) == 0 && pair_at(29) == 15, "16 pairs in slots 7..29, packed by slot 31");
     l_run = psum;
     // P_j and l are produced in this iteration, not sunk into the next one
 #pragma unroll
