@@ -12,7 +12,9 @@ namespace {
 constexpr int kHeadDim = 128;
 constexpr int kBlockTokens = 64;
 constexpr int kDecodeRecord = 132;          // floats per decode split record
-constexpr int kDefaultSplitTokens = 1024;   // keys per decode split when 0 is passed
+// split_tokens == 0: the key ranges of all requests are shared out equally
+// among this many waves (two per SIMD of a 256-CU device).
+constexpr int kStreamWaves = 2048;
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -23,10 +25,6 @@ inline bool group_ok(int Hq, int Hkv) {
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return false;
   const int g = Hq / Hkv;
   return (g <= 8 && 8 % g == 0) || (g % 8 == 0);
-}
-
-inline int decode_split_tokens(int split_tokens) {
-  return split_tokens == 0 ? kDefaultSplitTokens : split_tokens;
 }
 
 inline long long decode_n_split(int max_blocks, int split_tokens) {
@@ -129,8 +127,9 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_blocks, int spl
   if (B < 0 || Hq <= 0 || D != kHeadDim || max_blocks <= 0 || split_tokens < 0 ||
       split_tokens % kBlockTokens)
     return 0;
-  const int st = decode_split_tokens(split_tokens);
-  return (size_t)B * Hq * decode_n_split(max_blocks, st) * kDecodeRecord * sizeof(float);
+  if (split_tokens == 0)   // at most kStreamWaves + B*Hkv pieces of group records
+    return ((size_t)kStreamWaves + B) * Hq * kDecodeRecord * sizeof(float);
+  return (size_t)B * Hq * decode_n_split(max_blocks, split_tokens) * kDecodeRecord * sizeof(float);
 }
 
 int attn_decode(const void *q, const void *k_pool, const void *v_pool, int n_blocks,
@@ -146,18 +145,18 @@ int attn_decode(const void *q, const void *k_pool, const void *v_pool, int n_blo
   if (!q || !k_pool || !v_pool || !block_head || !block_table || !ctx_len || !o)
     return ATTN_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return ATTN_ERR_ALIGN;
-  const int st = decode_split_tokens(split_tokens);
-  const size_t need = attn_decode_workspace_bytes(B, Hq, D, max_blocks, st);
+  const size_t need = attn_decode_workspace_bytes(B, Hq, D, max_blocks, split_tokens);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
-  const long long n_split = decode_n_split(max_blocks, st);
+  const long long n_split = split_tokens ? decode_n_split(max_blocks, split_tokens) : 0;
   if (n_split > 0x7FFFFFFFLL) return ATTN_ERR_UNSUPPORTED;
   lcat::DecodeParams p{};
   p.q = q; p.k_pool = k_pool; p.v_pool = v_pool;
   p.block_head = block_head; p.block_table = block_table; p.ctx_len = ctx_len;
   p.o = o; p.lse = lse; p.ws = static_cast<float *>(workspace); p.dev_status = dev_status;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_blocks = max_blocks; p.n_blocks = n_blocks;
-  p.kv_head_base = kv_head_base; p.split_tokens = st; p.n_split = (int)n_split;
+  p.kv_head_base = kv_head_base; p.split_tokens = split_tokens; p.n_split = (int)n_split;
+  p.stream_waves = split_tokens ? 0 : kStreamWaves;
   p.scale = scale;
   return hip_status(lcat::launch_decode(p, static_cast<hipStream_t>(stream)));
 }

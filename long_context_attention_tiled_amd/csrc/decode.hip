@@ -37,21 +37,14 @@ struct BlockRegs {
 
 constexpr int BLOCK_BYTES = BT * HD * 2;   // 16 KiB: one K block or one V block
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_split_kernel(
-    DecodeParams p) {
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+// Blocks j_begin .. j_begin+nblk-1 of (request b, KV head g), nblk >= 1;
+// `tail` keys (1..64) are valid in the last one.  Writes the unnormalised
+// (O, m, l) record of every query head of the group: head qi of the group at
+// rec0 + qi * head_stride (floats).
+__device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g, int j_begin,
+                                             int nblk, int tail, float *rec0,
+                                             size_t head_stride) {
   const int lane = threadIdx.x;
-  int ctx = p.ctx_len[b];
-  if (ctx > p.max_blocks * BT) {   // longer than the block table: flag and clamp
-    if (split == 0 && g == 0 && lane == 0 && p.dev_status) p.dev_status[0] = 2;
-    ctx = p.max_blocks * BT;
-  }
-  const int t_begin = split * p.split_tokens;
-  if (t_begin >= ctx) return;
-  const int t_end = min(ctx, t_begin + p.split_tokens);
-  const int j_begin = t_begin / BT;
-  const int nblk = (t_end - t_begin + BT - 1) / BT;
-  const int tail = t_end - t_begin - (nblk - 1) * BT;   // keys in the last block (1..64)
   const int group = p.Hq / p.Hkv;
   const int qi = lane & 15;   // query (head within the group) owned by this lane
   const int g4 = lane >> 4;   // 8-wide K slice of the MFMA operands
@@ -201,7 +194,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   l_run += wave_shfl_xor(l_run, 16);
   l_run += wave_shfl_xor(l_run, 32);
   if (qi < group) {
-    float *rec = p.ws + (((size_t)b * p.Hq + g * group + qi) * p.n_split + split) * REC;
+    float *rec = rec0 + (size_t)qi * head_stride;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4 *>(rec + 16 * dt + 4 * g4) = acc[dt];
     if (g4 == 0) {
@@ -211,30 +204,150 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   }
 }
 
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_split_kernel(
+    DecodeParams p) {
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  int ctx = p.ctx_len[b];
+  if (ctx > p.max_blocks * BT) {   // longer than the block table: flag and clamp
+    if (split == 0 && g == 0 && lane == 0 && p.dev_status) p.dev_status[0] = 2;
+    ctx = p.max_blocks * BT;
+  }
+  const int t_begin = split * p.split_tokens;
+  if (t_begin >= ctx) return;
+  const int t_end = min(ctx, t_begin + p.split_tokens);
+  const int nblk = (t_end - t_begin + BT - 1) / BT;
+  const int tail = t_end - t_begin - (nblk - 1) * BT;   // keys in the last block (1..64)
+  const int group = p.Hq / p.Hkv;
+  decode_range(p, b, g, t_begin / BT, nblk, tail,
+               p.ws + (((size_t)b * p.Hq + g * group) * p.n_split + split) * REC,
+               (size_t)p.n_split * REC);
+}
+
+// ---- stream split: equal shares of all (request, KV head, block) work -----
+//
+// The work of a launch is the sequence of segments s = b * Hkv + g (request
+// b, KV head g), each of nblk(b) blocks, laid end to end: W units in all.
+// Wave w of P takes units [w W / P, (w+1) W / P), which may start and end
+// inside segments and cover several of them; for each segment piece it
+// writes one record, at index w + s (pieces are ordered both by w and by s,
+// so w + s numbers them without gaps or collisions).  Every wave gets the
+// same number of blocks whatever the context lengths, so there is no tail of
+// long splits, and no workgroup is launched for an empty key range.
+
+// Blocks of request r: its context clamped to the block table, rounded up.
+__device__ __forceinline__ int request_blocks(const DecodeParams &p, int r) {
+  const int ctx = min(max(p.ctx_len[r], 0), p.max_blocks * BT);
+  return (ctx + BT - 1) / BT;
+}
+
+__device__ __forceinline__ long long wave_scan_incl(long long v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Units before request `target` (target may be B) and in total.
+__device__ __forceinline__ void unit_prefix(const DecodeParams &p, int target, long long &before,
+                                            long long &total) {
+  const int lane = threadIdx.x & 63;
+  before = 0;
+  total = 0;
+  for (int c = 0; c < p.B; c += 64) {
+    const int r = c + lane;
+    const long long u = r < p.B ? (long long)p.Hkv * request_blocks(p, r) : 0;
+    const long long incl = wave_scan_incl(u, lane);
+    if (target >= c && target < c + 64)
+      before = total + __shfl(incl - u, target - c, 64);   // exclusive sum at `target`
+    total += __shfl(incl, 63, 64);
+  }
+  if (target >= p.B) before = total;
+}
+
+// Request containing unit `pos` (< total) and the first unit of that request.
+__device__ __forceinline__ void locate_unit(const DecodeParams &p, long long pos, int &req,
+                                            long long &req_start) {
+  const int lane = threadIdx.x & 63;
+  long long off = 0;
+  req = p.B - 1;
+  req_start = 0;
+  for (int c = 0; c < p.B; c += 64) {
+    const int r = c + lane;
+    const long long u = r < p.B ? (long long)p.Hkv * request_blocks(p, r) : 0;
+    const long long incl = off + wave_scan_incl(u, lane);
+    const unsigned long long hit = __ballot(r < p.B && incl > pos);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      req = c + l;
+      req_start = __shfl(incl - u, l, 64);
+      return;
+    }
+    off = __shfl(incl, 63, 64);
+  }
+}
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_stream_kernel(
+    DecodeParams p) {
+  const int w = blockIdx.x, lane = threadIdx.x;
+  const int P = p.stream_waves;
+  if (w == 0 && p.dev_status) {   // contexts longer than the block table are flagged and clamped
+    for (int r = lane; r < p.B; r += 64)
+      if (p.ctx_len[r] > p.max_blocks * BT) p.dev_status[0] = 2;
+  }
+  long long before, W;
+  unit_prefix(p, p.B, before, W);
+  const long long st = W * w / P, en = W * (w + 1) / P;
+  if (st >= en) return;
+  int b;
+  long long req_start;
+  locate_unit(p, st, b, req_start);
+  const int group = p.Hq / p.Hkv;
+  long long pos = st;
+  while (pos < en && b < p.B) {
+    const int nb = request_blocks(p, b);
+    const long long req_end = req_start + (long long)p.Hkv * nb;
+    if (pos >= req_end) {   // next request (skips empty ones)
+      req_start = req_end;
+      ++b;
+      continue;
+    }
+    const long long off = pos - req_start;
+    const int g = (int)(off / nb), blk = (int)(off - (long long)g * nb);
+    const long long stop = min(en, req_start + (long long)(g + 1) * nb);
+    const int n = (int)(stop - pos);
+    const int ctx = min(max(p.ctx_len[b], 0), p.max_blocks * BT);
+    const int tail = (blk + n == nb) ? ctx - (nb - 1) * BT : BT;
+    const long long seg = (long long)b * p.Hkv + g;
+    decode_range(p, b, g, blk, n, tail, p.ws + (size_t)(w + seg) * group * REC, REC);
+    pos = stop;
+  }
+}
+
 // One workgroup (4 waves) per (request, query head).  Wave w folds splits
 // w, w+4, ... with lane l owning output channels 2l and 2l+1, then the four
 // partial sums are combined through LDS.
 constexpr int MERGE_WAVES = 4;
 
-__global__ __launch_bounds__(64 * MERGE_WAVES) void decode_merge_kernel(DecodeParams p) {
+// Merge of the records (pieces) of one (request, query head): the global
+// max M of the piece maxima, then O = sum w_i O_i / sum w_i l_i with
+// w_i = 2^(m_i - M).  `rec(i)` is the record of piece i (NULL: no record).
+template <class RecOf>
+__device__ __forceinline__ void merge_records(const DecodeParams &p, int b, int h, int n_pieces,
+                                              RecOf rec) {
   __shared__ float part[MERGE_WAVES][HD + 2];
   __shared__ float wmax[MERGE_WAVES];
-  const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ctx = min(p.ctx_len[b], p.max_blocks * BT);
   bf16 *o = static_cast<bf16 *>(p.o) + ((size_t)b * p.Hq + h) * HD;
-  if (ctx <= 0) {
-    if (tid < HD) o[tid] = to_bf16(0.f);
-    if (p.lse && tid == 0) p.lse[(size_t)b * p.Hq + h] = -INFINITY;
-    return;
-  }
-  const int ns = (ctx + p.split_tokens - 1) / p.split_tokens;
-  const float *rec = p.ws + ((size_t)b * p.Hq + h) * p.n_split * REC;
 
-  // global max of the split maxima
   float M = -INFINITY;
-  for (int s = tid; s < ns; s += 64 * MERGE_WAVES) M = fmaxf(M, rec[(size_t)s * REC + HD]);
+  for (int s = tid; s < n_pieces; s += 64 * MERGE_WAVES) {
+    const float *r = rec(s);
+    if (r) M = fmaxf(M, r[HD]);
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, wave_shfl_xor(M, off));
   if (lane == 0) wmax[wave] = M;
@@ -244,8 +357,9 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void decode_merge_kernel(DecodePa
   float n0 = 0.f, n1 = 0.f, den = 0.f;
   if (M != -INFINITY) {
 #pragma unroll 4
-    for (int s = wave; s < ns; s += MERGE_WAVES) {
-      const float *r = rec + (size_t)s * REC;
+    for (int s = wave; s < n_pieces; s += MERGE_WAVES) {
+      const float *r = rec(s);
+      if (!r) continue;
       const float ms = r[HD];
       const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
       const float2 ov = *reinterpret_cast<const float2 *>(r + 2 * lane);
@@ -271,10 +385,60 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void decode_merge_kernel(DecodePa
   }
 }
 
+__device__ __forceinline__ void write_empty(const DecodeParams &p, int b, int h) {
+  bf16 *o = static_cast<bf16 *>(p.o) + ((size_t)b * p.Hq + h) * HD;
+  if (threadIdx.x < HD) o[threadIdx.x] = to_bf16(0.f);
+  if (p.lse && threadIdx.x == 0) p.lse[(size_t)b * p.Hq + h] = -INFINITY;
+}
+
+// Fixed splits: records [b][h][split].
+__global__ __launch_bounds__(64 * MERGE_WAVES) void decode_merge_kernel(DecodeParams p) {
+  const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+  const int ctx = min(p.ctx_len[b], p.max_blocks * BT);
+  if (ctx <= 0) {
+    write_empty(p, b, h);
+    return;
+  }
+  const int ns = (ctx + p.split_tokens - 1) / p.split_tokens;
+  const float *rec = p.ws + ((size_t)b * p.Hq + h) * p.n_split * REC;
+  merge_records(p, b, h, ns, [&](int s) -> const float * { return rec + (size_t)s * REC; });
+}
+
+// Stream split: the pieces of segment s = b * Hkv + g come from waves
+// w_first .. w_last (those whose unit range meets the segment), record w + s.
+__global__ __launch_bounds__(64 * MERGE_WAVES) void decode_merge_stream_kernel(DecodeParams p) {
+  const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+  const int group = p.Hq / p.Hkv, g = h / group, qh = h - g * group;
+  const int nb = request_blocks(p, b);
+  if (nb == 0) {
+    write_empty(p, b, h);
+    return;
+  }
+  const long long P = p.stream_waves;
+  long long before, W;
+  unit_prefix(p, b, before, W);
+  const long long s0 = before + (long long)g * nb, s1 = s0 + nb;
+  const long long w_first = ((s0 + 1) * P - 1) / W, w_last = (s1 * P - 1) / W;
+  const long long seg = (long long)b * p.Hkv + g;
+  merge_records(p, b, h, (int)(w_last - w_first + 1), [&](int i) -> const float * {
+    const long long w = w_first + i;
+    if (W * w / P == W * (w + 1) / P) return nullptr;   // wave with no units
+    return p.ws + ((size_t)(w + seg) * group + qh) * REC;
+  });
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
   if (p.B <= 0) return hipSuccess;
+  if (p.stream_waves > 0) {
+    hipLaunchKernelGGL(decode_stream_kernel, dim3(p.stream_waves), dim3(64), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_stream_kernel, dim3(p.B * p.Hq), dim3(64 * MERGE_WAVES), 0,
+                       stream, p);
+    return hipGetLastError();
+  }
   dim3 g1(p.n_split, p.Hkv, p.B), b1(64);
   hipLaunchKernelGGL(decode_split_kernel, g1, b1, 0, stream, p);
   hipError_t e = hipGetLastError();

@@ -47,10 +47,11 @@ struct DecodeParams {
   const int32_t *ctx_len;
   void *o;                  // [B][Hq][128]
   float *lse;               // [B][Hq] or null
-  float *ws;                // [B][Hq][n_split][130]
+  float *ws;                // split records (132 floats each), see launch_decode
   int32_t *dev_status;
   int B, Hq, Hkv, max_blocks, n_blocks, kv_head_base;
-  int split_tokens, n_split;
+  int split_tokens, n_split;   // fixed splits (stream_waves == 0)
+  int stream_waves;            // > 0: equal-share split over this many waves
   float scale;
 };
 

@@ -246,6 +246,34 @@ def test_decode_batch_order_and_block_placement_invariance():
     assert torch.equal(o3, o) and torch.equal(lse3, lse)
 
 
+def test_decode_equal_share_split_crosses_requests():
+    """Automatic split: the blocks of all (request, KV head) segments are
+    shared out equally among a fixed number of waves, so one wave's range can
+    start and end inside segments and cover several; empty requests give
+    o = 0 and lse = -inf.  Checked against the oracle row by row and against
+    a fixed 256-key split of the same cache."""
+    ctx = [0, 1, 8192, 64, 3000, 0, 777, 5000, 4096, 65] * 4   # 2680 (request, head, block) units
+    log(f"decode equal-share split, {len(ctx)} requests")
+    c = synth.decode_cache(seed=604, B=len(ctx), ctx_lens=ctx, Hq=16, Hkv=2, extra_blocks=3)
+    args = [to_dev(c[k]) for k in ("q", "k_pool", "v_pool", "block_head", "block_table", "ctx_len")]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o, lse = lcat.attn_decode(*args, split_tokens=0, dev_status=st)
+    o2, lse2 = lcat.attn_decode(*args, split_tokens=256)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    nz = [i for i, n in enumerate(ctx) if n > 0]
+    z = [i for i, n in enumerate(ctx) if n == 0]
+    ref, ref_lse = oracle.decode_attention(c["q"][nz], [c["k_seq"][i] for i in nz],
+                                           [c["v_seq"][i] for i in nz], c["ctx_len"][nz], c["scale"])
+    got = to_np64(o)
+    got_lse = lse.cpu().numpy()
+    e, r = assert_attention_close(got[nz], ref, got_lse[nz], ref_lse, what="equal-share decode")
+    log(f"  max abs {e:.3g} rel-L2 {r:.3g}")
+    assert np.all(got[z] == 0.0) and np.all(np.isneginf(got_lse[z]))
+    assert np.abs(got - to_np64(o2)).max() <= 1.6e-2   # two bf16 roundings of the same O
+    assert np.abs(got_lse[nz] - lse2.cpu().numpy()[nz]).max() <= 1e-4
+
+
 def test_decode_bad_tag_and_block_are_reported():
     c = synth.decode_cache(seed=603, B=2, ctx_lens=[200, 100], Hq=16, Hkv=2)
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
