@@ -9,10 +9,12 @@ over the unmasked causal pairs only: 4*D*Hq*S*(S+1)/2 FLOP).
 The same JSON line also carries, each measured in this run:
   roofline        the prefill kernel's average duration from HIP events on
                   its stream, against the bf16 dense MFMA peak;
-  decode          split-K paged decode, 32 requests with contexts uniform in
-                  [8192, 131072], KV bytes per second against 8 TB/s;
+  decode          paged decode with the key blocks of all requests shared out
+                  equally over the GPU's waves, 32 requests with contexts
+                  uniform in [8192, 131072], KV bytes per second against 8 TB/s;
   relayout        sequence-shard -> head-shard relayout of one rank's share of
-                  [4][16384][64|8][128] bf16 Q/K/V, bytes per second;
+                  [4][16384][64|8][128] bf16 Q/K/V (one launch), bytes per second;
+The decode and relayout times are means over calls enqueued back to back.
   prefill_64k     the relayout + RoPE + causal prefill pipeline at 65536;
   chunked_prefill 4 requests x 131072 tokens in 8192-token chunks;
   cpu_baseline    the fp64 CPU oracle timed on a bounded sample of query rows
@@ -98,6 +100,21 @@ class EventTimer:
         return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
 
 
+def back_to_back_ms(torch, fn, iters):
+    """Mean GPU time of ``fn`` over ``iters`` calls enqueued back to back
+    between one pair of events (one untimed call first keeps the stream busy,
+    so host-side launch latency does not enter the measurement)."""
+    fn()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
 def dev_tensor(torch, a):
     t = torch.from_numpy(np.ascontiguousarray(a))
     if a.dtype == np.uint16:
@@ -165,13 +182,8 @@ def bench_decode(torch, lcat, synth, iters=20):
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     for _ in range(3):
         lcat.attn_decode(*args, workspace=ws, o=o, lse=lse)
-    timer = EventTimer(torch)
     torch.cuda.synchronize()
-    for _ in range(iters):
-        with timer:
-            lcat.attn_decode(*args, workspace=ws, o=o, lse=lse)
-    torch.cuda.synchronize()
-    ms = timer.mean_ms()
+    ms = back_to_back_ms(torch, lambda: lcat.attn_decode(*args, workspace=ws, o=o, lse=lse), iters)
     ctx_total = int(c["ctx_len"].sum())
     nbytes = ctx_total * c["Hkv"] * D * 2 * 2 + 2 * B * Hq * D * 2 + B * Hq * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -180,7 +192,7 @@ def bench_decode(torch, lcat, synth, iters=20):
                 workload="32 requests, ctx U[8192,131072], 16 Q / 2 KV heads, paged 64-token blocks")
 
 
-def bench_relayout_and_prefill_64k(torch, lcat, iters=10):
+def bench_relayout_and_prefill_64k(torch, lcat, iters=20):
     SP, S_loc, Hq_tot, Hkv_tot = 4, 16384, 64, 8
     S = SP * S_loc
     qin = seeded_normal_bf16(torch, (SP, S_loc, Hq_tot, D), 31)
@@ -190,20 +202,13 @@ def bench_relayout_and_prefill_64k(torch, lcat, iters=10):
     ko = torch.empty((S, Hkv_tot // SP, D), dtype=torch.bfloat16, device="cuda")
     vo = torch.empty_like(ko)
 
-    def relayout():
-        lcat.seq_to_head_permute(qin, 0, out=qo)
-        lcat.seq_to_head_permute(kin, 0, out=ko)
-        lcat.seq_to_head_permute(vin, 0, out=vo)
+    def relayout():   # Q, K and V of rank 0 in one launch
+        lcat.seq_to_head_permute_qkv(qin, kin, vin, 0, outs=(qo, ko, vo))
 
     for _ in range(3):
         relayout()
-    timer = EventTimer(torch)
     torch.cuda.synchronize()
-    for _ in range(iters):
-        with timer:
-            relayout()
-    torch.cuda.synchronize()
-    ms = timer.mean_ms()
+    ms = back_to_back_ms(torch, relayout, iters)
     nbytes = 2 * (qo.numel() + ko.numel() + vo.numel()) * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     relay = dict(ms=round(ms, 4), GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4),

@@ -166,6 +166,17 @@ int rope_apply(void *x, const int32_t *positions, int S, int H, int D, float bas
 int seq_to_head_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
                         int elem_bytes, void *stream);
 
+/*
+ * seq_to_head_permute_qkv — the same gather for the Q, K and V of one rank in
+ * a single launch ([ULY] §2.2: the exchange moves all three tensors of the
+ * attention input).  Q has Hq_tot heads, K and V have Hkv_tot heads; each of
+ * the three is laid out and copied exactly as seq_to_head_permute describes.
+ * No output may overlap any input or another output (ATTN_ERR_SHAPE).
+ */
+int seq_to_head_permute_qkv(const void *q_in, const void *k_in, const void *v_in, void *q_out,
+                            void *k_out, void *v_out, int SP, int S_loc, int Hq_tot, int Hkv_tot,
+                            int D, int rank, int elem_bytes, void *stream);
+
 /* Static, human-readable text for an attn_status value. */
 const char *attn_status_string(int status);
 

@@ -24,7 +24,8 @@ from ._lib import (ATTN_DEV_BAD_BLOCK, ATTN_DEV_BAD_TAG, ATTN_DEV_OK, ATTN_DTYPE
 
 __all__ = [
     "attn_prefill", "attn_chunked_prefill", "attn_kv_append", "attn_decode",
-    "attn_decode_workspace_bytes", "rope_apply", "seq_to_head_permute", "attn_status_string",
+    "attn_decode_workspace_bytes", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv",
+    "attn_status_string",
     "AttnError", "ATTN_DEV_OK", "ATTN_DEV_BAD_TAG", "ATTN_DEV_BAD_BLOCK", "load_library",
 ]
 
@@ -213,6 +214,35 @@ def rope_apply(x, positions, base=10000.0, stream=None):
     st = _lib.load().rope_apply(_ptr(x), _ptr(positions), S, H, D, float(base), _stream(stream))
     _lib.check("rope_apply", st)
     return x
+
+
+def seq_to_head_permute_qkv(q, k, v, rank, outs=None, stream=None):
+    """Relayout of Q, K and V (``[SP][S_loc][H][D]`` each, K and V with the
+    same head count) for ``rank`` in one launch; returns ``(q_out, k_out, v_out)``."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n)
+    SP, S_loc, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (SP, S_loc, Hkv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [SP][S_loc][Hkv][D] with q's SP, S_loc and D")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if Hq % SP or Hkv % SP:
+        raise ValueError("head counts must be divisible by SP")
+    if outs is None:
+        outs = (torch.empty((SP * S_loc, Hq // SP, D), dtype=q.dtype, device=q.device),
+                torch.empty((SP * S_loc, Hkv // SP, D), dtype=q.dtype, device=q.device),
+                torch.empty((SP * S_loc, Hkv // SP, D), dtype=q.dtype, device=q.device))
+    qo, ko, vo = outs
+    _need(qo, "q_out", q.dtype, (SP * S_loc, Hq // SP, D))
+    _need(ko, "k_out", q.dtype, (SP * S_loc, Hkv // SP, D))
+    _need(vo, "v_out", q.dtype, (SP * S_loc, Hkv // SP, D))
+    st = _lib.load().seq_to_head_permute_qkv(_ptr(q), _ptr(k), _ptr(v), _ptr(qo), _ptr(ko), _ptr(vo),
+                                             SP, S_loc, Hq, Hkv, D, int(rank), q.element_size(),
+                                             _stream(stream))
+    _lib.check("seq_to_head_permute_qkv", st)
+    return qo, ko, vo
 
 
 def seq_to_head_permute(x, rank, out=None, stream=None):

@@ -188,4 +188,39 @@ int seq_to_head_permute(const void *in, void *out, int SP, int S_loc, int H_tot,
                                          static_cast<hipStream_t>(stream)));
 }
 
+int seq_to_head_permute_qkv(const void *q_in, const void *k_in, const void *v_in, void *q_out,
+                            void *k_out, void *v_out, int SP, int S_loc, int Hq_tot, int Hkv_tot,
+                            int D, int rank, int elem_bytes, void *stream) {
+  if (SP <= 0 || S_loc < 0 || Hq_tot <= 0 || Hkv_tot <= 0 || D <= 0 || Hq_tot % SP ||
+      Hkv_tot % SP)
+    return ATTN_ERR_SHAPE;
+  if (rank < 0 || rank >= SP) return ATTN_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return ATTN_ERR_DTYPE;
+  if (S_loc == 0) return ATTN_OK;
+  const void *in[3] = {q_in, k_in, v_in};
+  void *out[3] = {q_out, k_out, v_out};
+  const int H[3] = {Hq_tot, Hkv_tot, Hkv_tot};
+  for (int t = 0; t < 3; ++t)
+    if (!in[t] || !out[t]) return ATTN_ERR_NULL;
+  // no output may overlap any input or another output
+  long long in_bytes[3], out_bytes[3];
+  for (int t = 0; t < 3; ++t) {
+    out_bytes[t] = (long long)SP * S_loc * (H[t] / SP) * D * elem_bytes;
+    in_bytes[t] = (long long)SP * S_loc * H[t] * D * elem_bytes;
+  }
+  auto disjoint = [](const void *a, long long na, const void *b, long long nb) {
+    const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+    return x + na <= y || y + nb <= x;
+  };
+  for (int t = 0; t < 3; ++t) {
+    for (int u = 0; u < 3; ++u) {
+      if (!disjoint(out[t], out_bytes[t], in[u], in_bytes[u])) return ATTN_ERR_SHAPE;
+      if (u != t && !disjoint(out[t], out_bytes[t], out[u], out_bytes[u])) return ATTN_ERR_SHAPE;
+    }
+  }
+  return hip_status(lcat::launch_permute_qkv(in, out, H, SP, S_loc, D, rank, elem_bytes,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -21,27 +21,42 @@ namespace {
 constexpr int NT = 256;
 constexpr int UPT = 4;   // 16-byte units per thread
 
-__global__ __launch_bounds__(NT) void permute16_kernel(const char *__restrict__ in,
-                                                       char *__restrict__ out, long long n_units,
-                                                       int units_per_run, int S_loc, int H_tot,
-                                                       int H_loc, int rank, long long row_bytes) {
-  const long long base = (long long)blockIdx.x * (NT * UPT) + threadIdx.x;
+// One tensor's relayout in 16-byte units: unit u of the output is unit
+// (u mod units_per_run) of run (u div units_per_run), whose source row is
+// that token's first local head.
+struct Permute16Job {
+  const char *in;
+  char *out;
+  long long n_units;
+  long long wg_begin;    // first workgroup of this job in the launch
+  long long row_bytes;   // bytes of one head row (D * elem_bytes)
+  int units_per_run;     // 16-byte units per token run (H_loc heads)
+  int H_tot, H_loc, rank;
+};
+
+// Up to three jobs (Q, K, V) in one launch; each workgroup belongs to one job.
+__global__ __launch_bounds__(NT) void permute16_kernel(Permute16Job j0, Permute16Job j1,
+                                                       Permute16Job j2) {
+  const long long wg = blockIdx.x;
+  const Permute16Job &j = wg >= j2.wg_begin ? j2 : (wg >= j1.wg_begin ? j1 : j0);
+  const long long base = (wg - j.wg_begin) * (NT * UPT) + threadIdx.x;
   u32x4 buf[UPT];
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const long long u = base + (long long)i * NT;
-    if (u < n_units) {
-      const long long tok = u / units_per_run;
-      const int w = (int)(u - tok * units_per_run);
-      const long long src = (tok * H_tot + (long long)rank * H_loc) * row_bytes + 16LL * w;
-      buf[i] = ld_global_16(in + src);
+    if (u < j.n_units) {
+      const long long tok = u / j.units_per_run;
+      const int w = (int)(u - tok * j.units_per_run);
+      const long long src = (tok * j.H_tot + (long long)j.rank * j.H_loc) * j.row_bytes + 16LL * w;
+      buf[i] = ld_global_16(j.in + src);
     }
   }
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const long long u = base + (long long)i * NT;
     // streaming store: the output is not read again by this kernel
-    if (u < n_units) __builtin_nontemporal_store(buf[i], reinterpret_cast<u32x4 *>(out + 16LL * u));
+    if (u < j.n_units)
+      __builtin_nontemporal_store(buf[i], reinterpret_cast<u32x4 *>(j.out + 16LL * u));
   }
 }
 
@@ -59,24 +74,33 @@ __global__ __launch_bounds__(NT) void permute_elem_kernel(const T *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
-                          int elem_bytes, hipStream_t stream) {
-  const int H_loc = H_tot / SP;
-  const long long n_tok = (long long)SP * S_loc;
+namespace {
+
+bool fits16(const void *in, const void *out, int H_loc, int D, int elem_bytes) {
   const long long run_bytes = (long long)H_loc * D * elem_bytes;
-  if (n_tok == 0 || run_bytes == 0) return hipSuccess;
-  const bool aligned16 = (reinterpret_cast<uintptr_t>(in) % 16 == 0) &&
-                         (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (run_bytes % 16 == 0) &&
-                         (((long long)D * elem_bytes) % 16 == 0);
-  if (aligned16) {
-    const long long n_units = n_tok * (run_bytes / 16);
-    const long long n_wg = (n_units + NT * UPT - 1) / (NT * UPT);
-    hipLaunchKernelGGL(permute16_kernel, dim3((unsigned)n_wg), dim3(NT), 0, stream,
-                       static_cast<const char *>(in), static_cast<char *>(out), n_units,
-                       (int)(run_bytes / 16), S_loc, H_tot, H_loc, rank,
-                       (long long)D * elem_bytes);
-    return hipGetLastError();
-  }
+  return (reinterpret_cast<uintptr_t>(in) % 16 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0) &&
+         (run_bytes % 16 == 0) && (((long long)D * elem_bytes) % 16 == 0);
+}
+
+Permute16Job make_job(const void *in, void *out, long long n_tok, int H_tot, int SP, int D,
+                      int rank, int elem_bytes, long long wg_begin) {
+  Permute16Job j{};
+  j.in = static_cast<const char *>(in);
+  j.out = static_cast<char *>(out);
+  j.H_tot = H_tot;
+  j.H_loc = H_tot / SP;
+  j.rank = rank;
+  j.row_bytes = (long long)D * elem_bytes;
+  j.units_per_run = (int)((long long)j.H_loc * D * elem_bytes / 16);
+  j.n_units = n_tok * j.units_per_run;
+  j.wg_begin = wg_begin;
+  return j;
+}
+
+long long job_wgs(const Permute16Job &j) { return (j.n_units + NT * UPT - 1) / (NT * UPT); }
+
+hipError_t launch_elem(const void *in, void *out, long long n_tok, int H_tot, int H_loc, int D,
+                       int rank, int elem_bytes, hipStream_t stream) {
   const long long n_elem = n_tok * H_loc * D;
   const unsigned n_wg = (unsigned)((n_elem + NT - 1) / NT);
   const int run_elems = H_loc * D;
@@ -102,6 +126,49 @@ hipError_t launch_permute(const void *in, void *out, int SP, int S_loc, int H_to
                          run_elems, H_tot, H_loc, rank, D);
       break;
   }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
+                          int elem_bytes, hipStream_t stream) {
+  const int H_loc = H_tot / SP;
+  const long long n_tok = (long long)SP * S_loc;
+  if (n_tok == 0 || (long long)H_loc * D == 0) return hipSuccess;
+  if (!fits16(in, out, H_loc, D, elem_bytes))
+    return launch_elem(in, out, n_tok, H_tot, H_loc, D, rank, elem_bytes, stream);
+  const Permute16Job j = make_job(in, out, n_tok, H_tot, SP, D, rank, elem_bytes, 0);
+  const long long n_wg = job_wgs(j);
+  Permute16Job none = j;
+  none.wg_begin = n_wg;   // never selected
+  hipLaunchKernelGGL(permute16_kernel, dim3((unsigned)n_wg), dim3(NT), 0, stream, j, none, none);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_qkv(const void *const in[3], void *const out[3], const int H_tot[3],
+                              int SP, int S_loc, int D, int rank, int elem_bytes,
+                              hipStream_t stream) {
+  const long long n_tok = (long long)SP * S_loc;
+  if (n_tok == 0 || D == 0) return hipSuccess;
+  bool all16 = true;
+  for (int t = 0; t < 3; ++t) all16 = all16 && fits16(in[t], out[t], H_tot[t] / SP, D, elem_bytes);
+  if (!all16) {
+    for (int t = 0; t < 3; ++t) {
+      const hipError_t e = launch_permute(in[t], out[t], SP, S_loc, H_tot[t], D, rank, elem_bytes,
+                                          stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  Permute16Job j[3];
+  long long wg = 0;
+  for (int t = 0; t < 3; ++t) {
+    j[t] = make_job(in[t], out[t], n_tok, H_tot[t], SP, D, rank, elem_bytes, wg);
+    wg += job_wgs(j[t]);
+  }
+  if (wg == 0) return hipSuccess;
+  hipLaunchKernelGGL(permute16_kernel, dim3((unsigned)wg), dim3(NT), 0, stream, j[0], j[1], j[2]);
   return hipGetLastError();
 }
 

@@ -42,7 +42,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["attn_prefill", "attn_chunked_prefill", "attn_decode", "attn_decode_workspace_bytes",
-              "attn_kv_append", "rope_apply", "seq_to_head_permute", "attn_status_string"]:
+              "attn_kv_append", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv",
+              "attn_status_string"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
 
@@ -142,6 +143,18 @@ def test_rope_and_permute_validation(lib):
     assert p(A16, NUL, 4, 16, 8, 128, 0, 2, S0) == NULL
     assert p(NUL, NUL, 4, 0, 8, 128, 0, 2, S0) == OK
     assert p(A16, P(0x10000 + 64), 4, 16, 8, 128, 0, 2, S0) == SHAPE   # overlapping buffers
+
+    f = lib.seq_to_head_permute_qkv
+    q, k, v = P(0x10000), P(0x20000000), P(0x40000000)
+    qo, ko, vo = P(0x60000000), P(0x80000000), P(0xA0000000)
+    assert f(q, k, v, qo, ko, vo, 4, 16, 6, 8, 128, 0, 2, S0) == SHAPE      # 6 % 4
+    assert f(q, k, v, qo, ko, vo, 4, 16, 8, 6, 128, 0, 2, S0) == SHAPE      # 6 % 4
+    assert f(q, k, v, qo, ko, vo, 4, 16, 8, 8, 128, 4, 2, S0) == SHAPE      # rank out of range
+    assert f(q, k, v, qo, ko, vo, 4, 16, 8, 8, 128, 0, 3, S0) == DTYPE
+    assert f(q, k, NUL, qo, ko, vo, 4, 16, 8, 8, 128, 0, 2, S0) == NULL
+    assert f(NUL, NUL, NUL, NUL, NUL, NUL, 4, 0, 8, 8, 128, 0, 2, S0) == OK
+    assert f(q, k, v, qo, P(0x60000000 + 64), vo, 4, 16, 8, 8, 128, 0, 2, S0) == SHAPE  # outputs overlap
+    assert f(q, k, v, qo, ko, P(0x40000000 + 64), 4, 16, 8, 8, 128, 0, 2, S0) == SHAPE  # output on an input
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -63,6 +63,23 @@ def _rope_ref_bits_close(got_bits, ref):
     assert frac > 0.99, f"only {frac:.4f} correctly rounded"
 
 
+@pytest.mark.parametrize("SP,S_loc,Hq,Hkv,D,dtype", [(4, 37, 64, 8, 128, np.uint16),
+                                                     (2, 5, 4, 2, 3, np.uint16),
+                                                     (8, 3, 16, 8, 4, np.float64)])
+def test_permute_qkv_bit_exact(SP, S_loc, Hq, Hkv, D, dtype):
+    """Q, K and V relayout in one launch equals three oracle relayouts; the
+    second and third shapes are not 16-byte runs (element path)."""
+    rng = np.random.default_rng(SP * 100 + S_loc)
+    mk = lambda H: rng.integers(0, 2 ** 16, size=(SP, S_loc, H, D)).astype(dtype)
+    qs, ks, vs = mk(Hq), mk(Hkv), mk(Hkv)
+    for rank in (0, SP - 1):
+        qo, ko, vo = lcat.seq_to_head_permute_qkv(to_dev(qs), to_dev(ks), to_dev(vs), rank)
+        torch.cuda.synchronize()
+        for got, x in ((qo, qs), (ko, ks), (vo, vs)):
+            g = bits(got) if got.dtype == torch.bfloat16 else got.cpu().numpy()
+            assert np.array_equal(g, oracle.permute(x, rank))
+
+
 def test_rope_matches_oracle_large_positions():
     S, H, D = 1000, 16, 128
     log("rope S=1000 H=16 positions up to 131k")
