@@ -51,7 +51,7 @@ constexpr int NVS = VA + 2;             // V ring slots (after the K slots)
 constexpr int VBASE = NKS * TILE;       // LDS byte offset of the V ring
 constexpr int NPV = 4;                  // P V operands read before the barrier
 constexpr int NPK = 4;                  // K Q^T operands read before the barrier
-// Every iteration issues 4 DMA instructions per wave; iteration j ends by
+// Every iteration issues the same DMA count per DMA wave; iteration j ends by
 // waiting for those issued in iteration j-WD and earlier, and the barrier
 // then publishes them.  K_t is read from the end of iteration t-2
 // (first operands) to iteration t-1, V_t from the end of iteration t to
@@ -60,7 +60,11 @@ constexpr int NPK = 4;                  // K Q^T operands read before the barrie
 static_assert(KA >= WD + 3 && VA >= WD + 1, "tiles are published before their first read");
 static_assert(NKS >= KA && NVS >= VA + 2, "a slot is refilled only after its last reader");
 static_assert((NKS + NVS) * 16384 <= 160 * 1024, "LDS");
-static_assert(TILE / 1024 == 2 * NW, "each wave moves two 1 KiB pieces of a tile");
+// Waves that issue the tile DMAs: the four older ones in the dense causal
+// kernel (see the fetch below); all eight, two 1 KiB pieces each, in the
+// variants whose registers are tighter (paged, non-causal).
+template <bool PAGED, bool CAUSAL>
+constexpr int dma_waves() { return (!PAGED && CAUSAL) ? 4 : 8; }
 
 // K tile (and dense V tile): 64 key rows x 16 chunks of 8 dims (256 B rows).
 // Chunk c of K row r sits at position c ^ (r & 15): the 16 rows read by one
@@ -103,8 +107,8 @@ __device__ __forceinline__ bf16x8 mask_keys(bf16x8 a, int key_first, int nv) {
 // in each wave (a wave can issue about four VALU instructions between two
 // back-to-back MFMAs for free).  All 8 waves run the same schedule and meet
 // at one barrier per iteration.
-// Tile movement: iteration j fetches K_{j+KA} and V_{j+VA} (each wave moves
-// 2 KiB of each tile) and ends by waiting for the DMAs it issued WD
+// Tile movement: iteration j fetches K_{j+KA} and V_{j+VA} (the DMA waves
+// share each tile) and ends by waiting for the DMAs it issued WD
 // iterations earlier, so a tile has WD iterations to arrive.  A ring slot is
 // refilled one iteration after its last reader.  Before the barrier a wave
 // already reads the first operands of the next iteration (V_j for P_j V_j
@@ -307,19 +311,25 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     l_run = exp_half(sc, pc, 1, msc, exp_half(sc, pc, 0, msc, l_run));
   };
 
-  // ---- tile fetch: every wave moves 2 KiB of each K and V tile ------------
-  // DMA instruction i (0..1) of wave w fills LDS bytes [(2w + i) KiB, +1 KiB)
-  // of the slot: key rows 8w + 4i .. +3 (K, dense V) or dimension rows
-  // 16w + 8i .. +7 (paged V^T).  Each lane picks the global chunk whose
+  // ---- tile fetch: NDW waves move 16/NDW KiB of each K and V tile ---------
+  // With NDW = 4 only the older wave of each SIMD (waves w and w+4 share one)
+  // issues DMAs: it wins issue arbitration and finishes its MFMA slots
+  // first, so it fetches while the younger one starts computing.  DMA
+  // instruction i of wave w fills LDS bytes [(DPW w + i) KiB, +1 KiB) of the
+  // slot: key rows 4 (DPW w + i) .. +3 (K, dense V) or dimension rows
+  // 8 (DPW w + i) .. +7 (paged V^T).  Each lane picks the global chunk whose
   // swizzled position is its own LDS position.
+  constexpr int NDW = dma_waves<PAGED, CAUSAL>();
+  constexpr int DPW = TILE / 1024 / NDW;   // 1 KiB pieces per DMA wave, tile and tensor
+  const bool dma_wave = wave < NDW;
   const int rs = PAGED ? HD * 2 : p.Hkv * HD * 2;   // bytes between key rows
-  int koff[2], voff[2];
+  int koff[DPW], voff[DPW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 8 * wave + 4 * i + (lane >> 4), pos = lane & 15;
+  for (int i = 0; i < DPW; ++i) {
+    const int r = 4 * DPW * wave + 4 * i + (lane >> 4), pos = lane & 15;
     koff[i] = r * rs + 16 * k_pos(r, pos);
     if constexpr (PAGED) {
-      const int d = 16 * wave + 8 * i + (lane >> 3), pv = lane & 7;
+      const int d = 8 * DPW * wave + 8 * i + (lane >> 3), pv = lane & 7;
       voff[i] = d * (BN * 2) + 16 * vp_pos(d, pv);
     } else {
       voff[i] = r * rs + 16 * vd_pos(r, pos);
@@ -346,18 +356,12 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     return Stream{static_cast<const char *>(t0) + first * 2, p.Sk};
   };
   Stream ks_stream = dense_stream(p.k), vs_stream = dense_stream(p.v);
-  auto issue = [&](Stream &st, int tile, int blk, int slot_off, const int (&off)[2],
+  auto issue = [&](Stream &st, int tile, int blk, int slot_off, const int (&off)[DPW],
                    bool is_k) __attribute__((always_inline)) {
     u32x4 r;
     if constexpr (PAGED) {
       const bf16 *src = static_cast<const bf16 *>(is_k ? p.k : p.v);
-      const bool ok = blk >= 0 && blk < p.n_blocks;
-      if (is_k && tile < n_tiles && wave == 0 && lane == 0 && p.dev_status) {
-        if (!ok)
-          p.dev_status[0] = 2;
-        else if (((const const_i32 *)p.block_head)[blk] != p.kv_head_base + g)
-          p.dev_status[0] = 1;
-      }
+      const bool ok = blk >= 0 && blk < p.n_blocks;   // reported by the scan above
       r = rsrc_words(src + (size_t)(ok ? blk : 0) * (TILE / 2), ok && tile < n_tiles ? TILE : 0);
     } else {
       // the range ends at key row Sk of this batch (later rows read as zero)
@@ -367,16 +371,33 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
       st.base += tstride;
       st.rows_left -= BN;
     }
-    char *dst = smem + slot_off + wave * 2048;
-    dma_to_lds_16(r, dst, off[0]);
-    dma_to_lds_16(r, dst + 1024, off[1]);
+    char *dst = smem + slot_off + wave * (DPW * 1024);
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) dma_to_lds_16(r, dst + 1024 * i, off[i]);
   };
 
+  // Paged: wave 0 checks the ids and tags of all n_tiles blocks once, 64 at
+  // a time; an id out of range is replaced by an empty range (zeros) when
+  // its tile is fetched.
+  if (PAGED && wave == 0 && p.dev_status) {
+    bool bad_id = false, bad_tag = false;
+    for (int t = lane; t < n_tiles; t += 64) {
+      const int blk = table[t];
+      const bool ok = blk >= 0 && blk < p.n_blocks;
+      bad_id |= !ok;
+      bad_tag |= ok && p.block_head[blk] != p.kv_head_base + g;
+    }
+    const bool any_id = __ballot(bad_id) != 0, any_tag = __ballot(bad_tag) != 0;
+    if (lane == 0 && (any_id || any_tag)) p.dev_status[0] = any_id ? 2 : 1;
+  }
+
   // ---- prologue: K_0..K_{KA-1}, V_0..V_{VA-1} in flight, then S_0 --------
+  if (dma_wave) {
 #pragma unroll
-  for (int t = 0; t < KA; ++t) issue(ks_stream, t, block_of(t), t * TILE, koff, true);
+    for (int t = 0; t < KA; ++t) issue(ks_stream, t, block_of(t), t * TILE, koff, true);
 #pragma unroll
-  for (int t = 0; t < VA; ++t) issue(vs_stream, t, block_of(t), (NKS + t) * TILE, voff, false);
+    for (int t = 0; t < VA; ++t) issue(vs_stream, t, block_of(t), (NKS + t) * TILE, voff, false);
+  }
   int blk_k = block_of(KA), blk_v = block_of(VA);
   wait_vmcnt<0>();
   barrier_no_wait();
@@ -395,18 +416,20 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   static_assert(NKS == KA && NVS == VA + 2, "slot bookkeeping below");
   static_assert(NKS == 4 && NVS == 4, "the interleaved loop is unrolled over a 4-slot ring");
 
-  // Per-iteration tile fetch (4 DMA instructions per wave, always) into the
+  // Per-iteration tile fetch (2 DPW DMA instructions per DMA wave, always) into the
   // given K and V slots, and the wait that publishes the tiles fetched WD
   // iterations earlier, followed by the first operand reads of the next
   // iteration (V_j and K_{j+2}, from the given slots).
   auto fetch = [&](int j, int kdst, int vdst) __attribute__((always_inline)) {
-    issue(ks_stream, j + KA, blk_k, kdst, koff, true);
-    issue(vs_stream, j + VA, blk_v, vdst, voff, false);
-    blk_k = block_of(j + KA + 1);
-    blk_v = block_of(j + VA + 1);
+    if (dma_wave) {
+      issue(ks_stream, j + KA, blk_k, kdst, koff, true);
+      issue(vs_stream, j + VA, blk_v, vdst, voff, false);
+      blk_k = block_of(j + KA + 1);
+      blk_v = block_of(j + VA + 1);
+    }
   };
   auto finish = [&](int j, int v_next, int k_next2) __attribute__((always_inline)) {
-    wait_vmcnt<4 * WD>();   // DMAs of iterations j-WD+1 .. j may still fly
+    wait_vmcnt<2 * DPW * WD>();   // DMAs of iterations j-WD+1 .. j may still fly
     if (PAGED) asm volatile("" ::"s"(blk_k), "s"(blk_v));   // block ids land here
     if (j < wave_tiles) {
 #pragma unroll
