@@ -49,8 +49,9 @@ constexpr int VA = WD + 1;              // iteration j fetches V_{j+VA}
 constexpr int NKS = KA;                 // K ring slots
 constexpr int NVS = VA + 2;             // V ring slots (after the K slots)
 constexpr int VBASE = NKS * TILE;       // LDS byte offset of the V ring
-constexpr int NPV = 4;                  // P V operands read before the barrier
-constexpr int NPK = 4;                  // K Q^T operands read before the barrier
+constexpr int LA = 3;                   // operands are read LA MFMA slots before their use
+constexpr int NPV = LA;                 // P V operands read before the barrier
+constexpr int NPK = LA;                 // K Q^T operands read before the barrier
 // Every iteration issues the same DMA count per DMA wave; iteration j ends by
 // waiting for those issued in iteration j-WD and earlier, and the barrier
 // then publishes them.  K_t is read from the end of iteration t-2
@@ -458,12 +459,12 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     fetch(j, kdma, vdma);
     // The iteration is written as 32 MFMA slots, each fenced off from the
     // next: slot i issues MFMA i (16 of P V, then 16 of K Q^T), the LDS read
-    // of the operand used four slots later, and a fixed share of the
-    // softmax VALU work (the row max in slots 0-4, then the 16 bf16 pairs of
-    // P with their exp2, pack and row-sum steps spread over slots 5-30).
+    // of the operand used LA slots later, and a fixed share of the softmax
+    // VALU work (the row max in slots 0-4, then the 16 bf16 pairs of P with
+    // their exp2, pack and row-sum steps spread over slots 7-31).
     bf16x8 op[32];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < LA; ++i) {
       op[i] = vpre[i];
       op[16 + i] = kpre[i];
     }
@@ -481,10 +482,10 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     };
     static_for<32>([&](auto slot_tag) __attribute__((always_inline)) {
       constexpr int i = decltype(slot_tag)::value;
-      constexpr int nx = i + 4;   // operand read in this slot
+      constexpr int nx = i + LA;   // operand read in this slot
       if constexpr (nx < 16)
         op[nx] = read_v(vs, nx);
-      else if constexpr (nx >= 20 && nx < 32)
+      else if constexpr (nx >= 16 + NPK && nx < 32)
         op[nx] = read_k(ks, nx - 16);
       if constexpr (i == 16) sn[0] = sn[1] = f32x16{};
       if constexpr (i < 16)
