@@ -212,7 +212,8 @@ def bench_relayout_and_prefill_64k(torch, lcat, iters=20):
     nbytes = 2 * (qo.numel() + ko.numel() + vo.numel()) * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     relay = dict(ms=round(ms, 4), GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
-                 bytes=nbytes, workload="rank 0 of [4][16384][64|8][128] bf16 Q/K/V")
+                 bytes=nbytes, traffic=load_traffic("permute16_kernel", "relayout_qkv_64k"),
+                 workload="rank 0 of [4][16384][64|8][128] bf16 Q/K/V")
 
     pos = torch.arange(S, dtype=torch.int32, device="cuda")
     o = torch.empty((1, S, Hq_tot // SP, D), dtype=torch.bfloat16, device="cuda")
