@@ -83,6 +83,14 @@ __device__ __forceinline__ int vp_pos(int d, int c) { return c ^ (((d >> 1) ^ (d
 // fp32 (accumulators) and bf16 (P) hold without loss of relative precision;
 // the result is unchanged because O and l always share the same m.
 constexpr float kRescaleLog2 = 8.0f;
+// The interleaved iterations skip the tile maximum altogether: they
+// exponentiate against the running m as it stands and check the tile's row
+// sum afterwards.  Every exponential is at most the row sum, so a sum at or
+// below this bound (2^16) proves all of them are; fp32 and bf16 hold such
+// values with full relative precision, and O and l stay within fp32 range
+// for any realistic key count.  A larger sum (or inf) makes the wave redo
+// the tile with the exact maximum before P is used.
+constexpr float kSumLimit = 65536.0f;
 
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 
@@ -460,25 +468,25 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     // The iteration is written as 32 MFMA slots, each fenced off from the
     // next: slot i issues MFMA i (16 of P V, then 16 of K Q^T), the LDS read
     // of the operand used LA slots later, and a fixed share of the softmax
-    // VALU work (the row max in slots 0-4, then the 16 bf16 pairs of P with
-    // their exp2, pack and row-sum steps spread over slots 7-31).
+    // VALU work: pair pr of P (scores 2pr, 2pr+1 -> word pr & 3 of operand
+    // pr >> 2) is scaled and shifted in slot 2pr, exponentiated in slot
+    // 2pr+1 and packed and summed in slot 2pr+2, so every slot carries about
+    // four VALU instructions and no step waits for the one before it inside
+    // a slot.  No tile maximum is taken here (see kSumLimit).
     bf16x8 op[32];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       op[i] = vpre[i];
       op[16 + i] = kpre[i];
     }
-    float t[11], mxv = 0.f, alpha = 1.f, psum = 0.f, m_old = 0.f;
-    float xs[4][2];   // pairs in flight between the scale, exp2 and pack steps
-    bool grow = false;
-    // pair pr of P (scores 2pr, 2pr+1 -> word pr & 3 of operand pr >> 2) is
-    // scaled and shifted in slot pair_slot(pr), exponentiated one slot later
-    // and packed and summed one slot after that, so that no step waits for
-    // the one before it inside a slot.
-    constexpr auto pair_at = [](int slot) constexpr -> int {   // pair whose first step is here
-      if (slot < 7) return -1;
-      const int k = slot - 7;
-      return k % 3 == 2 ? -1 : 2 * (k / 3) + (k % 3);
+    float ts = 0.f;     // this tile's row sum (this lane's keys)
+    float xs[2][2];     // pairs in flight between the scale, exp2 and pack steps
+    auto pack_pair = [&](auto pr_tag) __attribute__((always_inline)) {
+      constexpr int pr = decltype(pr_tag)::value;
+      constexpr int u = pr >> 2;
+      pc[u][2 * (pr & 3)] = to_bf16(xs[pr & 1][0]);
+      pc[u][2 * (pr & 3) + 1] = to_bf16(xs[pr & 1][1]);
+      ts = add_bf16_pair(as_u32x4(pc[u])[pr & 3], ts);
     };
     static_for<32>([&](auto slot_tag) __attribute__((always_inline)) {
       constexpr int i = decltype(slot_tag)::value;
@@ -493,55 +501,34 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
       else
         sn[i & 1] = mfma_32x32x16(op[i], qf[(i - 16) >> 1], sn[i & 1]);
       // -- VALU share of slot i --
-      if constexpr (i < 3) {   // 11 partial maxima of three (two for the last) scores
-        static_for<4>([&](auto q_tag) __attribute__((always_inline)) {
-          constexpr int q = 4 * i + decltype(q_tag)::value;
-          constexpr int a = 3 * q, b2 = 3 * q + 1, c = 3 * q + 2;
-          if constexpr (q < 10)
-            t[q] = max3_raw(sc[a >> 4][a & 15], sc[b2 >> 4][b2 & 15], sc[c >> 4][c & 15]);
-          else if constexpr (q == 10)
-            t[q] = max_raw(sc[1][14], sc[1][15]);
-        });
-      } else if constexpr (i == 3) {
-        mxv = max3_raw(max3_raw(t[0], t[1], t[2]), max3_raw(t[3], t[4], t[5]),
-                       max3_raw(max3_raw(t[6], t[7], t[8]), t[9], t[10]));
-      } else if constexpr (i == 4) {
-        const float mx2 = pair_max32_raw(mxv) * c2;
-        grow = mx2 > m2 + kRescaleLog2;
-        m_old = m2;
-        m2 = grow ? mx2 : m2;
-      } else if constexpr (i == 5) {
-        alpha = fast_exp2(m_old - m2);   // 1 where the max did not move
-      } else if constexpr (i == 6) {
-        psum = l_run * alpha;
-      }
-      constexpr int pa = pair_at(i), pb = pair_at(i - 1), pcx = pair_at(i - 2);
-      if constexpr (pa >= 0) {
-        constexpr int hf = pa >> 3, r = 2 * (pa & 7);
-        xs[pa & 3][0] = fmaf(sc[hf][r], c2, -m2);
-        xs[pa & 3][1] = fmaf(sc[hf][r + 1], c2, -m2);
-      }
-      if constexpr (pb >= 0) {
-        xs[pb & 3][0] = fast_exp2(xs[pb & 3][0]);
-        xs[pb & 3][1] = fast_exp2(xs[pb & 3][1]);
-      }
-      if constexpr (pcx >= 0) {
-        constexpr int u = pcx >> 2;
-        pc[u][2 * (pcx & 3)] = to_bf16(xs[pcx & 3][0]);
-        pc[u][2 * (pcx & 3) + 1] = to_bf16(xs[pcx & 3][1]);
-        psum = add_bf16_pair(as_u32x4(pc[u])[pcx & 3], psum);
+      constexpr int pr = i >> 1;
+      if constexpr ((i & 1) == 0) {
+        constexpr int hf = pr >> 3, r = 2 * (pr & 7);
+        xs[pr & 1][0] = fmaf(sc[hf][r], c2, -m2);
+        xs[pr & 1][1] = fmaf(sc[hf][r + 1], c2, -m2);
+        if constexpr (pr >= 1) pack_pair(Int<pr - 1>{});
+      } else {
+        xs[pr & 1][0] = fast_exp2(xs[pr & 1][0]);
+        xs[pr & 1][1] = fast_exp2(xs[pr & 1][1]);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-    static_assert(pair_at(7) == 0 && pair_at(29) == 15, "16 pairs in slots 7..29, packed by slot 31");
-    l_run = psum;
+    pack_pair(Int<15>{});
     // P_j and l are produced in this iteration, not sunk into the next one
 #pragma unroll
     for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(pc[u]));
+    const float l_prev = l_run;
+    l_run = l_prev + ts;
     asm volatile("" ::"v"(l_run));
-    if (__ballot(grow)) {
+    if (__ballot(!(ts <= kSumLimit))) {
+      // rare: some exponential may exceed the bound; redo the tile against
+      // its exact maximum and rescale O (which now holds P_{j-1} V_{j-1})
+      const float m_new = fmaxf(m2, tile_max(sc) * c2);
+      const float alpha = fast_exp2(m2 - m_new);
+      m2 = m_new;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= alpha;   // after P_{j-1} V_{j-1}
+      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+      l_run = exp_half(sc, pc, 1, m2, exp_half(sc, pc, 0, m2, l_prev * alpha));
     }
     finish(j, vpre_s, kpre_s);
   };

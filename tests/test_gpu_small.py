@@ -205,6 +205,43 @@ def test_prefill_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+
+def _stepped_scores(seed, B, S, Hq, Hkv, step_keys, step=13.0, D=128):
+    """bf16 inputs whose scaled scores climb by about `step` (natural-log
+    units, i.e. ~18.8 in log2 units) every `step_keys` keys: every query row
+    shares one direction u (plus 10% noise) and key t is the multiple of u
+    that puts it on its level, plus N(0, 0.3^2) noise.  The running maximum
+    of a row then jumps far past any lazy-rescale bound deep inside the key
+    loop, not only in its first or last tile; with steps every 128 keys the
+    total climb passes 2^128, so exponentials taken against a stale maximum
+    would overflow fp32."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(D)
+    scale = 1.0 / np.sqrt(D)
+    q = u + 0.1 * rng.standard_normal((B, S, Hq, D))
+    coef = step * (np.arange(S) // step_keys) / (scale * (u @ u))
+    k = coef[None, :, None, None] * u + 0.3 * rng.standard_normal((B, S, Hkv, D))
+    v = rng.standard_normal((B, S, Hkv, D))
+    q, k, v = (synth.f32_to_bf16_bits(a.astype(np.float32)) for a in (q, k, v))
+    return dict(q=q, k=k, v=v, scale=scale)
+
+
+@pytest.mark.parametrize("S,B,causal,stepped", [
+    (2048, 1, True, False), (1100, 2, False, False), (2048, 1, True, True), (1100, 2, False, True),
+])
+def test_prefill_bf16_long_rows(S, B, causal, stepped):
+    """Sequences long enough for the interleaved key loop (five or more
+    full tiles before the diagonal), every row against the oracle; the
+    stepped inputs make that loop take its exact-maximum recovery path."""
+    log(f"prefill bf16 long S={S} B={B} causal={causal} stepped={stepped}")
+    d = (_stepped_scores(800 + S, B, S, 16, 2, step_keys=128) if stepped
+         else synth.dense_bf16(seed=800 + S, B=B, S=S, Hq=16, Hkv=2))
+    o, lse = lcat.attn_prefill(to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"]), causal=causal)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=causal)
+    e, r = assert_attention_close(to_np64(o), ref, lse.cpu().numpy(), ref_lse, what="prefill")
+    log(f"  max abs {e:.3g} rel-L2 {r:.3g}")
+
 # ---------------------------------------------------------------------------
 # decode over the paged cache
 # ---------------------------------------------------------------------------
@@ -350,6 +387,21 @@ def test_chunked_prefill_all_rows(S, C):
     np.testing.assert_array_equal(kg, d["k"])
     np.testing.assert_array_equal(vg, d["v"])
 
+
+
+@pytest.mark.parametrize("S,C,stepped", [(1500, 512, False), (1500, 1024, True)])
+def test_chunked_prefill_long_rows(S, C, stepped):
+    """Chunks deep enough for the interleaved key loop over cached blocks;
+    the stepped inputs make that loop take its exact-maximum recovery path."""
+    log(f"chunked long S={S} C={C} stepped={stepped}")
+    d = synth.chunked_prefill(seed=720 + S, B=2, S=S, C=C, Hq=16, Hkv=2, kv_head_base=2)
+    if stepped:
+        d.update(_stepped_scores(730 + S, 2, S, 16, 2, step_keys=128))
+    o, lse, k_pool, v_pool, st = _run_chunked(d, C, kv_head_base=2)
+    assert st.item() == 0
+    ref, ref_lse = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=True)
+    e, r = assert_attention_close(to_np64(o), ref, lse.cpu().numpy(), ref_lse, what="chunked")
+    log(f"  max abs {e:.3g} rel-L2 {r:.3g}")
 
 def test_chunked_equals_dense_prefill():
     """Chunked prefill of a sequence agrees with one dense causal prefill of
