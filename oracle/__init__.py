@@ -15,7 +15,8 @@ What it computes (each function cites the passage it follows):
   reading (rotate-half, ``base**(-2i/D)``); parity of that reading is pinned
   only by textbook RoPE properties, not by the pages.
 * :func:`permute` — the sequence-shard -> head-shard relayout of the same
-  article's §2.2.
+  article's §2.2; :func:`unpermute` — the reverse exchange of the same
+  section for the attention output (head shard back to sequence shards).
 * :func:`paged_gather` — read-back of the head-sharded paged KV cache of the
   article's §2.3.
 * :func:`partial_attention` / :func:`lse_merge` — the rescale identity of
@@ -63,6 +64,8 @@ def _load():
         lib.oracle_rope.restype = i32
         lib.oracle_permute.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64]
         lib.oracle_permute.restype = i32
+        lib.oracle_unpermute.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64]
+        lib.oracle_unpermute.restype = i32
         lib.oracle_paged_gather.argtypes = [vp, vp, i64, vp, i64, i64, i64, vp, i64, i64, vp, vp]
         lib.oracle_paged_gather.restype = i32
         _lib = lib
@@ -187,6 +190,25 @@ def permute(x, rank):
     rc = _load().oracle_permute(_ptr(x), _ptr(out), SP, S_loc, H_tot, D, int(rank), x.itemsize)
     if rc != 0:
         raise RuntimeError(f"oracle_permute failed ({rc})")
+    return out
+
+
+def unpermute(x, SP, H_tot, rank, out=None):
+    """``[SP*S_loc][H_tot/SP][D]`` of ``rank`` -> its head slice of
+    ``out [SP][S_loc][H_tot][D]`` (other slices untouched; zeros if ``out``
+    is not given)."""
+    x = np.ascontiguousarray(x)
+    T, H_loc, D = x.shape
+    if H_tot % SP or H_tot // SP != H_loc or T % SP:
+        raise ValueError("oracle: shape mismatch")
+    S_loc = T // SP
+    if out is None:
+        out = np.zeros((SP, S_loc, H_tot, D), dtype=x.dtype)
+    elif out.shape != (SP, S_loc, H_tot, D) or out.dtype != x.dtype or not out.flags.c_contiguous:
+        raise ValueError("oracle: bad out")
+    rc = _load().oracle_unpermute(_ptr(x), _ptr(out), SP, S_loc, H_tot, D, int(rank), x.itemsize)
+    if rc != 0:
+        raise RuntimeError(f"oracle_unpermute failed ({rc})")
     return out
 
 

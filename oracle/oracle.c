@@ -15,7 +15,8 @@
  *    recurrence the GPU uses is never used here.
  *  - rotary embedding at absolute token positions (Ulysses inference article,
  *    §3.2 and §5.3): angle p * base^(-2i/D), rotate-half pairing (i, i+D/2).
- *  - sequence-shard -> head-shard relayout (same article, §2.2).
+ *  - sequence-shard -> head-shard relayout (same article, §2.2), and its
+ *    inverse for the attention output (head shard back to sequence shards).
  *  - gather of a head-sharded paged KV cache (same article, §2.3) into
  *    contiguous order.
  *
@@ -164,6 +165,37 @@ int oracle_permute(const void *in, void *out, int64_t SP, int64_t S_loc, int64_t
         const int64_t dst_idx = (k * S_loc + s) * H_loc + h;
         memcpy(dst + dst_idx * row, src + src_idx * row, (size_t)row);
       }
+  return 0;
+}
+
+/*
+ * Head-shard -> sequence-shard relayout for one rank: the second exchange of
+ * the Ulysses inference article (§2.2), which returns the attention output of
+ * this rank's heads to the sequence shards; §2.3 places each head by its
+ * global index.
+ *   in  : [SP*S_loc][H_tot/SP][D]   this rank's heads, global token order
+ *   out : [SP][S_loc][H_tot][D]     the SP sequence shards, all heads
+ *   out[k][s][rank*(H_tot/SP) + h][:] = in[k*S_loc + s][h][:]
+ * Only this rank's head slice of out is written; every other byte of out is
+ * left as it was.  Payload bytes are copied unchanged.
+ */
+int oracle_unpermute(const void *in, void *out, int64_t SP, int64_t S_loc, int64_t H_tot,
+                     int64_t D, int64_t rank, int64_t elem_bytes) {
+  if (!in || !out || SP <= 0 || S_loc < 0 || H_tot <= 0 || D <= 0 || elem_bytes <= 0) return -1;
+  if (H_tot % SP || rank < 0 || rank >= SP) return -1;
+  const int64_t H_loc = H_tot / SP;
+  const int64_t row = D * elem_bytes;
+  const char *src = (const char *)in;
+  char *dst = (char *)out;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < SP * S_loc; ++t) {
+    const int64_t k = t / S_loc, s = t % S_loc;
+    for (int64_t h = 0; h < H_loc; ++h) {
+      const int64_t src_idx = t * H_loc + h;
+      const int64_t dst_idx = (k * S_loc + s) * H_tot + rank * H_loc + h;
+      memcpy(dst + dst_idx * row, src + src_idx * row, (size_t)row);
+    }
+  }
   return 0;
 }
 

@@ -341,6 +341,40 @@ def test_permute_all_ranks_is_a_bijection():
     np.testing.assert_array_equal(full.reshape(SP, S_loc, H, D), x)
 
 
+def test_unpermute_worked_example_reversed():
+    """The reverse exchange of the same worked example: rank r holds heads
+    2r, 2r+1 of all 64 tokens; sending every rank's heads back must leave
+    shard k with tokens 16k .. 16k+15 and all 8 heads, each head at its
+    global index."""
+    spec, heads = _read_golden("ulysses_relayout_example.txt")
+    SP, S_loc, H, D = spec["SP"], spec["S_loc"], spec["H_tot"], 3
+    T = spec["tokens_after"]
+    code = lambda t, h, d: (t * 100 + h) * 100 + d
+    out = np.full((SP, S_loc, H, D), -1, dtype=np.int64)
+    for r in range(SP):
+        x = np.array([[[code(t, hg, d) for d in range(D)] for hg in heads[r]] for t in range(T)],
+                     dtype=np.int64)
+        oracle.unpermute(x, SP, H, r, out=out)
+    for k_ in range(SP):
+        for s in range(S_loc):
+            for h in range(H):
+                for d in range(D):
+                    assert out[k_, s, h, d] == code(k_ * S_loc + s, h, d)
+
+
+def test_unpermute_inverts_permute_and_touches_only_its_heads():
+    rng = np.random.default_rng(25)
+    SP, S_loc, H, D = 4, 5, 8, 6
+    x = rng.integers(0, 2**16, size=(SP, S_loc, H, D), dtype=np.uint16)
+    back = np.zeros_like(x)
+    for r in range(SP):
+        before = back.copy()
+        oracle.unpermute(oracle.permute(x, r), SP, H, r, out=back)
+        changed = np.argwhere((back != before).any(axis=-1))
+        assert set(int(h) for h in changed[:, 2]) <= set(range(r * H // SP, (r + 1) * H // SP))
+    np.testing.assert_array_equal(back, x)
+
+
 # ---------------------------------------------------------------------------
 # Paged cache read-back
 # ---------------------------------------------------------------------------
