@@ -14,11 +14,13 @@ The same JSON line also carries, each measured in this run:
                   uniform in [8192, 131072], KV bytes per second against 8 TB/s;
   relayout        sequence-shard -> head-shard relayout of one rank's share of
                   [4][16384][64|8][128] bf16 Q/K/V (one launch), bytes per second;
-The decode and relayout times are means over calls enqueued back to back.
+  relayout_back   the reverse exchange: that rank's attention output
+                  [65536][16][128] back to its head slice of the shards;
   prefill_64k     the relayout + RoPE + causal prefill pipeline at 65536;
   chunked_prefill 4 requests x 131072 tokens in 8192-token chunks;
   cpu_baseline    the fp64 CPU oracle timed on a bounded sample of query rows
                   of the step workload, on this host's cores.
+The decode and relayout times are means over calls enqueued back to back.
 
 Inputs are seeded synthetic N(0,1) data resident in HBM before timing starts.
 """
@@ -237,7 +239,19 @@ def bench_relayout_and_prefill_64k(torch, lcat, iters=20):
                TFLOPs=round(flops / (kms * 1e-3) / 1e12, 1),
                frac_mfma=round(flops / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                workload="relayout + RoPE + causal prefill, seq 65536, 16 Q / 2 KV heads")
-    return relay, pre
+
+    # the reverse exchange: rank 0's output back to its head slice of the shards
+    o_back = torch.zeros((SP, S_loc, Hq_tot, D), dtype=torch.bfloat16, device="cuda")
+    back = lambda: lcat.head_to_seq_permute(o[0], SP, Hq_tot, 0, out=o_back)
+    for _ in range(3):
+        back()
+    torch.cuda.synchronize()
+    ms_b = back_to_back_ms(torch, back, iters)
+    nb = 2 * o[0].numel() * 2
+    gbs_b = nb / (ms_b * 1e-3) / 1e9
+    relay_back = dict(ms=round(ms_b, 4), GBps=round(gbs_b, 1), frac_hbm=round(gbs_b / PEAK_HBM_GBS, 4),
+                      bytes=nb, workload="rank 0's O [65536][16][128] bf16 -> [4][16384][64][128]")
+    return relay, pre, relay_back
 
 
 def bench_chunked(torch, lcat, synth):
@@ -324,7 +338,7 @@ def main():
         if args.only == "decode":
             res = bench_decode(torch, lcat, synth)
         elif args.only == "relayout":
-            res = bench_relayout_and_prefill_64k(torch, lcat)[0]
+            res = bench_relayout_and_prefill_64k(torch, lcat)
         else:
             res = bench_chunked(torch, lcat, synth)
         print(json.dumps({args.only: res}), flush=True)
@@ -345,7 +359,8 @@ def main():
         log("bench: decode")
         out["decode"] = bench_decode(torch, lcat, synth)
         log("bench: relayout + prefill 64k")
-        out["relayout"], out["prefill_64k"] = bench_relayout_and_prefill_64k(torch, lcat)
+        out["relayout"], out["prefill_64k"], out["relayout_back"] = \
+            bench_relayout_and_prefill_64k(torch, lcat)
         log("bench: chunked prefill")
         out["chunked_prefill"] = bench_chunked(torch, lcat, synth)
     if not args.no_cpu_baseline and not args.only:

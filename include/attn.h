@@ -177,6 +177,21 @@ int seq_to_head_permute_qkv(const void *q_in, const void *k_in, const void *v_in
                             void *k_out, void *v_out, int SP, int S_loc, int Hq_tot, int Hkv_tot,
                             int D, int rank, int elem_bytes, void *stream);
 
+/*
+ * head_to_seq_permute — the local half of the second Ulysses exchange
+ * ([ULY] §2.2; heads placed by global index as §2.3 describes): send this
+ * rank's attention output back to the sequence shards.
+ *   in  [SP*S_loc][H_tot/SP][D] (global token order, this rank's heads),
+ *   out [SP][S_loc][H_tot][D], elements of elem_bytes bytes (1, 2, 4 or 8),
+ *   copied bit for bit:
+ *   out[k][s][rank*(H_tot/SP) + h][:] = in[k*S_loc + s][h][:]
+ * Only this rank's head slice of out is written; the other ranks' slices are
+ * left untouched, so SP calls (one per rank) assemble the full output.
+ * in and out must not overlap (ATTN_ERR_SHAPE).
+ */
+int head_to_seq_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
+                        int elem_bytes, void *stream);
+
 /* Static, human-readable text for an attn_status value. */
 const char *attn_status_string(int status);
 

@@ -24,7 +24,7 @@ from ._lib import (ATTN_DEV_BAD_BLOCK, ATTN_DEV_BAD_TAG, ATTN_DEV_OK, ATTN_DTYPE
 
 __all__ = [
     "attn_prefill", "attn_chunked_prefill", "attn_kv_append", "attn_decode",
-    "attn_decode_workspace_bytes", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv",
+    "attn_decode_workspace_bytes", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv", "head_to_seq_permute",
     "attn_status_string",
     "AttnError", "ATTN_DEV_OK", "ATTN_DEV_BAD_TAG", "ATTN_DEV_BAD_BLOCK", "load_library",
 ]
@@ -258,4 +258,23 @@ def seq_to_head_permute(x, rank, out=None, stream=None):
     st = _lib.load().seq_to_head_permute(_ptr(x), _ptr(out), SP, S_loc, H_tot, D, int(rank),
                                          x.element_size(), _stream(stream))
     _lib.check("seq_to_head_permute", st)
+    return out
+
+
+def head_to_seq_permute(x, SP, H_tot, rank, out=None, stream=None):
+    """``x [SP*S_loc][H_tot/SP][D]`` (rank's heads) -> rank's head slice of
+    ``out [SP][S_loc][H_tot][D]``; the other slices of ``out`` are left as
+    they are (a new ``out`` is zero-filled first)."""
+    torch = _torch()
+    _need(x, "x")
+    T, H_loc, D = x.shape
+    if H_tot % SP or H_tot // SP != H_loc or T % SP:
+        raise ValueError("x must be [SP*S_loc][H_tot/SP][D]")
+    S_loc = T // SP
+    if out is None:
+        out = torch.zeros((SP, S_loc, H_tot, D), dtype=x.dtype, device=x.device)
+    _need(out, "out", x.dtype, (SP, S_loc, H_tot, D))
+    st = _lib.load().head_to_seq_permute(_ptr(x), _ptr(out), SP, S_loc, H_tot, D, int(rank),
+                                         x.element_size(), _stream(stream))
+    _lib.check("head_to_seq_permute", st)
     return out

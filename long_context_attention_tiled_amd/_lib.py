@@ -31,6 +31,7 @@ SIGNATURES = {
     "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "rope_apply": (_i, [_vp, _vp, _i, _i, _i, _f, _vp]),
     "seq_to_head_permute": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "head_to_seq_permute": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "seq_to_head_permute_qkv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                      _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),

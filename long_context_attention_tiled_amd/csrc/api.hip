@@ -188,6 +188,23 @@ int seq_to_head_permute(const void *in, void *out, int SP, int S_loc, int H_tot,
                                          static_cast<hipStream_t>(stream)));
 }
 
+int head_to_seq_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
+                        int elem_bytes, void *stream) {
+  if (SP <= 0 || S_loc < 0 || H_tot <= 0 || D <= 0 || H_tot % SP) return ATTN_ERR_SHAPE;
+  if (rank < 0 || rank >= SP) return ATTN_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return ATTN_ERR_DTYPE;
+  if (S_loc == 0) return ATTN_OK;
+  if (!in || !out) return ATTN_ERR_NULL;
+  const char *a = static_cast<const char *>(in);
+  char *c = static_cast<char *>(out);
+  const long long in_bytes = (long long)SP * S_loc * (H_tot / SP) * D * elem_bytes;
+  const long long out_bytes = (long long)SP * S_loc * H_tot * D * elem_bytes;
+  if (!(c + out_bytes <= a || a + in_bytes <= c)) return ATTN_ERR_SHAPE;   // overlap
+  return hip_status(lcat::launch_unpermute(in, out, SP, S_loc, H_tot, D, rank, elem_bytes,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int seq_to_head_permute_qkv(const void *q_in, const void *k_in, const void *v_in, void *q_out,
                             void *k_out, void *v_out, int SP, int S_loc, int Hq_tot, int Hkv_tot,
                             int D, int rank, int elem_bytes, void *stream) {

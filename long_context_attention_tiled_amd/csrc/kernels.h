@@ -63,6 +63,10 @@ hipError_t launch_rope(void *x, const int32_t *positions, int S, int H, int D, f
 hipError_t launch_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
                           int elem_bytes, hipStream_t stream);
 
+// The inverse: [SP*S_loc][H_tot/SP][D] -> rank's head slice of [SP][S_loc][H_tot][D].
+hipError_t launch_unpermute(const void *in, void *out, int SP, int S_loc, int H_tot, int D,
+                            int rank, int elem_bytes, hipStream_t stream);
+
 // Q, K and V (head counts H_tot[0..2]) in one launch.
 hipError_t launch_permute_qkv(const void *const in[3], void *const out[3], const int H_tot[3],
                               int SP, int S_loc, int D, int rank, int elem_bytes,

@@ -12,6 +12,11 @@
 // take consecutive units so every wave reads and writes whole cache lines.
 // Stores are non-temporal (streaming), which on gfx950 raises copy
 // bandwidth from about 5.5 to about 7 TB/s.
+//
+// The same kernel runs the reverse exchange of §2.2 (head shard back to
+// sequence shards, each head at its global index as §2.3 asks): the
+// contiguous side is then the input and the strided side the output,
+//     out[k][s][r*H_loc + h][:] = in[k*S_loc + s][h][:]
 #include "device.h"
 #include "kernels.h"
 
@@ -21,9 +26,11 @@ namespace {
 constexpr int NT = 256;
 constexpr int UPT = 4;   // 16-byte units per thread
 
-// One tensor's relayout in 16-byte units: unit u of the output is unit
-// (u mod units_per_run) of run (u div units_per_run), whose source row is
-// that token's first local head.
+// One tensor's relayout in 16-byte units.  Unit u of the head-sharded
+// (contiguous) side is unit (u mod units_per_run) of run (u div
+// units_per_run), whose row on the sequence-sharded side is that token's
+// first local head.  gather: strided in -> contiguous out; scatter: the
+// reverse.
 struct Permute16Job {
   const char *in;
   char *out;
@@ -32,6 +39,7 @@ struct Permute16Job {
   long long row_bytes;   // bytes of one head row (D * elem_bytes)
   int units_per_run;     // 16-byte units per token run (H_loc heads)
   int H_tot, H_loc, rank;
+  int scatter;           // 0: sequence -> head shard, 1: head -> sequence shards
 };
 
 // Up to three jobs (Q, K, V) in one launch; each workgroup belongs to one job.
@@ -41,22 +49,27 @@ __global__ __launch_bounds__(NT) void permute16_kernel(Permute16Job j0, Permute1
   const Permute16Job &j = wg >= j2.wg_begin ? j2 : (wg >= j1.wg_begin ? j1 : j0);
   const long long base = (wg - j.wg_begin) * (NT * UPT) + threadIdx.x;
   u32x4 buf[UPT];
+  long long strided[UPT];
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const long long u = base + (long long)i * NT;
-    if (u < j.n_units) {
-      const long long tok = u / j.units_per_run;
-      const int w = (int)(u - tok * j.units_per_run);
-      const long long src = (tok * j.H_tot + (long long)j.rank * j.H_loc) * j.row_bytes + 16LL * w;
-      buf[i] = ld_global_16(j.in + src);
-    }
+    const long long tok = u / j.units_per_run;
+    const int w = (int)(u - tok * j.units_per_run);
+    strided[i] = (tok * j.H_tot + (long long)j.rank * j.H_loc) * j.row_bytes + 16LL * w;
+  }
+  const bool sc = j.scatter != 0;   // uniform over the workgroup
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const long long u = base + (long long)i * NT;
+    if (u < j.n_units) buf[i] = ld_global_16(j.in + (sc ? 16LL * u : strided[i]));
   }
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const long long u = base + (long long)i * NT;
     // streaming store: the output is not read again by this kernel
     if (u < j.n_units)
-      __builtin_nontemporal_store(buf[i], reinterpret_cast<u32x4 *>(j.out + 16LL * u));
+      __builtin_nontemporal_store(buf[i],
+                                  reinterpret_cast<u32x4 *>(j.out + (sc ? strided[i] : 16LL * u)));
   }
 }
 
@@ -64,12 +77,16 @@ template <typename T>
 __global__ __launch_bounds__(NT) void permute_elem_kernel(const T *__restrict__ in,
                                                           T *__restrict__ out, long long n_elem,
                                                           int run_elems, int H_tot, int H_loc,
-                                                          int rank, int D) {
+                                                          int rank, int D, int scatter) {
   const long long e = (long long)blockIdx.x * NT + threadIdx.x;
   if (e >= n_elem) return;
   const long long tok = e / run_elems;
   const int w = (int)(e - tok * run_elems);
-  out[e] = in[(tok * H_tot + (long long)rank * H_loc) * D + w];
+  const long long strided = (tok * H_tot + (long long)rank * H_loc) * D + w;
+  if (scatter)
+    out[strided] = in[e];
+  else
+    out[e] = in[strided];
 }
 
 }  // namespace
@@ -83,8 +100,9 @@ bool fits16(const void *in, const void *out, int H_loc, int D, int elem_bytes) {
 }
 
 Permute16Job make_job(const void *in, void *out, long long n_tok, int H_tot, int SP, int D,
-                      int rank, int elem_bytes, long long wg_begin) {
+                      int rank, int elem_bytes, long long wg_begin, int scatter = 0) {
   Permute16Job j{};
+  j.scatter = scatter;
   j.in = static_cast<const char *>(in);
   j.out = static_cast<char *>(out);
   j.H_tot = H_tot;
@@ -100,7 +118,7 @@ Permute16Job make_job(const void *in, void *out, long long n_tok, int H_tot, int
 long long job_wgs(const Permute16Job &j) { return (j.n_units + NT * UPT - 1) / (NT * UPT); }
 
 hipError_t launch_elem(const void *in, void *out, long long n_tok, int H_tot, int H_loc, int D,
-                       int rank, int elem_bytes, hipStream_t stream) {
+                       int rank, int elem_bytes, int scatter, hipStream_t stream) {
   const long long n_elem = n_tok * H_loc * D;
   const unsigned n_wg = (unsigned)((n_elem + NT - 1) / NT);
   const int run_elems = H_loc * D;
@@ -108,22 +126,22 @@ hipError_t launch_elem(const void *in, void *out, long long n_tok, int H_tot, in
     case 1:
       hipLaunchKernelGGL(permute_elem_kernel<uint8_t>, dim3(n_wg), dim3(NT), 0, stream,
                          static_cast<const uint8_t *>(in), static_cast<uint8_t *>(out), n_elem,
-                         run_elems, H_tot, H_loc, rank, D);
+                         run_elems, H_tot, H_loc, rank, D, scatter);
       break;
     case 2:
       hipLaunchKernelGGL(permute_elem_kernel<uint16_t>, dim3(n_wg), dim3(NT), 0, stream,
                          static_cast<const uint16_t *>(in), static_cast<uint16_t *>(out), n_elem,
-                         run_elems, H_tot, H_loc, rank, D);
+                         run_elems, H_tot, H_loc, rank, D, scatter);
       break;
     case 4:
       hipLaunchKernelGGL(permute_elem_kernel<uint32_t>, dim3(n_wg), dim3(NT), 0, stream,
                          static_cast<const uint32_t *>(in), static_cast<uint32_t *>(out), n_elem,
-                         run_elems, H_tot, H_loc, rank, D);
+                         run_elems, H_tot, H_loc, rank, D, scatter);
       break;
     default:
       hipLaunchKernelGGL(permute_elem_kernel<uint64_t>, dim3(n_wg), dim3(NT), 0, stream,
                          static_cast<const uint64_t *>(in), static_cast<uint64_t *>(out), n_elem,
-                         run_elems, H_tot, H_loc, rank, D);
+                         run_elems, H_tot, H_loc, rank, D, scatter);
       break;
   }
   return hipGetLastError();
@@ -131,19 +149,33 @@ hipError_t launch_elem(const void *in, void *out, long long n_tok, int H_tot, in
 
 }  // namespace
 
-hipError_t launch_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
-                          int elem_bytes, hipStream_t stream) {
+namespace {
+
+hipError_t launch_one(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
+                      int elem_bytes, int scatter, hipStream_t stream) {
   const int H_loc = H_tot / SP;
   const long long n_tok = (long long)SP * S_loc;
   if (n_tok == 0 || (long long)H_loc * D == 0) return hipSuccess;
   if (!fits16(in, out, H_loc, D, elem_bytes))
-    return launch_elem(in, out, n_tok, H_tot, H_loc, D, rank, elem_bytes, stream);
-  const Permute16Job j = make_job(in, out, n_tok, H_tot, SP, D, rank, elem_bytes, 0);
+    return launch_elem(in, out, n_tok, H_tot, H_loc, D, rank, elem_bytes, scatter, stream);
+  const Permute16Job j = make_job(in, out, n_tok, H_tot, SP, D, rank, elem_bytes, 0, scatter);
   const long long n_wg = job_wgs(j);
   Permute16Job none = j;
   none.wg_begin = n_wg;   // never selected
   hipLaunchKernelGGL(permute16_kernel, dim3((unsigned)n_wg), dim3(NT), 0, stream, j, none, none);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
+                          int elem_bytes, hipStream_t stream) {
+  return launch_one(in, out, SP, S_loc, H_tot, D, rank, elem_bytes, 0, stream);
+}
+
+hipError_t launch_unpermute(const void *in, void *out, int SP, int S_loc, int H_tot, int D,
+                            int rank, int elem_bytes, hipStream_t stream) {
+  return launch_one(in, out, SP, S_loc, H_tot, D, rank, elem_bytes, 1, stream);
 }
 
 hipError_t launch_permute_qkv(const void *const in[3], void *const out[3], const int H_tot[3],

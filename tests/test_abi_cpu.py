@@ -43,6 +43,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["attn_prefill", "attn_chunked_prefill", "attn_decode", "attn_decode_workspace_bytes",
               "attn_kv_append", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv",
+              "head_to_seq_permute",
               "attn_status_string"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -143,6 +144,14 @@ def test_rope_and_permute_validation(lib):
     assert p(A16, NUL, 4, 16, 8, 128, 0, 2, S0) == NULL
     assert p(NUL, NUL, 4, 0, 8, 128, 0, 2, S0) == OK
     assert p(A16, P(0x10000 + 64), 4, 16, 8, 128, 0, 2, S0) == SHAPE   # overlapping buffers
+
+    u = lib.head_to_seq_permute
+    assert u(A16, P(0x90000000), 4, 16, 6, 128, 0, 2, S0) == SHAPE     # 6 % 4
+    assert u(A16, P(0x90000000), 4, 16, 8, 128, -1, 2, S0) == SHAPE    # rank out of range
+    assert u(A16, P(0x90000000), 4, 16, 8, 128, 0, 5, S0) == DTYPE
+    assert u(NUL, P(0x90000000), 4, 16, 8, 128, 0, 2, S0) == NULL
+    assert u(NUL, NUL, 4, 0, 8, 128, 0, 2, S0) == OK
+    assert u(P(0x10000 + 64), A16, 4, 16, 8, 128, 0, 2, S0) == SHAPE   # overlapping buffers
 
     f = lib.seq_to_head_permute_qkv
     q, k, v = P(0x10000), P(0x20000000), P(0x40000000)

@@ -106,6 +106,22 @@ def test_ulysses_relayout_rope_prefill_64k():
     log(f"C3: max abs {e:.3g} rel-L2 {r:.3g}")
 
 
+def test_ulysses_output_relayout_64k():
+    """The reverse exchange at the 64K shape: rank 0's output [65536][16][128]
+    back to its head slice of [4][16384][64][128], bit for bit, on a seeded
+    bf16 tensor of that shape; the other slices keep their prior contents."""
+    SP, S_loc, H_tot = 4, 16384, 64
+    x = synth.normal_bf16(36, (SP * S_loc, H_tot // SP, 128))
+    prior = synth.normal_bf16(37, (SP, S_loc, H_tot, 128))
+    out = to_dev(prior)
+    log("C3 output relayout: rank 0")
+    lcat.head_to_seq_permute(to_dev(x), SP, H_tot, 0, out=out)
+    torch.cuda.synchronize()
+    ref = prior.copy()
+    oracle.unpermute(x, SP, H_tot, 0, out=ref)
+    assert np.array_equal(bits(out), ref)
+
+
 def test_decode_paged_32_requests():
     log("C4: generating cache")
     c = synth.decode_cache(seed=4, B=32)

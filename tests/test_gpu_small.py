@@ -47,6 +47,31 @@ def test_permute_bit_exact(SP, S_loc, H, D, dtype):
         np.testing.assert_array_equal(out.cpu().numpy(), oracle.permute(x, r))
 
 
+@pytest.mark.parametrize("SP,S_loc,H,D,dtype", [
+    (4, 16, 8, 128, np.uint16),      # the article's worked example, bf16 payload
+    (4, 37, 64, 128, np.uint16),     # 64 global heads, ragged token count
+    (2, 5, 4, 3, np.uint8),          # odd run length -> element path
+    (4, 9, 8, 6, np.float64),
+    (8, 3, 16, 4, np.int32),
+])
+def test_unpermute_bit_exact(SP, S_loc, H, D, dtype):
+    """head -> sequence relayout of every rank into one pre-filled buffer:
+    after each call the buffer equals the oracle's, so the other ranks'
+    slices are untouched, and after all ranks it is the full output."""
+    log(f"unpermute SP={SP} S_loc={S_loc} H={H} D={D} {np.dtype(dtype).name}")
+    rng = np.random.default_rng(200 + SP + S_loc)
+    draw = ((lambda shape: rng.standard_normal(shape).astype(dtype)) if np.dtype(dtype).kind == "f"
+            else (lambda shape: rng.integers(0, np.iinfo(dtype).max, size=shape, dtype=dtype)))
+    ref = draw((SP, S_loc, H, D))                 # arbitrary prior contents
+    outd = torch.from_numpy(ref.copy()).cuda()
+    for r in range(SP):
+        x = draw((SP * S_loc, H // SP, D))
+        lcat.head_to_seq_permute(torch.from_numpy(x).cuda(), SP, H, r, out=outd)
+        torch.cuda.synchronize()
+        oracle.unpermute(x, SP, H, r, out=ref)
+        np.testing.assert_array_equal(outd.cpu().numpy(), ref)
+
+
 # ---------------------------------------------------------------------------
 # RoPE
 # ---------------------------------------------------------------------------
