@@ -13,10 +13,12 @@ The same JSON line also carries, each measured in this run:
                   equally over the GPU's waves, 32 requests with contexts
                   uniform in [8192, 131072], KV bytes per second against 8 TB/s;
   relayout        sequence-shard -> head-shard relayout of one rank's share of
-                  [4][16384][64|8][128] bf16 Q/K/V (one launch), bytes per second;
+                  [4][16384][64|8][128] bf16 Q/K/V (one launch), bytes per second,
+                  and (fused_rope) the same relayout with RoPE on Q and K;
   relayout_back   the reverse exchange: that rank's attention output
                   [65536][16][128] back to its head slice of the shards;
-  prefill_64k     the relayout + RoPE + causal prefill pipeline at 65536;
+  prefill_64k     the relayout + RoPE + causal prefill pipeline at 65536,
+                  with separate and with fused relayout + RoPE;
   chunked_prefill 4 requests x 131072 tokens in 8192-token chunks;
   cpu_baseline    the fp64 CPU oracle timed on a bounded sample of query rows
                   of the step workload, on this host's cores.
@@ -218,25 +220,40 @@ def bench_relayout_and_prefill_64k(torch, lcat, iters=20):
                  workload="rank 0 of [4][16384][64|8][128] bf16 Q/K/V")
 
     pos = torch.arange(S, dtype=torch.int32, device="cuda")
+
+    def relayout_rope():   # the same relayout with RoPE on Q and K in the same pass
+        lcat.seq_to_head_permute_qkv_rope(qin, kin, vin, 0, pos, outs=(qo, ko, vo))
+
+    for _ in range(3):
+        relayout_rope()
+    torch.cuda.synchronize()
+    ms_r = back_to_back_ms(torch, relayout_rope, iters)
+    gbs_r = nbytes / (ms_r * 1e-3) / 1e9
+    relay["fused_rope"] = dict(ms=round(ms_r, 4), GBps=round(gbs_r, 1),
+                               frac_hbm=round(gbs_r / PEAK_HBM_GBS, 4))
+
     o = torch.empty((1, S, Hq_tot // SP, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((1, Hq_tot // SP, S), dtype=torch.float32, device="cuda")
-    ptimer, ktimer = EventTimer(torch), EventTimer(torch)
+    ptimer, ftimer, ktimer = EventTimer(torch), EventTimer(torch), EventTimer(torch)
     for it in range(4):
-        with ptimer:
+        with ptimer:   # relayout, then RoPE in place, then prefill
             relayout()
             lcat.rope_apply(qo, pos)
             lcat.rope_apply(ko, pos)
             with ktimer:
                 lcat.attn_prefill(qo[None], ko[None], vo[None], causal=True, o=o, lse=lse)
+        with ftimer:   # fused relayout + RoPE, then prefill
+            relayout_rope()
+            lcat.attn_prefill(qo[None], ko[None], vo[None], causal=True, o=o, lse=lse)
         if it == 0:
             torch.cuda.synchronize()
-            ptimer.pairs.clear()
-            ktimer.pairs.clear()
+            for t in (ptimer, ftimer, ktimer):
+                t.pairs.clear()
     torch.cuda.synchronize()
     flops = causal_flops(1, S, Hq_tot // SP)
     kms = ktimer.mean_ms()
-    pre = dict(pipeline_ms=round(ptimer.mean_ms(), 3), kernel_ms=round(kms, 3),
-               TFLOPs=round(flops / (kms * 1e-3) / 1e12, 1),
+    pre = dict(pipeline_ms=round(ptimer.mean_ms(), 3), pipeline_fused_ms=round(ftimer.mean_ms(), 3),
+               kernel_ms=round(kms, 3), TFLOPs=round(flops / (kms * 1e-3) / 1e12, 1),
                frac_mfma=round(flops / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                workload="relayout + RoPE + causal prefill, seq 65536, 16 Q / 2 KV heads")
 

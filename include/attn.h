@@ -178,6 +178,22 @@ int seq_to_head_permute_qkv(const void *q_in, const void *k_in, const void *v_in
                             int D, int rank, int elem_bytes, void *stream);
 
 /*
+ * seq_to_head_permute_qkv_rope — seq_to_head_permute_qkv for bf16 tensors with
+ * RoPE applied to Q and K on the way ([ULY] §2.2 relayout; §3.2 RoPE at the
+ * absolute position of each token, taken from the global token index table),
+ * in one pass over memory.  positions[t] (int32, device, SP*S_loc entries) is
+ * the absolute position of token t in the output's global token order.  The
+ * outputs equal seq_to_head_permute_qkv followed by rope_apply on the Q and K
+ * outputs, bit for bit (same rotation arithmetic; V is copied unchanged).
+ * D must be a multiple of 16 and at most 256; every tensor 16-byte aligned;
+ * no output may overlap any input or another output (ATTN_ERR_SHAPE).
+ */
+int seq_to_head_permute_qkv_rope(const void *q_in, const void *k_in, const void *v_in,
+                                 void *q_out, void *k_out, void *v_out, const int32_t *positions,
+                                 int SP, int S_loc, int Hq_tot, int Hkv_tot, int D, int rank,
+                                 float base, void *stream);
+
+/*
  * head_to_seq_permute — the local half of the second Ulysses exchange
  * ([ULY] §2.2; heads placed by global index as §2.3 describes): send this
  * rank's attention output back to the sequence shards.

@@ -25,6 +25,7 @@ from ._lib import (ATTN_DEV_BAD_BLOCK, ATTN_DEV_BAD_TAG, ATTN_DEV_OK, ATTN_DTYPE
 __all__ = [
     "attn_prefill", "attn_chunked_prefill", "attn_kv_append", "attn_decode",
     "attn_decode_workspace_bytes", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv", "head_to_seq_permute",
+    "seq_to_head_permute_qkv_rope",
     "attn_status_string",
     "AttnError", "ATTN_DEV_OK", "ATTN_DEV_BAD_TAG", "ATTN_DEV_BAD_BLOCK", "load_library",
 ]
@@ -242,6 +243,34 @@ def seq_to_head_permute_qkv(q, k, v, rank, outs=None, stream=None):
                                              SP, S_loc, Hq, Hkv, D, int(rank), q.element_size(),
                                              _stream(stream))
     _lib.check("seq_to_head_permute_qkv", st)
+    return qo, ko, vo
+
+
+def seq_to_head_permute_qkv_rope(q, k, v, rank, positions, base=10000.0, outs=None, stream=None):
+    """:func:`seq_to_head_permute_qkv` of bf16 ``q, k, v`` with RoPE at
+    ``positions [SP*S_loc]`` (int32, absolute position of each output token)
+    applied to Q and K in the same pass; returns ``(q_out, k_out, v_out)``."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16)
+    SP, S_loc, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (SP, S_loc, Hkv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [SP][S_loc][Hkv][D] with q's SP, S_loc and D")
+    if Hq % SP or Hkv % SP:
+        raise ValueError("head counts must be divisible by SP")
+    _need(positions, "positions", torch.int32, (SP * S_loc,))
+    if outs is None:
+        outs = tuple(torch.empty((SP * S_loc, H // SP, D), dtype=q.dtype, device=q.device)
+                     for H in (Hq, Hkv, Hkv))
+    qo, ko, vo = outs
+    _need(qo, "q_out", q.dtype, (SP * S_loc, Hq // SP, D))
+    _need(ko, "k_out", q.dtype, (SP * S_loc, Hkv // SP, D))
+    _need(vo, "v_out", q.dtype, (SP * S_loc, Hkv // SP, D))
+    st = _lib.load().seq_to_head_permute_qkv_rope(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(qo), _ptr(ko), _ptr(vo), _ptr(positions), SP, S_loc, Hq,
+        Hkv, D, int(rank), float(base), _stream(stream))
+    _lib.check("seq_to_head_permute_qkv_rope", st)
     return qo, ko, vo
 
 

@@ -32,6 +32,8 @@ SIGNATURES = {
     "rope_apply": (_i, [_vp, _vp, _i, _i, _i, _f, _vp]),
     "seq_to_head_permute": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "head_to_seq_permute": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "seq_to_head_permute_qkv_rope": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                          _i, _f, _vp]),
     "seq_to_head_permute_qkv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                      _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),

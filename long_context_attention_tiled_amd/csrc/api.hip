@@ -18,6 +18,27 @@ constexpr int kStreamWaves = 2048;
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// No relayout output may overlap any input or another output.
+bool qkv_disjoint(const void *const in[3], void *const out[3], const int H[3], int SP, int S_loc,
+                  int D, int elem_bytes) {
+  long long in_bytes[3], out_bytes[3];
+  for (int t = 0; t < 3; ++t) {
+    out_bytes[t] = (long long)SP * S_loc * (H[t] / SP) * D * elem_bytes;
+    in_bytes[t] = (long long)SP * S_loc * H[t] * D * elem_bytes;
+  }
+  auto disjoint = [](const void *a, long long na, const void *b, long long nb) {
+    const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+    return x + na <= y || y + nb <= x;
+  };
+  for (int t = 0; t < 3; ++t) {
+    for (int u = 0; u < 3; ++u) {
+      if (!disjoint(out[t], out_bytes[t], in[u], in_bytes[u])) return false;
+      if (u != t && !disjoint(out[t], out_bytes[t], out[u], out_bytes[u])) return false;
+    }
+  }
+  return true;
+}
+
 inline int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
 // GQA group sizes the bf16 kernels handle: divisors of 8 or multiples of 8.
@@ -220,24 +241,33 @@ int seq_to_head_permute_qkv(const void *q_in, const void *k_in, const void *v_in
   const int H[3] = {Hq_tot, Hkv_tot, Hkv_tot};
   for (int t = 0; t < 3; ++t)
     if (!in[t] || !out[t]) return ATTN_ERR_NULL;
-  // no output may overlap any input or another output
-  long long in_bytes[3], out_bytes[3];
-  for (int t = 0; t < 3; ++t) {
-    out_bytes[t] = (long long)SP * S_loc * (H[t] / SP) * D * elem_bytes;
-    in_bytes[t] = (long long)SP * S_loc * H[t] * D * elem_bytes;
-  }
-  auto disjoint = [](const void *a, long long na, const void *b, long long nb) {
-    const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
-    return x + na <= y || y + nb <= x;
-  };
-  for (int t = 0; t < 3; ++t) {
-    for (int u = 0; u < 3; ++u) {
-      if (!disjoint(out[t], out_bytes[t], in[u], in_bytes[u])) return ATTN_ERR_SHAPE;
-      if (u != t && !disjoint(out[t], out_bytes[t], out[u], out_bytes[u])) return ATTN_ERR_SHAPE;
-    }
-  }
+  if (!qkv_disjoint(in, out, H, SP, S_loc, D, elem_bytes)) return ATTN_ERR_SHAPE;
   return hip_status(lcat::launch_permute_qkv(in, out, H, SP, S_loc, D, rank, elem_bytes,
                                              static_cast<hipStream_t>(stream)));
+}
+
+int seq_to_head_permute_qkv_rope(const void *q_in, const void *k_in, const void *v_in,
+                                 void *q_out, void *k_out, void *v_out, const int32_t *positions,
+                                 int SP, int S_loc, int Hq_tot, int Hkv_tot, int D, int rank,
+                                 float base, void *stream) {
+  if (SP <= 0 || S_loc < 0 || Hq_tot <= 0 || Hkv_tot <= 0 || D <= 0 || Hq_tot % SP ||
+      Hkv_tot % SP)
+    return ATTN_ERR_SHAPE;
+  if (rank < 0 || rank >= SP) return ATTN_ERR_SHAPE;
+  if (D % 16 || D > 256) return ATTN_ERR_UNSUPPORTED;
+  if (!(base > 0.f)) return ATTN_ERR_SHAPE;
+  if (S_loc == 0) return ATTN_OK;
+  const void *in[3] = {q_in, k_in, v_in};
+  void *out[3] = {q_out, k_out, v_out};
+  const int H[3] = {Hq_tot, Hkv_tot, Hkv_tot};
+  if (!positions) return ATTN_ERR_NULL;
+  for (int t = 0; t < 3; ++t) {
+    if (!in[t] || !out[t]) return ATTN_ERR_NULL;
+    if (!aligned16(in[t]) || !aligned16(out[t])) return ATTN_ERR_ALIGN;
+  }
+  if (!qkv_disjoint(in, out, H, SP, S_loc, D, 2)) return ATTN_ERR_SHAPE;
+  return hip_status(lcat::launch_permute_qkv_rope(in, out, H, positions, SP, S_loc, D, rank, base,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

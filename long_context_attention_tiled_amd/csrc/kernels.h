@@ -72,4 +72,11 @@ hipError_t launch_permute_qkv(const void *const in[3], void *const out[3], const
                               int SP, int S_loc, int D, int rank, int elem_bytes,
                               hipStream_t stream);
 
+// The same relayout of bf16 Q, K and V with RoPE at positions[t] (t in global
+// token order) applied to Q and K on the way; D % 16 == 0, D <= 256, all
+// pointers 16-byte aligned.
+hipError_t launch_permute_qkv_rope(const void *const in[3], void *const out[3], const int H_tot[3],
+                                   const int32_t *positions, int SP, int S_loc, int D, int rank,
+                                   float base, hipStream_t stream);
+
 }  // namespace lcat

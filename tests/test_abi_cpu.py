@@ -43,7 +43,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["attn_prefill", "attn_chunked_prefill", "attn_decode", "attn_decode_workspace_bytes",
               "attn_kv_append", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv",
-              "head_to_seq_permute",
+              "head_to_seq_permute", "seq_to_head_permute_qkv_rope",
               "attn_status_string"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -164,6 +164,19 @@ def test_rope_and_permute_validation(lib):
     assert f(NUL, NUL, NUL, NUL, NUL, NUL, 4, 0, 8, 8, 128, 0, 2, S0) == OK
     assert f(q, k, v, qo, P(0x60000000 + 64), vo, 4, 16, 8, 8, 128, 0, 2, S0) == SHAPE  # outputs overlap
     assert f(q, k, v, qo, ko, P(0x40000000 + 64), 4, 16, 8, 8, 128, 0, 2, S0) == SHAPE  # output on an input
+
+    g = lib.seq_to_head_permute_qkv_rope
+    pos = P(0xC0000000)
+    assert g(q, k, v, qo, ko, vo, pos, 4, 16, 6, 8, 128, 0, 1e4, S0) == SHAPE      # 6 % 4
+    assert g(q, k, v, qo, ko, vo, pos, 4, 16, 8, 8, 128, 4, 1e4, S0) == SHAPE      # rank out of range
+    assert g(q, k, v, qo, ko, vo, pos, 4, 16, 8, 8, 120, 0, 1e4, S0) == UNSUP      # D % 16
+    assert g(q, k, v, qo, ko, vo, pos, 4, 16, 8, 8, 272, 0, 1e4, S0) == UNSUP      # D > 256
+    assert g(q, k, v, qo, ko, vo, pos, 4, 16, 8, 8, 128, 0, 0.0, S0) == SHAPE      # base
+    assert g(q, k, v, qo, ko, vo, NUL, 4, 16, 8, 8, 128, 0, 1e4, S0) == NULL
+    assert g(q, NUL, v, qo, ko, vo, pos, 4, 16, 8, 8, 128, 0, 1e4, S0) == NULL
+    assert g(q, k, v, qo, P(0x80000000 + 8), vo, pos, 4, 16, 8, 8, 128, 0, 1e4, S0) == ALIGN
+    assert g(q, k, v, qo, P(0x60000000 + 64), vo, pos, 4, 16, 8, 8, 128, 0, 1e4, S0) == SHAPE
+    assert g(NUL, NUL, NUL, NUL, NUL, NUL, NUL, 4, 0, 8, 8, 128, 0, 1e4, S0) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

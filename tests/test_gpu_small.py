@@ -105,6 +105,34 @@ def test_permute_qkv_bit_exact(SP, S_loc, Hq, Hkv, D, dtype):
             assert np.array_equal(g, oracle.permute(x, rank))
 
 
+@pytest.mark.parametrize("SP,S_loc,Hq,Hkv,D", [(4, 37, 64, 8, 128), (2, 5, 4, 2, 16),
+                                             (8, 3, 16, 8, 256), (1, 700, 16, 2, 128),
+                                             (4, 33, 4, 4, 64)])
+def test_permute_qkv_rope(SP, S_loc, Hq, Hkv, D):
+    """Relayout + RoPE in one pass: Q and K against the oracle's rotation of
+    the oracle's relayout, V bit for bit against the relayout; and the whole
+    output bit for bit equal to the two-step path (relayout, then RoPE)."""
+    log(f"permute+rope SP={SP} S_loc={S_loc} Hq={Hq} Hkv={Hkv} D={D}")
+    seed = 300 + SP * 10 + S_loc
+    qs = synth.normal_bf16(seed, (SP, S_loc, Hq, D))
+    ks = synth.normal_bf16(seed + 1, (SP, S_loc, Hkv, D))
+    vs = synth.normal_bf16(seed + 2, (SP, S_loc, Hkv, D))
+    pos = np.random.default_rng(seed).integers(0, 2 ** 17, SP * S_loc).astype(np.int32)
+    posd = to_dev(pos)
+    for rank in (0, SP - 1):
+        qo, ko, vo = lcat.seq_to_head_permute_qkv_rope(to_dev(qs), to_dev(ks), to_dev(vs), rank,
+                                                       posd)
+        q2, k2, v2 = lcat.seq_to_head_permute_qkv(to_dev(qs), to_dev(ks), to_dev(vs), rank)
+        lcat.rope_apply(q2, posd)
+        lcat.rope_apply(k2, posd)
+        torch.cuda.synchronize()
+        _rope_ref_bits_close(bits(qo), oracle.rope(oracle.permute(qs, rank), pos))
+        _rope_ref_bits_close(bits(ko), oracle.rope(oracle.permute(ks, rank), pos))
+        assert np.array_equal(bits(vo), oracle.permute(vs, rank))
+        for a, b in ((qo, q2), (ko, k2), (vo, v2)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_rope_matches_oracle_large_positions():
     S, H, D = 1000, 16, 128
     log("rope S=1000 H=16 positions up to 131k")
