@@ -21,6 +21,12 @@ What it computes (each function cites the passage it follows):
   article's §2.3.
 * :func:`partial_attention` / :func:`lse_merge` — the rescale identity of
   §18.3 applied to key ranges; used only to cross-check :func:`attention`.
+* :func:`cp_tokens` — which tokens each context-parallel rank holds under the
+  contiguous (ring), striped (round-robin) and zigzag (in-seq-split) splits
+  of "LLM推理中的多卡切分" §3.5 / §3.5.1.
+* :func:`attention_positions` — attention whose causal mask is stated on
+  token positions, for such shards; :func:`merge_normalized` combines
+  normalised partial results (O, LSE) with the same rescale identity.
 
 Inputs may be float64, float32, or uint16 arrays of bf16 bit patterns.
 """
@@ -60,6 +66,9 @@ def _load():
         lib.oracle_attention_rows.argtypes = [vp, i32, vp, i32, vp, i32, i64, i64, i64, i64, i64,
                                               i64, vp, dbl, vp, vp]
         lib.oracle_attention_rows.restype = i32
+        lib.oracle_attention_positions.argtypes = [vp, i32, vp, i32, vp, i32, i64, i64, i64, i64,
+                                                   i64, i64, vp, vp, dbl, vp, vp]
+        lib.oracle_attention_positions.restype = i32
         lib.oracle_rope.argtypes = [vp, i32, vp, i64, i64, i64, dbl, vp]
         lib.oracle_rope.restype = i32
         lib.oracle_permute.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64]
@@ -233,6 +242,95 @@ def paged_gather(k_pool, v_pool, block_table, n_tok, T_max=None):
 # ---------------------------------------------------------------------------
 # Key-range partials and their merge (rescale identity, §18.3)
 # ---------------------------------------------------------------------------
+def attention_positions(q, k, v, q_pos, k_pos, scale):
+    """Attention of ``q [B][Sq][Hq][D]`` over ``k, v [B][Sk][Hkv][D]`` where a
+    query at position P attends the keys at positions <= P ("LLM推理中的多卡切分"
+    §3.5: the causal mask between two ranks' shards).  ``q_pos [B][Sq]``,
+    ``k_pos [B][Sk]``.  Returns (out [B][Sq][Hq][D], lse [B][Hq][Sq]); rows
+    with no allowed key get NaN and -inf."""
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if Bk != B or Dk != D or v.shape != k.shape:
+        raise ValueError("oracle: shape mismatch")
+    qp = np.ascontiguousarray(np.broadcast_to(np.asarray(q_pos, dtype=np.int64), (B, Sq)))
+    kp = np.ascontiguousarray(np.broadcast_to(np.asarray(k_pos, dtype=np.int64), (B, Sk)))
+    out = np.empty((B, Sq, Hq, D), dtype=np.float64)
+    lse = np.empty((B, Hq, Sq), dtype=np.float64)
+    rc = _load().oracle_attention_positions(_ptr(q), _dtype_code(q), _ptr(k), _dtype_code(k),
+                                            _ptr(v), _dtype_code(v), B, Sq, Sk, Hq, Hkv, D,
+                                            _ptr(qp), _ptr(kp), float(scale), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_positions failed ({rc})")
+    return out, lse
+
+
+CP_MODES = ("contiguous", "striped", "zigzag")
+
+
+def cp_tokens(S, N, mode, rank):
+    """Ascending token indices that context-parallel rank ``rank`` of ``N``
+    holds for a sequence of ``S`` tokens ("LLM推理中的多卡切分" §3.5, §3.5.1):
+
+    * ``contiguous`` — ring attention's split into N consecutive blocks;
+    * ``striped`` — round-robin: the tokens with index mod N == rank
+      (S % N == 0, the stated constraint);
+    * ``zigzag`` — in-seq-split: the sequence cut into 2N consecutive blocks,
+      rank i taking blocks i and 2N-1-i (S >= 2N, the stated constraint).
+
+    Block boundaries where S is not a multiple of the block count are a
+    reading: block b spans [floor(b*S/n), floor((b+1)*S/n)).
+    """
+    if not (0 <= rank < N):
+        raise ValueError("oracle: rank out of range")
+    bound = lambda b, n: (b * S) // n
+    if mode == "contiguous":
+        if S < N:
+            raise ValueError("oracle: S < N")
+        return np.arange(bound(rank, N), bound(rank + 1, N), dtype=np.int64)
+    if mode == "striped":
+        if S % N:
+            raise ValueError("oracle: S % N != 0")
+        return np.arange(rank, S, N, dtype=np.int64)
+    if mode == "zigzag":
+        if S < 2 * N:
+            raise ValueError("oracle: S < 2N")
+        a, b = rank, 2 * N - 1 - rank
+        return np.concatenate([np.arange(bound(a, 2 * N), bound(a + 1, 2 * N)),
+                               np.arange(bound(b, 2 * N), bound(b + 1, 2 * N))]).astype(np.int64)
+    raise ValueError(f"oracle: unknown CP mode {mode!r}")
+
+
+def merge_normalized(parts):
+    """Combine normalised partials [(O_s, LSE_s)] of the same queries over
+    disjoint key sets: M = max LSE_s, w_s = exp(LSE_s - M),
+    O = sum w_s O_s / sum w_s, LSE = M + ln sum w_s (the rescale identity of
+    "Flash Attention and distributed inference" §18.3).  Partials with
+    LSE = -inf (no key) get weight 0; if all do, O = 0 and LSE = -inf.
+    Layouts: O [B][S][H][D] with LSE [B][H][S] (the attention outputs), or
+    any O [..., D] with LSE [...]."""
+    Os = [np.asarray(O, dtype=np.float64) for O, _ in parts]
+    Ls = [np.asarray(L, dtype=np.float64) for _, L in parts]
+    four = Os[0].ndim == 4 and Ls[0].ndim == 3
+    if four:
+        Ls = [np.swapaxes(L, 1, 2) for L in Ls]      # -> [B][S][H]
+    M = np.max(np.stack(Ls), axis=0)
+    Ms = np.where(np.isfinite(M), M, 0.0)
+    num = np.zeros(Os[0].shape)
+    den = np.zeros(M.shape)
+    for O, L in zip(Os, Ls):
+        live = np.isfinite(L)
+        w = np.where(live, np.exp(np.where(live, L, 0.0) - Ms), 0.0)
+        num = num + w[..., None] * np.where(live[..., None], O, 0.0)
+        den = den + w
+    safe = np.where(den > 0, den, 1.0)
+    O = np.where(den[..., None] > 0, num / safe[..., None], 0.0)
+    lse = np.where(den > 0, Ms + np.log(safe), -np.inf)
+    if four:
+        lse = np.swapaxes(lse, 1, 2)
+    return O, lse
+
+
 def partial_attention(q_vec, k_rows, v_rows, scale):
     """Unnormalised partial of one query over a key range.
 

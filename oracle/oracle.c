@@ -19,6 +19,8 @@
  *    inverse for the attention output (head shard back to sequence shards).
  *  - gather of a head-sharded paged KV cache (same article, §2.3) into
  *    contiguous order.
+ *  - attention with the causal mask on token positions, for the sequence
+ *    shards of context-parallel ranks ("LLM推理中的多卡切分", §3.5).
  *
  * Inputs may be fp64, fp32 or bf16 bit patterns; they are widened to fp64
  * exactly on read.  OpenMP splits independent (batch, row, head) items only.
@@ -108,6 +110,78 @@ int oracle_attention_rows(const void *q_rows, int q_dtype, const void *k, int k_
       lse[(b * Hq + h) * R + r] = m + log(z);
     }
     free(s);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * Attention with the causal mask stated on token positions, for query and
+ * key sets that are arbitrary subsets of one sequence (the shards that
+ * context-parallel ranks hold: contiguous, striped or zigzag; "LLM推理中的
+ * 多卡切分", §3.5).  A query at position P may attend exactly the keys whose
+ * position is <= P, wherever those keys sit in the key array.
+ *   q      : [B][Sq][Hq][D],  q_pos : [B][Sq]
+ *   k, v   : [B][Sk][Hkv][D], k_pos : [B][Sk]
+ *   out    : [B][Sq][Hq][D] fp64, lse : [B][Hq][Sq]
+ * Rows with no allowed key get out = NaN and lse = -inf.  Three-pass softmax
+ * as in oracle_attention_rows.
+ */
+int oracle_attention_positions(const void *q, int q_dtype, const void *k, int k_dtype,
+                               const void *v, int v_dtype, int64_t B, int64_t Sq, int64_t Sk,
+                               int64_t Hq, int64_t Hkv, int64_t D, const int64_t *q_pos,
+                               const int64_t *k_pos, double scale, double *out, double *lse) {
+  if (!q || !k || !v || !q_pos || !k_pos || !out || !lse) return -1;
+  if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return -1;
+  const int64_t group = Hq / Hkv;
+  const int64_t n_items = B * Sq * Hq;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+    int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)(Sk > 0 ? Sk : 1));
+    if (!s || !key) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t item = 0; item < n_items; ++item) {
+      if (!s || !key) continue;
+      const int64_t h = item % Hq;
+      const int64_t r = (item / Hq) % Sq;
+      const int64_t b = item / (Hq * Sq);
+      const int64_t g = h / group;
+      double *o = out + ((b * Sq + r) * Hq + h) * D;
+      const int64_t q_off = ((b * Sq + r) * Hq + h) * D;
+      /* the allowed keys: position not after the query's */
+      int64_t n = 0;
+      for (int64_t j = 0; j < Sk; ++j)
+        if (k_pos[b * Sk + j] <= q_pos[b * Sq + r]) key[n++] = j;
+      if (n == 0) {
+        for (int64_t d = 0; d < D; ++d) o[d] = NAN;
+        lse[(b * Hq + h) * Sq + r] = -INFINITY;
+        continue;
+      }
+      for (int64_t t = 0; t < n; ++t) {
+        const int64_t k_off = ((b * Sk + key[t]) * Hkv + g) * D;
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d) acc += widen(q, q_dtype, q_off + d) * widen(k, k_dtype, k_off + d);
+        s[t] = scale * acc;
+      }
+      double m = -INFINITY;
+      for (int64_t t = 0; t < n; ++t)
+        if (s[t] > m) m = s[t];
+      double z = 0.0;
+      for (int64_t t = 0; t < n; ++t) z += exp(s[t] - m);
+      for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+      for (int64_t t = 0; t < n; ++t) {
+        const double a = exp(s[t] - m) / z;
+        const int64_t v_off = ((b * Sk + key[t]) * Hkv + g) * D;
+        for (int64_t d = 0; d < D; ++d) o[d] += a * widen(v, v_dtype, v_off + d);
+      }
+      lse[(b * Hq + h) * Sq + r] = m + log(z);
+    }
+    free(s);
+    free(key);
   }
   return failed ? -1 : 0;
 }

@@ -376,6 +376,104 @@ def test_unpermute_inverts_permute_and_touches_only_its_heads():
 
 
 # ---------------------------------------------------------------------------
+# Context-parallel splits and the position-stated causal mask
+# ---------------------------------------------------------------------------
+def test_cp_maps_worked_examples():
+    """The splits the CP section prints: ring (12 tokens, 4 GPUs), striped (16
+    tokens, 4 GPUs) and the zigzag block layout 0 7 1 6 2 5 3 4 (one token
+    per block)."""
+    n = 0
+    with open(os.path.join(GOLDEN, "cp_index_maps.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            head, toks = line.split(":")
+            mode, S, N, r = head.split()
+            want = [int(t) for t in toks.split()]
+            assert list(oracle.cp_tokens(int(S), int(N), mode, int(r))) == want, line
+            n += 1
+    assert n == 12
+
+
+@pytest.mark.parametrize("mode", ["contiguous", "striped", "zigzag"])
+@pytest.mark.parametrize("S,N", [(16, 4), (48, 4), (40, 2), (64, 8)])
+def test_cp_maps_partition_and_balance(mode, S, N):
+    """Every token belongs to exactly one rank, each rank's list ascends, and
+    the zigzag and striped splits balance causal work as the section says
+    (zigzag exactly when S % 2N == 0: sum of (t+1) equal over ranks)."""
+    parts = [oracle.cp_tokens(S, N, mode, r) for r in range(N)]
+    allt = np.concatenate(parts)
+    assert np.array_equal(np.sort(allt), np.arange(S))
+    for p_ in parts:
+        assert np.all(np.diff(p_) > 0)
+    work = [int(np.sum(p_ + 1)) for p_ in parts]
+    if mode == "zigzag" and S % (2 * N) == 0:
+        assert len(set(work)) == 1
+    if mode == "striped":
+        assert max(work) - min(work) <= S // N * (N - 1)
+    if mode == "contiguous" and S >= 2 * N:
+        assert work[-1] > work[0]          # the imbalance the section points out
+
+
+def test_attention_positions_is_causal_on_the_full_sequence():
+    d = synth.dense_bf16(seed=31, B=1, S=70, Hq=4, Hkv=2, D=16)
+    pos = np.arange(70)
+    o1, l1 = oracle.attention_positions(d["q"], d["k"], d["v"], pos, pos, d["scale"])
+    o2, l2 = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=True)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-12) and np.allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+def test_attention_positions_brute_force():
+    """Against a full-matrix numpy softmax with the mask built from positions
+    (scattered, unsorted query and key positions; one query sees no key)."""
+    rng = np.random.default_rng(32)
+    Sq, Sk, D = 9, 11, 8
+    q = rng.standard_normal((1, Sq, 1, D))
+    k = rng.standard_normal((1, Sk, 1, D))
+    v = rng.standard_normal((1, Sk, 1, D))
+    qp = rng.permutation(40)[:Sq]
+    kp = rng.permutation(40)[:Sk]
+    qp[0] = min(kp) - 1 if min(kp) > 0 else qp[0]
+    o, l = oracle.attention_positions(q, k, v, qp, kp, 0.3)
+    for i in range(Sq):
+        vis = kp <= qp[i]
+        if not vis.any():
+            assert np.isnan(o[0, i, 0]).all() and l[0, 0, i] == -np.inf
+            continue
+        s = 0.3 * (k[0, vis, 0] @ q[0, i, 0])
+        w = np.exp(s - s.max())
+        assert np.allclose(o[0, i, 0], (w / w.sum()) @ v[0, vis, 0], rtol=0, atol=1e-12)
+        assert abs(l[0, 0, i] - (s.max() + np.log(w.sum()))) < 1e-12
+
+
+@pytest.mark.parametrize("mode", ["contiguous", "striped", "zigzag"])
+def test_cp_partials_merge_to_the_causal_rows(mode):
+    """Ring attention on one rank: its queries against every rank's key
+    shard, merged by LSE, equal the causal attention rows of its tokens;
+    and the normalised merge agrees with the unnormalised one."""
+    S, N = 48, 4
+    d = synth.dense_bf16(seed=33, B=1, S=S, Hq=4, Hkv=2, D=16)
+    for r in range(N):
+        tq = oracle.cp_tokens(S, N, mode, r)
+        parts = []
+        for s_ in range(N):
+            tk = oracle.cp_tokens(S, N, mode, s_)
+            parts.append(oracle.attention_positions(d["q"][:, tq], d["k"][:, tk], d["v"][:, tk], tq,
+                                                    tk, d["scale"]))
+        o, l = oracle.merge_normalized(parts)
+        ref, ref_l = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=True, rows=tq)
+        assert np.allclose(o, ref, rtol=0, atol=1e-12) and np.allclose(l, ref_l, rtol=0, atol=1e-12)
+    # one row through the unnormalised identity as well
+    q0 = oracle.widen(d["q"][0, S - 1, 0])
+    raw = [oracle.partial_attention(q0, d["k"][0, tk, 0], d["v"][0, tk, 0], d["scale"])
+           for tk in (np.arange(0, 20), np.arange(20, 48))]
+    o_u, l_u = oracle.lse_merge(raw)
+    o_n, l_n = oracle.merge_normalized([(p_[2] / p_[1], p_[0] + np.log(p_[1])) for p_ in raw])
+    assert np.allclose(o_u, o_n, rtol=0, atol=1e-12) and abs(l_u - l_n) < 1e-12
+
+
+# ---------------------------------------------------------------------------
 # Paged cache read-back
 # ---------------------------------------------------------------------------
 def test_paged_gather_hand_example():
