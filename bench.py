@@ -20,6 +20,8 @@ The same JSON line also carries, each measured in this run:
   prefill_64k     the relayout + RoPE + causal prefill pipeline at 65536,
                   with separate and with fused relayout + RoPE;
   chunked_prefill 4 requests x 131072 tokens in 8192-token chunks;
+  cp_zigzag_64k   one rank of zigzag context parallelism (4 ranks, 65536
+                  tokens): partials against every key shard + LSE merges;
   cpu_baseline    the fp64 CPU oracle timed on a bounded sample of query rows
                   of the step workload, on this host's cores.
 The decode and relayout times are means over calls enqueued back to back.
@@ -304,6 +306,50 @@ def bench_chunked(torch, lcat, synth):
                 workload="4 requests x 131072 tokens, 8192-token chunks, 16 Q / 2 KV heads")
 
 
+def bench_cp(torch, lcat, iters=3):
+    """Zigzag context parallelism, 4 ranks over 65536 tokens, 16 Q / 2 KV heads:
+    the work of one rank (its queries against every rank's key shard with
+    position-derived limits, then the LSE merges), all shards resident."""
+    S, N, Hq, Hkv, mode = 65536, 4, 16, 2, "zigzag"
+    q = seeded_normal_bf16(torch, (S, Hq, D), 61)
+    k = seeded_normal_bf16(torch, (S, Hkv, D), 62)
+    v = seeded_normal_bf16(torch, (S, Hkv, D), 63)
+    shards = [(lcat.cp_shard(k, N, s_, mode), lcat.cp_shard(v, N, s_, mode)[0]) for s_ in range(N)]
+    res = {}
+    for rank in (0, N - 1):
+        qr, qpos = lcat.cp_shard(q, N, rank, mode)
+        n = qr.shape[0]
+        lims = [torch.empty((1, n), dtype=torch.int32, device="cuda") for _ in range(N)]
+        parts = [(torch.empty((1, n, Hq, D), dtype=torch.bfloat16, device="cuda"),
+                  torch.empty((1, Hq, n), dtype=torch.float32, device="cuda")) for _ in range(N)]
+
+        def rank_step():
+            for s_, ((ks, kpos), vs) in enumerate(shards):
+                lcat.attn_key_limits(qpos, kpos, out=lims[s_])
+                lcat.attn_prefill_limited(qr[None], ks[None], vs[None], lims[s_], o=parts[s_][0],
+                                          lse=parts[s_][1])
+            for s_ in range(1, N):
+                lcat.attn_merge(parts[0][0], parts[0][1], parts[s_][0], parts[s_][1],
+                                o=parts[0][0], lse=parts[0][1])
+
+        rank_step()
+        torch.cuda.synchronize()
+        timer = EventTimer(torch)
+        for _ in range(iters):
+            with timer:
+                rank_step()
+        torch.cuda.synchronize()
+        ms = timer.mean_ms()
+        pairs = float((qpos.long() + 1).sum().item())      # causal: keys at positions <= p
+        flops = 4.0 * D * Hq * pairs
+        tf = flops / (ms * 1e-3) / 1e12
+        res[f"rank{rank}"] = dict(ms=round(ms, 3), TFLOPs=round(tf, 1),
+                                  frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4), flop=flops)
+    res["workload"] = ("zigzag context parallelism, 4 ranks over 65536 tokens, 16 Q / 2 KV heads: "
+                       "one rank's 4 partials (key limits + prefix-limited prefill) and 3 LSE merges")
+    return res
+
+
 def cpu_baseline(d, target_rows=1024):
     """fp64 oracle on a seeded sample of query rows of the step workload
     (RoPE of those rows and of all keys, then causal attention)."""
@@ -332,7 +378,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="time only the step workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "decode", "relayout", "chunked"],
+    ap.add_argument("--only", choices=["step", "decode", "relayout", "chunked", "cp"],
                     help="run a single leg (for profiling); prints its own JSON object")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -356,6 +402,8 @@ def main():
             res = bench_decode(torch, lcat, synth)
         elif args.only == "relayout":
             res = bench_relayout_and_prefill_64k(torch, lcat)
+        elif args.only == "cp":
+            res = bench_cp(torch, lcat)
         else:
             res = bench_chunked(torch, lcat, synth)
         print(json.dumps({args.only: res}), flush=True)
@@ -380,6 +428,8 @@ def main():
             bench_relayout_and_prefill_64k(torch, lcat)
         log("bench: chunked prefill")
         out["chunked_prefill"] = bench_chunked(torch, lcat, synth)
+        log("bench: context parallelism (zigzag, 4 ranks, 64k)")
+        out["cp_zigzag_64k"] = bench_cp(torch, lcat)
     if not args.no_cpu_baseline and not args.only:
         log("bench: cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(d)

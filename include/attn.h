@@ -13,7 +13,8 @@
  *            global head index, §3.2 RoPE at absolute token positions,
  *            §3.5 1e-3 numeric alignment, §5.3 full-sequence causal mask.
  *  [MGP]     "LLM推理中的多卡切分" (multi-GPU partitioning in LLM inference):
- *            §2.1 request-token -> KV-slot allocation, §2.2 chunked prefill.
+ *            §2.1 request-token -> KV-slot allocation, §2.2 chunked prefill,
+ *            §3.5 / §3.5.1 context parallelism (ring, striped, zigzag).
  *
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -66,6 +67,13 @@ enum attn_status {
 enum attn_dtype { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 };
 
 enum attn_dev_status { ATTN_DEV_OK = 0, ATTN_DEV_BAD_TAG = 1, ATTN_DEV_BAD_BLOCK = 2 };
+
+/* Context-parallel splits of a sequence over N ranks ([MGP] §3.5, §3.5.1). */
+enum attn_cp_mode {
+  ATTN_CP_CONTIGUOUS = 0, /* ring attention: N consecutive blocks */
+  ATTN_CP_STRIPED = 1,    /* round-robin: tokens with index mod N == rank; S % N == 0 */
+  ATTN_CP_ZIGZAG = 2      /* in-seq-split: 2N blocks, rank i holds blocks i and 2N-1-i; S >= 2N */
+};
 
 /*
  * attn_prefill — exact softmax attention over dense Q/K/V ([FA18] §18.2 for
@@ -207,6 +215,73 @@ int seq_to_head_permute_qkv_rope(const void *q_in, const void *k_in, const void 
  */
 int head_to_seq_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
                         int elem_bytes, void *stream);
+
+/*
+ * Context parallelism on one GPU ([MGP] §3.5: ring, striped and zigzag
+ * attention; §3.5.1: round-robin-split and in-seq-split).  Block b of a split
+ * into n blocks spans tokens [floor(b*S/n), floor((b+1)*S/n)) (a reading: the
+ * pages only state S % N == 0 for round-robin and S >= 2N for in-seq-split).
+ * A rank's tokens are listed in ascending order.
+ *
+ * cp_shard_tokens — number of tokens rank `rank` of N holds, or
+ *   -ATTN_ERR_SHAPE / -ATTN_ERR_UNSUPPORTED if the split is not defined.
+ *   Host only; touches no memory.
+ */
+long long cp_shard_tokens(long long S, int N, int rank, int mode);
+
+/*
+ * cp_shard — gather rank `rank`'s tokens: full [S][H][D] -> shard [n][H][D]
+ *   (n = cp_shard_tokens), rows of H*D elements of elem_bytes bytes copied bit
+ *   for bit, and positions[i] (int32, nullable) = global index of local token
+ *   i — the global token index table of [ULY] §3.2 for this shard.
+ * cp_unshard — the inverse: shard [n][H][D] back into its rows of full
+ *   [S][H][D]; the other ranks' rows are left untouched.
+ * Input and output must not overlap (ATTN_ERR_SHAPE).
+ */
+int cp_shard(const void *full, void *shard, int32_t *positions, long long S, int H, int D,
+             int elem_bytes, int N, int rank, int mode, void *stream);
+int cp_unshard(const void *shard, void *full, long long S, int H, int D, int elem_bytes, int N,
+               int rank, int mode, void *stream);
+
+/*
+ * attn_key_limits — per-row key counts for a causal mask stated on positions
+ * ([MGP] §3.5: between two ranks' shards the causal rule compares original
+ * token positions):
+ *   key_limit[b][i] = #{ j : k_pos[b][j] <= q_pos[b][i] }
+ * q_pos [B][Sq], k_pos [B][Sk], key_limit [B][Sq], all int32 on the device.
+ * k_pos must be ascending (each rank's shard is); then the allowed keys of
+ * every row are a prefix of the key array, which is what
+ * attn_prefill_limited consumes.
+ */
+int attn_key_limits(const int32_t *q_pos, const int32_t *k_pos, int32_t *key_limit, int B, int Sq,
+                    int Sk, void *stream);
+
+/*
+ * attn_prefill_limited — attn_prefill (bf16, D = 128) where row i of batch b
+ * attends keys [0, key_limit[b][i]) of k/v [B][Sk][Hkv][D], Sk >= 1 ([FA18] §18.3
+ * online softmax over that prefix).  Limits are clamped to [0, Sk] and must
+ * not decrease along i (for each b); a row with limit 0 gets O = 0 and
+ * LSE = -inf, i.e. weight 0 in attn_merge.  q, o [B][Sq][Hq][D]; lse
+ * [B][Hq][Sq] (nullable).  This is the partial attention of one rank's
+ * queries against one key shard in ring / striped / zigzag attention.
+ */
+int attn_prefill_limited(const void *q, const void *k, const void *v, const int32_t *key_limit,
+                         void *o, float *lse, int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                         float scale, void *stream);
+
+/*
+ * attn_merge — combine two normalised partial results of the same rows over
+ * disjoint key sets ([FA18] §18.3 rescale identity, as the log-sum-exp merge
+ * of partial attention):
+ *   M = max(La, Lb), wa = e^(La-M), wb = e^(Lb-M),
+ *   O = (wa Oa + wb Ob) / (wa + wb),  LSE = M + ln(wa + wb)
+ * A side with LSE = -inf has weight 0; if both do, O = 0 and LSE = -inf.
+ * O* [B][S][H][D] bf16, LSE* [B][H][S] fp32 (the layouts attn_prefill
+ * writes); lse is nullable.  D % 8 == 0 and D/8 divides 64.  o may be o_a or
+ * o_b itself (in place), lse likewise; any other overlap is ATTN_ERR_SHAPE.
+ */
+int attn_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, void *o,
+               float *lse, int B, int S, int H, int D, void *stream);
 
 /* Static, human-readable text for an attn_status value. */
 const char *attn_status_string(int status);

@@ -19,19 +19,22 @@ from __future__ import annotations
 import ctypes
 
 from . import _lib
-from ._lib import (ATTN_DEV_BAD_BLOCK, ATTN_DEV_BAD_TAG, ATTN_DEV_OK, ATTN_DTYPE_BF16,
-                   ATTN_DTYPE_F32, AttnError)
+from ._lib import (ATTN_CP_CONTIGUOUS, ATTN_CP_STRIPED, ATTN_CP_ZIGZAG, ATTN_DEV_BAD_BLOCK,
+                   ATTN_DEV_BAD_TAG, ATTN_DEV_OK, ATTN_DTYPE_BF16, ATTN_DTYPE_F32, AttnError)
 
 __all__ = [
     "attn_prefill", "attn_chunked_prefill", "attn_kv_append", "attn_decode",
     "attn_decode_workspace_bytes", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv", "head_to_seq_permute",
-    "seq_to_head_permute_qkv_rope",
+    "seq_to_head_permute_qkv_rope", "cp_shard_tokens", "cp_shard", "cp_unshard",
+    "attn_key_limits", "attn_prefill_limited", "attn_merge", "CP_MODES",
     "attn_status_string",
     "AttnError", "ATTN_DEV_OK", "ATTN_DEV_BAD_TAG", "ATTN_DEV_BAD_BLOCK", "load_library",
 ]
 
 HEAD_DIM = 128
 BLOCK_TOKENS = 64
+# context-parallel split names -> enum attn_cp_mode
+CP_MODES = {"contiguous": ATTN_CP_CONTIGUOUS, "striped": ATTN_CP_STRIPED, "zigzag": ATTN_CP_ZIGZAG}
 
 
 def load_library():
@@ -307,3 +310,114 @@ def head_to_seq_permute(x, SP, H_tot, rank, out=None, stream=None):
                                          x.element_size(), _stream(stream))
     _lib.check("head_to_seq_permute", st)
     return out
+
+
+def _cp_mode(mode):
+    if mode not in CP_MODES:
+        raise ValueError(f"mode must be one of {sorted(CP_MODES)}")
+    return CP_MODES[mode]
+
+
+def cp_shard_tokens(S, N, rank, mode) -> int:
+    """Tokens that CP rank ``rank`` of ``N`` holds under ``mode`` (host only)."""
+    n = _lib.load().cp_shard_tokens(int(S), int(N), int(rank), _cp_mode(mode))
+    if n < 0:
+        _lib.check("cp_shard_tokens", -n)
+    return n
+
+
+def cp_shard(x, N, rank, mode, out=None, positions=None, stream=None):
+    """Rank's tokens of ``x [S][H][D]`` -> ``(out [n][H][D], positions [n] int32)``."""
+    torch = _torch()
+    _need(x, "x")
+    S, H, D = x.shape
+    n = cp_shard_tokens(S, N, rank, mode)
+    if out is None:
+        out = torch.empty((n, H, D), dtype=x.dtype, device=x.device)
+    _need(out, "out", x.dtype, (n, H, D))
+    if positions is None:
+        positions = torch.empty((n,), dtype=torch.int32, device=x.device)
+    _need(positions, "positions", torch.int32, (n,))
+    st = _lib.load().cp_shard(_ptr(x), _ptr(out), _ptr(positions), S, H, D, x.element_size(),
+                              int(N), int(rank), _cp_mode(mode), _stream(stream))
+    _lib.check("cp_shard", st)
+    return out, positions
+
+
+def cp_unshard(x, S, N, rank, mode, out=None, stream=None):
+    """``x [n][H][D]`` of rank back into its rows of ``out [S][H][D]`` (other
+    rows untouched; a new ``out`` is zero-filled first)."""
+    torch = _torch()
+    _need(x, "x")
+    n, H, D = x.shape
+    if n != cp_shard_tokens(S, N, rank, mode):
+        raise ValueError("x does not hold this rank's token count")
+    if out is None:
+        out = torch.zeros((S, H, D), dtype=x.dtype, device=x.device)
+    _need(out, "out", x.dtype, (S, H, D))
+    st = _lib.load().cp_unshard(_ptr(x), _ptr(out), S, H, D, x.element_size(), int(N), int(rank),
+                                _cp_mode(mode), _stream(stream))
+    _lib.check("cp_unshard", st)
+    return out
+
+
+def attn_key_limits(q_pos, k_pos, out=None, stream=None):
+    """``key_limit[b][i] = #{j : k_pos[b][j] <= q_pos[b][i]}`` (int32; k_pos
+    ascending); ``q_pos [B][Sq]`` or ``[Sq]``, ``k_pos`` likewise."""
+    torch = _torch()
+    qp = q_pos if q_pos.dim() == 2 else q_pos[None]
+    kp = k_pos if k_pos.dim() == 2 else k_pos[None]
+    B, Sq = qp.shape
+    Sk = kp.shape[1]
+    _need(qp, "q_pos", torch.int32, (B, Sq))
+    _need(kp, "k_pos", torch.int32, (B, Sk))
+    if out is None:
+        out = torch.empty((B, Sq), dtype=torch.int32, device=qp.device)
+    _need(out, "key_limit", torch.int32, (B, Sq))
+    st = _lib.load().attn_key_limits(_ptr(qp), _ptr(kp), _ptr(out), B, Sq, Sk, _stream(stream))
+    _lib.check("attn_key_limits", st)
+    return out
+
+
+def attn_prefill_limited(q, k, v, key_limit, scale=None, o=None, lse=None, stream=None):
+    """bf16 attention where row i of batch b sees keys ``[0, key_limit[b][i])``;
+    q ``[B][Sq][Hq][128]``, k/v ``[B][Sk][Hkv][128]``; returns ``(o, lse)``."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    _need(k, "k", torch.bfloat16, (B, Sk, Hkv, D))
+    _need(v, "v", torch.bfloat16, (B, Sk, Hkv, D))
+    _need(key_limit, "key_limit", torch.int32, (B, Sq))
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, q.shape)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, (B, Hq, Sq))
+    scale = float(D ** -0.5) if scale is None else float(scale)
+    st = _lib.load().attn_prefill_limited(_ptr(q), _ptr(k), _ptr(v), _ptr(key_limit), _ptr(o),
+                                          _ptr(lse), B, Sq, Sk, Hq, Hkv, D, scale, _stream(stream))
+    _lib.check("attn_prefill_limited", st)
+    return o, lse
+
+
+def attn_merge(o_a, lse_a, o_b, lse_b, o=None, lse=None, stream=None):
+    """Merge two normalised partials (bf16 O ``[B][S][H][D]``, fp32 LSE
+    ``[B][H][S]``) of the same rows; ``o``/``lse`` may be ``o_a``/``lse_a``."""
+    torch = _torch()
+    _need(o_a, "o_a", torch.bfloat16)
+    B, S, H, D = o_a.shape
+    _need(o_b, "o_b", torch.bfloat16, (B, S, H, D))
+    _need(lse_a, "lse_a", torch.float32, (B, H, S))
+    _need(lse_b, "lse_b", torch.float32, (B, H, S))
+    if o is None:
+        o = torch.empty_like(o_a)
+    _need(o, "o", torch.bfloat16, (B, S, H, D))
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    _need(lse, "lse", torch.float32, (B, H, S))
+    st = _lib.load().attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(lse),
+                                B, S, H, D, _stream(stream))
+    _lib.check("attn_merge", st)
+    return o, lse

@@ -14,11 +14,15 @@ ATTN_DTYPE_BF16 = 1
 ATTN_DEV_OK = 0
 ATTN_DEV_BAD_TAG = 1
 ATTN_DEV_BAD_BLOCK = 2
+ATTN_CP_CONTIGUOUS = 0
+ATTN_CP_STRIPED = 1
+ATTN_CP_ZIGZAG = 2
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
 _sz = ctypes.c_size_t
+_ll = ctypes.c_longlong
 
 SIGNATURES = {
     "attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
@@ -36,6 +40,12 @@ SIGNATURES = {
                                           _i, _f, _vp]),
     "seq_to_head_permute_qkv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                      _vp]),
+    "cp_shard_tokens": (_ll, [_ll, _i, _i, _i]),
+    "cp_shard": (_i, [_vp, _vp, _vp, _ll, _i, _i, _i, _i, _i, _i, _vp]),
+    "cp_unshard": (_i, [_vp, _vp, _ll, _i, _i, _i, _i, _i, _i, _vp]),
+    "attn_key_limits": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
+    "attn_prefill_limited": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp]),
+    "attn_merge": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
 }
 

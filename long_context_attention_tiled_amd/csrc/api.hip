@@ -53,6 +53,41 @@ inline long long decode_n_split(int max_blocks, int split_tokens) {
   return (keys + split_tokens - 1) / split_tokens;
 }
 
+// Map of CP rank `rank` of N for a sequence of S tokens, or false if the
+// split is not defined for these sizes.
+bool cp_map(long long S, int N, int rank, int mode, lcat::CpMap &m, long long &n_tok) {
+  if (S < 0 || N <= 0 || rank < 0 || rank >= N) return false;
+  auto bound = [&](long long b, long long n) { return b * S / n; };
+  m.start_b = 0;
+  m.stride = 1;
+  switch (mode) {
+    case ATTN_CP_CONTIGUOUS:
+      if (S < N) return false;
+      m.start_a = bound(rank, N);
+      m.len_a = bound(rank + 1, N) - m.start_a;
+      n_tok = m.len_a;
+      return true;
+    case ATTN_CP_STRIPED:
+      if (S % N) return false;
+      m.start_a = rank;
+      m.stride = N;
+      m.len_a = S / N;
+      n_tok = m.len_a;
+      return true;
+    case ATTN_CP_ZIGZAG: {
+      if (S < 2LL * N) return false;
+      const long long a = rank, b = 2LL * N - 1 - rank;
+      m.start_a = bound(a, 2LL * N);
+      m.len_a = bound(a + 1, 2LL * N) - m.start_a;
+      m.start_b = bound(b, 2LL * N);
+      n_tok = m.len_a + (bound(b + 1, 2LL * N) - m.start_b);
+      return true;
+    }
+    default:
+      return false;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -268,6 +303,90 @@ int seq_to_head_permute_qkv_rope(const void *q_in, const void *k_in, const void 
   if (!qkv_disjoint(in, out, H, SP, S_loc, D, 2)) return ATTN_ERR_SHAPE;
   return hip_status(lcat::launch_permute_qkv_rope(in, out, H, positions, SP, S_loc, D, rank, base,
                                                   static_cast<hipStream_t>(stream)));
+}
+
+long long cp_shard_tokens(long long S, int N, int rank, int mode) {
+  lcat::CpMap m{};
+  long long n = 0;
+  if (mode != ATTN_CP_CONTIGUOUS && mode != ATTN_CP_STRIPED && mode != ATTN_CP_ZIGZAG)
+    return -ATTN_ERR_UNSUPPORTED;
+  return cp_map(S, N, rank, mode, m, n) ? n : -ATTN_ERR_SHAPE;
+}
+
+static int cp_copy(const void *in, void *out, int32_t *positions, long long S, int H, int D,
+                   int elem_bytes, int N, int rank, int mode, int scatter, void *stream) {
+  if (S < 0 || H <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return ATTN_ERR_DTYPE;
+  if (mode != ATTN_CP_CONTIGUOUS && mode != ATTN_CP_STRIPED && mode != ATTN_CP_ZIGZAG)
+    return ATTN_ERR_UNSUPPORTED;
+  lcat::CpMap m{};
+  long long n_tok = 0;
+  if (!cp_map(S, N, rank, mode, m, n_tok)) return ATTN_ERR_SHAPE;
+  if (S == 0) return ATTN_OK;
+  if (!in || !out) return ATTN_ERR_NULL;
+  const long long row = (long long)H * D * elem_bytes;
+  const char *a = static_cast<const char *>(in);
+  const char *c = static_cast<const char *>(out);
+  const long long in_bytes = (scatter ? n_tok : S) * row, out_bytes = (scatter ? S : n_tok) * row;
+  if (!(c + out_bytes <= a || a + in_bytes <= c)) return ATTN_ERR_SHAPE;   // overlap
+  return hip_status(lcat::launch_cp_copy(in, out, m, n_tok, row, scatter, positions,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int cp_shard(const void *full, void *shard, int32_t *positions, long long S, int H, int D,
+             int elem_bytes, int N, int rank, int mode, void *stream) {
+  return cp_copy(full, shard, positions, S, H, D, elem_bytes, N, rank, mode, 0, stream);
+}
+
+int cp_unshard(const void *shard, void *full, long long S, int H, int D, int elem_bytes, int N,
+               int rank, int mode, void *stream) {
+  return cp_copy(shard, full, nullptr, S, H, D, elem_bytes, N, rank, mode, 1, stream);
+}
+
+int attn_key_limits(const int32_t *q_pos, const int32_t *k_pos, int32_t *key_limit, int B, int Sq,
+                    int Sk, void *stream) {
+  if (B < 0 || Sq < 0 || Sk < 0) return ATTN_ERR_SHAPE;
+  if (B == 0 || Sq == 0) return ATTN_OK;
+  if (!q_pos || !key_limit || (Sk > 0 && !k_pos)) return ATTN_ERR_NULL;
+  return hip_status(lcat::launch_key_limits(q_pos, k_pos, key_limit, B, Sq, Sk,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int attn_prefill_limited(const void *q, const void *k, const void *v, const int32_t *key_limit,
+                         void *o, float *lse, int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                         float scale, void *stream) {
+  if (B < 0 || Sq < 0 || Sk <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return ATTN_ERR_SHAPE;
+  if (D != kHeadDim || !group_ok(Hq, Hkv)) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !key_limit) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+  lcat::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv;
+  p.causal = 1;
+  p.key_limit = key_limit;
+  p.scale = scale;
+  return hip_status(lcat::launch_prefill_bf16(p, false, static_cast<hipStream_t>(stream)));
+}
+
+int attn_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, void *o,
+               float *lse, int B, int S, int H, int D, void *stream) {
+  if (B < 0 || S < 0 || H <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+  if (D % 8 || 64 % (D / 8)) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || S == 0) return ATTN_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o) return ATTN_ERR_NULL;
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o)) return ATTN_ERR_ALIGN;
+  // o may be o_a or o_b exactly (in place), but no other overlap
+  const long long ob_ = (long long)B * S * H * D * 2, lb_ = (long long)B * S * H * 4;
+  auto part = [](const void *x, long long nx, const void *y, long long ny) {
+    const char *a = static_cast<const char *>(x), *b = static_cast<const char *>(y);
+    return a != b && !(a + nx <= b || b + ny <= a);
+  };
+  if (part(o, ob_, o_a, ob_) || part(o, ob_, o_b, ob_)) return ATTN_ERR_SHAPE;
+  if (lse && (part(lse, lb_, lse_a, lb_) || part(lse, lb_, lse_b, lb_))) return ATTN_ERR_SHAPE;
+  return hip_status(lcat::launch_merge(o_a, lse_a, o_b, lse_b, o, lse, B, S, H, D,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

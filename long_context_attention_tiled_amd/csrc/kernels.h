@@ -25,6 +25,7 @@ struct PrefillParams {
   int max_blocks, n_blocks, kv_head_base;
   int causal;
   float scale;
+  const int32_t *key_limit;  // dense only, or null: row i sees keys [0, key_limit[b][i])
 };
 
 hipError_t launch_prefill_bf16(const PrefillParams &p, bool paged, hipStream_t stream);
@@ -78,5 +79,26 @@ hipError_t launch_permute_qkv(const void *const in[3], void *const out[3], const
 hipError_t launch_permute_qkv_rope(const void *const in[3], void *const out[3], const int H_tot[3],
                                    const int32_t *positions, int SP, int S_loc, int D, int rank,
                                    float base, hipStream_t stream);
+
+// Context-parallel shard of a sequence: local token i is global token
+//   i < len_a ? start_a + i * stride : start_b + (i - len_a) * stride.
+struct CpMap {
+  long long start_a, len_a, start_b, stride;
+};
+
+// Gather (scatter = 0: full [S][row] -> shard [n_tok][row]) or scatter back
+// (scatter = 1); positions (nullable) receives the global index of each
+// local token.
+hipError_t launch_cp_copy(const void *in, void *out, const CpMap &m, long long n_tok,
+                          long long row_bytes, int scatter, int32_t *positions,
+                          hipStream_t stream);
+
+// lim[b][i] = #{j : k_pos[b][j] <= q_pos[b][i]} for ascending k_pos.
+hipError_t launch_key_limits(const int32_t *q_pos, const int32_t *k_pos, int32_t *lim, int B,
+                             int Sq, int Sk, hipStream_t stream);
+
+// Merge of two normalised partial attention results (bf16 O, fp32 LSE).
+hipError_t launch_merge(const void *oa, const float *la, const void *ob, const float *lb, void *o,
+                        float *lse, int B, int S, int H, int D, hipStream_t stream);
 
 }  // namespace lcat

@@ -124,9 +124,12 @@ __device__ __forceinline__ bf16x8 mask_keys(bf16x8 a, int key_first, int nv) {
 // and K_{j+2} for S_{j+2}).
 // Tiles that need the causal/length mask, and the first and last
 // iterations, take a plain sequential path instead of the interleaved one.
-template <bool PAGED, bool CAUSAL>
+// LIMITS (dense, with CAUSAL): row i of batch b sees keys [0, key_limit[b][i])
+// instead of [0, i]; the limits must not decrease along the rows.
+template <bool PAGED, bool CAUSAL, bool LIMITS = false>
 __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_per_wg,
                                                      int head_slices, int n_qblk) {
+  static_assert(!LIMITS || (CAUSAL && !PAGED), "key limits replace the dense causal rule");
   __shared__ __attribute__((aligned(1024))) char smem[(NKS + NVS) * TILE];
 
   const int tid = threadIdx.x;
@@ -157,7 +160,16 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   }
   const int n_keys = PAGED ? qoff + p.Sq : p.Sk;
   int wave_keys = n_keys, wg_keys = n_keys;
-  if (CAUSAL) {
+  int first_keys = n_keys;   // keys visible to every row of this wave (LIMITS)
+  if constexpr (LIMITS) {
+    // keys visible to query row r, clamped to the key count
+    auto row_keys = [&](int r) -> int {
+      return min(max(p.key_limit[(size_t)b * p.Sq + r], 0), n_keys);
+    };
+    wave_keys = row_keys(min(row0 + 31, p.Sq - 1));
+    wg_keys = row_keys(min(qblk * rows_wg + rows_wg - 1, p.Sq - 1));
+    first_keys = row_keys(min(row0, p.Sq - 1));
+  } else if (CAUSAL) {
     wave_keys = min(n_keys, qoff + min(row0 + 31, p.Sq - 1) + 1);
     wg_keys = min(n_keys, qoff + min(qblk * rows_wg + rows_wg - 1, p.Sq - 1) + 1);
   }
@@ -228,7 +240,12 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   auto next_v = [](int x) { return x + TILE == (NKS + NVS) * TILE ? NKS * TILE : x + TILE; };
 
   const float c2 = p.scale * kLog2e;   // scores -> log2 units
-  const int qpos = qoff + qrow;
+  // last key this lane's row may see
+  int qlast;
+  if constexpr (LIMITS)
+    qlast = min(max(p.key_limit[(size_t)b * p.Sq + min(qrow, p.Sq - 1)], 0), n_keys) - 1;
+  else
+    qlast = CAUSAL ? min(n_keys - 1, qoff + qrow) : n_keys - 1;
 
   f32x16 acc[4];
 #pragma unroll
@@ -296,9 +313,10 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   };
   auto softmax_plain = [&](int t, f32x16 (&sc)[2], bf16x8 (&pc)[4]) __attribute__((always_inline)) {
     const int key0 = t * BN;
-    const bool need_mask = (key0 + BN > n_keys) || (CAUSAL && key0 + BN - 1 > qoff + row0);
+    const bool need_mask = LIMITS ? key0 + BN > first_keys
+                                  : (key0 + BN > n_keys) || (CAUSAL && key0 + BN - 1 > qoff + row0);
     if (need_mask) {
-      const int lim = CAUSAL ? min(n_keys - 1, qpos) : n_keys - 1;   // last visible key
+      const int lim = qlast;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = key0 + 16 * (r >> 3) + 8 * gq + (r & 7);
@@ -550,7 +568,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   // Iterations 1 .. fused_end-1 need no mask and have all three parts; the
   // interleaved loop takes them four at a time (ring positions 1, 2, 3, 0).
   int fused_end = min(n_keys / BN, wave_tiles - 1);
-  if (CAUSAL) fused_end = min(fused_end, (qoff + row0 + 1) / BN);
+  if (LIMITS) fused_end = min(fused_end, first_keys / BN);
+  else if (CAUSAL) fused_end = min(fused_end, (qoff + row0 + 1) / BN);
   plain(0, Int<0>{});
   int j = 1;
 #pragma clang loop unroll(disable)
@@ -606,6 +625,9 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, bool paged, hipStream_t s
   if (paged) {
     hipLaunchKernelGGL((prefill_kernel<true, true>), grid, block, 0, stream, p, heads_per_wg,
                        head_slices, n_qblk);
+  } else if (p.key_limit) {
+    hipLaunchKernelGGL((prefill_kernel<false, true, true>), grid, block, 0, stream, p,
+                       heads_per_wg, head_slices, n_qblk);
   } else if (causal) {
     hipLaunchKernelGGL((prefill_kernel<false, true>), grid, block, 0, stream, p, heads_per_wg,
                        head_slices, n_qblk);

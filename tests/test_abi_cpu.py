@@ -29,7 +29,7 @@ S0 = P(0)             # stream
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:[a-z_0-9]+\s+)+\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -43,7 +43,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["attn_prefill", "attn_chunked_prefill", "attn_decode", "attn_decode_workspace_bytes",
               "attn_kv_append", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv",
-              "head_to_seq_permute", "seq_to_head_permute_qkv_rope",
+              "head_to_seq_permute", "seq_to_head_permute_qkv_rope", "cp_shard_tokens",
+              "cp_shard", "cp_unshard", "attn_key_limits", "attn_prefill_limited", "attn_merge",
               "attn_status_string"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -177,6 +178,55 @@ def test_rope_and_permute_validation(lib):
     assert g(q, k, v, qo, P(0x80000000 + 8), vo, pos, 4, 16, 8, 8, 128, 0, 1e4, S0) == ALIGN
     assert g(q, k, v, qo, P(0x60000000 + 64), vo, pos, 4, 16, 8, 8, 128, 0, 1e4, S0) == SHAPE
     assert g(NUL, NUL, NUL, NUL, NUL, NUL, NUL, 4, 0, 8, 8, 128, 0, 1e4, S0) == OK
+
+
+def test_cp_shard_tokens_match_the_oracle_split(lib):
+    import oracle
+    for mode, code in (("contiguous", 0), ("striped", 1), ("zigzag", 2)):
+        for S, N in ((16, 4), (50, 4), (48, 4), (7, 3), (131072, 4)):
+            for r in range(N):
+                try:
+                    want = len(oracle.cp_tokens(S, N, mode, r))
+                except ValueError:
+                    want = -SHAPE
+                assert lib.cp_shard_tokens(S, N, r, code) == want, (mode, S, N, r)
+    assert lib.cp_shard_tokens(16, 4, 0, 3) == -UNSUP
+    assert lib.cp_shard_tokens(16, 4, 4, 0) == -SHAPE
+    assert lib.cp_shard_tokens(16, 0, 0, 0) == -SHAPE
+
+
+def test_cp_and_merge_validation(lib):
+    sh = lib.cp_shard
+    pos = P(0xC0000000)
+    assert sh(A16, P(0x90000000), pos, 16, 8, 128, 2, 4, 0, 5, S0) == UNSUP     # mode
+    assert sh(A16, P(0x90000000), pos, 18, 8, 128, 2, 4, 0, 1, S0) == SHAPE     # striped S % N
+    assert sh(A16, P(0x90000000), pos, 7, 8, 128, 2, 4, 0, 2, S0) == SHAPE      # zigzag S < 2N
+    assert sh(A16, P(0x90000000), pos, 16, 8, 128, 3, 4, 0, 0, S0) == DTYPE
+    assert sh(NUL, P(0x90000000), pos, 16, 8, 128, 2, 4, 0, 0, S0) == NULL
+    assert sh(A16, P(0x10000 + 64), pos, 16, 8, 128, 2, 4, 0, 0, S0) == SHAPE   # overlap
+    assert sh(NUL, NUL, NUL, 0, 8, 128, 2, 4, 0, 2, S0) == SHAPE                # 0 < 2N
+    assert sh(NUL, NUL, NUL, 0, 8, 128, 2, 1, 0, 1, S0) == OK
+    un = lib.cp_unshard
+    assert un(A16, P(0x90000000), 16, 8, 128, 2, 4, 4, 0, S0) == SHAPE         # rank
+    assert un(P(0x10000 + 64), A16, 16, 8, 128, 2, 4, 0, 0, S0) == SHAPE       # overlap
+    kl = lib.attn_key_limits
+    assert kl(A16, NUL, P(0x90000000), 1, 10, 10, S0) == NULL
+    assert kl(A16, A16, P(0x90000000), 1, -1, 10, S0) == SHAPE
+    assert kl(NUL, NUL, NUL, 1, 0, 10, S0) == OK
+    pl = lib.attn_prefill_limited
+    q, k, v, o = P(0x10000), P(0x20000000), P(0x40000000), P(0x60000000)
+    assert pl(q, k, v, pos, o, NUL, 1, 64, 64, 16, 2, 64, 0.1, S0) == UNSUP   # D
+    assert pl(q, k, v, pos, o, NUL, 1, 64, 64, 16, 3, 128, 0.1, S0) == SHAPE  # Hq % Hkv
+    assert pl(q, k, v, NUL, o, NUL, 1, 64, 64, 16, 2, 128, 0.1, S0) == NULL
+    assert pl(q, k, v, pos, P(0x60000000 + 8), NUL, 1, 64, 64, 16, 2, 128, 0.1, S0) == ALIGN
+    assert pl(NUL, NUL, NUL, NUL, NUL, NUL, 1, 0, 64, 16, 2, 128, 0.1, S0) == OK
+    mg = lib.attn_merge
+    la, lb = P(0xA0000000), P(0xB0000000)
+    assert mg(q, la, k, lb, o, NUL, 1, 64, 16, 100, S0) == UNSUP               # D % 8
+    assert mg(q, la, k, lb, o, NUL, 1, 64, 16, 24, S0) == UNSUP                # 64 % (D/8)
+    assert mg(q, NUL, k, lb, o, NUL, 1, 64, 16, 128, S0) == NULL
+    assert mg(q, la, k, lb, P(0x10000 + 256), NUL, 1, 64, 16, 128, S0) == SHAPE   # partial overlap
+    assert mg(q, la, k, lb, o, P(0xA0000000 + 4), 1, 64, 16, 128, S0) == SHAPE   # lse overlap
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -8,7 +8,9 @@ benchmark times.
 * split-K decode of 32 requests with contexts uniform in [8192, 131072] over
   a shuffled, NaN-poisoned paged cache (every output row checked);
 * chunked prefill of 4 x 131072 tokens in 8192-token chunks against the
-  growing paged cache.
+  growing paged cache;
+* one rank of zigzag context parallelism (4 ranks) over 65536 tokens: its
+  queries against every rank's key shard, merged by LSE.
 
 Large outputs are compared on a seeded sample of >= 512 query rows per head
 plus forced rows (first/last, tile edges, shard and chunk boundaries); the
@@ -120,6 +122,42 @@ def test_ulysses_output_relayout_64k():
     ref = prior.copy()
     oracle.unpermute(x, SP, H_tot, 0, out=ref)
     assert np.array_equal(bits(out), ref)
+
+
+def run_cp_rank(q, k, v, S, N, rank, mode):
+    """One rank's ring attention on one GPU: shard, key limits from the
+    positions, prefix-limited partials against every key shard, LSE merge."""
+    qr, qpos = lcat.cp_shard(q, N, rank, mode)
+    o = lse = None
+    for s_ in range(N):
+        ks, kpos = lcat.cp_shard(k, N, s_, mode)
+        vs, _ = lcat.cp_shard(v, N, s_, mode)
+        lim = lcat.attn_key_limits(qpos, kpos)
+        op, lp = lcat.attn_prefill_limited(qr[None], ks[None], vs[None], lim)
+        if o is None:
+            o, lse = op, lp
+        else:
+            lcat.attn_merge(o, lse, op, lp, o=o, lse=lse)
+    return o, lse
+
+
+@pytest.mark.parametrize("rank", [0, 3])
+def test_cp_zigzag_64k(rank):
+    S, N = 65536, 4
+    log(f"CP zigzag 64K rank {rank}: generating")
+    d = synth.dense_bf16(seed=920, B=1, S=S, Hq=16, Hkv=2)
+    q, k, v = (to_dev(d[n][0]) for n in ("q", "k", "v"))
+    o, lse = run_cp_rank(q, k, v, S, N, rank, "zigzag")
+    torch.cuda.synchronize()
+    toks = oracle.cp_tokens(S, N, "zigzag", rank)
+    L = toks.size // 2
+    local = synth.sample_rows(921 + rank, toks.size, N_SAMPLE, [0, 1, L - 1, L, L + 1, 2 * L - 1])
+    log(f"CP zigzag 64K rank {rank}: oracle on {local.size} rows x 16 heads")
+    ref, ref_lse = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=True, rows=toks[local])
+    idx = torch.from_numpy(local).cuda()
+    e, r = assert_attention_close(to_np64(o[:, idx]), ref, lse[:, :, idx].cpu().numpy(), ref_lse,
+                                  what="CP zigzag")
+    log(f"CP zigzag 64K rank {rank}: max abs {e:.3g} rel-L2 {r:.3g}")
 
 
 def test_decode_paged_32_requests():

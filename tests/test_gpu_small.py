@@ -400,6 +400,143 @@ def test_decode_bad_tag_and_block_are_reported():
 
 
 # ---------------------------------------------------------------------------
+# context parallelism on one GPU
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["contiguous", "striped", "zigzag"])
+@pytest.mark.parametrize("S,N,H,D,dtype", [(48, 4, 16, 128, np.int16), (50, 4, 2, 128, np.int16),
+                                           (64, 8, 1, 3, np.int16), (40, 2, 3, 8, np.float32)])
+def test_cp_shard_round_trip(mode, S, N, H, D, dtype):
+    """Each rank's shard equals the oracle's token list of the full tensor bit
+    for bit, positions are those tokens, and unsharding every rank rebuilds
+    the full tensor (rows of other ranks untouched in between)."""
+    if mode == "striped" and S % N:
+        pytest.skip("striped needs S % N == 0")
+    log(f"cp shard {mode} S={S} N={N} H={H} D={D}")
+    rng = np.random.default_rng(S * 10 + N)
+    x = rng.integers(-2 ** 15, 2 ** 15, size=(S, H, D)).astype(np.int16)
+    if dtype == np.float32:
+        x = rng.standard_normal((S, H, D)).astype(np.float32)
+    xd = torch.from_numpy(x).cuda()
+    back = torch.zeros_like(xd)
+    for r in range(N):
+        toks = oracle.cp_tokens(S, N, mode, r)
+        sh, pos = lcat.cp_shard(xd, N, r, mode)
+        torch.cuda.synchronize()
+        assert np.array_equal(sh.cpu().numpy(), x[toks])
+        assert np.array_equal(pos.cpu().numpy(), toks)
+        lcat.cp_unshard(sh, S, N, r, mode, out=back)
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().numpy(), x)
+
+
+def test_key_limits_count_keys_at_or_before_each_query():
+    rng = np.random.default_rng(900)
+    B, Sq, Sk = 2, 300, 257
+    qp = np.sort(rng.integers(0, 5000, size=(B, Sq)), axis=1).astype(np.int32)
+    kp = np.sort(rng.choice(5000, size=(B, Sk), replace=True), axis=1).astype(np.int32)
+    qp[0, :5] = -3                         # before every key
+    lim = lcat.attn_key_limits(to_dev(qp), to_dev(kp))
+    torch.cuda.synchronize()
+    want = np.array([[int(np.sum(kp[b] <= p_)) for p_ in qp[b]] for b in range(B)])
+    assert np.array_equal(lim.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("Sq,Sk", [(700, 900), (333, 64), (256, 1500)])
+def test_prefill_limited_vs_oracle(Sq, Sk):
+    """Rows attend a caller-given prefix of the keys (nondecreasing limits,
+    some zero, some ragged, some past Sk); rows with no key give O = 0 and
+    LSE = -inf."""
+    log(f"prefill limited Sq={Sq} Sk={Sk}")
+    B, Hq, Hkv = 2, 16, 2
+    rng = np.random.default_rng(Sq + Sk)
+    sq_, sk_, sv_ = np.random.SeedSequence(Sq * Sk).spawn(3)
+    q = synth.normal_bf16(sq_, (B, Sq, Hq, 128))
+    k = synth.normal_bf16(sk_, (B, Sk, Hkv, 128))
+    v = synth.normal_bf16(sv_, (B, Sk, Hkv, 128))
+    lim = np.sort(rng.integers(0, Sk + 40, size=(B, Sq)), axis=1).astype(np.int32)
+    lim[:, : Sq // 10] = 0
+    o, lse = lcat.attn_prefill_limited(to_dev(q), to_dev(k), to_dev(v), to_dev(lim))
+    torch.cuda.synchronize()
+    eff = np.minimum(lim, Sk)
+    ref, ref_lse = oracle.attention_rows(q, k, v, eff.astype(np.int64), 128 ** -0.5)
+    got, got_lse = to_np64(o), lse.cpu().numpy()
+    live = eff > 0
+    assert np.all(got[~live] == 0) and np.all(got_lse.transpose(0, 2, 1)[~live] == -np.inf)
+    e, r = assert_attention_close(got[live], ref[live], got_lse.transpose(0, 2, 1)[live],
+                                  ref_lse.transpose(0, 2, 1)[live], what="limited")
+    log(f"  max abs {e:.3g} rel-L2 {r:.3g}")
+
+
+def test_merge_vs_oracle():
+    """Seeded partials (bf16 O, fp32 LSE with -inf entries on either or both
+    sides) merged on the GPU, in place and out of place, against the oracle's
+    merge."""
+    B, S, H, D = 2, 77, 4, 128
+    rng = np.random.default_rng(901)
+    oa = synth.normal_bf16(902, (B, S, H, D))
+    ob = synth.normal_bf16(903, (B, S, H, D))
+    la = rng.normal(0, 4, size=(B, H, S)).astype(np.float32)
+    lb = rng.normal(0, 4, size=(B, H, S)).astype(np.float32)
+    la[:, :, :5] = -np.inf
+    lb[:, :, 3:8] = -np.inf
+    ref, ref_l = oracle.merge_normalized([(synth.bf16_bits_to_f32(oa), la),
+                                          (synth.bf16_bits_to_f32(ob), lb)])
+    o, l = lcat.attn_merge(to_dev(oa), to_dev(la), to_dev(ob), to_dev(lb))
+    oad, lad = to_dev(oa), to_dev(la)
+    lcat.attn_merge(oad, lad, to_dev(ob), to_dev(lb), o=oad, lse=lad)
+    torch.cuda.synchronize()
+    for got_o, got_l in ((o, l), (oad, lad)):
+        g = to_np64(got_o)
+        assert np.all(np.abs(g - ref) <= 2 ** -8 * np.abs(ref) + 1e-6)
+        gl = got_l.cpu().numpy()
+        fin = np.isfinite(ref_l)
+        assert np.array_equal(np.isfinite(gl), fin)
+        assert np.all(np.abs(gl[fin] - ref_l[fin]) <= 1e-5 + 1e-6 * np.abs(ref_l[fin]))
+    assert np.all(to_np64(o)[:, 3:5] == 0)            # both sides empty
+
+
+@pytest.mark.parametrize("mode", ["contiguous", "striped", "zigzag"])
+def test_cp_ring_attention_on_one_gpu(mode):
+    """One rank's ring attention, all on one GPU: shard Q/K/V, attend the
+    rank's queries to every rank's key shard with the position-derived
+    limits, merge the partials; the result is the causal attention of the
+    rank's tokens (oracle, full sequence).  Every partial is also checked
+    against the oracle's position-masked attention (rows that see no key of
+    that shard: O = 0, LSE = -inf)."""
+    S, N, Hq, Hkv = 1536, 4, 16, 2
+    log(f"cp ring {mode} S={S} N={N}")
+    d = synth.dense_bf16(seed=910, B=1, S=S, Hq=Hq, Hkv=Hkv)
+    q, k, v = (to_dev(d[n][0]) for n in ("q", "k", "v"))
+    shards = [(lcat.cp_shard(k, N, s_, mode)[0], lcat.cp_shard(v, N, s_, mode)[0],
+               lcat.cp_shard(k, N, s_, mode)[1]) for s_ in range(N)]
+    for r in (0, N - 1):
+        qr, qpos = lcat.cp_shard(q, N, r, mode)
+        o = lse = None
+        for s_, (ks, vs, kpos) in enumerate(shards):
+            lim = lcat.attn_key_limits(qpos, kpos)
+            op, lp = lcat.attn_prefill_limited(qr[None], ks[None], vs[None], lim)
+            torch.cuda.synchronize()
+            tq, tk = oracle.cp_tokens(S, N, mode, r), oracle.cp_tokens(S, N, mode, s_)
+            pr, pl = oracle.attention_positions(d["q"][:, tq], d["k"][:, tk], d["v"][:, tk], tq, tk,
+                                                d["scale"])
+            live = np.isfinite(pl[0, 0])
+            assert np.all(to_np64(op)[:, ~live] == 0)
+            assert np.all(lp.cpu().numpy()[..., ~live] == -np.inf)
+            if live.any():
+                assert_attention_close(to_np64(op)[:, live], pr[:, live], lp.cpu().numpy()[..., live],
+                                       pl[..., live], what="cp partial")
+            if o is None:
+                o, lse = op, lp
+            else:
+                lcat.attn_merge(o, lse, op, lp, o=o, lse=lse)
+        torch.cuda.synchronize()
+        rows = oracle.cp_tokens(S, N, mode, r)
+        ref, ref_lse = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=True, rows=rows)
+        e, rl = assert_attention_close(to_np64(o), ref, lse.cpu().numpy(), ref_lse, what="cp ring")
+        log(f"  rank {r}: max abs {e:.3g} rel-L2 {rl:.3g}")
+
+
+# ---------------------------------------------------------------------------
 # chunked prefill against the paged cache
 # ---------------------------------------------------------------------------
 def _run_chunked(d, C, kv_head_base=0):
