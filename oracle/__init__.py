@@ -21,6 +21,8 @@ What it computes (each function cites the passage it follows):
   article's §2.3.
 * :func:`partial_attention` / :func:`lse_merge` — the rescale identity of
   §18.3 applied to key ranges; used only to cross-check :func:`attention`.
+* :mod:`oracle.fp8` — OCP e4m3 encode/decode and the per-token quantisation
+  of the paged KV cache (the FP8 cache variant; format reading stated there).
 * :func:`cp_tokens` — which tokens each context-parallel rank holds under the
   contiguous (ring), striped (round-robin) and zigzag (in-seq-split) splits
   of "LLM推理中的多卡切分" §3.5 / §3.5.1.

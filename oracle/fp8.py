@@ -1,0 +1,125 @@
+"""FP8 (OCP e4m3) quantisation of the KV cache — TEST INFRASTRUCTURE ONLY.
+
+Written from the format definition, not from any implementation.  Where the
+pages mention quantised attention they leave the number format open: the
+FP8 path of "Flash Attention and distributed inference" (FA3 section)
+quantises blocks to 8-bit floats, and the Ulysses inference article (§5.4)
+stores a KV cache quantised in groups.  Reading taken here: the OCP 8-bit
+e4m3 format (the one gfx950 implements), with one fp32 scale per group of
+one token's head vector (a K row or a V column of a 64-token block).
+
+e4m3: sign bit, 4 exponent bits (bias 7), 3 mantissa bits.  Exponent field
+0 holds the subnormals m * 2^-9; fields 1..15 hold (1 + m/8) * 2^(e-7),
+except e = 15, m = 7, which is NaN.  There are no infinities; the largest
+finite magnitude is 448.
+
+Quantising a group x: scale = amax(|x|) / 448 (fp32 division), each
+element y = x / scale (fp32 division), rounded to the nearest e4m3 value
+with ties to the even code, magnitudes at or above 448 saturating to 448.
+A group of zeros gets scale 0 and codes 0.  Dequantised value:
+decode(code) * scale.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _magnitudes() -> np.ndarray:
+    """Value of codes 0 .. 126 (sign bit clear, NaN code 127 excluded)."""
+    vals = []
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals, dtype=np.float64)
+
+
+E4M3_MAG = _magnitudes()          # ascending
+E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """uint8 codes -> float64 values (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, E4M3_MAG[np.minimum(c & 0x7F, 126)])
+    return np.where(c & 0x80, -mag, mag)
+
+
+def fp8_e4m3_encode(x) -> np.ndarray:
+    """Values -> uint8 codes: nearest e4m3 value, ties to the even code,
+    saturating at +-448; the sign bit is the sign bit of x (so -0 and
+    negative values that round to zero give 0x80).  Finite inputs only."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("oracle: fp8 encode of a non-finite value")
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(E4M3_MAG, a, side="left")          # first magnitude >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - E4M3_MAG[lo]
+    d_hi = E4M3_MAG[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(E4M3_MAG[hi] == a, hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def quantize_groups(x) -> tuple[np.ndarray, np.ndarray]:
+    """Quantise each group (last axis) of fp32-representable values.
+    Returns (codes uint8, same shape; scale fp32, shape[:-1])."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    y = (x / safe[..., None]).astype(np.float32)            # fp32 division, as the kernel
+    codes = fp8_e4m3_encode(y)
+    codes = np.where((scale > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
+    return codes, scale
+
+
+def dequantize_groups(codes, scale) -> np.ndarray:
+    return fp8_e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def quantize_kv_pool(k_pool_bits, v_pool_bits):
+    """Paged bf16 pools -> fp8 pools with one scale per token and block.
+
+    k_pool [n][64][D] (token-major): group = one token's K row.
+    v_pool [n][D][64] (dimension-major): group = one token's V column.
+    Returns (k8 [n][64][D], v8 [n][D][64], k_scale [n][64], v_scale [n][64]).
+    """
+    kb = np.asarray(k_pool_bits, dtype=np.uint16)
+    vb = np.asarray(v_pool_bits, dtype=np.uint16)
+    kf = (kb.astype(np.uint32) << 16).view(np.float32)
+    vf = (vb.astype(np.uint32) << 16).view(np.float32)
+    k8, ks = quantize_groups(kf)
+    v8t, vs = quantize_groups(np.swapaxes(vf, 1, 2))        # [n][64][D]: token groups
+    return k8, np.ascontiguousarray(np.swapaxes(v8t, 1, 2)), ks, vs
+
+
+def dequantize_kv_pool(k8, v8, k_scale, v_scale):
+    """fp64 K [n][64][D] and V [n][D][64] of an fp8 pool."""
+    k = dequantize_groups(k8, k_scale)
+    v = np.swapaxes(dequantize_groups(np.swapaxes(v8, 1, 2), v_scale), 1, 2)
+    return k, v
+
+
+def gather_dequantized(k8, v8, k_scale, v_scale, block_table, ctx_len):
+    """Per request b, the dequantised K and V of its first ctx_len[b] tokens in
+    order, [ctx][Hkv][D] fp64 each: token t of KV head g sits in slot t % 64
+    of physical block block_table[b][g][t // 64] (the paged layout of the
+    Ulysses inference article, §2.3)."""
+    k, v = dequantize_kv_pool(k8, v8, k_scale, v_scale)        # [n][64][D], [n][D][64]
+    table = np.asarray(block_table)
+    B, Hkv, _ = table.shape
+    ks, vs = [], []
+    for b in range(B):
+        T = int(ctx_len[b])
+        t = np.arange(T)
+        kb = np.empty((T, Hkv, k.shape[2]))
+        vb = np.empty((T, Hkv, k.shape[2]))
+        for g in range(Hkv):
+            blk = table[b, g, t // 64]
+            kb[:, g] = k[blk, t % 64]
+            vb[:, g] = v[blk, :, t % 64]
+        ks.append(kb)
+        vs.append(vb)
+    return ks, vs

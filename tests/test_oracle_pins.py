@@ -474,6 +474,75 @@ def test_cp_partials_merge_to_the_causal_rows(mode):
 
 
 # ---------------------------------------------------------------------------
+# FP8 (OCP e4m3) KV quantisation
+# ---------------------------------------------------------------------------
+from oracle import fp8  # noqa: E402
+
+
+def test_fp8_decode_matches_the_format_definition():
+    """Closed-form values of e4m3: bias 7, subnormals m*2^-9, max 448, one
+    NaN pattern per sign, no infinities."""
+    dec = fp8.fp8_e4m3_decode
+    want = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+            0x39: 1.125, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in want.items():
+        assert dec([c])[0] == v, hex(c)
+    assert np.isnan(dec([0x7F])[0]) and np.isnan(dec([0xFF])[0])
+    assert np.signbit(dec([0x80])[0])
+    finite = dec(np.arange(256, dtype=np.uint8))
+    assert np.sum(np.isnan(finite)) == 2 and np.nanmax(finite) == 448.0
+
+
+def test_fp8_encode_inverts_decode_and_rounds_to_nearest_even():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    assert np.array_equal(fp8.fp8_e4m3_encode(fp8.fp8_e4m3_decode(codes)), codes)
+    enc = lambda v: int(fp8.fp8_e4m3_encode([v])[0])
+    assert enc(1.0625) == 0x38            # tie between 1 (0x38) and 1.125 (0x39): even
+    assert enc(1.1875) == 0x3A            # tie between 1.125 and 1.25: even
+    assert enc(1.0626) == 0x39
+    assert enc(2.0 ** -10) == 0x00        # tie between 0 and the smallest subnormal
+    assert enc(3 * 2.0 ** -10) == 0x02    # tie between 1 and 2 * 2^-9: even
+    assert enc(464.0) == 0x7E and enc(1e6) == 0x7E and enc(-1e6) == 0xFE   # saturate
+    assert enc(-1e-30) == 0x80
+
+
+def test_fp8_error_bound():
+    rng = np.random.default_rng(40)
+    x = np.exp(rng.uniform(np.log(2.0 ** -6), np.log(448.0), 20000)) * rng.choice([-1, 1], 20000)
+    y = fp8.fp8_e4m3_decode(fp8.fp8_e4m3_encode(x))
+    assert np.all(np.abs(y - x) <= np.abs(x) * 2.0 ** -4)            # half an ulp, normal range
+    xs = rng.uniform(-2.0 ** -6, 2.0 ** -6, 5000)
+    ys = fp8.fp8_e4m3_decode(fp8.fp8_e4m3_encode(xs))
+    assert np.all(np.abs(ys - xs) <= 2.0 ** -10)                      # half a subnormal step
+
+
+def test_fp8_group_quantisation():
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal((50, 128)) * np.exp(rng.uniform(-8, 8, (50, 1)))).astype(np.float32)
+    x[3] = 0.0
+    codes, scale = fp8.quantize_groups(x)
+    assert scale[3] == 0 and np.all(codes[3] == 0)
+    y = fp8.dequantize_groups(codes, scale)
+    amax = np.abs(x).max(axis=1)
+    assert np.all(np.abs(y - x) <= 2.0 ** -4 * amax[:, None] + 1e-30)
+    i = np.argmax(np.abs(x), axis=1)
+    assert np.all((codes[np.arange(50), i] & 0x7F)[amax > 0] == 0x7E)      # the max maps to 448
+
+
+def test_fp8_pool_groups_are_k_rows_and_v_columns():
+    """K groups are token rows of a block, V groups are token columns of the
+    dimension-major V block: scaling token j by 2^j scales exactly its group."""
+    row = synth.bf16_bits_to_f32(synth.normal_bf16(42, (128,)))
+    f = np.broadcast_to(row, (1, 64, 128)).astype(np.float32)     # the same vector per token
+    tok = 2.0 ** np.arange(64, dtype=np.float32)
+    kb = synth.f32_to_bf16_bits(f * tok[None, :, None])
+    vb = synth.f32_to_bf16_bits(np.swapaxes(f, 1, 2) * tok[None, None, :])
+    k8, v8, ks, vs = fp8.quantize_kv_pool(kb, vb)
+    assert np.allclose(ks[0] / ks[0, 0], tok) and np.allclose(vs[0] / vs[0, 0], tok)
+    assert np.array_equal(k8, np.swapaxes(v8, 1, 2))     # same values per token, transposed
+
+
+# ---------------------------------------------------------------------------
 # Paged cache read-back
 # ---------------------------------------------------------------------------
 def test_paged_gather_hand_example():
