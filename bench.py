@@ -12,6 +12,7 @@ The same JSON line also carries, each measured in this run:
   decode          paged decode with the key blocks of all requests shared out
                   equally over the GPU's waves, 32 requests with contexts
                   uniform in [8192, 131072], KV bytes per second against 8 TB/s;
+                  and (fp8_cache) the same decode over the FP8 copy of the cache;
   relayout        sequence-shard -> head-shard relayout of one rank's share of
                   [4][16384][64|8][128] bf16 Q/K/V (one launch), bytes per second,
                   and (fused_rope) the same relayout with RoPE on Q and K;
@@ -193,9 +194,24 @@ def bench_decode(torch, lcat, synth, iters=20):
     ctx_total = int(c["ctx_len"].sum())
     nbytes = ctx_total * c["Hkv"] * D * 2 * 2 + 2 * B * Hq * D * 2 + B * Hq * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return dict(ms=round(ms, 4), GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
-                bytes=nbytes, context_tokens=ctx_total, requests=B,
-                workload="32 requests, ctx U[8192,131072], 16 Q / 2 KV heads, paged 64-token blocks")
+    res = dict(ms=round(ms, 4), GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
+               bytes=nbytes, context_tokens=ctx_total, requests=B,
+               workload="32 requests, ctx U[8192,131072], 16 Q / 2 KV heads, paged 64-token blocks")
+
+    # the same cache in FP8 (e4m3 + one fp32 scale per token for K and for V)
+    k8, v8, ks, vs = lcat.attn_kv_quantize_fp8(k_pool, v_pool)
+    args8 = [args[0], k8, v8, ks, vs] + args[3:]
+    for _ in range(3):
+        lcat.attn_decode_fp8(*args8, workspace=ws, o=o, lse=lse)
+    torch.cuda.synchronize()
+    ms8 = back_to_back_ms(torch, lambda: lcat.attn_decode_fp8(*args8, workspace=ws, o=o, lse=lse),
+                          iters)
+    nbytes8 = ctx_total * c["Hkv"] * (2 * D + 8) + 2 * B * Hq * D * 2 + B * Hq * 4
+    gbs8 = nbytes8 / (ms8 * 1e-3) / 1e9
+    res["fp8_cache"] = dict(ms=round(ms8, 4), GBps=round(gbs8, 1),
+                            frac_hbm=round(gbs8 / PEAK_HBM_GBS, 4), bytes=nbytes8,
+                            speedup_vs_bf16=round(ms / ms8, 3))
+    return res
 
 
 def bench_relayout_and_prefill_64k(torch, lcat, iters=20):

@@ -151,6 +151,36 @@ int attn_decode(const void *q, const void *k_pool, const void *v_pool, int n_blo
 size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_blocks, int split_tokens);
 
 /*
+ * FP8 KV cache ([ULY] §5.4 keeps the cache quantised in groups; FA3's FP8
+ * path in [FA18] quantises blocks to 8-bit floats).  Reading taken: OCP e4m3
+ * codes with one fp32 scale per token — per K row and per V column of each
+ * 64-token block — scale = amax / 448, code = x / scale rounded to nearest
+ * e4m3 (ties to even, magnitudes clamped to 448), all-zero groups get scale
+ * 0 and codes 0.  Dequantised value = e4m3(code) * scale.
+ *   k8_pool [n_blocks][64][D] and v8_pool [n_blocks][D][64] bytes (the bf16
+ *   layouts with 1-byte elements), k_scale / v_scale [n_blocks][64] fp32.
+ *
+ * attn_kv_quantize_fp8 — quantise whole bf16 pools into that form.  D = 128.
+ *   Codes are fixed by the definition above (IEEE fp32 divisions).
+ */
+int attn_kv_quantize_fp8(const void *k_pool, const void *v_pool, void *k8_pool, void *v8_pool,
+                         float *k_scale, float *v_scale, int n_blocks, int D, void *stream);
+
+/*
+ * attn_decode_fp8 — attn_decode over the FP8 cache: the same arguments,
+ * splits, workspace (attn_decode_workspace_bytes), tag and block checks and
+ * outputs, with the e4m3 pools and their per-token scales in place of the
+ * bf16 pools.  Scores use the dequantised keys, P V the dequantised values;
+ * q stays bf16.  Reads 16.5 KiB per block and KV head instead of 32 KiB.
+ */
+int attn_decode_fp8(const void *q, const void *k8_pool, const void *v8_pool, const float *k_scale,
+                    const float *v_scale, int n_blocks, const int32_t *block_head,
+                    const int32_t *block_table, int max_blocks, const int32_t *ctx_len, void *o,
+                    float *lse, int B, int Hq, int Hkv, int D, int kv_head_base, float scale,
+                    int split_tokens, void *workspace, size_t workspace_bytes,
+                    int32_t *dev_status, void *stream);
+
+/*
  * rope_apply — rotary position embedding at absolute token positions, in
  * place ([ULY] §3.2 global token index table, §5.3).
  *   x [S][H][D] bf16, positions [S] int32 (device).

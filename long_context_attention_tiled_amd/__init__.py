@@ -26,7 +26,8 @@ __all__ = [
     "attn_prefill", "attn_chunked_prefill", "attn_kv_append", "attn_decode",
     "attn_decode_workspace_bytes", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv", "head_to_seq_permute",
     "seq_to_head_permute_qkv_rope", "cp_shard_tokens", "cp_shard", "cp_unshard",
-    "attn_key_limits", "attn_prefill_limited", "attn_merge", "CP_MODES",
+    "attn_key_limits", "attn_prefill_limited", "attn_merge", "CP_MODES", "attn_decode_fp8",
+    "attn_kv_quantize_fp8",
     "attn_status_string",
     "AttnError", "ATTN_DEV_OK", "ATTN_DEV_BAD_TAG", "ATTN_DEV_BAD_BLOCK", "load_library",
 ]
@@ -206,6 +207,72 @@ def attn_decode(q, k_pool, v_pool, block_head, block_table, ctx_len, kv_head_bas
         int(split_tokens), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(dev_status), _stream(stream))
     _lib.check("attn_decode", st)
+    return o, lse
+
+
+def attn_kv_quantize_fp8(k_pool, v_pool, k8_pool=None, v8_pool=None, k_scale=None, v_scale=None,
+                         stream=None):
+    """bf16 pools -> (k8_pool, v8_pool, k_scale, v_scale): e4m3 bytes (uint8)
+    in the same layouts and one fp32 scale per token and block."""
+    torch = _torch()
+    n_blocks = k_pool.shape[0]
+    _need(k_pool, "k_pool", torch.bfloat16, (n_blocks, BLOCK_TOKENS, HEAD_DIM))
+    _need(v_pool, "v_pool", torch.bfloat16, (n_blocks, HEAD_DIM, BLOCK_TOKENS))
+    dev = k_pool.device
+    if k8_pool is None:
+        k8_pool = torch.empty((n_blocks, BLOCK_TOKENS, HEAD_DIM), dtype=torch.uint8, device=dev)
+    if v8_pool is None:
+        v8_pool = torch.empty((n_blocks, HEAD_DIM, BLOCK_TOKENS), dtype=torch.uint8, device=dev)
+    if k_scale is None:
+        k_scale = torch.empty((n_blocks, BLOCK_TOKENS), dtype=torch.float32, device=dev)
+    if v_scale is None:
+        v_scale = torch.empty((n_blocks, BLOCK_TOKENS), dtype=torch.float32, device=dev)
+    _need(k8_pool, "k8_pool", torch.uint8, (n_blocks, BLOCK_TOKENS, HEAD_DIM))
+    _need(v8_pool, "v8_pool", torch.uint8, (n_blocks, HEAD_DIM, BLOCK_TOKENS))
+    _need(k_scale, "k_scale", torch.float32, (n_blocks, BLOCK_TOKENS))
+    _need(v_scale, "v_scale", torch.float32, (n_blocks, BLOCK_TOKENS))
+    st = _lib.load().attn_kv_quantize_fp8(_ptr(k_pool), _ptr(v_pool), _ptr(k8_pool), _ptr(v8_pool),
+                                          _ptr(k_scale), _ptr(v_scale), n_blocks, HEAD_DIM,
+                                          _stream(stream))
+    _lib.check("attn_kv_quantize_fp8", st)
+    return k8_pool, v8_pool, k_scale, v_scale
+
+
+def attn_decode_fp8(q, k8_pool, v8_pool, k_scale, v_scale, block_head, block_table, ctx_len,
+                    kv_head_base=0, scale=None, split_tokens=0, workspace=None, o=None, lse=None,
+                    dev_status=None, stream=None):
+    """:func:`attn_decode` over the FP8 cache of :func:`attn_kv_quantize_fp8`."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    B, Hq, D = q.shape
+    n_blocks = k8_pool.shape[0]
+    _need(k8_pool, "k8_pool", torch.uint8, (n_blocks, BLOCK_TOKENS, D))
+    _need(v8_pool, "v8_pool", torch.uint8, (n_blocks, D, BLOCK_TOKENS))
+    _need(k_scale, "k_scale", torch.float32, (n_blocks, BLOCK_TOKENS))
+    _need(v_scale, "v_scale", torch.float32, (n_blocks, BLOCK_TOKENS))
+    _need(block_head, "block_head", torch.int32, (n_blocks,))
+    _need(block_table, "block_table", torch.int32)
+    Hkv, max_blocks = block_table.shape[1], block_table.shape[2]
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][Hkv][max_blocks]")
+    _need(ctx_len, "ctx_len", torch.int32, (B,))
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, q.shape)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, (B, Hq))
+    need = attn_decode_workspace_bytes(B, Hq, max_blocks, split_tokens, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace")
+    scale = float(D ** -0.5) if scale is None else float(scale)
+    st = _lib.load().attn_decode_fp8(
+        _ptr(q), _ptr(k8_pool), _ptr(v8_pool), _ptr(k_scale), _ptr(v_scale), n_blocks,
+        _ptr(block_head), _ptr(block_table), max_blocks, _ptr(ctx_len), _ptr(o), _ptr(lse), B, Hq,
+        Hkv, D, int(kv_head_base), scale, int(split_tokens), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(dev_status), _stream(stream))
+    _lib.check("attn_decode_fp8", st)
     return o, lse
 
 

@@ -20,6 +20,14 @@
 //  * K and V of a 64-token block go straight from HBM to registers; no LDS.
 //  * Slots at or past ctx_len are excluded by index: scores are set to -inf
 //    and their V entries to zero before any multiply (they may hold NaN).
+//
+// FP8 cache (OCP e4m3 with one fp32 scale per token for K and for V, the
+// group-quantised cache of the Ulysses inference article, §5.4): the same
+// loop reads 8 KiB K and V blocks, widens each 16-byte load to two bf16
+// operands in registers (exact: every e4m3 value is a bf16 value),
+// multiplies each score by its key's K scale and folds the V scale into P
+// before P V.  Which head dims and keys a lane holds is relabelled so that
+// one 16-byte load feeds two MFMA operands; Q is loaded in the same order.
 #include "device.h"
 #include "kernels.h"
 
@@ -36,11 +44,29 @@ struct BlockRegs {
 };
 
 constexpr int BLOCK_BYTES = BT * HD * 2;   // 16 KiB: one K block or one V block
+constexpr int BLOCK_BYTES8 = BT * HD;     // 8 KiB: one fp8 K or V block
+
+struct BlockRegs8 {
+  u32x4 k[4][2];   // K rows of the four 16-key sub-tiles, two 64-wide d halves (16 dims each)
+  u32x4 v[8];      // V^T: eight 16-row d tiles, 16 keys each
+  f32x4 ks[4];     // K scale of the keys whose scores land in s[t]
+  f32x4 vs[4];     // V scale of the same keys
+};
+
+// Eight e4m3 values (two words) -> eight bf16 values, exactly.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
 
 // Blocks j_begin .. j_begin+nblk-1 of (request b, KV head g), nblk >= 1;
 // `tail` keys (1..64) are valid in the last one.  Writes the unnormalised
 // (O, m, l) record of every query head of the group: head qi of the group at
 // rec0 + qi * head_stride (floats).
+template <bool FP8>
 __device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g, int j_begin,
                                              int nblk, int tail, float *rec0,
                                              size_t head_stride) {
@@ -55,9 +81,13 @@ __device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g
   bf16x8 qf[4];
   {
     const int qh = g * group + min(qi, group - 1);   // padding lanes reuse a real head
-    const bf16 *src = static_cast<const bf16 *>(p.q) + ((size_t)b * p.Hq + qh) * HD + 8 * g4;
+    const bf16 *src = static_cast<const bf16 *>(p.q) + ((size_t)b * p.Hq + qh) * HD;
+    // MFMA step s covers dims 32s + 8*g4 .. +7 (bf16 cache), or
+    // 64*(s/2) + 16*g4 + 8*(s%2) .. +7 (fp8 cache: one 16-byte K load per two steps)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(ld_global_16(src + 32 * s));
+    for (int s = 0; s < 4; ++s)
+      qf[s] = as_bf16x8(ld_global_16(src + (FP8 ? 64 * (s >> 1) + 16 * g4 + 8 * (s & 1)
+                                                : 32 * s + 8 * g4)));
   }
 
   // Physical ids of this split's blocks, 64 per vector register (lane i holds
@@ -179,17 +209,125 @@ __device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g
     if (has_next) load_v(R, blk_next);
   };
 
-  int blk = block_id(0);
-  load_k(R, blk);
-  load_v(R, blk);
-  for (int i = 0; i + 1 < nblk; ++i) {
-    const int blk_next = block_id(i + 1);
-    step(Int<0>{}, blk_next, true, BT);
+  if constexpr (!FP8) {
+    int blk = block_id(0);
+    load_k(R, blk);
+    load_v(R, blk);
+    for (int i = 0; i + 1 < nblk; ++i) {
+      const int blk_next = block_id(i + 1);
+      step(Int<0>{}, blk_next, true, BT);
+    }
+    if (tail == BT)
+      step(Int<0>{}, 0, false, BT);
+    else
+      step(Int<1>{}, 0, false, tail);
+  } else {
+    // K row read by this lane for sub-tile t: 16*(qi>>2) + 4t + (qi&3); its
+    // score lands in register r of lane group g4 as key 16*g4 + 4t + r, which
+    // is where the B operand of P V expects it (V^T operand w of a lane holds
+    // keys 16*g4 + 8w .. +7).
+    const uint8_t *kp8 = static_cast<const uint8_t *>(p.k_pool);
+    const uint8_t *vp8 = static_cast<const uint8_t *>(p.v_pool);
+    const int k8_voff = (16 * (qi >> 2) + (qi & 3)) * HD + 16 * g4;
+    const int v8_voff = qi * BT + 16 * g4;
+    const int sc_voff = 64 * g4;   // bytes: scales of keys 16*g4 ..
+    BlockRegs8 R8;
+    auto load_k8 = [&](int blk) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(kp8 + (size_t)blk * BLOCK_BYTES8, BLOCK_BYTES8);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) R8.k[t][u] = buf_load_16(r, k8_voff + 64 * u, 512 * t);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.k_scale + (size_t)blk * BT, BT * 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        R8.ks[t] = __builtin_bit_cast(f32x4, buf_load_16(rs, sc_voff, 16 * t));
+    };
+    auto load_v8 = [&](int blk) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(vp8 + (size_t)blk * BLOCK_BYTES8, BLOCK_BYTES8);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) R8.v[dt] = buf_load_16(r, v8_voff, 1024 * dt);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.v_scale + (size_t)blk * BT, BT * 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        R8.vs[t] = __builtin_bit_cast(f32x4, buf_load_16(rs, sc_voff, 16 * t));
+    };
+    auto step8 = [&](auto masked_tag, int blk_next, bool has_next, int nv) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked_tag)::value != 0;
+      f32x4 s[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        s[t] = f32x4{};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          s[t] = mfma_16x16x32(fp8x8_to_bf16(R8.k[t][u][0], R8.k[t][u][1]), qf[2 * u], s[t]);
+          s[t] = mfma_16x16x32(fp8x8_to_bf16(R8.k[t][u][2], R8.k[t][u][3]), qf[2 * u + 1], s[t]);
+        }
+        s[t] *= R8.ks[t];
+      }
+      if (has_next) load_k8(blk_next);
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * g4 + 4 * t + r >= nv) s[t][r] = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {   // word e holds keys 16*g4 + 4e .. +3
+          const int k0 = 16 * g4 + 4 * e;
+          uint32_t keep = 0;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) keep |= (k0 + x < nv ? 0xFFu : 0u) << (8 * x);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) R8.v[dt][e] &= keep;
+        }
+      }
+
+      float mx = s[0][0];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[t][r]);
+      mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+      mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float msc = (m_new == -INFINITY) ? 0.f : m_new * c2;
+      const float alpha = fast_exp2(m_run * c2 - msc);
+      m_run = m_new;
+
+      bf16x8 pb[2];
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv = fast_exp2(fmaf(s[t][r], c2, -msc));
+          psum += pv;
+          float pw = pv * R8.vs[t][r];   // V scale folded into P
+          if (MASKED && 16 * g4 + 4 * t + r >= nv) pw = 0.f;   // its scale may be anything
+          pb[t >> 1][4 * (t & 1) + r] = to_bf16(pw);
+        }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        acc[dt] *= alpha;
+        acc[dt] = mfma_16x16x32(fp8x8_to_bf16(R8.v[dt][0], R8.v[dt][1]), pb[0], acc[dt]);
+        acc[dt] = mfma_16x16x32(fp8x8_to_bf16(R8.v[dt][2], R8.v[dt][3]), pb[1], acc[dt]);
+      }
+      if (has_next) load_v8(blk_next);
+    };
+    int blk = block_id(0);
+    load_k8(blk);
+    load_v8(blk);
+    for (int i = 0; i + 1 < nblk; ++i) {
+      const int blk_next = block_id(i + 1);
+      step8(Int<0>{}, blk_next, true, BT);
+    }
+    if (tail == BT)
+      step8(Int<0>{}, 0, false, BT);
+    else
+      step8(Int<1>{}, 0, false, tail);
   }
-  if (tail == BT)
-    step(Int<0>{}, 0, false, BT);
-  else
-    step(Int<1>{}, 0, false, tail);
 
   l_run += wave_shfl_xor(l_run, 16);
   l_run += wave_shfl_xor(l_run, 32);
@@ -204,6 +342,7 @@ __device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g
   }
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_split_kernel(
     DecodeParams p) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -219,7 +358,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   const int nblk = (t_end - t_begin + BT - 1) / BT;
   const int tail = t_end - t_begin - (nblk - 1) * BT;   // keys in the last block (1..64)
   const int group = p.Hq / p.Hkv;
-  decode_range(p, b, g, t_begin / BT, nblk, tail,
+  decode_range<FP8>(p, b, g, t_begin / BT, nblk, tail,
                p.ws + (((size_t)b * p.Hq + g * group) * p.n_split + split) * REC,
                (size_t)p.n_split * REC);
 }
@@ -289,6 +428,7 @@ __device__ __forceinline__ void locate_unit(const DecodeParams &p, long long pos
   }
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_stream_kernel(
     DecodeParams p) {
   const int w = blockIdx.x, lane = threadIdx.x;
@@ -321,7 +461,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     const int ctx = min(max(p.ctx_len[b], 0), p.max_blocks * BT);
     const int tail = (blk + n == nb) ? ctx - (nb - 1) * BT : BT;
     const long long seg = (long long)b * p.Hkv + g;
-    decode_range(p, b, g, blk, n, tail, p.ws + (size_t)(w + seg) * group * REC, REC);
+    decode_range<FP8>(p, b, g, blk, n, tail, p.ws + (size_t)(w + seg) * group * REC, REC);
     pos = stop;
   }
 }
@@ -432,7 +572,10 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void decode_merge_stream_kernel(D
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
   if (p.B <= 0) return hipSuccess;
   if (p.stream_waves > 0) {
-    hipLaunchKernelGGL(decode_stream_kernel, dim3(p.stream_waves), dim3(64), 0, stream, p);
+    if (p.fp8)
+      hipLaunchKernelGGL(decode_stream_kernel<true>, dim3(p.stream_waves), dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL(decode_stream_kernel<false>, dim3(p.stream_waves), dim3(64), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_stream_kernel, dim3(p.B * p.Hq), dim3(64 * MERGE_WAVES), 0,
@@ -440,7 +583,10 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
     return hipGetLastError();
   }
   dim3 g1(p.n_split, p.Hkv, p.B), b1(64);
-  hipLaunchKernelGGL(decode_split_kernel, g1, b1, 0, stream, p);
+  if (p.fp8)
+    hipLaunchKernelGGL(decode_split_kernel<true>, g1, b1, 0, stream, p);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<false>, g1, b1, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(p.B * p.Hq), b2(64 * MERGE_WAVES);

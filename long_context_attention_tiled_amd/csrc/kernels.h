@@ -41,8 +41,11 @@ hipError_t launch_kv_append(const void *k_new, const void *v_new, void *k_pool, 
 
 struct DecodeParams {
   const void *q;            // [B][Hq][128]
-  const void *k_pool;       // [n_blocks][64][128]
+  const void *k_pool;       // [n_blocks][64][128] (bf16, or e4m3 bytes when fp8)
   const void *v_pool;       // [n_blocks][128][64]
+  const float *k_scale;     // fp8: [n_blocks][64] per-token K scales
+  const float *v_scale;     // fp8: [n_blocks][64] per-token V scales
+  int fp8;
   const int32_t *block_head;
   const int32_t *block_table;
   const int32_t *ctx_len;
@@ -57,6 +60,12 @@ struct DecodeParams {
 };
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+
+// bf16 pools -> e4m3 pools (k8 [n][64][128], v8 [n][128][64]) with per-token
+// scales k_scale / v_scale [n][64].
+hipError_t launch_kv_quantize_fp8(const void *k_pool, const void *v_pool, void *k8, void *v8,
+                                  float *k_scale, float *v_scale, int n_blocks,
+                                  hipStream_t stream);
 
 hipError_t launch_rope(void *x, const int32_t *positions, int S, int H, int D, float base,
                        hipStream_t stream);

@@ -45,6 +45,7 @@ def test_header_declares_the_boundary():
               "attn_kv_append", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv",
               "head_to_seq_permute", "seq_to_head_permute_qkv_rope", "cp_shard_tokens",
               "cp_shard", "cp_unshard", "attn_key_limits", "attn_prefill_limited", "attn_merge",
+              "attn_decode_fp8", "attn_kv_quantize_fp8",
               "attn_status_string"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -227,6 +228,26 @@ def test_cp_and_merge_validation(lib):
     assert mg(q, NUL, k, lb, o, NUL, 1, 64, 16, 128, S0) == NULL
     assert mg(q, la, k, lb, P(0x10000 + 256), NUL, 1, 64, 16, 128, S0) == SHAPE   # partial overlap
     assert mg(q, la, k, lb, o, P(0xA0000000 + 4), 1, 64, 16, 128, S0) == SHAPE   # lse overlap
+
+
+def test_fp8_validation(lib):
+    qz = lib.attn_kv_quantize_fp8
+    k, v, k8, v8, ks, vs = (P(0x10000 * (i + 1)) for i in range(6))
+    assert qz(k, v, k8, v8, ks, vs, 4, 64, S0) == UNSUP
+    assert qz(k, v, k8, v8, ks, vs, -1, 128, S0) == SHAPE
+    assert qz(k, v, k8, NUL, ks, vs, 4, 128, S0) == NULL
+    assert qz(k, v, k8, v8, P(0x30000 + 4), vs, 4, 128, S0) == ALIGN
+    assert qz(NUL, NUL, NUL, NUL, NUL, NUL, 0, 128, S0) == OK
+    d = lib.attn_decode_fp8
+    q, bh, bt, cl, o, ws = (P(0x100000 * (i + 1)) for i in range(6))
+    args = lambda **kw: [kw.get("q", q), k8, v8, kw.get("ks", ks), vs, 8, bh, bt, 4, cl, o, NUL,
+                         2, 16, 2, kw.get("D", 128), 0, 0.1, kw.get("split", 0), ws,
+                         kw.get("wsb", 1 << 30), NUL, S0]
+    assert d(*args(D=64)) == UNSUP
+    assert d(*args(split=100)) == SHAPE
+    assert d(*args(ks=NUL)) == NULL
+    assert d(*args(ks=P(0x30000 + 8))) == ALIGN
+    assert d(*args(wsb=16)) == WS
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

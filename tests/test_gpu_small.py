@@ -537,6 +537,90 @@ def test_cp_ring_attention_on_one_gpu(mode):
 
 
 # ---------------------------------------------------------------------------
+# FP8 KV cache
+# ---------------------------------------------------------------------------
+from oracle import fp8 as ofp8  # noqa: E402
+
+
+def _fp8_pools_from_oracle(c):
+    """Oracle-quantised pools of a decode cache; slots past ctx_len (and spare
+    blocks) get the NaN code and NaN scales, so reading them is caught."""
+    kb, vb = c["k_pool"].copy(), c["v_pool"].copy()
+    kb[np.isnan(synth.bf16_bits_to_f32(kb))] = 0
+    vb[np.isnan(synth.bf16_bits_to_f32(vb))] = 0
+    k8, v8, ks, vs = ofp8.quantize_kv_pool(kb, vb)
+    valid = np.zeros((c["n_blocks"], 64), dtype=bool)
+    table = c["block_table"]
+    for b, ctx in enumerate(c["ctx_len"]):
+        for g in range(table.shape[1]):
+            for j in range((int(ctx) + 63) // 64):
+                valid[table[b, g, j], : min(64, int(ctx) - 64 * j)] = True
+    k8[~valid] = 0x7F
+    v8.transpose(0, 2, 1)[~valid] = 0x7F
+    ks[~valid] = np.nan
+    vs[~valid] = np.nan
+    return k8, v8, ks, vs
+
+
+def test_kv_quantize_fp8_bit_exact():
+    """GPU quantisation of bf16 pools equals the oracle's codes and scales bit
+    for bit (token groups spanning a wide range of magnitudes, an all-zero
+    token, values that round to subnormal codes)."""
+    n = 9
+    kf = synth.bf16_bits_to_f32(synth.normal_bf16(950, (n, 64, 128)))
+    vf = synth.bf16_bits_to_f32(synth.normal_bf16(951, (n, 128, 64)))
+    mag = np.exp(np.random.default_rng(952).uniform(-30, 30, size=(n, 64))).astype(np.float32)
+    kf = kf * mag[:, :, None]
+    vf = vf * mag[:, None, :]
+    kf[0, 5] = 0.0
+    vf[1, :, 7] = 0.0
+    kf[2, 9, :64] *= 1e-4                   # small entries next to a large one: subnormal codes
+    kb, vb = synth.f32_to_bf16_bits(kf), synth.f32_to_bf16_bits(vf)
+    k8, v8, ks, vs = lcat.attn_kv_quantize_fp8(to_dev(kb), to_dev(vb))
+    torch.cuda.synchronize()
+    rk8, rv8, rks, rvs = ofp8.quantize_kv_pool(kb, vb)
+    assert np.array_equal(ks.cpu().numpy(), rks) and np.array_equal(vs.cpu().numpy(), rvs)
+    assert np.array_equal(k8.cpu().numpy(), rk8)
+    assert np.array_equal(v8.cpu().numpy(), rv8)
+
+
+@pytest.mark.parametrize("split", [64, 256, 0])
+def test_decode_fp8_vs_oracle(split):
+    ctx = [1, 2, 63, 64, 65, 127, 128, 1000, 3001]
+    log(f"decode fp8 ctx={ctx} split={split}")
+    c = synth.decode_cache(seed=960, B=len(ctx), ctx_lens=ctx, Hq=16, Hkv=2, kv_head_base=2,
+                           extra_blocks=5)
+    k8, v8, ks, vs = _fp8_pools_from_oracle(c)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o, lse = lcat.attn_decode_fp8(to_dev(c["q"]), torch.from_numpy(k8).cuda(),
+                                  torch.from_numpy(v8).cuda(), to_dev(ks), to_dev(vs),
+                                  to_dev(c["block_head"]), to_dev(c["block_table"]),
+                                  to_dev(c["ctx_len"]), kv_head_base=2, split_tokens=split,
+                                  dev_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    kq, vq = ofp8.gather_dequantized(k8, v8, ks, vs, c["block_table"], c["ctx_len"])
+    ref, ref_lse = oracle.decode_attention(c["q"], kq, vq, c["ctx_len"], c["scale"])
+    e, r = assert_attention_close(to_np64(o), ref, lse.cpu().numpy(), ref_lse, what="decode fp8")
+    log(f"  max abs {e:.3g} rel-L2 {r:.3g}")
+
+
+@pytest.mark.parametrize("group", [1, 4, 16])
+def test_decode_fp8_group_sizes(group):
+    Hkv = 2
+    c = synth.decode_cache(seed=961 + group, B=3, ctx_lens=[700, 64, 129], Hq=group * Hkv, Hkv=Hkv)
+    k8, v8, ks, vs = _fp8_pools_from_oracle(c)
+    o, lse = lcat.attn_decode_fp8(to_dev(c["q"]), torch.from_numpy(k8).cuda(),
+                                  torch.from_numpy(v8).cuda(), to_dev(ks), to_dev(vs),
+                                  to_dev(c["block_head"]), to_dev(c["block_table"]),
+                                  to_dev(c["ctx_len"]))
+    torch.cuda.synchronize()
+    kq, vq = ofp8.gather_dequantized(k8, v8, ks, vs, c["block_table"], c["ctx_len"])
+    ref, ref_lse = oracle.decode_attention(c["q"], kq, vq, c["ctx_len"], c["scale"])
+    assert_attention_close(to_np64(o), ref, lse.cpu().numpy(), ref_lse, what="decode fp8")
+
+
+# ---------------------------------------------------------------------------
 # chunked prefill against the paged cache
 # ---------------------------------------------------------------------------
 def _run_chunked(d, C, kv_head_base=0):
