@@ -102,24 +102,27 @@ def dequantize_kv_pool(k8, v8, k_scale, v_scale):
     return k, v
 
 
-def gather_dequantized(k8, v8, k_scale, v_scale, block_table, ctx_len):
-    """Per request b, the dequantised K and V of its first ctx_len[b] tokens in
-    order, [ctx][Hkv][D] fp64 each: token t of KV head g sits in slot t % 64
-    of physical block block_table[b][g][t // 64] (the paged layout of the
-    Ulysses inference article, §2.3)."""
-    k, v = dequantize_kv_pool(k8, v8, k_scale, v_scale)        # [n][64][D], [n][D][64]
+def gather_dequantized(k8, v8, k_scale, v_scale, block_table, ctx_len, requests=None):
+    """Per request b (all, or those listed in ``requests``), the dequantised K
+    and V of its first ctx_len[b] tokens in order, [ctx][Hkv][D] fp64 each:
+    token t of KV head g sits in slot t % 64 of physical block
+    block_table[b][g][t // 64] (the paged layout of the Ulysses inference
+    article, §2.3).  Only the blocks of those requests are dequantised."""
     table = np.asarray(block_table)
     B, Hkv, _ = table.shape
+    D = np.asarray(k8).shape[2]
     ks, vs = [], []
-    for b in range(B):
+    for b in (range(B) if requests is None else requests):
         T = int(ctx_len[b])
-        t = np.arange(T)
-        kb = np.empty((T, Hkv, k.shape[2]))
-        vb = np.empty((T, Hkv, k.shape[2]))
+        nb = (T + 63) // 64
+        kb = np.empty((T, Hkv, D))
+        vb = np.empty((T, Hkv, D))
         for g in range(Hkv):
-            blk = table[b, g, t // 64]
-            kb[:, g] = k[blk, t % 64]
-            vb[:, g] = v[blk, :, t % 64]
+            blk = table[b, g, :nb]
+            k = dequantize_groups(k8[blk], k_scale[blk])                        # [nb][64][D]
+            v = dequantize_groups(np.swapaxes(v8[blk], 1, 2), v_scale[blk])     # [nb][64][D]
+            kb[:, g] = k.reshape(nb * 64, D)[:T]
+            vb[:, g] = v.reshape(nb * 64, D)[:T]
         ks.append(kb)
         vs.append(vb)
     return ks, vs

@@ -174,6 +174,56 @@ def test_decode_paged_32_requests():
     log(f"C4: max abs {e:.3g} rel-L2 {r:.3g}")
 
 
+def test_decode_fp8_32_requests():
+    """FP8-cache decode at the 32-request shape, in the launch configuration
+    the benchmark times (equal-share split): seeded e4m3 codes (exponent
+    fields 3..10, random signs) and per-token scales for every cached token,
+    the NaN code and NaN scales in unused slots; four sampled requests (all
+    16 heads, whole contexts) against the oracle over the dequantised cache."""
+    from oracle import fp8 as ofp8
+    log("C4 fp8: generating cache")
+    c = synth.decode_cache(seed=4, B=32, with_content=False)
+    n = c["n_blocks"]
+    rng = np.random.default_rng(930)
+
+    def codes(shape):
+        e = rng.integers(3, 11, size=shape, dtype=np.uint8)
+        m = rng.integers(0, 8, size=shape, dtype=np.uint8)
+        sgn = rng.integers(0, 2, size=shape, dtype=np.uint8)
+        return (sgn << 7) | (e << 3) | m
+
+    k8, v8 = codes((n, 64, 128)), codes((n, 128, 64))
+    ks = rng.uniform(0.02, 0.1, size=(n, 64)).astype(np.float32)
+    vs = rng.uniform(0.02, 0.1, size=(n, 64)).astype(np.float32)
+    valid = np.zeros((n, 64), dtype=bool)
+    table = c["block_table"]
+    for b, ctx in enumerate(c["ctx_len"]):
+        nb = (int(ctx) + 63) // 64
+        for g in range(table.shape[1]):
+            valid[table[b, g, :nb - 1]] = True
+            valid[table[b, g, nb - 1], : int(ctx) - 64 * (nb - 1)] = True
+    k8[~valid] = 0x7F
+    v8.transpose(0, 2, 1)[~valid] = 0x7F
+    ks[~valid] = np.nan
+    vs[~valid] = np.nan
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    log(f"C4 fp8: decode, total context {int(c['ctx_len'].sum())} tokens")
+    o, lse = lcat.attn_decode_fp8(to_dev(c["q"]), torch.from_numpy(k8).cuda(),
+                                  torch.from_numpy(v8).cuda(), to_dev(ks), to_dev(vs),
+                                  to_dev(c["block_head"]), to_dev(table), to_dev(c["ctx_len"]),
+                                  dev_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    sel = sorted(set(np.random.default_rng(931).choice(32, 3, replace=False).tolist())
+                 | {int(np.argmax(c["ctx_len"]))})
+    log(f"C4 fp8: oracle on requests {sel}")
+    kq, vq = ofp8.gather_dequantized(k8, v8, ks, vs, table, c["ctx_len"], requests=sel)
+    ref, ref_lse = oracle.decode_attention(c["q"][sel], kq, vq, c["ctx_len"][sel], c["scale"])
+    e, r = assert_attention_close(to_np64(o)[sel], ref, lse.cpu().numpy()[sel], ref_lse,
+                                  what="C4 fp8")
+    log(f"C4 fp8: max abs {e:.3g} rel-L2 {r:.3g}")
+
+
 def test_chunked_prefill_4x131072():
     B, S, C = 4, 131072, 8192
     log("C5: generating inputs")
