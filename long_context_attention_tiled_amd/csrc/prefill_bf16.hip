@@ -49,7 +49,7 @@ constexpr int VA = WD + 1;              // iteration j fetches V_{j+VA}
 constexpr int NKS = KA;                 // K ring slots
 constexpr int NVS = VA + 2;             // V ring slots (after the K slots)
 constexpr int VBASE = NKS * TILE;       // LDS byte offset of the V ring
-constexpr int LA = 3;                   // operands are read LA MFMA slots before their use
+constexpr int LA = 2;                   // operands are read LA MFMA slots before their use
 constexpr int NPV = LA;                 // P V operands read before the barrier
 constexpr int NPK = LA;                 // K Q^T operands read before the barrier
 // Every iteration issues the same DMA count per DMA wave; iteration j ends by
