@@ -112,9 +112,9 @@ def test_decode_validation(lib):
     f = lib.attn_decode
     need = lib.attn_decode_workspace_bytes(32, 16, 128, 2048, 1024)
     assert need == 32 * 16 * 128 * 132 * 4
-    # 0 = automatic: records of at most 2048 waves + one per (request, KV head)
+    # 0 = automatic: records of at most 768 waves + one per (request, KV head)
     # piece boundary, each holding 132 floats per query head
-    assert lib.attn_decode_workspace_bytes(32, 16, 128, 2048, 0) == (2048 + 32) * 16 * 132 * 4
+    assert lib.attn_decode_workspace_bytes(32, 16, 128, 2048, 0) == (768 + 32) * 16 * 132 * 4
     assert lib.attn_decode_workspace_bytes(32, 16, 128, 2048, 100) == 0    # not a multiple of 64
     assert lib.attn_decode_workspace_bytes(32, 16, 64, 2048, 0) == 0
 
