@@ -61,11 +61,9 @@ constexpr int NPK = LA;                 // K Q^T operands read before the barrie
 static_assert(KA >= WD + 3 && VA >= WD + 1, "tiles are published before their first read");
 static_assert(NKS >= KA && NVS >= VA + 2, "a slot is refilled only after its last reader");
 static_assert((NKS + NVS) * 16384 <= 160 * 1024, "LDS");
-// Waves that issue the tile DMAs: the four older ones in the dense causal
-// kernel (see the fetch below); all eight, two 1 KiB pieces each, in the
-// variants whose registers are tighter (paged, non-causal).
-template <bool PAGED, bool CAUSAL>
-constexpr int dma_waves() { return (!PAGED && CAUSAL) ? 4 : 8; }
+// Waves that issue the tile DMAs: the four older ones, 4 KiB of each tile
+// apiece (see the fetch below).
+constexpr int NDW = 4;
 
 // K tile (and dense V tile): 64 key rows x 16 chunks of 8 dims (256 B rows).
 // Chunk c of K row r sits at position c ^ (r & 15): the 16 rows read by one
@@ -346,7 +344,6 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   // slot: key rows 4 (DPW w + i) .. +3 (K, dense V) or dimension rows
   // 8 (DPW w + i) .. +7 (paged V^T).  Each lane picks the global chunk whose
   // swizzled position is its own LDS position.
-  constexpr int NDW = dma_waves<PAGED, CAUSAL>();
   constexpr int DPW = TILE / 1024 / NDW;   // 1 KiB pieces per DMA wave, tile and tensor
   const bool dma_wave = wave < NDW;
   const int rs = PAGED ? HD * 2 : p.Hkv * HD * 2;   // bytes between key rows
