@@ -167,6 +167,19 @@ int attn_kv_quantize_fp8(const void *k_pool, const void *v_pool, void *k8_pool, 
                          float *k_scale, float *v_scale, int n_blocks, int D, void *stream);
 
 /*
+ * attn_kv_append_fp8 — attn_kv_append into the FP8 pools: the same token ->
+ * slot map, block checks and dev_status codes; each appended token's K row
+ * and V vector are quantised with their own scales exactly as
+ * attn_kv_quantize_fp8 would ([ULY] §5.4 grouped quantised cache), and no
+ * other token's codes or scales change.  k_new, v_new [B][T][Hkv][D] bf16.
+ */
+int attn_kv_append_fp8(const void *k_new, const void *v_new, void *k8_pool, void *v8_pool,
+                       float *k_scale, float *v_scale, int n_blocks, const int32_t *block_head,
+                       const int32_t *block_table, int max_blocks, const int32_t *start_pos, int T,
+                       int B, int Hkv, int D, int kv_head_base, int32_t *dev_status,
+                       void *stream);
+
+/*
  * attn_decode_fp8 — attn_decode over the FP8 cache: the same arguments,
  * splits, workspace (attn_decode_workspace_bytes), tag and block checks and
  * outputs, with the e4m3 pools and their per-token scales in place of the

@@ -27,7 +27,7 @@ __all__ = [
     "attn_decode_workspace_bytes", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv", "head_to_seq_permute",
     "seq_to_head_permute_qkv_rope", "cp_shard_tokens", "cp_shard", "cp_unshard",
     "attn_key_limits", "attn_prefill_limited", "attn_merge", "CP_MODES", "attn_decode_fp8",
-    "attn_kv_quantize_fp8",
+    "attn_kv_quantize_fp8", "attn_kv_append_fp8",
     "attn_status_string",
     "AttnError", "ATTN_DEV_OK", "ATTN_DEV_BAD_TAG", "ATTN_DEV_BAD_BLOCK", "load_library",
 ]
@@ -236,6 +236,31 @@ def attn_kv_quantize_fp8(k_pool, v_pool, k8_pool=None, v8_pool=None, k_scale=Non
                                           _stream(stream))
     _lib.check("attn_kv_quantize_fp8", st)
     return k8_pool, v8_pool, k_scale, v_scale
+
+
+def attn_kv_append_fp8(k_new, v_new, k8_pool, v8_pool, k_scale, v_scale, block_head, block_table,
+                       start_pos, kv_head_base=0, dev_status=None, stream=None):
+    """Quantise and write ``k_new/v_new [B][T][Hkv][128]`` (bf16) into the fp8
+    pools at positions ``start_pos[b] + t``."""
+    torch = _torch()
+    _need(k_new, "k_new", torch.bfloat16)
+    B, T, Hkv, D = k_new.shape
+    _need(v_new, "v_new", torch.bfloat16, k_new.shape)
+    n_blocks = k8_pool.shape[0]
+    _need(k8_pool, "k8_pool", torch.uint8, (n_blocks, BLOCK_TOKENS, D))
+    _need(v8_pool, "v8_pool", torch.uint8, (n_blocks, D, BLOCK_TOKENS))
+    _need(k_scale, "k_scale", torch.float32, (n_blocks, BLOCK_TOKENS))
+    _need(v_scale, "v_scale", torch.float32, (n_blocks, BLOCK_TOKENS))
+    _need(block_head, "block_head", torch.int32, (n_blocks,))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.shape[:2] != (B, Hkv):
+        raise ValueError("block_table must be [B][Hkv][max_blocks]")
+    _need(start_pos, "start_pos", torch.int32, (B,))
+    st = _lib.load().attn_kv_append_fp8(
+        _ptr(k_new), _ptr(v_new), _ptr(k8_pool), _ptr(v8_pool), _ptr(k_scale), _ptr(v_scale),
+        n_blocks, _ptr(block_head), _ptr(block_table), block_table.shape[2], _ptr(start_pos), T, B,
+        Hkv, D, int(kv_head_base), _ptr(dev_status), _stream(stream))
+    _lib.check("attn_kv_append_fp8", st)
 
 
 def attn_decode_fp8(q, k8_pool, v8_pool, k_scale, v_scale, block_head, block_table, ctx_len,

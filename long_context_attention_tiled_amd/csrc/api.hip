@@ -245,6 +245,25 @@ int attn_decode_fp8(const void *q, const void *k8_pool, const void *v8_pool, con
                        scale, split_tokens, workspace, workspace_bytes, dev_status, stream);
 }
 
+int attn_kv_append_fp8(const void *k_new, const void *v_new, void *k8_pool, void *v8_pool,
+                       float *k_scale, float *v_scale, int n_blocks, const int32_t *block_head,
+                       const int32_t *block_table, int max_blocks, const int32_t *start_pos, int T,
+                       int B, int Hkv, int D, int kv_head_base, int32_t *dev_status,
+                       void *stream) {
+  if (T < 0 || B < 0 || Hkv <= 0 || n_blocks <= 0 || max_blocks <= 0) return ATTN_ERR_SHAPE;
+  if (D != kHeadDim) return ATTN_ERR_UNSUPPORTED;
+  if (T == 0 || B == 0) return ATTN_OK;
+  if (!k_new || !v_new || !k8_pool || !v8_pool || !k_scale || !v_scale || !block_head ||
+      !block_table || !start_pos)
+    return ATTN_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k8_pool) || !aligned16(v8_pool))
+    return ATTN_ERR_ALIGN;
+  return hip_status(lcat::launch_kv_append_fp8(k_new, v_new, k8_pool, v8_pool, k_scale, v_scale,
+                                               n_blocks, block_head, block_table, max_blocks,
+                                               start_pos, T, B, Hkv, kv_head_base, dev_status,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int attn_kv_quantize_fp8(const void *k_pool, const void *v_pool, void *k8_pool, void *v8_pool,
                          float *k_scale, float *v_scale, int n_blocks, int D, void *stream) {
   if (n_blocks < 0) return ATTN_ERR_SHAPE;

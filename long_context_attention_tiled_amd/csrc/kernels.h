@@ -67,6 +67,13 @@ hipError_t launch_kv_quantize_fp8(const void *k_pool, const void *v_pool, void *
                                   float *k_scale, float *v_scale, int n_blocks,
                                   hipStream_t stream);
 
+// attn_kv_append into the fp8 pools, quantising each appended token.
+hipError_t launch_kv_append_fp8(const void *k_new, const void *v_new, void *k8, void *v8,
+                                float *k_scale, float *v_scale, int n_blocks,
+                                const int32_t *block_head, const int32_t *block_table,
+                                int max_blocks, const int32_t *start_pos, int T, int B, int Hkv,
+                                int kv_head_base, int32_t *dev_status, hipStream_t stream);
+
 hipError_t launch_rope(void *x, const int32_t *positions, int S, int H, int D, float base,
                        hipStream_t stream);
 

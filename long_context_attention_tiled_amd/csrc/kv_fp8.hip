@@ -113,7 +113,108 @@ __global__ __launch_bounds__(256) void kv_quantize_fp8_kernel(const bf16 *__rest
   if (tid < BT) v_scale[blk * BT + tid] = __builtin_bit_cast(float, colmax[tid]) / kE4M3Max;
 }
 
+// Append T new tokens per request straight into the fp8 pools (the token ->
+// slot map of attn_kv_append), quantising each token's K row and V vector
+// with its own scale exactly as the pool quantiser does.  One workgroup per
+// (touched block, KV head, request); four threads per token, 32 elements
+// each.  The V codes are staged in LDS and written dimension row by
+// dimension row, one byte per lane (consecutive slots), so earlier tokens of
+// a partially filled block are left as they are.
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(
+    const bf16 *__restrict__ k_new, const bf16 *__restrict__ v_new, uint8_t *__restrict__ k8,
+    uint8_t *__restrict__ v8, float *__restrict__ k_scale, float *__restrict__ v_scale,
+    int n_blocks, const int32_t *__restrict__ block_head, const int32_t *__restrict__ block_table,
+    int max_blocks, const int32_t *__restrict__ start_pos, int T, int Hkv, int kv_head_base,
+    int32_t *dev_status) {
+  __shared__ uint8_t vcodes[BT * (HD + 4)];   // [slot][dim], rows padded by 4 bytes
+  const int tid = threadIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int start = start_pos[b];
+  if (start < 0 || (long long)start + T > (long long)max_blocks * BT) {
+    if (blockIdx.x == 0 && tid == 0 && dev_status) dev_status[0] = 2;
+    return;
+  }
+  const int j = start / BT + (int)blockIdx.x;          // logical block of this workgroup
+  const int lo = max(start, j * BT), hi = min(start + T, (j + 1) * BT);
+  if (lo >= hi) return;
+  const int blk = block_table[((size_t)b * Hkv + g) * max_blocks + j];
+  if (blk < 0 || blk >= n_blocks) {
+    if (tid == 0 && dev_status) dev_status[0] = 2;
+    return;
+  }
+  if (block_head[blk] != kv_head_base + g) {
+    if (tid == 0 && dev_status) dev_status[0] = 1;
+    return;
+  }
+  const int s_lo = lo - j * BT, s_hi = hi - j * BT;     // slot range [s_lo, s_hi)
+  const int slot = tid >> 2, qd = tid & 3;
+  const bool live = slot >= s_lo && slot < s_hi;        // uniform over each group of 4 lanes
+  const size_t src = live ? (((size_t)b * T + (j * BT + slot - start)) * Hkv + g) * HD + 32 * qd : 0;
+  for (int which = 0; which < 2; ++which) {
+    const bf16 *in = which == 0 ? k_new : v_new;
+    bf16x8 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = live ? as_bf16x8(ld_global_16(in + src + 8 * i)) : bf16x8{};
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)x[i][e]));
+    amax = fmaxf(amax, wave_shfl_xor(amax, 1));
+    amax = fmaxf(amax, wave_shfl_xor(amax, 2));
+    const float scale = amax / kE4M3Max;
+    u32x4 out[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = scale > 0.f ? (float)x[i][e] / scale : 0.f;
+      const u32x2 w = to_fp8x8(y);
+      out[i >> 1][2 * (i & 1)] = w[0];
+      out[i >> 1][2 * (i & 1) + 1] = w[1];
+    }
+    if (which == 0) {
+      if (live) {
+        uint8_t *dst = k8 + ((size_t)blk * BT + slot) * HD + 32 * qd;
+        st_global_16(dst, out[0]);
+        st_global_16(dst + 16, out[1]);
+        if (qd == 0) k_scale[(size_t)blk * BT + slot] = scale;
+      }
+    } else {
+      uint32_t *row = reinterpret_cast<uint32_t *>(vcodes + slot * (HD + 4) + 32 * qd);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        row[e] = out[0][e];
+        row[4 + e] = out[1][e];
+      }
+      if (live && qd == 0) v_scale[(size_t)blk * BT + slot] = scale;
+    }
+  }
+  __syncthreads();
+  // V^T rows: lane = slot, each wave walks a quarter of the dimensions
+  const int ls = tid & 63;
+  if (ls >= s_lo && ls < s_hi) {
+    uint8_t *dst = v8 + (size_t)blk * HD * BT + ls;
+    for (int d = tid >> 6; d < HD; d += 4) dst[(size_t)d * BT] = vcodes[ls * (HD + 4) + d];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kv_append_fp8(const void *k_new, const void *v_new, void *k8, void *v8,
+                                float *k_scale, float *v_scale, int n_blocks,
+                                const int32_t *block_head, const int32_t *block_table,
+                                int max_blocks, const int32_t *start_pos, int T, int B, int Hkv,
+                                int kv_head_base, int32_t *dev_status, hipStream_t stream) {
+  if (T <= 0 || B <= 0) return hipSuccess;
+  dim3 grid((T + BT - 1) / BT + 1, Hkv, B), block(256);
+  hipLaunchKernelGGL(kv_append_fp8_kernel, grid, block, 0, stream,
+                     static_cast<const bf16 *>(k_new), static_cast<const bf16 *>(v_new),
+                     static_cast<uint8_t *>(k8), static_cast<uint8_t *>(v8), k_scale, v_scale,
+                     n_blocks, block_head, block_table, max_blocks, start_pos, T, Hkv,
+                     kv_head_base, dev_status);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_quantize_fp8(const void *k_pool, const void *v_pool, void *k8, void *v8,
                                   float *k_scale, float *v_scale, int n_blocks,

@@ -45,7 +45,7 @@ def test_header_declares_the_boundary():
               "attn_kv_append", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv",
               "head_to_seq_permute", "seq_to_head_permute_qkv_rope", "cp_shard_tokens",
               "cp_shard", "cp_unshard", "attn_key_limits", "attn_prefill_limited", "attn_merge",
-              "attn_decode_fp8", "attn_kv_quantize_fp8",
+              "attn_decode_fp8", "attn_kv_quantize_fp8", "attn_kv_append_fp8",
               "attn_status_string"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -238,6 +238,13 @@ def test_fp8_validation(lib):
     assert qz(k, v, k8, NUL, ks, vs, 4, 128, S0) == NULL
     assert qz(k, v, k8, v8, P(0x30000 + 4), vs, 4, 128, S0) == ALIGN
     assert qz(NUL, NUL, NUL, NUL, NUL, NUL, 0, 128, S0) == OK
+    ap = lib.attn_kv_append_fp8
+    kn, vn, bh, bt, sp = (P(0x1000000 * (i + 1)) for i in range(5))
+    assert ap(kn, vn, k8, v8, ks, vs, 8, bh, bt, 4, sp, 10, 2, 2, 64, 0, NUL, S0) == UNSUP
+    assert ap(kn, vn, k8, v8, ks, vs, 0, bh, bt, 4, sp, 10, 2, 2, 128, 0, NUL, S0) == SHAPE
+    assert ap(kn, vn, k8, v8, NUL, vs, 8, bh, bt, 4, sp, 10, 2, 2, 128, 0, NUL, S0) == NULL
+    assert ap(MIS, vn, k8, v8, ks, vs, 8, bh, bt, 4, sp, 10, 2, 2, 128, 0, NUL, S0) == ALIGN
+    assert ap(NUL, NUL, NUL, NUL, NUL, NUL, 8, NUL, NUL, 4, NUL, 0, 2, 2, 128, 0, NUL, S0) == OK
     d = lib.attn_decode_fp8
     q, bh, bt, cl, o, ws = (P(0x100000 * (i + 1)) for i in range(6))
     args = lambda **kw: [kw.get("q", q), k8, v8, kw.get("ks", ks), vs, 8, bh, bt, 4, cl, o, NUL,

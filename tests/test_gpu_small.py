@@ -584,6 +584,47 @@ def test_kv_quantize_fp8_bit_exact():
     assert np.array_equal(v8.cpu().numpy(), rv8)
 
 
+def test_kv_append_fp8_bit_exact():
+    """Appending tokens into fp8 pools writes each token's oracle codes and
+    scales at its slot (partial first and last blocks, several requests and
+    heads) and leaves every other slot of the pools untouched."""
+    B, Hkv, T = 3, 2, 100
+    starts = np.array([0, 70, 130], dtype=np.int32)
+    max_blocks = 5
+    rng = np.random.default_rng(970)
+    n = B * Hkv * max_blocks + 4
+    ids = rng.permutation(n)[: B * Hkv * max_blocks].reshape(B, Hkv, max_blocks).astype(np.int32)
+    tags = np.full((n,), -1, dtype=np.int32)
+    for g in range(Hkv):
+        tags[ids[:, g]] = 3 + g
+    k8 = rng.integers(0, 256, size=(n, 64, 128), dtype=np.uint8)
+    v8 = rng.integers(0, 256, size=(n, 128, 64), dtype=np.uint8)
+    ks = rng.uniform(0.1, 1, size=(n, 64)).astype(np.float32)
+    vs = rng.uniform(0.1, 1, size=(n, 64)).astype(np.float32)
+    kn = synth.normal_bf16(971, (B, T, Hkv, 128))
+    vn = synth.normal_bf16(972, (B, T, Hkv, 128))
+    kn_f = synth.bf16_bits_to_f32(kn) * np.exp(rng.uniform(-5, 5, (B, T, Hkv, 1))).astype(np.float32)
+    kn = synth.f32_to_bf16_bits(kn_f)
+    d8 = [torch.from_numpy(a.copy()).cuda() for a in (k8, v8)]
+    dsc = [to_dev(a.copy()) for a in (ks, vs)]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lcat.attn_kv_append_fp8(to_dev(kn), to_dev(vn), d8[0], d8[1], dsc[0], dsc[1], to_dev(tags),
+                            to_dev(ids), to_dev(starts), kv_head_base=3, dev_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    ck, sk = ofp8.quantize_groups(synth.bf16_bits_to_f32(kn))     # [B][T][Hkv][128], [B][T][Hkv]
+    cv, sv = ofp8.quantize_groups(synth.bf16_bits_to_f32(vn))
+    for b in range(B):
+        for t in range(T):
+            pos = starts[b] + t
+            for g in range(Hkv):
+                blk, sl = ids[b, g, pos // 64], pos % 64
+                k8[blk, sl], ks[blk, sl] = ck[b, t, g], sk[b, t, g]
+                v8[blk, :, sl], vs[blk, sl] = cv[b, t, g], sv[b, t, g]
+    assert np.array_equal(d8[0].cpu().numpy(), k8) and np.array_equal(d8[1].cpu().numpy(), v8)
+    assert np.array_equal(dsc[0].cpu().numpy(), ks) and np.array_equal(dsc[1].cpu().numpy(), vs)
+
+
 @pytest.mark.parametrize("split", [64, 256, 0])
 def test_decode_fp8_vs_oracle(split):
     ctx = [1, 2, 63, 64, 65, 127, 128, 1000, 3001]
