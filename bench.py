@@ -22,7 +22,7 @@ The same JSON line also carries, each measured in this run:
                   with separate and with fused relayout + RoPE;
   chunked_prefill 4 requests x 131072 tokens in 8192-token chunks;
   cp_zigzag_64k   one rank of zigzag context parallelism (4 ranks, 65536
-                  tokens): partials against every key shard + LSE merges;
+                  tokens): partials against every key shard, merged by LSE;
   cpu_baseline    the fp64 CPU oracle timed on a bounded sample of query rows
                   of the step workload, on this host's cores.
 The decode and relayout times are means over calls enqueued back to back.
@@ -325,7 +325,8 @@ def bench_chunked(torch, lcat, synth):
 def bench_cp(torch, lcat, iters=3):
     """Zigzag context parallelism, 4 ranks over 65536 tokens, 16 Q / 2 KV heads:
     the work of one rank (its queries against every rank's key shard with
-    position-derived limits, then the LSE merges), all shards resident."""
+    position-derived limits, the partials combined by the LSE rescale), all
+    shards resident."""
     S, N, Hq, Hkv, mode = 65536, 4, 16, 2, "zigzag"
     q = seeded_normal_bf16(torch, (S, Hq, D), 61)
     k = seeded_normal_bf16(torch, (S, Hkv, D), 62)
@@ -339,7 +340,7 @@ def bench_cp(torch, lcat, iters=3):
         parts = [(torch.empty((1, n, Hq, D), dtype=torch.bfloat16, device="cuda"),
                   torch.empty((1, Hq, n), dtype=torch.float32, device="cuda")) for _ in range(N)]
 
-        def rank_step():
+        def rank_step_merge():   # partials, then the LSE merge kernel
             for s_, ((ks, kpos), vs) in enumerate(shards):
                 lcat.attn_key_limits(qpos, kpos, out=lims[s_])
                 lcat.attn_prefill_limited(qr[None], ks[None], vs[None], lims[s_], o=parts[s_][0],
@@ -348,21 +349,33 @@ def bench_cp(torch, lcat, iters=3):
                 lcat.attn_merge(parts[0][0], parts[0][1], parts[s_][0], parts[s_][1],
                                 o=parts[0][0], lse=parts[0][1])
 
-        rank_step()
-        torch.cuda.synchronize()
-        timer = EventTimer(torch)
-        for _ in range(iters):
-            with timer:
-                rank_step()
-        torch.cuda.synchronize()
-        ms = timer.mean_ms()
+        def rank_step():   # each partial merged into the running result in its epilogue
+            for s_, ((ks, kpos), vs) in enumerate(shards):
+                lcat.attn_key_limits(qpos, kpos, out=lims[s_])
+                lcat.attn_prefill_limited(qr[None], ks[None], vs[None], lims[s_], o=parts[0][0],
+                                          lse=parts[0][1], accumulate=s_ > 0)
+
+        times = {}
+        for name, fn in (("merge_kernels", rank_step_merge), ("accumulate", rank_step)):
+            fn()
+            torch.cuda.synchronize()
+            timer = EventTimer(torch)
+            for _ in range(iters):
+                with timer:
+                    fn()
+            torch.cuda.synchronize()
+            times[name] = timer.mean_ms()
+        ms = times["accumulate"]
         pairs = float((qpos.long() + 1).sum().item())      # causal: keys at positions <= p
         flops = 4.0 * D * Hq * pairs
         tf = flops / (ms * 1e-3) / 1e12
         res[f"rank{rank}"] = dict(ms=round(ms, 3), TFLOPs=round(tf, 1),
-                                  frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4), flop=flops)
+                                  frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4), flop=flops,
+                                  ms_with_merge_kernels=round(times["merge_kernels"], 3))
     res["workload"] = ("zigzag context parallelism, 4 ranks over 65536 tokens, 16 Q / 2 KV heads: "
-                       "one rank's 4 partials (key limits + prefix-limited prefill) and 3 LSE merges")
+                       "one rank's 4 partials (key limits + prefix-limited prefill), each merged "
+                       "into the running (O, LSE) in its epilogue; ms_with_merge_kernels: the same "
+                       "with separate LSE merge launches")
     return res
 
 

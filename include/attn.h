@@ -307,10 +307,14 @@ int attn_key_limits(const int32_t *q_pos, const int32_t *k_pos, int32_t *key_lim
  * LSE = -inf, i.e. weight 0 in attn_merge.  q, o [B][Sq][Hq][D]; lse
  * [B][Hq][Sq] (nullable).  This is the partial attention of one rank's
  * queries against one key shard in ring / striped / zigzag attention.
+ * accumulate = 1: o and lse (then required) already hold a normalised
+ * partial of the same rows over other keys, and this call merges its own
+ * partial into them in place with attn_merge's rule, so a ring of shards
+ * needs no separate merge pass.
  */
 int attn_prefill_limited(const void *q, const void *k, const void *v, const int32_t *key_limit,
                          void *o, float *lse, int B, int Sq, int Sk, int Hq, int Hkv, int D,
-                         float scale, void *stream);
+                         float scale, int accumulate, void *stream);
 
 /*
  * attn_merge — combine two normalised partial results of the same rows over

@@ -471,9 +471,12 @@ def attn_key_limits(q_pos, k_pos, out=None, stream=None):
     return out
 
 
-def attn_prefill_limited(q, k, v, key_limit, scale=None, o=None, lse=None, stream=None):
+def attn_prefill_limited(q, k, v, key_limit, scale=None, o=None, lse=None, accumulate=False,
+                         stream=None):
     """bf16 attention where row i of batch b sees keys ``[0, key_limit[b][i])``;
-    q ``[B][Sq][Hq][128]``, k/v ``[B][Sk][Hkv][128]``; returns ``(o, lse)``."""
+    q ``[B][Sq][Hq][128]``, k/v ``[B][Sk][Hkv][128]``; returns ``(o, lse)``.
+    With ``accumulate``, ``o``/``lse`` hold a partial over other keys and this
+    call merges into them in place."""
     torch = _torch()
     _need(q, "q", torch.bfloat16)
     B, Sq, Hq, D = q.shape
@@ -481,6 +484,8 @@ def attn_prefill_limited(q, k, v, key_limit, scale=None, o=None, lse=None, strea
     _need(k, "k", torch.bfloat16, (B, Sk, Hkv, D))
     _need(v, "v", torch.bfloat16, (B, Sk, Hkv, D))
     _need(key_limit, "key_limit", torch.int32, (B, Sq))
+    if accumulate and (o is None or lse is None):
+        raise ValueError("accumulate needs the partial to merge into: pass o and lse")
     if o is None:
         o = torch.empty_like(q)
     _need(o, "o", torch.bfloat16, q.shape)
@@ -489,7 +494,8 @@ def attn_prefill_limited(q, k, v, key_limit, scale=None, o=None, lse=None, strea
     _need(lse, "lse", torch.float32, (B, Hq, Sq))
     scale = float(D ** -0.5) if scale is None else float(scale)
     st = _lib.load().attn_prefill_limited(_ptr(q), _ptr(k), _ptr(v), _ptr(key_limit), _ptr(o),
-                                          _ptr(lse), B, Sq, Sk, Hq, Hkv, D, scale, _stream(stream))
+                                          _ptr(lse), B, Sq, Sk, Hq, Hkv, D, scale,
+                                          int(bool(accumulate)), _stream(stream))
     _lib.check("attn_prefill_limited", st)
     return o, lse
 

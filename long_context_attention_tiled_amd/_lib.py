@@ -49,7 +49,8 @@ SIGNATURES = {
     "cp_shard": (_i, [_vp, _vp, _vp, _ll, _i, _i, _i, _i, _i, _i, _vp]),
     "cp_unshard": (_i, [_vp, _vp, _ll, _i, _i, _i, _i, _i, _i, _vp]),
     "attn_key_limits": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
-    "attn_prefill_limited": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp]),
+    "attn_prefill_limited": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
+                                  _vp]),
     "attn_merge": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
 }

@@ -416,17 +416,18 @@ int attn_key_limits(const int32_t *q_pos, const int32_t *k_pos, int32_t *key_lim
 
 int attn_prefill_limited(const void *q, const void *k, const void *v, const int32_t *key_limit,
                          void *o, float *lse, int B, int Sq, int Sk, int Hq, int Hkv, int D,
-                         float scale, void *stream) {
+                         float scale, int accumulate, void *stream) {
   if (B < 0 || Sq < 0 || Sk <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return ATTN_ERR_SHAPE;
   if (D != kHeadDim || !group_ok(Hq, Hkv)) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || Sq == 0) return ATTN_OK;
-  if (!q || !k || !v || !o || !key_limit) return ATTN_ERR_NULL;
+  if (!q || !k || !v || !o || !key_limit || (accumulate && !lse)) return ATTN_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
   lcat::PrefillParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv;
   p.causal = 1;
   p.key_limit = key_limit;
+  p.accumulate = accumulate != 0;
   p.scale = scale;
   return hip_status(lcat::launch_prefill_bf16(p, false, static_cast<hipStream_t>(stream)));
 }

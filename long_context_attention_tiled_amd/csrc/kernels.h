@@ -26,6 +26,7 @@ struct PrefillParams {
   int causal;
   float scale;
   const int32_t *key_limit;  // dense only, or null: row i sees keys [0, key_limit[b][i])
+  int accumulate;            // with key_limit: merge into the partial already in o / lse
 };
 
 hipError_t launch_prefill_bf16(const PrefillParams &p, bool paged, hipStream_t stream);

@@ -588,21 +588,44 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   // ---- epilogue: divide by l once, store O (bf16) and LSE ----------------
   const float l_tot = pair_sum32(l_run);
   if (qrow < p.Sq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     bf16 *op = static_cast<bf16 *>(p.o) + (((size_t)b * p.Sq + qrow) * p.Hq + h) * HD;
+    float *lp = p.lse + ((size_t)b * p.Hq + h) * p.Sq + qrow;
+    float lse2 = l_tot > 0.f ? m2 + __log2f(l_tot) : -INFINITY;   // log2 units
+    float w_prev = 0.f;
+    if (LIMITS && p.accumulate) {
+      // o / lse hold a normalised partial of this row over other keys: merge
+      // with the log-sum-exp rescale (weights 2^(L - M), empty sides weigh 0)
+      const float prev2 = *lp * kLog2e;
+      const float M = fmaxf(prev2, lse2);
+      if (M != -INFINITY) {
+        w_prev = prev2 == -INFINITY ? 0.f : fast_exp2(prev2 - M);
+        const float w_cur = lse2 == -INFINITY ? 0.f : fast_exp2(lse2 - M);
+        const float den = w_prev + w_cur;
+        inv = w_cur * inv / den;
+        w_prev /= den;
+        lse2 = M + __log2f(den);
+      }
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
+        bf16x4 *dst = reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * rq + 4 * gq);
         bf16x4 w;
+        if (LIMITS && p.accumulate) {
+          const bf16x4 prev = *dst;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = to_bf16(acc[db][4 * rq + e] * inv);
-        *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * rq + 4 * gq) = w;
+          for (int e = 0; e < 4; ++e)
+            w[e] = to_bf16(acc[db][4 * rq + e] * inv + (w_prev > 0.f ? w_prev * (float)prev[e] : 0.f));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = to_bf16(acc[db][4 * rq + e] * inv);
+        }
+        *dst = w;
       }
     }
-    if (p.lse && gq == 0)
-      p.lse[((size_t)b * p.Hq + h) * p.Sq + qrow] =
-          l_tot > 0.f ? (m2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (p.lse && gq == 0) *lp = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
   }
 }
 

@@ -216,11 +216,13 @@ def test_cp_and_merge_validation(lib):
     assert kl(NUL, NUL, NUL, 1, 0, 10, S0) == OK
     pl = lib.attn_prefill_limited
     q, k, v, o = P(0x10000), P(0x20000000), P(0x40000000), P(0x60000000)
-    assert pl(q, k, v, pos, o, NUL, 1, 64, 64, 16, 2, 64, 0.1, S0) == UNSUP   # D
-    assert pl(q, k, v, pos, o, NUL, 1, 64, 64, 16, 3, 128, 0.1, S0) == SHAPE  # Hq % Hkv
-    assert pl(q, k, v, NUL, o, NUL, 1, 64, 64, 16, 2, 128, 0.1, S0) == NULL
-    assert pl(q, k, v, pos, P(0x60000000 + 8), NUL, 1, 64, 64, 16, 2, 128, 0.1, S0) == ALIGN
-    assert pl(NUL, NUL, NUL, NUL, NUL, NUL, 1, 0, 64, 16, 2, 128, 0.1, S0) == OK
+    assert pl(q, k, v, pos, o, NUL, 1, 64, 64, 16, 2, 64, 0.1, 0, S0) == UNSUP   # D
+    assert pl(q, k, v, pos, o, NUL, 1, 64, 64, 16, 3, 128, 0.1, 0, S0) == SHAPE  # Hq % Hkv
+    assert pl(q, k, v, pos, o, NUL, 1, 64, 0, 16, 2, 128, 0.1, 0, S0) == SHAPE   # Sk = 0
+    assert pl(q, k, v, NUL, o, NUL, 1, 64, 64, 16, 2, 128, 0.1, 0, S0) == NULL
+    assert pl(q, k, v, pos, o, NUL, 1, 64, 64, 16, 2, 128, 0.1, 1, S0) == NULL   # accumulate, no lse
+    assert pl(q, k, v, pos, P(0x60000000 + 8), NUL, 1, 64, 64, 16, 2, 128, 0.1, 0, S0) == ALIGN
+    assert pl(NUL, NUL, NUL, NUL, NUL, NUL, 1, 0, 64, 16, 2, 128, 0.1, 0, S0) == OK
     mg = lib.attn_merge
     la, lb = P(0xA0000000), P(0xB0000000)
     assert mg(q, la, k, lb, o, NUL, 1, 64, 16, 100, S0) == UNSUP               # D % 8

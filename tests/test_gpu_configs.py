@@ -124,15 +124,20 @@ def test_ulysses_output_relayout_64k():
     assert np.array_equal(bits(out), ref)
 
 
-def run_cp_rank(q, k, v, S, N, rank, mode):
+def run_cp_rank(q, k, v, S, N, rank, mode, accumulate):
     """One rank's ring attention on one GPU: shard, key limits from the
-    positions, prefix-limited partials against every key shard, LSE merge."""
+    positions, prefix-limited partials against every key shard, combined by
+    the LSE merge kernel or merged in each partial's epilogue."""
     qr, qpos = lcat.cp_shard(q, N, rank, mode)
     o = lse = None
     for s_ in range(N):
         ks, kpos = lcat.cp_shard(k, N, s_, mode)
         vs, _ = lcat.cp_shard(v, N, s_, mode)
         lim = lcat.attn_key_limits(qpos, kpos)
+        if accumulate:
+            o, lse = lcat.attn_prefill_limited(qr[None], ks[None], vs[None], lim, o=o, lse=lse,
+                                               accumulate=s_ > 0)
+            continue
         op, lp = lcat.attn_prefill_limited(qr[None], ks[None], vs[None], lim)
         if o is None:
             o, lse = op, lp
@@ -141,13 +146,13 @@ def run_cp_rank(q, k, v, S, N, rank, mode):
     return o, lse
 
 
-@pytest.mark.parametrize("rank", [0, 3])
-def test_cp_zigzag_64k(rank):
+@pytest.mark.parametrize("rank,accumulate", [(0, False), (3, True)])
+def test_cp_zigzag_64k(rank, accumulate):
     S, N = 65536, 4
     log(f"CP zigzag 64K rank {rank}: generating")
     d = synth.dense_bf16(seed=920, B=1, S=S, Hq=16, Hkv=2)
     q, k, v = (to_dev(d[n][0]) for n in ("q", "k", "v"))
-    o, lse = run_cp_rank(q, k, v, S, N, rank, "zigzag")
+    o, lse = run_cp_rank(q, k, v, S, N, rank, "zigzag", accumulate)
     torch.cuda.synchronize()
     toks = oracle.cp_tokens(S, N, "zigzag", rank)
     L = toks.size // 2

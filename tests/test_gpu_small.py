@@ -529,11 +529,21 @@ def test_cp_ring_attention_on_one_gpu(mode):
                 o, lse = op, lp
             else:
                 lcat.attn_merge(o, lse, op, lp, o=o, lse=lse)
+        # the same ring with the merge folded into each partial's epilogue
+        oa = torch.empty_like(o)
+        la = torch.empty_like(lse)
+        for s_, (ks, vs, kpos) in enumerate(shards):
+            lim = lcat.attn_key_limits(qpos, kpos)
+            lcat.attn_prefill_limited(qr[None], ks[None], vs[None], lim, o=oa, lse=la,
+                                      accumulate=s_ > 0)
         torch.cuda.synchronize()
         rows = oracle.cp_tokens(S, N, mode, r)
         ref, ref_lse = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=True, rows=rows)
         e, rl = assert_attention_close(to_np64(o), ref, lse.cpu().numpy(), ref_lse, what="cp ring")
         log(f"  rank {r}: max abs {e:.3g} rel-L2 {rl:.3g}")
+        e, rl = assert_attention_close(to_np64(oa), ref, la.cpu().numpy(), ref_lse,
+                                       what="cp ring, merged in the epilogue")
+        log(f"  rank {r} (accumulate): max abs {e:.3g} rel-L2 {rl:.3g}")
 
 
 # ---------------------------------------------------------------------------
