@@ -196,6 +196,7 @@ def bench_decode(torch, lcat, synth, iters=20):
     gbs = nbytes / (ms * 1e-3) / 1e9
     res = dict(ms=round(ms, 4), GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
                bytes=nbytes, context_tokens=ctx_total, requests=B,
+               traffic=load_traffic("decode_stream_kernel", "decode_32req_bf16"),
                workload="32 requests, ctx U[8192,131072], 16 Q / 2 KV heads, paged 64-token blocks")
 
     # the same cache in FP8 (e4m3 + one fp32 scale per token for K and for V)
@@ -210,6 +211,7 @@ def bench_decode(torch, lcat, synth, iters=20):
     gbs8 = nbytes8 / (ms8 * 1e-3) / 1e9
     res["fp8_cache"] = dict(ms=round(ms8, 4), GBps=round(gbs8, 1),
                             frac_hbm=round(gbs8 / PEAK_HBM_GBS, 4), bytes=nbytes8,
+                            traffic=load_traffic("decode_stream_kernel", "decode_32req_fp8"),
                             speedup_vs_bf16=round(ms / ms8, 3))
     return res
 
