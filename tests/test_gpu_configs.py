@@ -4,7 +4,8 @@ benchmark times.
 * causal GQA prefill with RoPE, 1 x 32768 tokens, 16 Q / 2 KV heads, D=128;
 * sequence-shard input [4][16384][64 heads][128] relayed out to one rank's
   [65536][16][128] (bit-exact against the oracle relayout), RoPE at global
-  positions 0..65535, causal prefill;
+  positions 0..65535, causal prefill; the same relayout with RoPE fused in,
+  and the reverse relayout of the output;
 * split-K decode of 32 requests with contexts uniform in [8192, 131072] over
   a shuffled, NaN-poisoned paged cache (every output row checked);
 * chunked prefill of 4 x 131072 tokens in 8192-token chunks against the
@@ -106,6 +107,35 @@ def test_ulysses_relayout_rope_prefill_64k():
     e, r = assert_attention_close(to_np64(o[:, idx]), ref, lse[:, :, idx].cpu().numpy(), ref_lse,
                                   what="C3")
     log(f"C3: max abs {e:.3g} rel-L2 {r:.3g}")
+
+
+def test_ulysses_relayout_with_rope_64k():
+    """The fused relayout + RoPE at the 64K shape the benchmark times: V bit
+    for bit over the whole tensor, Q and K on sampled tokens (shard
+    boundaries included) against the oracle's rotation of the oracle's
+    relayout, and the whole output bit for bit equal to relayout followed by
+    rope_apply."""
+    SP, S_loc = 4, 16384
+    S = SP * S_loc
+    log("C3 fused: generating shard inputs")
+    d = synth.ulysses_shards(seed=3, SP=SP, S_loc=S_loc)
+    gpos = d["shard_positions"].reshape(-1)
+    posd = to_dev(gpos.astype(np.int32))
+    qin, kin, vin = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
+    qo, ko, vo = lcat.seq_to_head_permute_qkv_rope(qin, kin, vin, 0, posd)
+    q2, k2, v2 = lcat.seq_to_head_permute_qkv(qin, kin, vin, 0)
+    lcat.rope_apply(q2, posd)
+    lcat.rope_apply(k2, posd)
+    torch.cuda.synchronize()
+    for a, b2 in ((qo, q2), (ko, k2), (vo, v2)):
+        assert torch.equal(a.view(torch.int16), b2.view(torch.int16))
+    assert np.array_equal(bits(vo), oracle.permute(d["v"], 0))
+    toks = synth.sample_rows(34, S, N_SAMPLE, [S_loc * i + j for i in range(1, SP) for j in (-1, 0, 1)])
+    log(f"C3 fused: oracle RoPE on {toks.size} tokens")
+    for got, x in ((qo, d["q"]), (ko, d["k"])):
+        ref = oracle.rope(oracle.permute(x, 0)[toks], gpos[toks])
+        g = synth.bf16_bits_to_f32(bits(got)[toks]).astype(np.float64)
+        assert np.all(np.abs(g - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-6)
 
 
 def test_ulysses_output_relayout_64k():
