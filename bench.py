@@ -9,6 +9,10 @@ over the unmasked causal pairs only: 4*D*Hq*S*(S+1)/2 FLOP).
 The same JSON line also carries, each measured in this run:
   roofline        the prefill kernel's average duration from HIP events on
                   its stream, against the bf16 dense MFMA peak;
+  mfma_sustained  the bf16 MFMA rate this device sustains on random operands
+                  held in registers (no memory or LDS traffic), the most any
+                  bf16 matrix kernel reaches here; the prefill kernel's rate
+                  is also given as a fraction of it (frac_of_sustained);
   decode          paged decode with the key blocks of all requests shared out
                   equally over the GPU's waves, 32 requests with contexts
                   uniform in [8192, 131072], KV bytes per second against 8 TB/s;
@@ -60,11 +64,17 @@ def causal_flops(B, S, Hq, D=D, ctx_before=0):
     return 4.0 * D * Hq * B * pairs
 
 
+# Sources that build no attention-path kernel (the sustained-MFMA yardstick):
+# a change there leaves the recorded traffic of the path's kernels valid.
+NOT_PATH_SOURCES = {"measure.hip"}
+
+
 def kernel_source_hash():
+    """sha256 over the attention-path kernel sources (csrc/*.hip, *.h)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_attention_tiled_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
+        if name.endswith((".hip", ".h")) and name not in NOT_PATH_SOURCES:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -173,6 +183,24 @@ def bench_step(torch, lcat, synth, steps, warmup):
                       unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
                       traffic=traffic, kernel="prefill_kernel<dense,causal>",
                       kernel_ms=round(k_ms, 4), flop_per_launch=flops))
+
+
+def bench_mfma_rate(torch, lcat, reps=3, n_wg=1024, iters=65536):
+    out = torch.empty(n_wg * 512, dtype=torch.float32, device="cuda")
+    lcat.measure_mfma_rate(n_wg, iters, out=out)   # warm-up: clocks settle under load
+    torch.cuda.synchronize()
+    timer = EventTimer(torch)
+    for r in range(reps):
+        with timer:
+            lcat.measure_mfma_rate(n_wg, iters, seed=r + 2, out=out)
+    torch.cuda.synchronize()
+    ms = timer.mean_ms()
+    tflops = lcat.mfma_rate_flops(n_wg, iters) / (ms * 1e-3) / 1e12
+    return dict(tflops=round(tflops, 1), frac_of_peak=round(tflops / PEAK_BF16_TFLOPS, 4),
+                ms_per_launch=round(ms, 3),
+                kernel="mfma_rate_kernel: v_mfma_f32_32x32x16_bf16, 4 chains x 2 waves per SIMD, "
+                       "uniform random bf16 operands in [-1, 1) from registers",
+                launch=f"{n_wg} workgroups x 8 waves, {4 * iters} MFMA per wave")
 
 
 def bench_decode(torch, lcat, synth, iters=20):
@@ -409,7 +437,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="time only the step workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "decode", "relayout", "chunked", "cp"],
+    ap.add_argument("--only", choices=["step", "decode", "relayout", "chunked", "cp", "mfma"],
                     help="run a single leg (for profiling); prints its own JSON object")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -435,6 +463,8 @@ def main():
             res = bench_relayout_and_prefill_64k(torch, lcat)
         elif args.only == "cp":
             res = bench_cp(torch, lcat)
+        elif args.only == "mfma":
+            res = bench_mfma_rate(torch, lcat)
         else:
             res = bench_chunked(torch, lcat, synth)
         print(json.dumps({args.only: res}), flush=True)
@@ -452,6 +482,10 @@ def main():
         "roofline": step["roofline"],
     }
     if not args.no_extra and not args.only:
+        log("bench: sustained MFMA rate")
+        out["mfma_sustained"] = bench_mfma_rate(torch, lcat)
+        out["roofline"]["frac_of_sustained"] = round(
+            out["roofline"]["achieved"] / out["mfma_sustained"]["tflops"], 4)
         log("bench: decode")
         out["decode"] = bench_decode(torch, lcat, synth)
         log("bench: relayout + prefill 64k")

@@ -28,7 +28,7 @@ __all__ = [
     "seq_to_head_permute_qkv_rope", "cp_shard_tokens", "cp_shard", "cp_unshard",
     "attn_key_limits", "attn_prefill_limited", "attn_merge", "CP_MODES", "attn_decode_fp8",
     "attn_kv_quantize_fp8", "attn_kv_append_fp8",
-    "attn_status_string",
+    "attn_status_string", "measure_mfma_rate", "mfma_rate_flops",
     "AttnError", "ATTN_DEV_OK", "ATTN_DEV_BAD_TAG", "ATTN_DEV_BAD_BLOCK", "load_library",
 ]
 
@@ -519,3 +519,25 @@ def attn_merge(o_a, lse_a, o_b, lse_b, o=None, lse=None, stream=None):
                                 B, S, H, D, _stream(stream))
     _lib.check("attn_merge", st)
     return o, lse
+
+
+def mfma_rate_flops(n_wg, iters) -> int:
+    """Floating-point operations of one :func:`measure_mfma_rate` launch."""
+    return int(n_wg) * 8 * int(iters) * 4 * 32768
+
+
+def measure_mfma_rate(n_wg=1024, iters=65536, seed=1, out=None, stream=None):
+    """Enqueue one launch of the sustained-MFMA yardstick (bf16 32x32x16 MFMA
+    on random operands in registers, ``mfma_rate_flops(n_wg, iters)`` flops);
+    ``out`` is a float32 device buffer of ``n_wg * 512`` elements.  Time it
+    with events on ``stream``."""
+    torch = _torch()
+    if n_wg < 1 or n_wg > 65536 or iters < 4 or iters > (1 << 24) or iters % 4:
+        raise ValueError("n_wg must be in [1, 65536] and iters a multiple of 4 in [4, 2^24]")
+    if out is None:
+        out = torch.empty(n_wg * 512, dtype=torch.float32, device="cuda")
+    _need(out, "out", torch.float32, (n_wg * 512,))
+    st = _lib.load().attn_measure_mfma_rate(_ptr(out), int(n_wg), int(iters), int(seed) & 0xFFFFFFFF,
+                                            _stream(stream))
+    _lib.check("attn_measure_mfma_rate", st)
+    return out

@@ -1,4 +1,5 @@
-"""ctypes loader for ``libattn.so`` with the C signatures of ``include/attn.h``."""
+"""ctypes loader for ``libattn.so`` with the C signatures of ``include/attn.h`` and
+``include/attn_measure.h``."""
 from __future__ import annotations
 
 import ctypes
@@ -53,6 +54,8 @@ SIGNATURES = {
                                   _vp]),
     "attn_merge": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
+    # include/attn_measure.h
+    "attn_measure_mfma_rate": (_i, [_vp, _i, _i, ctypes.c_uint32, _vp]),
 }
 
 

@@ -1,12 +1,13 @@
 """Host-side checks of the C ABI (no GPU needed).
 
 The library loads on a machine without a GPU (only the HIP runtime library
-is needed), exports every function ``include/attn.h`` declares, and rejects
+is needed), exports every function the ``include/*.h`` headers declare, and rejects
 invalid arguments with the documented status codes before touching HIP.
 Every call here fails validation (or is an empty no-op), so no fake pointer
 ever reaches a launch.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -16,7 +17,7 @@ import long_context_attention_tiled_amd as lcat
 from long_context_attention_tiled_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, HIP = range(8)
 P = ctypes.c_void_p
@@ -27,9 +28,11 @@ S0 = P(0)             # stream
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:[a-z_0-9]+\s+)+\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"^\s*(?:[a-z_0-9]+\s+)+\*?\s*([a-z_0-9]+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -46,7 +49,7 @@ def test_header_declares_the_boundary():
               "head_to_seq_permute", "seq_to_head_permute_qkv_rope", "cp_shard_tokens",
               "cp_shard", "cp_unshard", "attn_key_limits", "attn_prefill_limited", "attn_merge",
               "attn_decode_fp8", "attn_kv_quantize_fp8", "attn_kv_append_fp8",
-              "attn_status_string"]:
+              "attn_status_string", "attn_measure_mfma_rate"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
 
@@ -257,6 +260,19 @@ def test_fp8_validation(lib):
     assert d(*args(ks=NUL)) == NULL
     assert d(*args(ks=P(0x30000 + 8))) == ALIGN
     assert d(*args(wsb=16)) == WS
+
+
+def test_measure_validation(lib):
+    m = lib.attn_measure_mfma_rate
+    out = P(0x10000)
+    assert m(NUL, 256, 64, 1, S0) == NULL
+    assert m(out, 0, 64, 1, S0) == SHAPE
+    assert m(out, 65537, 64, 1, S0) == SHAPE
+    assert m(out, 256, 6, 1, S0) == SHAPE     # not a multiple of 4
+    assert m(out, 256, 0, 1, S0) == SHAPE
+    assert m(out, 256, (1 << 24) + 4, 1, S0) == SHAPE
+    with pytest.raises(ValueError):
+        lcat.measure_mfma_rate(n_wg=16, iters=10)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

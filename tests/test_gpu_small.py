@@ -737,3 +737,18 @@ def test_chunked_equals_dense_prefill():
     torch.cuda.synchronize()
     assert (o.float() - od.float()).abs().max().item() <= BF16_ATOL
     assert (lse - lsed).abs().max().item() <= 2e-3
+
+
+# ---------------------------------------------------------------------------
+# sustained-MFMA yardstick (measurement helper, not part of the path)
+# ---------------------------------------------------------------------------
+def test_measure_mfma_rate_runs():
+    log("measure_mfma_rate n_wg=16 iters=64")
+    a = lcat.measure_mfma_rate(n_wg=16, iters=64, seed=5)
+    b = lcat.measure_mfma_rate(n_wg=16, iters=64, seed=5)
+    c = lcat.measure_mfma_rate(n_wg=16, iters=64, seed=6)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a).all()
+    assert torch.equal(a, b)          # the operands depend only on the seed
+    assert not torch.equal(a, c)
+    assert lcat.mfma_rate_flops(16, 64) == 16 * 8 * 64 * 4 * 32768
