@@ -15,11 +15,15 @@ The same JSON line also carries, each measured in this run:
                   is also given as a fraction of it (frac_of_sustained);
   decode          paged decode with the key blocks of all requests shared out
                   equally over the GPU's waves, 32 requests with contexts
-                  uniform in [8192, 131072], KV bytes per second against 8 TB/s;
-                  and (fp8_cache) the same decode over the FP8 copy of the cache;
+                  uniform in [8192, 131072], KV bytes per second against 8 TB/s
+                  and against a plain streaming read of as many bytes
+                  (read_sustained); and (fp8_cache) the same decode over the
+                  FP8 copy of the cache;
   relayout        sequence-shard -> head-shard relayout of one rank's share of
                   [4][16384][64|8][128] bf16 Q/K/V (one launch), bytes per second,
-                  and (fused_rope) the same relayout with RoPE on Q and K;
+                  also against a plain streaming copy of as many bytes
+                  (copy_sustained), and (fused_rope) the same relayout with
+                  RoPE on Q and K;
   relayout_back   the reverse exchange: that rank's attention output
                   [65536][16][128] back to its head slice of the shards;
   prefill_64k     the relayout + RoPE + causal prefill pipeline at 65536,
@@ -29,7 +33,10 @@ The same JSON line also carries, each measured in this run:
                   tokens): partials against every key shard, merged by LSE;
   cpu_baseline    the fp64 CPU oracle timed on a bounded sample of query rows
                   of the step workload, on this host's cores.
-The decode and relayout times are means over calls enqueued back to back.
+The decode and relayout times are means over calls enqueued back to back;
+the relayouts cycle through 4 separate buffer sets so that no call reads data
+an earlier call left in the last-level cache (the decode reads 2.35 GB per
+call, far more than that cache holds).
 
 Inputs are seeded synthetic N(0,1) data resident in HBM before timing starts.
 """
@@ -227,6 +234,19 @@ def bench_decode(torch, lcat, synth, iters=20):
                traffic=load_traffic("decode_stream_kernel", "decode_32req_bf16"),
                workload="32 requests, ctx U[8192,131072], 16 Q / 2 KV heads, paged 64-token blocks")
 
+    # yardstick: a plain streaming read of the same number of bytes
+    buf = torch.empty(nbytes // 16 * 16, dtype=torch.uint8, device="cuda")
+    rd_out, rd_bytes = lcat.measure_hbm_read(buf)
+    torch.cuda.synchronize()
+    ms_rd = back_to_back_ms(torch, lambda: lcat.measure_hbm_read(buf, out=rd_out), iters)
+    del buf
+    rd_gbs = rd_bytes / (ms_rd * 1e-3) / 1e9
+    res["read_sustained"] = dict(GBps=round(rd_gbs, 1), frac_hbm=round(rd_gbs / PEAK_HBM_GBS, 4),
+                                 bytes=rd_bytes,
+                                 kernel="hbm_read_kernel: 4096 waves, contiguous shares, "
+                                        "32 x 16-byte loads per lane in flight")
+    res["frac_of_sustained_read"] = round(gbs / rd_gbs, 4)
+
     # the same cache in FP8 (e4m3 + one fp32 scale per token for K and for V)
     k8, v8, ks, vs = lcat.attn_kv_quantize_fp8(k_pool, v_pool)
     args8 = [args[0], k8, v8, ks, vs] + args[3:]
@@ -240,45 +260,82 @@ def bench_decode(torch, lcat, synth, iters=20):
     res["fp8_cache"] = dict(ms=round(ms8, 4), GBps=round(gbs8, 1),
                             frac_hbm=round(gbs8 / PEAK_HBM_GBS, 4), bytes=nbytes8,
                             traffic=load_traffic("decode_stream_kernel", "decode_32req_fp8"),
+                            frac_of_sustained_read=round(gbs8 / rd_gbs, 4),
                             speedup_vs_bf16=round(ms / ms8, 3))
     return res
 
 
-def bench_relayout_and_prefill_64k(torch, lcat, iters=20):
+def rotating(fns):
+    """One call per invocation, cycling through ``fns``."""
+    it = [0]
+
+    def call():
+        fns[it[0] % len(fns)]()
+        it[0] += 1
+    return call
+
+
+def bench_relayout_and_prefill_64k(torch, lcat, iters=20, n_sets=4):
+    """The relayouts and the copy yardstick cycle through ``n_sets`` separate
+    input/output sets (1.25 GiB of inputs each), so no call finds its data in
+    the 256 MB last-level cache from an earlier call: the rates are HBM rates."""
     SP, S_loc, Hq_tot, Hkv_tot = 4, 16384, 64, 8
     S = SP * S_loc
-    qin = seeded_normal_bf16(torch, (SP, S_loc, Hq_tot, D), 31)
-    kin = seeded_normal_bf16(torch, (SP, S_loc, Hkv_tot, D), 32)
-    vin = seeded_normal_bf16(torch, (SP, S_loc, Hkv_tot, D), 33)
-    qo = torch.empty((S, Hq_tot // SP, D), dtype=torch.bfloat16, device="cuda")
-    ko = torch.empty((S, Hkv_tot // SP, D), dtype=torch.bfloat16, device="cuda")
-    vo = torch.empty_like(ko)
+    sets = []
+    for r in range(n_sets):
+        qin = seeded_normal_bf16(torch, (SP, S_loc, Hq_tot, D), 31 + 10 * r)
+        kin = seeded_normal_bf16(torch, (SP, S_loc, Hkv_tot, D), 32 + 10 * r)
+        vin = seeded_normal_bf16(torch, (SP, S_loc, Hkv_tot, D), 33 + 10 * r)
+        qo = torch.empty((S, Hq_tot // SP, D), dtype=torch.bfloat16, device="cuda")
+        ko = torch.empty((S, Hkv_tot // SP, D), dtype=torch.bfloat16, device="cuda")
+        vo = torch.empty_like(ko)
+        back = torch.zeros((SP, S_loc, Hq_tot, D), dtype=torch.bfloat16, device="cuda")
+        sets.append((qin, kin, vin, qo, ko, vo, back))
+    qin, kin, vin, qo, ko, vo, _ = sets[0]
 
-    def relayout():   # Q, K and V of rank 0 in one launch
-        lcat.seq_to_head_permute_qkv(qin, kin, vin, 0, outs=(qo, ko, vo))
+    def relayout(st=sets[0]):   # Q, K and V of rank 0 in one launch
+        lcat.seq_to_head_permute_qkv(st[0], st[1], st[2], 0, outs=(st[3], st[4], st[5]))
 
-    for _ in range(3):
-        relayout()
+    relayout_all = rotating([lambda st=st: relayout(st) for st in sets])
+    for _ in range(n_sets):
+        relayout_all()
     torch.cuda.synchronize()
-    ms = back_to_back_ms(torch, relayout, iters)
+    ms = back_to_back_ms(torch, relayout_all, iters)
     nbytes = 2 * (qo.numel() + ko.numel() + vo.numel()) * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     relay = dict(ms=round(ms, 4), GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
                  bytes=nbytes, traffic=load_traffic("permute16_kernel", "relayout_qkv_64k"),
-                 workload="rank 0 of [4][16384][64|8][128] bf16 Q/K/V")
+                 workload="rank 0 of [4][16384][64|8][128] bf16 Q/K/V",
+                 buffer_sets=n_sets)
+
+    # yardstick: a plain streaming copy moving the same bytes (half read, half written)
+    pairs = [(st[0].view(-1)[: nbytes // 4], st[6].view(-1)[: nbytes // 4]) for st in sets]
+    copy_all = rotating([lambda pr=pr: lcat.measure_hbm_copy(pr[0], pr[1]) for pr in pairs])
+    for _ in range(n_sets):
+        copy_all()
+    torch.cuda.synchronize()
+    ms_c = back_to_back_ms(torch, copy_all, iters)
+    cp_gbs = nbytes / (ms_c * 1e-3) / 1e9
+    relay["copy_sustained"] = dict(GBps=round(cp_gbs, 1), frac_hbm=round(cp_gbs / PEAK_HBM_GBS, 4),
+                                   bytes=nbytes,
+                                   kernel="hbm_copy_kernel: contiguous, 4 x 16 B per thread, "
+                                          "non-temporal stores")
+    relay["frac_of_sustained_copy"] = round(gbs / cp_gbs, 4)
 
     pos = torch.arange(S, dtype=torch.int32, device="cuda")
 
-    def relayout_rope():   # the same relayout with RoPE on Q and K in the same pass
-        lcat.seq_to_head_permute_qkv_rope(qin, kin, vin, 0, pos, outs=(qo, ko, vo))
+    def relayout_rope(st=sets[0]):   # the same relayout with RoPE on Q and K in the same pass
+        lcat.seq_to_head_permute_qkv_rope(st[0], st[1], st[2], 0, pos, outs=(st[3], st[4], st[5]))
 
-    for _ in range(3):
-        relayout_rope()
+    rope_all = rotating([lambda st=st: relayout_rope(st) for st in sets])
+    for _ in range(n_sets):
+        rope_all()
     torch.cuda.synchronize()
-    ms_r = back_to_back_ms(torch, relayout_rope, iters)
+    ms_r = back_to_back_ms(torch, rope_all, iters)
     gbs_r = nbytes / (ms_r * 1e-3) / 1e9
     relay["fused_rope"] = dict(ms=round(ms_r, 4), GBps=round(gbs_r, 1),
-                               frac_hbm=round(gbs_r / PEAK_HBM_GBS, 4))
+                               frac_hbm=round(gbs_r / PEAK_HBM_GBS, 4),
+                               frac_of_sustained_copy=round(gbs_r / cp_gbs, 4))
 
     o = torch.empty((1, S, Hq_tot // SP, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((1, Hq_tot // SP, S), dtype=torch.float32, device="cuda")
@@ -305,16 +362,20 @@ def bench_relayout_and_prefill_64k(torch, lcat, iters=20):
                frac_mfma=round(flops / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                workload="relayout + RoPE + causal prefill, seq 65536, 16 Q / 2 KV heads")
 
-    # the reverse exchange: rank 0's output back to its head slice of the shards
-    o_back = torch.zeros((SP, S_loc, Hq_tot, D), dtype=torch.bfloat16, device="cuda")
-    back = lambda: lcat.head_to_seq_permute(o[0], SP, Hq_tot, 0, out=o_back)
-    for _ in range(3):
-        back()
+    # the reverse exchange: rank 0's output [S][16][D] back to its head slice
+    # of the shards (set 0's input is the prefill output, the others stand in
+    # with the same shape)
+    outs = [o[0]] + [st[3] for st in sets[1:]]
+    back_all = rotating([lambda x=x, st=st: lcat.head_to_seq_permute(x, SP, Hq_tot, 0, out=st[6])
+                         for x, st in zip(outs, sets)])
+    for _ in range(n_sets):
+        back_all()
     torch.cuda.synchronize()
-    ms_b = back_to_back_ms(torch, back, iters)
+    ms_b = back_to_back_ms(torch, back_all, iters)
     nb = 2 * o[0].numel() * 2
     gbs_b = nb / (ms_b * 1e-3) / 1e9
     relay_back = dict(ms=round(ms_b, 4), GBps=round(gbs_b, 1), frac_hbm=round(gbs_b / PEAK_HBM_GBS, 4),
+                      frac_of_sustained_copy=round(gbs_b / cp_gbs, 4), buffer_sets=n_sets,
                       bytes=nb, workload="rank 0's O [65536][16][128] bf16 -> [4][16384][64][128]")
     return relay, pre, relay_back
 

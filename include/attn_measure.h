@@ -1,8 +1,12 @@
 /*
- * libattn measurement helper.  It is not part of the attention path and
- * computes nothing that path uses; it gives the bf16 matrix-core rate the
- * device sustains on changing operands, against which the prefill kernel's
- * throughput is read next to the published dense peak.
+ * libattn measurement helpers.  They are not part of the attention path and
+ * compute nothing that path uses.  They give rates the device sustains, against
+ * which the path's kernels are read next to the published peaks:
+ *  - the bf16 matrix-core rate on changing operands (for prefill);
+ *  - plain streaming HBM read and copy rates (for decode and the relayouts).
+ * Conventions as in attn.h: device pointers owned by the caller, `stream` a
+ * hipStream_t passed as void* (NULL = default stream), calls only enqueue,
+ * argument errors are found before anything is enqueued.
  */
 #ifndef LCAT_ATTN_MEASURE_H
 #define LCAT_ATTN_MEASURE_H
@@ -15,8 +19,9 @@ extern "C" {
 
 enum attn_measure_status {
   ATTN_MEASURE_OK = 0,
-  ATTN_MEASURE_ERR_NULL = 1,  /* out is NULL */
-  ATTN_MEASURE_ERR_SHAPE = 2, /* n_wg outside [1, 65536], or iters outside [4, 2^24] or not a multiple of 4 */
+  ATTN_MEASURE_ERR_NULL = 1,  /* a required pointer is NULL */
+  ATTN_MEASURE_ERR_SHAPE = 2, /* a size outside its documented range, or overlapping buffers */
+  ATTN_MEASURE_ERR_ALIGN = 4, /* a buffer is not 16-byte aligned */
   ATTN_MEASURE_ERR_HIP = 7    /* the HIP runtime rejected the launch */
 };
 
@@ -34,6 +39,27 @@ enum attn_measure_status {
  * before anything is enqueued.
  */
 int attn_measure_mfma_rate(float *out, int n_wg, int iters, uint32_t seed, void *stream);
+
+/*
+ * attn_measure_hbm_read — streaming read of `buf`: `waves` single-wave
+ * workgroups each read one contiguous share of floor(bytes / 16 / waves)
+ * 16-byte units (32 loads per lane in flight); the bytes read per launch are
+ * attn_measure_hbm_read_bytes(bytes, waves).  `out` (device uint32[waves * 64])
+ * receives one fold of the data per lane.  Needs waves in [1, 65536] and
+ * bytes / 16 >= waves (ATTN_MEASURE_ERR_SHAPE); buf 16-byte aligned.
+ */
+int attn_measure_hbm_read(const void *buf, long long bytes, uint32_t *out, int waves,
+                          void *stream);
+
+/* Bytes one attn_measure_hbm_read launch reads (0 for invalid sizes). */
+long long attn_measure_hbm_read_bytes(long long bytes, int waves);
+
+/*
+ * attn_measure_hbm_copy — dst[0, bytes) = src[0, bytes) with 16-byte loads
+ * and non-temporal 16-byte stores, 4 per thread; bytes a positive multiple
+ * of 16, both pointers 16-byte aligned, no overlap (ATTN_MEASURE_ERR_SHAPE).
+ */
+int attn_measure_hbm_copy(const void *src, void *dst, long long bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,8 @@ __all__ = [
     "seq_to_head_permute_qkv_rope", "cp_shard_tokens", "cp_shard", "cp_unshard",
     "attn_key_limits", "attn_prefill_limited", "attn_merge", "CP_MODES", "attn_decode_fp8",
     "attn_kv_quantize_fp8", "attn_kv_append_fp8",
-    "attn_status_string", "measure_mfma_rate", "mfma_rate_flops",
+    "attn_status_string", "measure_mfma_rate", "mfma_rate_flops", "measure_hbm_read",
+    "measure_hbm_copy",
     "AttnError", "ATTN_DEV_OK", "ATTN_DEV_BAD_TAG", "ATTN_DEV_BAD_BLOCK", "load_library",
 ]
 
@@ -541,3 +542,31 @@ def measure_mfma_rate(n_wg=1024, iters=65536, seed=1, out=None, stream=None):
                                             _stream(stream))
     _lib.check("attn_measure_mfma_rate", st)
     return out
+
+
+def measure_hbm_read(buf, waves=4096, out=None, stream=None):
+    """Enqueue one streaming read of the device tensor ``buf`` (16-byte
+    aligned) by ``waves`` waves; returns ``(out, bytes_read)``."""
+    torch = _torch()
+    _need(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(waves * 64, dtype=torch.int32, device=buf.device)
+    _need(out, "out", torch.int32, (waves * 64,))
+    lib = _lib.load()
+    st = lib.attn_measure_hbm_read(_ptr(buf), nbytes, _ptr(out), int(waves), _stream(stream))
+    _lib.check("attn_measure_hbm_read", st)
+    return out, int(lib.attn_measure_hbm_read_bytes(nbytes, int(waves)))
+
+
+def measure_hbm_copy(src, dst, stream=None):
+    """Enqueue a streaming copy of ``src`` into ``dst`` (same byte size,
+    16-byte aligned, not overlapping); returns the bytes copied."""
+    _need(src, "src")
+    _need(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same byte size")
+    st = _lib.load().attn_measure_hbm_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream))
+    _lib.check("attn_measure_hbm_copy", st)
+    return nbytes

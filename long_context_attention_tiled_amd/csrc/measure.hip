@@ -1,5 +1,6 @@
-// Sustained bf16 MFMA rate of the device, as a yardstick for the prefill
-// kernel besides the published dense peak.
+// Yardsticks for the path's kernels, besides the published peaks: the
+// sustained bf16 MFMA rate (for prefill), and plain streaming HBM read and
+// copy rates (for decode and the relayouts).
 //
 // Every wave runs four independent accumulator chains of
 // v_mfma_f32_32x32x16_bf16 on operands held in registers: no LDS, no memory
@@ -68,8 +69,87 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(float *out, int ite
   out[(long long)blockIdx.x * kThreads + tid] = sum + (float)pad[(tid * 7) & 1023];
 }
 
+// Streaming read: wave w reads units [w * per_wave, (w + 1) * per_wave) of
+// 16 bytes, 32 loads per lane in flight, and folds them into one word per
+// lane so the loads are live.
+constexpr int kReadUnroll = 32;
+
+__global__ __launch_bounds__(64) void hbm_read_kernel(const u32x4 *__restrict__ in,
+                                                      uint32_t *out, long long per_wave) {
+  const long long base = (long long)blockIdx.x * per_wave;
+  u32x4 acc = {0, 0, 0, 0};
+  for (long long u = threadIdx.x; u < per_wave; u += 64 * kReadUnroll) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int i = 0; i < kReadUnroll; ++i) {
+      const long long x = u + 64LL * i;
+      v[i] = x < per_wave ? in[base + x] : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < kReadUnroll; ++i) acc ^= v[i];
+  }
+  out[(long long)blockIdx.x * 64 + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+// Streaming copy of 16-byte units: 4 per thread, loads before stores,
+// non-temporal stores.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(kCopyThreads) void hbm_copy_kernel(const u32x4 *__restrict__ in,
+                                                               u32x4 *__restrict__ out,
+                                                               long long n_units) {
+  const long long base = (long long)blockIdx.x * (kCopyThreads * kCopyUnroll) + threadIdx.x;
+  u32x4 v[kCopyUnroll];
+#pragma unroll
+  for (int i = 0; i < kCopyUnroll; ++i) {
+    const long long u = base + (long long)i * kCopyThreads;
+    if (u < n_units) v[i] = in[u];
+  }
+#pragma unroll
+  for (int i = 0; i < kCopyUnroll; ++i) {
+    const long long u = base + (long long)i * kCopyThreads;
+    if (u < n_units) __builtin_nontemporal_store(v[i], out + u);
+  }
+}
+
 }  // namespace
 }  // namespace lcat
+
+extern "C" long long attn_measure_hbm_read_bytes(long long bytes, int waves) {
+  if (bytes < 16 || waves < 1 || waves > 65536) return 0;
+  return (bytes / 16 / waves) * 16 * waves;
+}
+
+extern "C" int attn_measure_hbm_read(const void *buf, long long bytes, uint32_t *out, int waves,
+                                     void *stream) {
+  if (!buf || !out) return ATTN_MEASURE_ERR_NULL;
+  if (waves < 1 || waves > 65536 || bytes / 16 < waves) return ATTN_MEASURE_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(buf) % 16) return ATTN_MEASURE_ERR_ALIGN;
+  const long long per_wave = bytes / 16 / waves;
+  hipLaunchKernelGGL(lcat::hbm_read_kernel, dim3(waves), dim3(64), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const lcat::u32x4 *>(buf), out,
+                     per_wave);
+  return hipGetLastError() == hipSuccess ? ATTN_MEASURE_OK : ATTN_MEASURE_ERR_HIP;
+}
+
+extern "C" int attn_measure_hbm_copy(const void *src, void *dst, long long bytes, void *stream) {
+  if (!src || !dst) return ATTN_MEASURE_ERR_NULL;
+  if (bytes < 16 || bytes % 16) return ATTN_MEASURE_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16)
+    return ATTN_MEASURE_ERR_ALIGN;
+  const char *s = static_cast<const char *>(src);
+  const char *d = static_cast<const char *>(dst);
+  if (s < d + bytes && d < s + bytes) return ATTN_MEASURE_ERR_SHAPE;   // overlap
+  const long long n_units = bytes / 16;
+  const long long per_wg = lcat::kCopyThreads * lcat::kCopyUnroll;
+  const long long n_wg = (n_units + per_wg - 1) / per_wg;
+  if (n_wg > 0x7fffffffLL) return ATTN_MEASURE_ERR_SHAPE;
+  hipLaunchKernelGGL(lcat::hbm_copy_kernel, dim3((unsigned)n_wg), dim3(lcat::kCopyThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const lcat::u32x4 *>(src),
+                     static_cast<lcat::u32x4 *>(dst), n_units);
+  return hipGetLastError() == hipSuccess ? ATTN_MEASURE_OK : ATTN_MEASURE_ERR_HIP;
+}
 
 extern "C" int attn_measure_mfma_rate(float *out, int n_wg, int iters, uint32_t seed,
                                       void *stream) {

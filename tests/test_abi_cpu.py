@@ -273,6 +273,20 @@ def test_measure_validation(lib):
     assert m(out, 256, (1 << 24) + 4, 1, S0) == SHAPE
     with pytest.raises(ValueError):
         lcat.measure_mfma_rate(n_wg=16, iters=10)
+    rd, rb, cp = lib.attn_measure_hbm_read, lib.attn_measure_hbm_read_bytes, lib.attn_measure_hbm_copy
+    buf, o2 = P(0x100000), P(0x200000)
+    assert rd(NUL, 1 << 20, out, 64, S0) == NULL
+    assert rd(buf, 1 << 20, NUL, 64, S0) == NULL
+    assert rd(buf, 1 << 20, out, 0, S0) == SHAPE
+    assert rd(buf, 16 * 63, out, 64, S0) == SHAPE        # fewer units than waves
+    assert rd(P(0x100004), 1 << 20, out, 64, S0) == ALIGN
+    assert rb(1000 * 16 + 5, 64) == (1000 // 64) * 64 * 16
+    assert rb(8, 64) == 0 and rb(1 << 20, 0) == 0
+    assert cp(NUL, o2, 1024, S0) == NULL
+    assert cp(buf, o2, 1000, S0) == SHAPE                # not a multiple of 16
+    assert cp(buf, o2, 0, S0) == SHAPE
+    assert cp(buf, P(0x100000 + 512), 1024, S0) == SHAPE # overlap
+    assert cp(P(0x100008), o2, 1024, S0) == ALIGN
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -752,3 +752,25 @@ def test_measure_mfma_rate_runs():
     assert torch.equal(a, b)          # the operands depend only on the seed
     assert not torch.equal(a, c)
     assert lcat.mfma_rate_flops(16, 64) == 16 * 8 * 64 * 4 * 32768
+
+
+def test_measure_hbm_read_and_copy():
+    log("measure_hbm_read 16 waves x 1000 units, measure_hbm_copy 1 MiB + 48 B")
+    rng = np.random.default_rng(77)
+    words = rng.integers(0, 2**32, size=(16 * 1000 + 7) * 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    out, nread = lcat.measure_hbm_read(buf, waves=16)
+    torch.cuda.synchronize()
+    assert nread == 16 * 1000 * 16
+    # lane l of wave w folds units w*1000 + l + 64k (k >= 0) of its share
+    units = words[: 16 * 1000 * 4].reshape(16, 1000, 4)
+    fold = np.bitwise_xor.reduce(units, axis=2)              # the 4 words of a unit
+    want = np.zeros((16, 64), dtype=np.uint32)
+    for lane in range(64):
+        want[:, lane] = np.bitwise_xor.reduce(fold[:, lane::64], axis=1)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32).reshape(16, 64), want)
+    src = torch.from_numpy(rng.integers(0, 255, size=(1 << 20) + 48, dtype=np.uint8)).cuda()
+    dst = torch.zeros_like(src)
+    assert lcat.measure_hbm_copy(src, dst) == (1 << 20) + 48
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
