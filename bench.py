@@ -11,8 +11,11 @@ The same JSON line also carries, each measured in this run:
                   its stream, against the bf16 dense MFMA peak;
   mfma_sustained  the bf16 MFMA rate this device sustains on random operands
                   held in registers (no memory or LDS traffic), the most any
-                  bf16 matrix kernel reaches here; the prefill kernel's rate
-                  is also given as a fraction of it (frac_of_sustained);
+                  bf16 matrix kernel reaches here, and (a_from_lds) the rate
+                  when each MFMA's A operand is read from LDS, as the
+                  attention kernels read K and V; the prefill kernel's rate
+                  is also given as a fraction of both (frac_of_sustained,
+                  frac_of_sustained_lds);
   decode          paged decode with the key blocks of all requests shared out
                   equally over the GPU's waves, 32 requests with contexts
                   uniform in [8192, 131072], KV bytes per second against 8 TB/s
@@ -194,20 +197,27 @@ def bench_step(torch, lcat, synth, steps, warmup):
 
 def bench_mfma_rate(torch, lcat, reps=3, n_wg=1024, iters=65536):
     out = torch.empty(n_wg * 512, dtype=torch.float32, device="cuda")
-    lcat.measure_mfma_rate(n_wg, iters, out=out)   # warm-up: clocks settle under load
-    torch.cuda.synchronize()
-    timer = EventTimer(torch)
-    for r in range(reps):
-        with timer:
-            lcat.measure_mfma_rate(n_wg, iters, seed=r + 2, out=out)
-    torch.cuda.synchronize()
-    ms = timer.mean_ms()
-    tflops = lcat.mfma_rate_flops(n_wg, iters) / (ms * 1e-3) / 1e12
-    return dict(tflops=round(tflops, 1), frac_of_peak=round(tflops / PEAK_BF16_TFLOPS, 4),
-                ms_per_launch=round(ms, 3),
-                kernel="mfma_rate_kernel: v_mfma_f32_32x32x16_bf16, 4 chains x 2 waves per SIMD, "
-                       "uniform random bf16 operands in [-1, 1) from registers",
-                launch=f"{n_wg} workgroups x 8 waves, {4 * iters} MFMA per wave")
+    res = {}
+    for lds in (False, True):
+        lcat.measure_mfma_rate(n_wg, iters, a_from_lds=lds, out=out)   # warm-up: clocks settle
+        torch.cuda.synchronize()
+        timer = EventTimer(torch)
+        for r in range(reps):
+            with timer:
+                lcat.measure_mfma_rate(n_wg, iters, seed=r + 2, a_from_lds=lds, out=out)
+        torch.cuda.synchronize()
+        ms = timer.mean_ms()
+        tflops = lcat.mfma_rate_flops(n_wg, iters) / (ms * 1e-3) / 1e12
+        res[lds] = dict(tflops=round(tflops, 1), frac_of_peak=round(tflops / PEAK_BF16_TFLOPS, 4),
+                        ms_per_launch=round(ms, 3))
+    out_d = dict(res[False],
+                 kernel="mfma_rate_kernel: v_mfma_f32_32x32x16_bf16, 4 chains x 2 waves per SIMD, "
+                        "uniform random bf16 operands in [-1, 1) from registers",
+                 launch=f"{n_wg} workgroups x 8 waves, {4 * iters} MFMA per wave")
+    out_d["a_from_lds"] = dict(res[True],
+                               kernel="mfma_lds_rate_kernel: the same, with each MFMA's A "
+                                      "operand read from LDS (16 B per lane) just before it")
+    return out_d
 
 
 def bench_decode(torch, lcat, synth, iters=20):
@@ -547,6 +557,8 @@ def main():
         out["mfma_sustained"] = bench_mfma_rate(torch, lcat)
         out["roofline"]["frac_of_sustained"] = round(
             out["roofline"]["achieved"] / out["mfma_sustained"]["tflops"], 4)
+        out["roofline"]["frac_of_sustained_lds"] = round(
+            out["roofline"]["achieved"] / out["mfma_sustained"]["a_from_lds"]["tflops"], 4)
         log("bench: decode")
         out["decode"] = bench_decode(torch, lcat, synth)
         log("bench: relayout + prefill 64k")

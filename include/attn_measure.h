@@ -28,9 +28,13 @@ enum attn_measure_status {
 /*
  * attn_measure_mfma_rate — enqueue one launch of n_wg workgroups of 8 waves;
  * each wave issues 4 * iters v_mfma_f32_32x32x16_bf16 on uniform random bf16
- * operands in [-1, 1) held in registers (seeded by `seed`), so one launch
- * performs n_wg * 8 * iters * 4 * 32768 floating-point operations.  Each
- * workgroup reserves enough LDS to be alone on its CU.
+ * operands in [-1, 1) (seeded by `seed`), so one launch performs
+ * n_wg * 8 * iters * 4 * 32768 floating-point operations.  Each workgroup
+ * reserves enough LDS to be alone on its CU.
+ *   a_from_lds  0: both operands held in registers;
+ *               1: each MFMA's A operand read from LDS just before it (one
+ *               16-byte read per lane per MFMA, 64 KiB of random bf16 in
+ *               LDS), B from registers.  Other values: ATTN_MEASURE_ERR_SHAPE.
  *   out    device float[n_wg * 512], caller-owned; receives one sum of the
  *          accumulators per thread (kept only so the products are live).
  *   stream hipStream_t as void* (NULL = default stream); the call only
@@ -38,7 +42,8 @@ enum attn_measure_status {
  * Returns ATTN_MEASURE_OK or an error code above; argument errors are found
  * before anything is enqueued.
  */
-int attn_measure_mfma_rate(float *out, int n_wg, int iters, uint32_t seed, void *stream);
+int attn_measure_mfma_rate(float *out, int n_wg, int iters, uint32_t seed, int a_from_lds,
+                           void *stream);
 
 /*
  * attn_measure_hbm_read — streaming read of `buf`: `waves` single-wave

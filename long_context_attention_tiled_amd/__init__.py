@@ -527,9 +527,10 @@ def mfma_rate_flops(n_wg, iters) -> int:
     return int(n_wg) * 8 * int(iters) * 4 * 32768
 
 
-def measure_mfma_rate(n_wg=1024, iters=65536, seed=1, out=None, stream=None):
+def measure_mfma_rate(n_wg=1024, iters=65536, seed=1, a_from_lds=False, out=None, stream=None):
     """Enqueue one launch of the sustained-MFMA yardstick (bf16 32x32x16 MFMA
-    on random operands in registers, ``mfma_rate_flops(n_wg, iters)`` flops);
+    on random operands, ``mfma_rate_flops(n_wg, iters)`` flops; with
+    ``a_from_lds`` each MFMA's A operand is read from LDS just before it);
     ``out`` is a float32 device buffer of ``n_wg * 512`` elements.  Time it
     with events on ``stream``."""
     torch = _torch()
@@ -539,7 +540,7 @@ def measure_mfma_rate(n_wg=1024, iters=65536, seed=1, out=None, stream=None):
         out = torch.empty(n_wg * 512, dtype=torch.float32, device="cuda")
     _need(out, "out", torch.float32, (n_wg * 512,))
     st = _lib.load().attn_measure_mfma_rate(_ptr(out), int(n_wg), int(iters), int(seed) & 0xFFFFFFFF,
-                                            _stream(stream))
+                                            int(bool(a_from_lds)), _stream(stream))
     _lib.check("attn_measure_mfma_rate", st)
     return out
 

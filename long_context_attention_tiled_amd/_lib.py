@@ -55,7 +55,7 @@ SIGNATURES = {
     "attn_merge": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
     # include/attn_measure.h
-    "attn_measure_mfma_rate": (_i, [_vp, _i, _i, ctypes.c_uint32, _vp]),
+    "attn_measure_mfma_rate": (_i, [_vp, _i, _i, ctypes.c_uint32, _i, _vp]),
     "attn_measure_hbm_read": (_i, [_vp, _ll, _vp, _i, _vp]),
     "attn_measure_hbm_read_bytes": (_ll, [_ll, _i]),
     "attn_measure_hbm_copy": (_i, [_vp, _vp, _ll, _vp]),

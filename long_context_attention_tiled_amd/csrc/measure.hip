@@ -1,6 +1,7 @@
 // Yardsticks for the path's kernels, besides the published peaks: the
-// sustained bf16 MFMA rate (for prefill), and plain streaming HBM read and
-// copy rates (for decode and the relayouts).
+// sustained bf16 MFMA rate with operands in registers or with the A operand
+// streamed from LDS (for prefill), and plain streaming HBM read and copy
+// rates (for decode and the relayouts).
 //
 // Every wave runs four independent accumulator chains of
 // v_mfma_f32_32x32x16_bf16 on operands held in registers: no LDS, no memory
@@ -58,6 +59,49 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(float *out, int ite
       for (int i = 0; i < 4; ++i)
         c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s + (i & 1)], b[(s + i) % kSets], c[i],
                                                        0, 0, 0);
+    }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += c[i][r];
+  __syncthreads();
+  out[(long long)blockIdx.x * kThreads + tid] = sum + (float)pad[(tid * 7) & 1023];
+}
+
+// The same chains with each MFMA's A operand read from LDS just before it
+// (one 16-byte ds_read per lane per MFMA, as the attention kernels read K and
+// V tiles): 64 KiB of random bf16 in LDS, each wave cycling through its own
+// 8 KiB window; B operands from four register sets.  The LDS array plus a pad
+// keep one workgroup per CU.
+constexpr int kLdsBytes = 65536;
+constexpr int kLdsPad2 = 40000;
+
+__global__ __launch_bounds__(kThreads) void mfma_lds_rate_kernel(float *out, int iters,
+                                                                 uint32_t seed) {
+  __shared__ __attribute__((aligned(16))) char tile[kLdsBytes];
+  __shared__ char pad[kLdsPad2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t h = (blockIdx.x * (uint32_t)kThreads + tid) * 2654435761u + seed;
+  if (h == 0) h = 1;
+  for (int i = tid; i < kLdsBytes / 2; i += kThreads) reinterpret_cast<__bf16 *>(tile)[i] = uniform_bf16(h);
+  if (tid == 0) pad[blockIdx.x & 1023] = 0;
+  bf16x8 b[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[s][i] = uniform_bf16(h);
+  __syncthreads();
+  f32x16 c[4] = {};
+  const int base = wave * 8192 + lane * 16;   // 16-byte aligned, inside the tile
+  int off = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(tile + base + off);
+      off = (off + 1024) & 8191;
+      c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[i], c[i], 0, 0, 0);
     }
   }
   float sum = 0.0f;
@@ -152,11 +196,16 @@ extern "C" int attn_measure_hbm_copy(const void *src, void *dst, long long bytes
 }
 
 extern "C" int attn_measure_mfma_rate(float *out, int n_wg, int iters, uint32_t seed,
-                                      void *stream) {
+                                      int a_from_lds, void *stream) {
   if (!out) return ATTN_MEASURE_ERR_NULL;
-  if (n_wg < 1 || n_wg > 65536 || iters < 4 || iters > (1 << 24) || iters % 4)
+  if (n_wg < 1 || n_wg > 65536 || iters < 4 || iters > (1 << 24) || iters % 4 ||
+      (a_from_lds != 0 && a_from_lds != 1))
     return ATTN_MEASURE_ERR_SHAPE;
-  hipLaunchKernelGGL(lcat::mfma_rate_kernel, dim3(n_wg), dim3(lcat::kThreads), 0,
-                     static_cast<hipStream_t>(stream), out, iters, seed);
+  if (a_from_lds)
+    hipLaunchKernelGGL(lcat::mfma_lds_rate_kernel, dim3(n_wg), dim3(lcat::kThreads), 0,
+                       static_cast<hipStream_t>(stream), out, iters, seed);
+  else
+    hipLaunchKernelGGL(lcat::mfma_rate_kernel, dim3(n_wg), dim3(lcat::kThreads), 0,
+                       static_cast<hipStream_t>(stream), out, iters, seed);
   return hipGetLastError() == hipSuccess ? ATTN_MEASURE_OK : ATTN_MEASURE_ERR_HIP;
 }

@@ -265,12 +265,13 @@ def test_fp8_validation(lib):
 def test_measure_validation(lib):
     m = lib.attn_measure_mfma_rate
     out = P(0x10000)
-    assert m(NUL, 256, 64, 1, S0) == NULL
-    assert m(out, 0, 64, 1, S0) == SHAPE
-    assert m(out, 65537, 64, 1, S0) == SHAPE
-    assert m(out, 256, 6, 1, S0) == SHAPE     # not a multiple of 4
-    assert m(out, 256, 0, 1, S0) == SHAPE
-    assert m(out, 256, (1 << 24) + 4, 1, S0) == SHAPE
+    assert m(NUL, 256, 64, 1, 0, S0) == NULL
+    assert m(out, 0, 64, 1, 0, S0) == SHAPE
+    assert m(out, 65537, 64, 1, 1, S0) == SHAPE
+    assert m(out, 256, 6, 1, 0, S0) == SHAPE     # not a multiple of 4
+    assert m(out, 256, 0, 1, 1, S0) == SHAPE
+    assert m(out, 256, (1 << 24) + 4, 1, 0, S0) == SHAPE
+    assert m(out, 256, 64, 1, 2, S0) == SHAPE    # a_from_lds is 0 or 1
     with pytest.raises(ValueError):
         lcat.measure_mfma_rate(n_wg=16, iters=10)
     rd, rb, cp = lib.attn_measure_hbm_read, lib.attn_measure_hbm_read_bytes, lib.attn_measure_hbm_copy

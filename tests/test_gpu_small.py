@@ -742,11 +742,12 @@ def test_chunked_equals_dense_prefill():
 # ---------------------------------------------------------------------------
 # sustained-MFMA yardstick (measurement helper, not part of the path)
 # ---------------------------------------------------------------------------
-def test_measure_mfma_rate_runs():
-    log("measure_mfma_rate n_wg=16 iters=64")
-    a = lcat.measure_mfma_rate(n_wg=16, iters=64, seed=5)
-    b = lcat.measure_mfma_rate(n_wg=16, iters=64, seed=5)
-    c = lcat.measure_mfma_rate(n_wg=16, iters=64, seed=6)
+@pytest.mark.parametrize("a_from_lds", [False, True])
+def test_measure_mfma_rate_runs(a_from_lds):
+    log(f"measure_mfma_rate n_wg=16 iters=64 a_from_lds={a_from_lds}")
+    a = lcat.measure_mfma_rate(n_wg=16, iters=64, seed=5, a_from_lds=a_from_lds)
+    b = lcat.measure_mfma_rate(n_wg=16, iters=64, seed=5, a_from_lds=a_from_lds)
+    c = lcat.measure_mfma_rate(n_wg=16, iters=64, seed=6, a_from_lds=a_from_lds)
     torch.cuda.synchronize()
     assert torch.isfinite(a).all()
     assert torch.equal(a, b)          # the operands depend only on the seed
