@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(float *out, int ite
 #pragma unroll
     for (int r = 0; r < 16; ++r) sum += c[i][r];
   __syncthreads();
-  out[(long long)blockIdx.x * kThreads + tid] = sum + (float)pad[(tid * 7) & 1023];
+  out[(long long)blockIdx.x * kThreads + tid] = sum + (float)pad[blockIdx.x & 1023];
 }
 
 // The same chains with each MFMA's A operand read from LDS just before it
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void mfma_lds_rate_kernel(float *out, int
 #pragma unroll
     for (int r = 0; r < 16; ++r) sum += c[i][r];
   __syncthreads();
-  out[(long long)blockIdx.x * kThreads + tid] = sum + (float)pad[(tid * 7) & 1023];
+  out[(long long)blockIdx.x * kThreads + tid] = sum + (float)pad[blockIdx.x & 1023];
 }
 
 // Streaming read: wave w reads units [w * per_wave, (w + 1) * per_wave) of
