@@ -176,8 +176,11 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   const int wave_tiles = (wave_keys + BN - 1) / BN;
 
   // ---- this wave's 32 query rows -> registers (B operand of S^T = K Q^T) --
-  // qf[s] = dims 16s + 8gq .. +7 of query row row0 + lr.  Rows past the end
+  // qf[s] = dims 16s + 8gq .. +7 of query row row0 + lr, multiplied by
+  // scale * log2(e) and rounded to bf16, so that the MFMAs produce scores
+  // already in log2 units (the softmax uses exp2).  Rows past the end
   // repeat the last row (finite data) and are never stored.
+  const float c2 = p.scale * kLog2e;
   const int qrow = row0 + lr;
   bf16x8 qf[8];
   {
@@ -185,6 +188,10 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     const bf16 *qp = static_cast<const bf16 *>(p.q) + (((size_t)b * p.Sq + qr) * p.Hq + h) * HD;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(ld_global_16(qp + 16 * s + 8 * gq));
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = to_bf16((float)qf[s][e] * c2);
 #pragma unroll
     for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(qf[s]));   // wait for Q here, not in the loop
   }
@@ -237,7 +244,6 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   auto next_k = [](int x) { return x + TILE == NKS * TILE ? 0 : x + TILE; };
   auto next_v = [](int x) { return x + TILE == (NKS + NVS) * TILE ? NKS * TILE : x + TILE; };
 
-  const float c2 = p.scale * kLog2e;   // scores -> log2 units
   // last key this lane's row may see
   int qlast;
   if constexpr (LIMITS)
@@ -263,6 +269,17 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   for (int i = 0; i < NPK; ++i) kpre[i] = bf16x8{};
   float m2 = -INFINITY;   // running max of this lane's row, log2 units
   float l_run = 0.f;      // lane-partial denominator (keys of this lane)
+  // Score tiles hold (scale * log2 e) * s - m2 (or - 0 while m2 is -inf):
+  // every S^T accumulator chain starts from negm, a register tile filled
+  // with that shift, so the softmax exponentiates MFMA outputs directly.
+  // When m2 rises, a score tile already computed for a later key tile is
+  // moved by the same amount.
+  f32x16 negm = f32x16{};
+  auto set_shift = [&]() __attribute__((always_inline)) {
+    const float sh = m2 == -INFINITY ? 0.f : -m2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = sh;
+  };
 
   // ---- plain (sequential) pieces, used for edge iterations ----------------
   auto pv_plain = [&](int t, int vs, const bf16x8 (&pp)[4]) __attribute__((always_inline)) {
@@ -275,11 +292,10 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     }
   };
   auto s_plain = [&](int ks, f32x16 (&sn)[2], bool use_pre) __attribute__((always_inline)) {
-    sn[0] = sn[1] = f32x16{};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const bf16x8 a = (i < NPK && use_pre) ? kpre[i < NPK ? i : 0] : read_k(ks, i);
-      sn[i & 1] = mfma_32x32x16(a, qf[i >> 1], sn[i & 1]);
+      sn[i & 1] = mfma_32x32x16(a, qf[i >> 1], i < 2 ? negm : sn[i & 1]);
     }
   };
   // Row max of a score tile (tree of max3) and the lazily raised running max.
@@ -295,14 +311,14 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(t[9], t[10]);
     return pair_max32(fmaxf(fmaxf(u0, u1), fmaxf(u2, u3)));
   };
-  // exp2 of half hf of the scores into P (bf16), returning the partial row sum
-  auto exp_half = [&](const f32x16 (&sc)[2], bf16x8 (&pc)[4], int hf, float msc,
+  // exp2(score - d) of half hf of a score tile into P (bf16), returning the
+  // partial row sum
+  auto exp_half = [&](const f32x16 (&sc)[2], bf16x8 (&pc)[4], int hf, float d,
                       float psum) __attribute__((always_inline)) -> float {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pc[2 * hf + u][e] = to_bf16(fast_exp2(fmaf(sc[hf][8 * u + e], c2, -msc)));
+      for (int e = 0; e < 8; ++e) pc[2 * hf + u][e] = to_bf16(fast_exp2(sc[hf][8 * u + e] - d));
       const u32x4 w = as_u32x4(pc[2 * hf + u]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) psum = add_bf16_pair(w[e], psum);
@@ -322,7 +338,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
         if (kk + 32 > lim) sc[1][r] = -INFINITY;
       }
     }
-    const float mx2 = tile_max(sc) * c2;
+    const float sh = m2 == -INFINITY ? 0.f : m2;   // shift the tile was computed with
+    const float mx2 = tile_max(sc) + sh;
     const bool grow = mx2 > m2 + kRescaleLog2;
     if (__ballot(grow)) {
       const float m_new = grow ? mx2 : m2;
@@ -331,32 +348,42 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+      set_shift();
     }
-    const float msc = (m2 == -INFINITY) ? 0.f : m2;
-    l_run = exp_half(sc, pc, 1, msc, exp_half(sc, pc, 0, msc, l_run));
+    const float d = (m2 == -INFINITY) ? 0.f : m2 - sh;
+    l_run = exp_half(sc, pc, 1, d, exp_half(sc, pc, 0, d, l_run));
   };
 
   // ---- tile fetch: NDW waves move 16/NDW KiB of each K and V tile ---------
   // With NDW = 4 only the older wave of each SIMD (waves w and w+4 share one)
   // issues DMAs: it wins issue arbitration and finishes its MFMA slots
-  // first, so it fetches while the younger one starts computing.  DMA
-  // instruction i of wave w fills LDS bytes [(DPW w + i) KiB, +1 KiB) of the
-  // slot: key rows 4 (DPW w + i) .. +3 (K, dense V) or dimension rows
-  // 8 (DPW w + i) .. +7 (paged V^T).  Each lane picks the global chunk whose
-  // swizzled position is its own LDS position.
+  // first, so it fetches while the younger one starts computing.  Each lane
+  // picks the global chunk whose swizzled position is its own LDS position.
+  //  * K and dense V: DMA instruction i of wave w fills key rows
+  //    16 i + 4 w .. +3, LDS bytes [4096 i + 1024 w, +1 KiB) of the slot.
+  //    Rows 16 apart share one chunk permutation, so a wave's instructions
+  //    differ only by the uniform source stride of 16 rows, added to one
+  //    base offset register per tensor.
+  //  * Paged V^T: instruction i of wave w fills dimension rows
+  //    32 i + 8 w .. +7, LDS bytes [4096 i + 1024 w, +1 KiB).  Rows 64 apart
+  //    share one chunk permutation, so instructions i and i + 2 differ by a
+  //    uniform 8 KiB of source: two offset registers per wave.
   constexpr int DPW = TILE / 1024 / NDW;   // 1 KiB pieces per DMA wave, tile and tensor
+  static_assert(DPW * NDW * 4 == BN && NDW * 4 == 16, "row mapping of the K / dense V DMAs");
   const bool dma_wave = wave < NDW;
   const int rs = PAGED ? HD * 2 : p.Hkv * HD * 2;   // bytes between key rows
-  int koff[DPW], voff[DPW];
-#pragma unroll
-  for (int i = 0; i < DPW; ++i) {
-    const int r = 4 * DPW * wave + 4 * i + (lane >> 4), pos = lane & 15;
-    koff[i] = r * rs + 16 * k_pos(r, pos);
+  const int rstep = 16 * rs;                         // source bytes between a wave's DMAs
+  static_assert(!PAGED || DPW == 4, "row mapping of the paged V^T DMAs");
+  int kbase, vbase = 0, vodd = 0;
+  {
+    const int r = 4 * wave + (lane >> 4), pos = lane & 15;
+    kbase = r * rs + 16 * k_pos(r, pos);
     if constexpr (PAGED) {
-      const int d = 8 * DPW * wave + 8 * i + (lane >> 3), pv = lane & 7;
-      voff[i] = d * (BN * 2) + 16 * vp_pos(d, pv);
+      const int d = 8 * wave + (lane >> 3), pv = lane & 7;
+      vbase = d * (BN * 2) + 16 * vp_pos(d, pv);
+      vodd = (d + 32) * (BN * 2) + 16 * vp_pos(d + 32, pv);
     } else {
-      voff[i] = r * rs + 16 * vd_pos(r, pos);
+      vbase = r * rs + 16 * vd_pos(r, pos);
     }
   }
   const int32_t *table =
@@ -380,7 +407,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     return Stream{static_cast<const char *>(t0) + first * 2, p.Sk};
   };
   Stream ks_stream = dense_stream(p.k), vs_stream = dense_stream(p.v);
-  auto issue = [&](Stream &st, int tile, int blk, int slot_off, const int (&off)[DPW],
+  auto issue = [&](Stream &st, int tile, int blk, int slot_off,
                    bool is_k) __attribute__((always_inline)) {
     u32x4 r;
     if constexpr (PAGED) {
@@ -395,9 +422,20 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
       st.base += tstride;
       st.rows_left -= BN;
     }
-    char *dst = smem + slot_off + wave * (DPW * 1024);
+    if (PAGED && !is_k) {
+      const int b0 = opaque(vbase), b1 = opaque(vodd);
+      char *dst = smem + slot_off + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < DPW; ++i) dma_to_lds_16(r, dst + 1024 * i, off[i]);
+      for (int i = 0; i < DPW; ++i)
+        dma_to_lds_16(r, dst + 4096 * i, (i & 1 ? b1 : b0) + (i >> 1) * (64 * BN * 2));
+    } else {
+      // the per-instruction offsets are recomputed here (one add each)
+      // rather than held in registers across the loop
+      const int base = opaque(is_k ? kbase : vbase);
+      char *dst = smem + slot_off + wave * 1024;
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) dma_to_lds_16(r, dst + 4096 * i, base + i * rstep);
+    }
   };
 
   // Paged: wave 0 checks the ids and tags of all n_tiles blocks once, 64 at
@@ -418,9 +456,9 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   // ---- prologue: K_0..K_{KA-1}, V_0..V_{VA-1} in flight, then S_0 --------
   if (dma_wave) {
 #pragma unroll
-    for (int t = 0; t < KA; ++t) issue(ks_stream, t, block_of(t), t * TILE, koff, true);
+    for (int t = 0; t < KA; ++t) issue(ks_stream, t, block_of(t), t * TILE, true);
 #pragma unroll
-    for (int t = 0; t < VA; ++t) issue(vs_stream, t, block_of(t), (NKS + t) * TILE, voff, false);
+    for (int t = 0; t < VA; ++t) issue(vs_stream, t, block_of(t), (NKS + t) * TILE, false);
   }
   int blk_k = block_of(KA), blk_v = block_of(VA);
   wait_vmcnt<0>();
@@ -446,8 +484,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   // iteration (V_j and K_{j+2}, from the given slots).
   auto fetch = [&](int j, int kdst, int vdst) __attribute__((always_inline)) {
     if (dma_wave) {
-      issue(ks_stream, j + KA, blk_k, kdst, koff, true);
-      issue(vs_stream, j + VA, blk_v, vdst, voff, false);
+      issue(ks_stream, j + KA, blk_k, kdst, true);
+      issue(vs_stream, j + VA, blk_v, vdst, false);
       blk_k = block_of(j + KA + 1);
       blk_v = block_of(j + VA + 1);
     }
@@ -484,10 +522,12 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     // next: slot i issues MFMA i (16 of P V, then 16 of K Q^T), the LDS read
     // of the operand used LA slots later, and a fixed share of the softmax
     // VALU work: pair pr of P (scores 2pr, 2pr+1 -> word pr & 3 of operand
-    // pr >> 2) is scaled and shifted in slot 2pr, exponentiated in slot
-    // 2pr+1 and packed and summed in slot 2pr+2, so every slot carries about
-    // four VALU instructions and no step waits for the one before it inside
-    // a slot.  No tile maximum is taken here (see kSumLimit).
+    // pr >> 2) has its first score exponentiated in slot 2pr and its second
+    // in slot 2pr+1; it is packed to bf16 in slot 2pr+2 and added to the row
+    // sum in slot 2pr+3, so every slot carries one exp2 and one more VALU
+    // instruction, and no step waits for the one before it inside a slot.
+    // The scores arrive scaled and shifted by the running maximum (negm);
+    // no tile maximum is taken here (see kSumLimit).
     bf16x8 op[32];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
@@ -495,13 +535,16 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
       op[16 + i] = kpre[i];
     }
     float ts = 0.f;     // this tile's row sum (this lane's keys)
-    float xs[2][2];     // pairs in flight between the scale, exp2 and pack steps
+    float xs[2][2];     // pairs in flight between the exp2 and pack steps
     auto pack_pair = [&](auto pr_tag) __attribute__((always_inline)) {
       constexpr int pr = decltype(pr_tag)::value;
       constexpr int u = pr >> 2;
       pc[u][2 * (pr & 3)] = to_bf16(xs[pr & 1][0]);
       pc[u][2 * (pr & 3) + 1] = to_bf16(xs[pr & 1][1]);
-      ts = add_bf16_pair(as_u32x4(pc[u])[pr & 3], ts);
+    };
+    auto sum_pair = [&](auto pr_tag) __attribute__((always_inline)) {
+      constexpr int pr = decltype(pr_tag)::value;
+      ts = add_bf16_pair(as_u32x4(pc[pr >> 2])[pr & 3], ts);
     };
     static_for<32>([&](auto slot_tag) __attribute__((always_inline)) {
       constexpr int i = decltype(slot_tag)::value;
@@ -510,25 +553,26 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
         op[nx] = read_v(vs, nx);
       else if constexpr (nx >= 16 + NPK && nx < 32)
         op[nx] = read_k(ks, nx - 16);
-      if constexpr (i == 16) sn[0] = sn[1] = f32x16{};
       if constexpr (i < 16)
         acc[i & 3] = mfma_32x32x16(op[i], pp[i >> 2], acc[i & 3]);
+      else if constexpr (i < 18)
+        sn[i & 1] = mfma_32x32x16(op[i], qf[(i - 16) >> 1], negm);
       else
         sn[i & 1] = mfma_32x32x16(op[i], qf[(i - 16) >> 1], sn[i & 1]);
       // -- VALU share of slot i --
       constexpr int pr = i >> 1;
-      if constexpr ((i & 1) == 0) {
-        constexpr int hf = pr >> 3, r = 2 * (pr & 7);
-        xs[pr & 1][0] = fmaf(sc[hf][r], c2, -m2);
-        xs[pr & 1][1] = fmaf(sc[hf][r + 1], c2, -m2);
-        if constexpr (pr >= 1) pack_pair(Int<pr - 1>{});
-      } else {
-        xs[pr & 1][0] = fast_exp2(xs[pr & 1][0]);
-        xs[pr & 1][1] = fast_exp2(xs[pr & 1][1]);
+      constexpr int hf = pr >> 3, r = 2 * (pr & 7) + (i & 1);
+      xs[pr & 1][i & 1] = fast_exp2(sc[hf][r]);
+      if constexpr (pr >= 1) {
+        if constexpr ((i & 1) == 0)
+          pack_pair(Int<pr - 1>{});
+        else
+          sum_pair(Int<pr - 1>{});
       }
       __builtin_amdgcn_sched_barrier(0);
     });
     pack_pair(Int<15>{});
+    sum_pair(Int<15>{});
     // P_j and l are produced in this iteration, not sunk into the next one
 #pragma unroll
     for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(pc[u]));
@@ -537,13 +581,22 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     asm volatile("" ::"v"(l_run));
     if (__ballot(!(ts <= kSumLimit))) {
       // rare: some exponential may exceed the bound; redo the tile against
-      // its exact maximum and rescale O (which now holds P_{j-1} V_{j-1})
-      const float m_new = fmaxf(m2, tile_max(sc) * c2);
-      const float alpha = fast_exp2(m2 - m_new);
-      m2 = m_new;
+      // its exact maximum and rescale O (which now holds P_{j-1} V_{j-1}).
+      // m2 is finite here (every row of the wave has seen key tile 0), and
+      // the tile's scores are relative to it.
+      const float dm = fmaxf(tile_max(sc), 0.f);
+      const float alpha = fast_exp2(-dm);
+      m2 += dm;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] *= alpha;
-      l_run = exp_half(sc, pc, 1, m2, exp_half(sc, pc, 0, m2, l_prev * alpha));
+      l_run = exp_half(sc, pc, 1, dm, exp_half(sc, pc, 0, dm, l_prev * alpha));
+      // the next tile's scores were computed against the old maximum
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sn[0][r] -= dm;
+        sn[1][r] -= dm;
+      }
+      set_shift();
     }
     finish(j, vpre_s, kpre_s);
   };
