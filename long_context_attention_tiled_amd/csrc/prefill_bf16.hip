@@ -175,6 +175,11 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   const int n_tiles = (wg_keys + BN - 1) / BN;
   const int wave_tiles = (wave_keys + BN - 1) / BN;
 
+  // No row of this workgroup sees a key of this shard (limits do not
+  // decrease, so the last row decides; the test is workgroup-uniform):
+  // merging an empty partial into the running result changes nothing.
+  if (LIMITS && p.accumulate && wg_keys == 0) return;
+
   // ---- this wave's 32 query rows -> registers (B operand of S^T = K Q^T) --
   // qf[s] = dims 16s + 8gq .. +7 of query row row0 + lr, multiplied by
   // scale * log2(e) and rounded to bf16, so that the MFMAs produce scores
