@@ -84,7 +84,14 @@ enum attn_cp_mode {
  * head h / (Hq/Hkv); with causal != 0 only keys j <= i are visible (global
  * token indices, [ULY] §5.3).  lse[b,h,i] = log sum_j exp(scale * q_i . k_j).
  *   dtype ATTN_DTYPE_BF16: D must be 128, Hq/Hkv must divide 8 or be a
- *         multiple of 8; bf16 MFMA products with fp32 accumulation.
+ *         multiple of 8; bf16 MFMA products with fp32 accumulation.  Each
+ *         query row is multiplied by scale * log2(e) and rounded to bf16
+ *         once, so every product term of a score carries one extra relative
+ *         rounding of at most 2^-9 (as large as the bf16 rounding of the
+ *         inputs); lse then differs from its exact value by at most 2^-9
+ *         times the magnitude of the scores that carry the softmax weight.
+ *         P is rounded to bf16 before P V.  The same holds for
+ *         attn_chunked_prefill and attn_prefill_limited.
  *   dtype ATTN_DTYPE_F32 : D must be 64 or 128; fp32 arithmetic throughout.
  * S = 0 or B = 0 is a no-op.
  */
