@@ -19,6 +19,8 @@
 // the loads are issued before the table is built), with the arithmetic
 // of rope_math.h so results match the in-place RoPE kernel bit for bit.  V
 // takes the same path without the rotation.  Stores are non-temporal.
+#include <algorithm>
+
 #include "device.h"
 #include "kernels.h"
 #include "rope_math.h"
@@ -28,10 +30,6 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int UPT = 2;   // pairs per thread (four 16-byte loads in flight)
-// Table entries a workgroup may need: tokens spanned by NT*UPT pairs, times
-// D/2 frequencies.  With hc = D/16 chunks per half and one head per token this
-// is (NT*UPT/hc + 2) * 8*hc <= NT*UPT*8 + 16*hc <= 4096 + 256 for D <= 256.
-constexpr int MAX_CS = 4352;
 
 struct RopeJob {
   const char *in;        // [SP][S_loc][H_tot][D] bf16
@@ -42,11 +40,15 @@ struct RopeJob {
   int rotate;            // 1: Q or K (rotate), 0: V (copy)
 };
 
+// Dynamic LDS: theta_i for i < D/2 (doubles), then the (cos, sin) table,
+// sized by the launch for the largest table any workgroup builds (a smaller
+// table leaves room for more resident workgroups).
 __global__ __launch_bounds__(NT) void permute_rope_kernel(RopeJob j0, RopeJob j1, RopeJob j2,
                                                           const int32_t *__restrict__ positions,
                                                           int D, double log2_base) {
-  __shared__ float2 cs[MAX_CS];
-  __shared__ double theta[128];   // theta_i for i < D/2
+  extern __shared__ __attribute__((aligned(16))) char rope_lds[];
+  double *theta = reinterpret_cast<double *>(rope_lds);
+  float2 *cs = reinterpret_cast<float2 *>(rope_lds + (D >> 1) * sizeof(double));
   const long long wg = blockIdx.x;
   const RopeJob &j = wg >= j2.wg_begin ? j2 : (wg >= j1.wg_begin ? j1 : j0);
   const int tid = threadIdx.x;
@@ -127,8 +129,18 @@ hipError_t launch_permute_qkv_rope(const void *const in[3], void *const out[3], 
     wg += (j[t].n_pairs + NT * UPT - 1) / (NT * UPT);
   }
   if (wg == 0) return hipSuccess;
-  hipLaunchKernelGGL(permute_rope_kernel, dim3((unsigned)wg), dim3(NT), 0, stream, j[0], j[1], j[2],
-                     positions, D, log2((double)base));
+  // Largest table: the NT*UPT pairs of a workgroup span at most
+  // ceil(NT*UPT / pairs-per-token) + 1 tokens, each with D/2 frequencies.
+  long long max_tab = 0;
+  for (int t = 0; t < 2; ++t) {
+    const long long per_tok = (long long)j[t].H_loc * hc;
+    if (j[t].n_pairs > 0 && per_tok > 0)
+      max_tab = std::max(max_tab, ((NT * UPT + per_tok - 1) / per_tok + 1) * (D / 2));
+  }
+  const size_t lds = (size_t)(D / 2) * sizeof(double) + (size_t)max_tab * sizeof(float2);
+  if (lds > 64 * 1024) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(permute_rope_kernel, dim3((unsigned)wg), dim3(NT), lds, stream, j[0], j[1],
+                     j[2], positions, D, log2((double)base));
   return hipGetLastError();
 }
 
