@@ -2,7 +2,7 @@
 // ("Ulysses sequence parallelism in long-context inference", §3.2 and §5.3;
 // the angle arithmetic and its precision are described in rope_math.h).
 //
-// A workgroup handles a few consecutive tokens: it first builds the
+// A workgroup handles a few consecutive tokens: it builds theta once and the
 // (cos, sin) table of those tokens in LDS (each angle once, shared by all
 // heads), then streams the heads with 16-byte loads and stores.
 #include "device.h"
@@ -13,37 +13,68 @@ namespace lcat {
 namespace {
 
 constexpr int NT = 256;
+constexpr int UPT = 2;            // items per thread and batch
 constexpr int MAX_TABLE = 4096;   // (token, frequency) pairs per workgroup
 
+// Dynamic LDS: theta_i for i < D/2 (doubles), then the (cos, sin) table of
+// the workgroup's tokens.  The first batch of loads is issued before the
+// table is built, so its latency is hidden behind that arithmetic.
 __global__ __launch_bounds__(NT) void rope_kernel(bf16 *__restrict__ x,
                                                   const int32_t *__restrict__ positions, int S,
                                                   int H, int D, double log2_base, int tok_per_wg) {
-  __shared__ float2 cs[MAX_TABLE];
-  const int tid = threadIdx.x;
+  extern __shared__ __attribute__((aligned(16))) char rope_lds[];
   const int half = D >> 1;
+  double *theta = reinterpret_cast<double *>(rope_lds);
+  float2 *cs = reinterpret_cast<float2 *>(rope_lds + half * sizeof(double));
+  const int tid = threadIdx.x;
   const int t0 = blockIdx.x * tok_per_wg;
   const int nt = min(tok_per_wg, S - t0);
   if (nt <= 0) return;
 
-  for (int idx = tid; idx < nt * half; idx += NT) {
-    const int t = idx / half, i = idx % half;
-    cs[idx] = rope_cos_sin(rope_theta(i, D, log2_base), positions[t0 + t]);
-  }
-  __syncthreads();
-
   const int chunks = half >> 3;                      // 8-element chunks per half
   const int items = nt * H * chunks;
-  for (int it = tid; it < items; it += NT) {
-    const int c = it % chunks;
+  bf16x8 lo[UPT], hi[UPT];
+  auto row_of = [&](int it, int &c, int &t) __attribute__((always_inline)) -> bf16 * {
+    c = it % chunks;
     const int th = it / chunks;
-    const int h = th % H, t = th / H;
-    bf16 *row = x + ((size_t)(t0 + t) * H + h) * D;
-    const bf16x8 lo = as_bf16x8(ld_global_16(row + 8 * c));
-    const bf16x8 hi = as_bf16x8(ld_global_16(row + half + 8 * c));
-    bf16x8 nlo, nhi;
-    rope_rotate8(lo, hi, &cs[t * half + 8 * c], nlo, nhi);
-    st_global_16(row + 8 * c, as_u32x4(nlo));
-    st_global_16(row + half + 8 * c, as_u32x4(nhi));
+    const int h = th % H;
+    t = th / H;
+    return x + ((size_t)(t0 + t) * H + h) * D;
+  };
+  auto load = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int it = base + tid + u * NT;
+      if (it < items) {
+        int c, t;
+        const bf16 *row = row_of(it, c, t);
+        lo[u] = as_bf16x8(ld_global_16(row + 8 * c));
+        hi[u] = as_bf16x8(ld_global_16(row + half + 8 * c));
+      }
+    }
+  };
+  load(0);
+
+  for (int i = tid; i < half; i += NT) theta[i] = rope_theta(i, D, log2_base);
+  __syncthreads();
+  for (int idx = tid; idx < nt * half; idx += NT)
+    cs[idx] = rope_cos_sin(theta[idx % half], positions[t0 + idx / half]);
+  __syncthreads();
+
+  for (int base = 0; base < items; base += NT * UPT) {
+    if (base > 0) load(base);
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int it = base + tid + u * NT;
+      if (it < items) {
+        int c, t;
+        bf16 *row = row_of(it, c, t);
+        bf16x8 nlo, nhi;
+        rope_rotate8(lo[u], hi[u], &cs[t * half + 8 * c], nlo, nhi);
+        st_global_16(row + 8 * c, as_u32x4(nlo));
+        st_global_16(row + half + 8 * c, as_u32x4(nhi));
+      }
+    }
   }
 }
 
@@ -53,13 +84,14 @@ hipError_t launch_rope(void *x, const int32_t *positions, int S, int H, int D, f
                        hipStream_t stream) {
   if (S <= 0 || H <= 0) return hipSuccess;
   const int chunks = D / 16;
-  int tok = 512 / (H * chunks);
+  int tok = NT * UPT / (H * chunks);
   if (tok < 1) tok = 1;
   if (tok > 64) tok = 64;
   while (tok > 1 && tok * (D / 2) > MAX_TABLE) --tok;
+  const size_t lds = (size_t)(D / 2) * sizeof(double) + (size_t)tok * (D / 2) * sizeof(float2);
   dim3 grid((S + tok - 1) / tok), block(NT);
-  hipLaunchKernelGGL(rope_kernel, grid, block, 0, stream, static_cast<bf16 *>(x), positions, S, H,
-                     D, log2((double)base), tok);
+  hipLaunchKernelGGL(rope_kernel, grid, block, lds, stream, static_cast<bf16 *>(x), positions, S,
+                     H, D, log2((double)base), tok);
   return hipGetLastError();
 }
 
