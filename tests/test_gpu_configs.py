@@ -176,7 +176,7 @@ def run_cp_rank(q, k, v, S, N, rank, mode, accumulate):
     return o, lse
 
 
-@pytest.mark.parametrize("rank,accumulate", [(0, False), (3, True)])
+@pytest.mark.parametrize("rank,accumulate", [(0, False), (0, True), (3, True)])
 def test_cp_zigzag_64k(rank, accumulate):
     S, N = 65536, 4
     log(f"CP zigzag 64K rank {rank}: generating")
