@@ -109,6 +109,46 @@ def test_ulysses_relayout_rope_prefill_64k():
     log(f"C3: max abs {e:.3g} rel-L2 {r:.3g}")
 
 
+def test_ulysses_all_ranks_equal_full_head_attention():
+    """The one-GPU emulation of the sequence-parallel step: every rank r of
+    SP=4 relays out its heads from the four sequence shards, applies RoPE at
+    global positions and runs causal attention; the ranks' head slices, put
+    side by side, must equal attention over the full 64-query-head /
+    8-KV-head problem (oracle on sampled rows).  Ranks 0 and 2 take the
+    separate relayout and RoPE kernels, ranks 1 and 3 the fused one."""
+    SP, S_loc, Hq_tot, Hkv_tot = 4, 1024, 64, 8
+    S = SP * S_loc
+    d = synth.ulysses_shards(seed=930, SP=SP, S_loc=S_loc, Hq_tot=Hq_tot, Hkv_tot=Hkv_tot)
+    gpos = d["shard_positions"].reshape(-1)
+    posd = to_dev(gpos.astype(np.int32))
+    qs, ks, vs = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
+    o_full = torch.empty((1, S, Hq_tot, 128), dtype=torch.bfloat16, device="cuda")
+    lse_full = torch.empty((1, Hq_tot, S), dtype=torch.float32, device="cuda")
+    hq, hk = Hq_tot // SP, Hkv_tot // SP
+    for r in range(SP):
+        log(f"ulysses emulation: rank {r}")
+        if r % 2 == 0:
+            qd, kd, vd = lcat.seq_to_head_permute_qkv(qs, ks, vs, r)
+            lcat.rope_apply(qd, posd)
+            lcat.rope_apply(kd, posd)
+        else:
+            qd, kd, vd = lcat.seq_to_head_permute_qkv_rope(qs, ks, vs, r, posd)
+        o, lse = lcat.attn_prefill(qd[None], kd[None], vd[None], causal=True)
+        o_full[:, :, hq * r:hq * (r + 1)] = o
+        lse_full[:, hq * r:hq * (r + 1)] = lse
+    torch.cuda.synchronize()
+    boundaries = [S_loc * i + j for i in range(1, SP) for j in (-1, 0, 1)]
+    rows = synth.sample_rows(931, S, 128, forced_rows(S, boundaries))
+    full = lambda x: x.reshape(1, S, x.shape[2], x.shape[3])     # shards in order = global order
+    log(f"ulysses emulation: oracle on {rows.size} rows x {Hq_tot} heads")
+    ref, ref_lse = prefill_reference(full(d["q"]), full(d["k"]), full(d["v"]),
+                                     gpos.astype(np.int64), rows, d["scale"])
+    idx = torch.from_numpy(rows).cuda()
+    e, r_ = assert_attention_close(to_np64(o_full[:, idx]), ref, lse_full[:, :, idx].cpu().numpy(),
+                                   ref_lse, what="Ulysses emulation")
+    log(f"ulysses emulation: max abs {e:.3g} rel-L2 {r_:.3g}")
+
+
 def test_ulysses_relayout_with_rope_64k():
     """The fused relayout + RoPE at the 64K shape the benchmark times: V bit
     for bit over the whole tensor, Q and K on sampled tokens (shard

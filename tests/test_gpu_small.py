@@ -249,6 +249,38 @@ def test_prefill_needle():
         assert np.abs(got[:, h] - want[:, h // (Hq // Hkv)]).max() < 0.05
 
 
+def test_prefill_closed_forms():
+    """Closed forms on the kernel itself (no oracle): q = 0 makes every score
+    0, so causal row i returns the mean of V[0..i] with LSE = ln(i+1); causal
+    row 0 returns V[0] exactly whatever q is; a single key returns V[0] with
+    LSE = scale * q.k0."""
+    S, Hq, Hkv = 300, 16, 2
+    g = Hq // Hkv
+    d = synth.dense_bf16(seed=950, B=1, S=S, Hq=Hq, Hkv=Hkv)
+    v64 = synth.bf16_bits_to_f32(d["v"]).astype(np.float64)[0]          # [S][Hkv][D]
+    mean = np.cumsum(v64, axis=0) / np.arange(1, S + 1)[:, None, None]
+    zero_q = np.zeros_like(d["q"])
+    o, lse = lcat.attn_prefill(to_dev(zero_q), to_dev(d["k"]), to_dev(d["v"]), causal=True)
+    torch.cuda.synchronize()
+    want = np.repeat(mean, g, axis=1)[None]                                # [1][S][Hq][D]
+    want_lse = np.broadcast_to(np.log(np.arange(1, S + 1))[None, None, :], (1, Hq, S))
+    assert_attention_close(to_np64(o), want, lse.cpu().numpy(), want_lse, what="q = 0")
+    # causal row 0 sees only key 0: P = 1 exactly, so O is V[0] bit for bit
+    o, _ = lcat.attn_prefill(to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"]), causal=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o)[0, 0], np.repeat(d["v"][0, 0], g, axis=0))
+    # a single key
+    d1 = synth.dense_bf16(seed=951, B=2, S=1, Hq=Hq, Hkv=Hkv)
+    o, lse = lcat.attn_prefill(to_dev(d1["q"]), to_dev(d1["k"]), to_dev(d1["v"]), causal=False)
+    torch.cuda.synchronize()
+    q64, k64 = (synth.bf16_bits_to_f32(d1[n]).astype(np.float64) for n in ("q", "k"))
+    s0 = np.einsum("bhd,bhd->bh", q64[:, 0], np.repeat(k64[:, 0], g, axis=1)) * d1["scale"]
+    assert np.array_equal(bits(o)[:, 0], np.repeat(d1["v"][:, 0], g, axis=1))
+    assert_attention_close(to_np64(o), np.repeat(synth.bf16_bits_to_f32(d1["v"]).astype(np.float64),
+                                                 g, axis=2), lse.cpu().numpy(), s0[:, :, None],
+                           what="single key")
+
+
 def test_prefill_deterministic():
     d = synth.dense_bf16(seed=502, B=1, S=500, Hq=16, Hkv=2)
     q, k, v = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
