@@ -668,17 +668,30 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        bf16x4 *dst = reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * rq + 4 * gq);
-        bf16x4 w;
-        if (LIMITS && p.accumulate) {
-          const bf16x4 prev = *dst;
+      for (int hp = 0; hp < 2; ++hp) {
+        // acc[db] register 4 rq + e holds dim 32 db + 8 rq + 4 gq + e of this
+        // lane's row.  One swap with lane l ^ 32 per value pair leaves
+        // dims 32 db + 16 hp + 8 gq .. +7 in f[0..7], so each lane stores
+        // 16 contiguous bytes (32 per row and instruction) instead of 8.
+        float f[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[e] = to_bf16(acc[db][4 * rq + e] * inv + (w_prev > 0.f ? w_prev * (float)prev[e] : 0.f));
+        for (int e = 0; e < 4; ++e) {
+          const auto r = __builtin_amdgcn_permlane32_swap(
+              __builtin_bit_cast(uint32_t, acc[db][4 * (2 * hp) + e] * inv),
+              __builtin_bit_cast(uint32_t, acc[db][4 * (2 * hp + 1) + e] * inv), false, false);
+          f[e] = __builtin_bit_cast(float, (uint32_t)r[0]);
+          f[4 + e] = __builtin_bit_cast(float, (uint32_t)r[1]);
+        }
+        bf16x8 *dst = reinterpret_cast<bf16x8 *>(op + 32 * db + 16 * hp + 8 * gq);
+        bf16x8 w;
+        if (LIMITS && p.accumulate) {
+          const bf16x8 prev = *dst;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            w[e] = to_bf16(f[e] + (w_prev > 0.f ? w_prev * (float)prev[e] : 0.f));
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = to_bf16(acc[db][4 * rq + e] * inv);
+          for (int e = 0; e < 8; ++e) w[e] = to_bf16(f[e]);
         }
         *dst = w;
       }
