@@ -466,7 +466,11 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     for (int t = 0; t < VA; ++t) issue(vs_stream, t, block_of(t), (NKS + t) * TILE, false);
   }
   int blk_k = block_of(KA), blk_v = block_of(VA);
-  wait_vmcnt<0>();
+  // S_0 and the operand reads before the next barrier need K_0 and K_1
+  // only; K_2.., V_0.. may still fly (the first iteration's wait covers
+  // them).  Waves that issued no DMA have nothing left in flight.
+  static_assert(KA >= 2, "K_0 and K_1 are waited for separately");
+  wait_vmcnt<(KA - 2 + VA) * DPW>();
   barrier_no_wait();
   if (wave_tiles > 0) s_plain(0, S[0], false);   // K_0 in slot 0
   if (1 < wave_tiles) {
