@@ -95,13 +95,6 @@ def quantize_kv_pool(k_pool_bits, v_pool_bits):
     return k8, np.ascontiguousarray(np.swapaxes(v8t, 1, 2)), ks, vs
 
 
-def dequantize_kv_pool(k8, v8, k_scale, v_scale):
-    """fp64 K [n][64][D] and V [n][D][64] of an fp8 pool."""
-    k = dequantize_groups(k8, k_scale)
-    v = np.swapaxes(dequantize_groups(np.swapaxes(v8, 1, 2), v_scale), 1, 2)
-    return k, v
-
-
 def gather_dequantized(k8, v8, k_scale, v_scale, block_table, ctx_len, requests=None):
     """Per request b (all, or those listed in ``requests``), the dequantised K
     and V of its first ctx_len[b] tokens in order, [ctx][Hkv][D] fp64 each:

@@ -571,3 +571,105 @@ def test_paged_gather_roundtrip_decode_cache():
     bad[0, 0, 0] = 10**6
     with pytest.raises(RuntimeError):
         oracle.paged_gather(c["k_pool"], c["v_pool"], bad, c["ctx_len"])
+
+
+# ---------------------------------------------------------------------------
+# Decode over per-request contexts, and the dequantising gather of the FP8 cache
+# ---------------------------------------------------------------------------
+def _softmax_matrix_decode(q, k_seq, v_seq, ctx_len, scale, group):
+    """numpy full-matrix form, head by head: softmax(scale * K q) V over the
+    first ctx_len keys, KV head h // group (an independent formulation of the
+    naive attention of "Flash Attention and distributed inference" §18.2)."""
+    B, Hq, D = q.shape
+    out = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        n = int(ctx_len[b])
+        for h in range(Hq):
+            K = k_seq[b][:n, h // group]
+            V = v_seq[b][:n, h // group]
+            s = scale * (K @ q[b, h])
+            w = np.exp(s - s.max())
+            out[b, h] = (w / w.sum()) @ V
+            lse[b, h] = s.max() + np.log(w.sum())
+    return out, lse
+
+
+def test_decode_attention_brute_force_and_closed_forms():
+    """Three requests of 1, 64 and 70 keys (a partial last block), GQA 2:1:
+    every one of the ctx_len keys is visible and no other (Ulysses inference
+    article §2.3: the head-sharded cache holds the whole history; the new
+    token's own K/V included).  Also the single-key closed form (O = V_0,
+    LSE = s_0) and q = 0 -> mean of the ctx_len values."""
+    rng = np.random.default_rng(90)
+    Hq, Hkv, D, scale = 4, 2, 8, 0.5
+    ctx = np.array([1, 64, 70])
+    q = rand(rng, 3, Hq, D)
+    k_seq = [rand(rng, n + 5, Hkv, D) for n in ctx]     # 5 trailing keys that must not count
+    v_seq = [rand(rng, n + 5, Hkv, D) for n in ctx]
+    out, lse = oracle.decode_attention(q, k_seq, v_seq, ctx, scale)
+    ref, ref_lse = _softmax_matrix_decode(q, k_seq, v_seq, ctx, scale, Hq // Hkv)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-13)
+    for h in range(Hq):                                   # ctx = 1: V_0 and its score
+        np.testing.assert_allclose(out[0, h], v_seq[0][0, h // 2], rtol=0, atol=1e-15)
+        assert abs(lse[0, h] - scale * q[0, h] @ k_seq[0][0, h // 2]) <= 1e-14
+    z, zl = oracle.decode_attention(np.zeros_like(q), k_seq, v_seq, ctx, scale)
+    for b, n in enumerate(ctx):
+        for h in range(Hq):
+            np.testing.assert_allclose(z[b, h], v_seq[b][:n, h // 2].mean(axis=0), atol=1e-14)
+            assert abs(zl[b, h] - np.log(n)) <= 1e-13
+
+
+def test_gather_dequantized_hand_example():
+    """Literal values: one KV head, request 0 owns blocks 2 then 0 (a
+    shuffled table), request 1 owns block 1; 70 and 3 tokens.  e4m3 codes
+    0x38 = 1, 0x40 = 2, 0xB8 = -1 (the format's closed forms) times the
+    token's scale.  K token t sits in row t % 64 of its block, V token t in
+    column t % 64 of the dimension-major V block."""
+    D = 2
+    k8 = np.zeros((3, 64, D), np.uint8)
+    v8 = np.zeros((3, D, 64), np.uint8)
+    ks = np.zeros((3, 64), np.float32)
+    vs = np.zeros((3, 64), np.float32)
+    k8[2, 0] = [0x38, 0x40]; ks[2, 0] = 0.5          # request 0, token 0
+    v8[2, :, 0] = [0x40, 0xB8]; vs[2, 0] = 0.25
+    k8[0, 5] = [0xB8, 0x38]; ks[0, 5] = 4.0          # request 0, token 69
+    v8[0, :, 5] = [0x38, 0x38]; vs[0, 5] = 3.0
+    k8[1, 2] = [0x40, 0x40]; ks[1, 2] = 1.5          # request 1, token 2
+    v8[1, :, 2] = [0xB8, 0x40]; vs[1, 2] = 2.0
+    table = np.array([[[2, 0]], [[1, -1]]], np.int32)
+    kq, vq = fp8.gather_dequantized(k8, v8, ks, vs, table, [70, 3])
+    assert kq[0].shape == (70, 1, D) and kq[1].shape == (3, 1, D)
+    assert list(kq[0][0, 0]) == [0.5, 1.0] and list(vq[0][0, 0]) == [0.5, -0.25]
+    assert list(kq[0][69, 0]) == [-4.0, 4.0] and list(vq[0][69, 0]) == [3.0, 3.0]
+    assert list(kq[1][2, 0]) == [3.0, 3.0] and list(vq[1][2, 0]) == [-2.0, 4.0]
+    assert not kq[0][1:69].any() and not vq[1][:2].any()
+    only1 = fp8.gather_dequantized(k8, v8, ks, vs, table, [70, 3], requests=[1])
+    assert len(only1[0]) == 1 and np.array_equal(only1[0][0], kq[1])
+
+
+def test_gather_dequantized_equals_paged_gather_then_dequantize():
+    """On a seeded shuffled cache (partial tails, NaN-free codes, 2 KV heads):
+    the dequantising gather equals the pinned paged gather of the codes
+    followed by the pinned group dequantisation, token by token.  The scales
+    are routed through the same gather as slot indices."""
+    c = synth.decode_cache(seed=91, B=3, ctx_lens=[1, 64, 150], Hq=4, Hkv=2, D=16)
+    unused = lambda pool: np.where(pool == synth.BF16_NAN_BITS, np.uint16(0), pool)
+    k8, v8, ks, vs = fp8.quantize_kv_pool(unused(c["k_pool"]), unused(c["v_pool"]))
+    n, D = k8.shape[0], k8.shape[2]
+    kc, vc = oracle.paged_gather(k8.astype(np.uint16), v8.astype(np.uint16), c["block_table"],
+                                 c["ctx_len"])
+    slot = np.arange(n * 64, dtype=np.uint16).reshape(n, 64, 1)     # index of (block, slot)
+    si, _ = oracle.paged_gather(slot, np.swapaxes(slot, 1, 2), c["block_table"], c["ctx_len"])
+    kq, vq = fp8.gather_dequantized(k8, v8, ks, vs, c["block_table"], c["ctx_len"])
+    for b, T in enumerate(c["ctx_len"]):
+        idx = si[b, :T, :, 0].astype(np.int64)                       # [T][Hkv]
+        k_ref = fp8.fp8_e4m3_decode(kc[b, :T]) * ks.reshape(-1)[idx][..., None]
+        v_ref = fp8.fp8_e4m3_decode(vc[b, :T]) * vs.reshape(-1)[idx][..., None]
+        np.testing.assert_array_equal(kq[b], k_ref)
+        np.testing.assert_array_equal(vq[b], v_ref)
+    # and the values are the quantised versions of the tokens placed there
+    for b, T in enumerate(c["ctx_len"]):
+        x = synth.bf16_bits_to_f32(c["k_seq"][b]).astype(np.float64)
+        assert np.all(np.abs(kq[b] - x) <= 2.0 ** -4 * np.abs(x).max(axis=-1, keepdims=True))
