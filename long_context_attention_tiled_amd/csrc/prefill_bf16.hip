@@ -467,8 +467,9 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   }
   int blk_k = block_of(KA), blk_v = block_of(VA);
   // S_0 and the operand reads before the next barrier need K_0 and K_1
-  // only; K_2.., V_0.. may still fly (the first iteration's wait covers
-  // them).  Waves that issued no DMA have nothing left in flight.
+  // only, so the first barrier publishes just those; the other prologue
+  // tiles keep flying while S_0 is computed.  Waves that issued no DMA have
+  // nothing in flight.
   static_assert(KA >= 2, "K_0 and K_1 are waited for separately");
   wait_vmcnt<(KA - 2 + VA) * DPW>();
   barrier_no_wait();
@@ -477,7 +478,11 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
 #pragma unroll
     for (int i = 0; i < NPK; ++i) kpre[i] = read_k(TILE, i);
   }
-  // every wave is done with K_0 before iteration 0 refills its slot with K_KA
+  // Iteration 0 reads operands of V_0 and K_2 before its own barrier, and
+  // every wave's DMAs wrote rows of them: all prologue DMAs have landed
+  // before this barrier, which publishes them.  It also keeps iteration 0
+  // from refilling K_0's slot while a wave still reads K_0.
+  wait_vmcnt<0>();
   barrier_no_wait();
 
   // kc: K slot of tile j (= slot of K_{j+KA}, refilled in iteration j);
