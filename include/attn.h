@@ -209,7 +209,8 @@ int attn_decode_fp8(const void *q, const void *k8_pool, const void *v8_pool, con
  *   x'[i+D/2] = x[i + D/2] cos a + x[i] sin a
  * The angle is formed and range-reduced in fp64, sin/cos and the rotation
  * run in fp32, results are rounded to bf16 (nearest-even).
- * D must be even and at most 256; S = 0 is a no-op.
+ * D must be a multiple of 16 and at most 256 (ATTN_ERR_UNSUPPORTED
+ * otherwise); x must be 16-byte aligned; S = 0 is a no-op.
  */
 int rope_apply(void *x, const int32_t *positions, int S, int H, int D, float base, void *stream);
 
@@ -339,6 +340,14 @@ int attn_merge(const void *o_a, const float *lse_a, const void *o_b, const float
 
 /* Static, human-readable text for an attn_status value. */
 const char *attn_status_string(int status);
+
+/*
+ * attn_build_id — static text identifying the sources this library was
+ * built from (a hash over its kernel sources, headers and compile flags), so
+ * that a loader can refuse a build that does not match the sources it ships
+ * with.  Never NULL; "unknown" when the build did not set it.
+ */
+const char *attn_build_id(void);
 
 #ifdef __cplusplus
 }

@@ -54,6 +54,7 @@ SIGNATURES = {
                                   _vp]),
     "attn_merge": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
+    "attn_build_id": (ctypes.c_char_p, []),
     # include/attn_measure.h
     "attn_measure_mfma_rate": (_i, [_vp, _i, _i, ctypes.c_uint32, _i, _vp]),
     "attn_measure_hbm_read": (_i, [_vp, _ll, _vp, _i, _vp]),
@@ -73,19 +74,26 @@ class AttnError(RuntimeError):
 _lib = None
 
 
+BUILD_HINT = "(python -c 'import __graft_entry__ as g; g.build()')"
+
+
 def load() -> ctypes.CDLL:
-    """Load the HIP library; fails loudly when it has not been built."""
+    """Load the HIP library; fails loudly when it has not been built, or when
+    it was built from sources other than the ones next to it."""
     global _lib
     if _lib is None:
+        from . import _build
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is missing: build the HIP extension first "
-                "(python -c 'import __graft_entry__ as g; g.build()')")
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP extension first {BUILD_HINT}")
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        built, want = lib.attn_build_id().decode(), _build.source_hash()
+        if built != want:
+            raise RuntimeError(f"{LIB_PATH} was built from sources {built}, but the sources here "
+                               f"hash to {want}: rebuild it {BUILD_HINT}")
         _lib = lib
     return _lib
 

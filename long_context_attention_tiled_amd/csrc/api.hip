@@ -7,6 +7,10 @@
 #include "../../include/attn.h"
 #include "kernels.h"
 
+#ifndef LCAT_BUILD_ID
+#define LCAT_BUILD_ID "unknown"   // set by the build to the hash of the sources
+#endif
+
 namespace {
 
 constexpr int kHeadDim = 128;
@@ -91,6 +95,54 @@ bool cp_map(long long S, int N, int rank, int mode, lcat::CpMap &m, long long &n
   }
 }
 
+// Argument checks, then the workspace: `get_ws(need, &ptr)` points ptr
+// at a buffer for `need` bytes of split records, or returns an error status.
+template <class GetWs>
+int decode_common(const void *q, const void *k_pool, const void *v_pool, const float *k_scale,
+                  const float *v_scale, int fp8, int n_blocks, const int32_t *block_head,
+                  const int32_t *block_table, int max_blocks, const int32_t *ctx_len, void *o,
+                  float *lse, int B, int Hq, int Hkv, int D, int kv_head_base, float scale,
+                  int split_tokens, GetWs get_ws, int32_t *dev_status, void *stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n_blocks <= 0 || max_blocks <= 0)
+    return ATTN_ERR_SHAPE;
+  if (split_tokens < 0 || split_tokens % kBlockTokens) return ATTN_ERR_SHAPE;
+  if (D != kHeadDim || Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0) return ATTN_OK;
+  if (!q || !k_pool || !v_pool || !block_head || !block_table || !ctx_len || !o)
+    return ATTN_ERR_NULL;
+  if (fp8 && (!k_scale || !v_scale)) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return ATTN_ERR_ALIGN;
+  if (fp8 && (!aligned16(k_scale) || !aligned16(v_scale))) return ATTN_ERR_ALIGN;
+  const size_t need = attn_decode_workspace_bytes(B, Hq, D, max_blocks, split_tokens);
+  void *workspace = nullptr;
+  const int ws_status = get_ws(need, &workspace);
+  if (ws_status != ATTN_OK) return ws_status;
+  const long long n_split = split_tokens ? decode_n_split(max_blocks, split_tokens) : 0;
+  if (n_split > 0x7FFFFFFFLL) return ATTN_ERR_UNSUPPORTED;
+  lcat::DecodeParams p{};
+  p.q = q; p.k_pool = k_pool; p.v_pool = v_pool;
+  p.k_scale = k_scale; p.v_scale = v_scale; p.fp8 = fp8;
+  p.block_head = block_head; p.block_table = block_table; p.ctx_len = ctx_len;
+  p.o = o; p.lse = lse; p.ws = static_cast<float *>(workspace); p.dev_status = dev_status;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_blocks = max_blocks; p.n_blocks = n_blocks;
+  p.kv_head_base = kv_head_base; p.split_tokens = split_tokens; p.n_split = (int)n_split;
+  p.stream_waves = split_tokens ? 0 : kStreamWaves;
+  p.scale = scale;
+  return hip_status(lcat::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+// The caller's workspace: at least `need` bytes, 16-byte aligned.
+struct CallerWorkspace {
+  void *ptr;
+  size_t bytes;
+  int operator()(size_t need, void **out) const {
+    if (!ptr || bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(ptr)) return ATTN_ERR_ALIGN;
+    *out = ptr;
+    return ATTN_OK;
+  }
+};
+
 }  // namespace
 
 extern "C" {
@@ -108,6 +160,8 @@ const char *attn_status_string(int status) {
     default: return "unknown status";
   }
 }
+
+const char *attn_build_id(void) { return LCAT_BUILD_ID; }
 
 int attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int B, int S,
                  int Hq, int Hkv, int D, int dtype, int causal, float scale, void *stream) {
@@ -191,39 +245,6 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_blocks, int spl
   return (size_t)B * Hq * decode_n_split(max_blocks, split_tokens) * kDecodeRecord * sizeof(float);
 }
 
-static int decode_common(const void *q, const void *k_pool, const void *v_pool,
-                         const float *k_scale, const float *v_scale, int fp8, int n_blocks,
-                         const int32_t *block_head, const int32_t *block_table, int max_blocks,
-                         const int32_t *ctx_len, void *o, float *lse, int B, int Hq, int Hkv, int D,
-                         int kv_head_base, float scale, int split_tokens, void *workspace,
-                         size_t workspace_bytes, int32_t *dev_status, void *stream) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n_blocks <= 0 || max_blocks <= 0)
-    return ATTN_ERR_SHAPE;
-  if (split_tokens < 0 || split_tokens % kBlockTokens) return ATTN_ERR_SHAPE;
-  if (D != kHeadDim || Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
-  if (B == 0) return ATTN_OK;
-  if (!q || !k_pool || !v_pool || !block_head || !block_table || !ctx_len || !o)
-    return ATTN_ERR_NULL;
-  if (fp8 && (!k_scale || !v_scale)) return ATTN_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return ATTN_ERR_ALIGN;
-  if (fp8 && (!aligned16(k_scale) || !aligned16(v_scale))) return ATTN_ERR_ALIGN;
-  const size_t need = attn_decode_workspace_bytes(B, Hq, D, max_blocks, split_tokens);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
-  const long long n_split = split_tokens ? decode_n_split(max_blocks, split_tokens) : 0;
-  if (n_split > 0x7FFFFFFFLL) return ATTN_ERR_UNSUPPORTED;
-  lcat::DecodeParams p{};
-  p.q = q; p.k_pool = k_pool; p.v_pool = v_pool;
-  p.k_scale = k_scale; p.v_scale = v_scale; p.fp8 = fp8;
-  p.block_head = block_head; p.block_table = block_table; p.ctx_len = ctx_len;
-  p.o = o; p.lse = lse; p.ws = static_cast<float *>(workspace); p.dev_status = dev_status;
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_blocks = max_blocks; p.n_blocks = n_blocks;
-  p.kv_head_base = kv_head_base; p.split_tokens = split_tokens; p.n_split = (int)n_split;
-  p.stream_waves = split_tokens ? 0 : kStreamWaves;
-  p.scale = scale;
-  return hip_status(lcat::launch_decode(p, static_cast<hipStream_t>(stream)));
-}
-
 int attn_decode(const void *q, const void *k_pool, const void *v_pool, int n_blocks,
                 const int32_t *block_head, const int32_t *block_table, int max_blocks,
                 const int32_t *ctx_len, void *o, float *lse, int B, int Hq, int Hkv, int D,
@@ -231,7 +252,8 @@ int attn_decode(const void *q, const void *k_pool, const void *v_pool, int n_blo
                 size_t workspace_bytes, int32_t *dev_status, void *stream) {
   return decode_common(q, k_pool, v_pool, nullptr, nullptr, 0, n_blocks, block_head, block_table,
                        max_blocks, ctx_len, o, lse, B, Hq, Hkv, D, kv_head_base, scale,
-                       split_tokens, workspace, workspace_bytes, dev_status, stream);
+                       split_tokens, CallerWorkspace{workspace, workspace_bytes}, dev_status,
+                       stream);
 }
 
 int attn_decode_fp8(const void *q, const void *k8_pool, const void *v8_pool, const float *k_scale,
@@ -242,7 +264,8 @@ int attn_decode_fp8(const void *q, const void *k8_pool, const void *v8_pool, con
                     int32_t *dev_status, void *stream) {
   return decode_common(q, k8_pool, v8_pool, k_scale, v_scale, 1, n_blocks, block_head,
                        block_table, max_blocks, ctx_len, o, lse, B, Hq, Hkv, D, kv_head_base,
-                       scale, split_tokens, workspace, workspace_bytes, dev_status, stream);
+                       scale, split_tokens, CallerWorkspace{workspace, workspace_bytes},
+                       dev_status, stream);
 }
 
 int attn_kv_append_fp8(const void *k_new, const void *v_new, void *k8_pool, void *v8_pool,

@@ -49,7 +49,7 @@ def test_header_declares_the_boundary():
               "head_to_seq_permute", "seq_to_head_permute_qkv_rope", "cp_shard_tokens",
               "cp_shard", "cp_unshard", "attn_key_limits", "attn_prefill_limited", "attn_merge",
               "attn_decode_fp8", "attn_kv_quantize_fp8", "attn_kv_append_fp8",
-              "attn_status_string", "attn_measure_mfma_rate"]:
+              "attn_status_string", "attn_build_id", "attn_measure_mfma_rate"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
 
@@ -295,3 +295,9 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def test_library_matches_its_sources(lib):
+    """The loader only accepts a library built from the sources next to it."""
+    from long_context_attention_tiled_amd import _build
+    assert lib.attn_build_id().decode() == _build.source_hash()
