@@ -63,6 +63,19 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 D = 128
 
+# Seeds of every synthetic input (numpy SeedSequence for synth's generators,
+# torch.Generator for tensors drawn on the GPU).
+SEEDS = {
+    "tiny_fp32": 1,                       # synth.tiny_exact
+    "causal_gqa_32k": 2,                  # synth.causal_gqa
+    "decode_32req": 4,                    # synth.decode_cache (lengths, tables, q)
+    "decode_pools": [41, 42],             # torch: K pool, V pool
+    "relayout_64k": [31, 32, 33],         # torch: Q, K, V of buffer set r (+10 r)
+    "chunked_4x131072": [51, 52, 53],     # torch: Q, K, V
+    "cp_zigzag_64k": [61, 62, 63],        # torch: Q, K, V
+    "cpu_sample_rows": 77,                # synth.sample_rows
+}
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -157,15 +170,24 @@ def seeded_normal_bf16(torch, shape, seed):
 
 # ---------------------------------------------------------------------------
 def bench_step(torch, lcat, synth, steps, warmup):
+    """The timed step.  RoPE rotates Q and K in place, so every step (warm-up
+    included) runs on its own copy of the unrotated inputs, staged in HBM
+    before timing starts (144 MB per step): each timed step is the
+    configured workload, not a re-rotation of the previous step's output."""
     S, Hq, Hkv = 32768, 16, 2
-    d = synth.causal_gqa(seed=2, S=S, Hq=Hq, Hkv=Hkv)
-    q, k, v = dev_tensor(torch, d["q"]), dev_tensor(torch, d["k"]), dev_tensor(torch, d["v"])
+    d = synth.causal_gqa(seed=SEEDS["causal_gqa_32k"], S=S, Hq=Hq, Hkv=Hkv)
+    q0, k0, v = dev_tensor(torch, d["q"]), dev_tensor(torch, d["k"]), dev_tensor(torch, d["v"])
     pos = dev_tensor(torch, d["positions"])
-    o = torch.empty_like(q)
+    n = warmup + steps
+    qs = [q0.clone() for _ in range(n)]
+    ks = [k0.clone() for _ in range(n)]
+    del q0, k0
+    o = torch.empty_like(qs[0])
     lse = torch.empty((1, Hq, S), dtype=torch.float32, device="cuda")
     timer = EventTimer(torch)
 
-    def step(time_kernel):
+    def step(i, time_kernel):
+        q, k = qs[i], ks[i]
         lcat.rope_apply(q[0], pos)
         lcat.rope_apply(k[0], pos)
         if time_kernel:
@@ -174,25 +196,29 @@ def bench_step(torch, lcat, synth, steps, warmup):
         else:
             lcat.attn_prefill(q, k, v, causal=True, o=o, lse=lse)
 
-    for _ in range(warmup):
-        step(False)
+    for i in range(warmup):
+        step(i, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step(True)
+    for i in range(warmup, n):
+        step(i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    del qs, ks
     flops = causal_flops(1, S, Hq)
     ms_step = wall * 1e3 / steps
     k_ms = timer.mean_ms()
     achieved = flops / (k_ms * 1e-3) / 1e12
     traffic = load_traffic("prefill_kernel", "causal_gqa_32k")
-    return d, dict(
+    check = dict(d=d, o=o, lse=lse)
+    return check, dict(
         value=flops / (wall / steps) / 1e12, ms_per_step=ms_step,
         roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
                       unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
                       traffic=traffic, kernel="prefill_kernel<dense,causal>",
-                      kernel_ms=round(k_ms, 4), flop_per_launch=flops))
+                      kernel_ms=round(k_ms, 4), flop_per_launch=flops,
+                      timed_launches=f"prefill launches {warmup + 1}..{n} of this process "
+                                     f"(the first {warmup} are warm-up)"))
 
 
 def bench_mfma_rate(torch, lcat, reps=3, n_wg=1024, iters=65536):
@@ -221,10 +247,10 @@ def bench_mfma_rate(torch, lcat, reps=3, n_wg=1024, iters=65536):
 
 
 def bench_decode(torch, lcat, synth, iters=20):
-    c = synth.decode_cache(seed=4, B=32, with_content=False)
+    c = synth.decode_cache(seed=SEEDS["decode_32req"], B=32, with_content=False)
     n_blocks = c["n_blocks"]
-    k_pool = seeded_normal_bf16(torch, (n_blocks, 64, D), 41)
-    v_pool = seeded_normal_bf16(torch, (n_blocks, D, 64), 42)
+    k_pool = seeded_normal_bf16(torch, (n_blocks, 64, D), SEEDS["decode_pools"][0])
+    v_pool = seeded_normal_bf16(torch, (n_blocks, D, 64), SEEDS["decode_pools"][1])
     args = [dev_tensor(torch, c["q"]), k_pool, v_pool, dev_tensor(torch, c["block_head"]),
             dev_tensor(torch, c["block_table"]), dev_tensor(torch, c["ctx_len"])]
     B, Hq = c["q"].shape[:2]
@@ -260,10 +286,11 @@ def bench_decode(torch, lcat, synth, iters=20):
     # the same cache in FP8 (e4m3 + one fp32 scale per token for K and for V)
     k8, v8, ks, vs = lcat.attn_kv_quantize_fp8(k_pool, v_pool)
     args8 = [args[0], k8, v8, ks, vs] + args[3:]
+    o8, lse8 = torch.empty_like(o), torch.empty_like(lse)
     for _ in range(3):
-        lcat.attn_decode_fp8(*args8, workspace=ws, o=o, lse=lse)
+        lcat.attn_decode_fp8(*args8, workspace=ws, o=o8, lse=lse8)
     torch.cuda.synchronize()
-    ms8 = back_to_back_ms(torch, lambda: lcat.attn_decode_fp8(*args8, workspace=ws, o=o, lse=lse),
+    ms8 = back_to_back_ms(torch, lambda: lcat.attn_decode_fp8(*args8, workspace=ws, o=o8, lse=lse8),
                           iters)
     nbytes8 = ctx_total * c["Hkv"] * (2 * D + 8) + 2 * B * Hq * D * 2 + B * Hq * 4
     gbs8 = nbytes8 / (ms8 * 1e-3) / 1e9
@@ -272,7 +299,9 @@ def bench_decode(torch, lcat, synth, iters=20):
                             traffic=load_traffic("decode_stream_kernel", "decode_32req_fp8"),
                             frac_of_sustained_read=round(gbs8 / rd_gbs, 4),
                             speedup_vs_bf16=round(ms / ms8, 3))
-    return res
+    del k8, v8, ks, vs
+    check = dict(c=c, q=args[0], k_pool=k_pool, v_pool=v_pool, o=o, lse=lse)
+    return check, res
 
 
 def rotating(fns):
@@ -293,9 +322,10 @@ def bench_relayout_and_prefill_64k(torch, lcat, iters=20, n_sets=4):
     S = SP * S_loc
     sets = []
     for r in range(n_sets):
-        qin = seeded_normal_bf16(torch, (SP, S_loc, Hq_tot, D), 31 + 10 * r)
-        kin = seeded_normal_bf16(torch, (SP, S_loc, Hkv_tot, D), 32 + 10 * r)
-        vin = seeded_normal_bf16(torch, (SP, S_loc, Hkv_tot, D), 33 + 10 * r)
+        sq, sk, sv = (x + 10 * r for x in SEEDS["relayout_64k"])
+        qin = seeded_normal_bf16(torch, (SP, S_loc, Hq_tot, D), sq)
+        kin = seeded_normal_bf16(torch, (SP, S_loc, Hkv_tot, D), sk)
+        vin = seeded_normal_bf16(torch, (SP, S_loc, Hkv_tot, D), sv)
         qo = torch.empty((S, Hq_tot // SP, D), dtype=torch.bfloat16, device="cuda")
         ko = torch.empty((S, Hkv_tot // SP, D), dtype=torch.bfloat16, device="cuda")
         vo = torch.empty_like(ko)
@@ -387,15 +417,17 @@ def bench_relayout_and_prefill_64k(torch, lcat, iters=20, n_sets=4):
     relay_back = dict(ms=round(ms_b, 4), GBps=round(gbs_b, 1), frac_hbm=round(gbs_b / PEAK_HBM_GBS, 4),
                       frac_of_sustained_copy=round(gbs_b / cp_gbs, 4), buffer_sets=n_sets,
                       bytes=nb, workload="rank 0's O [65536][16][128] bf16 -> [4][16384][64][128]")
-    return relay, pre, relay_back
+    # o and lse are the prefill of set 0 after the fused relayout + RoPE of rank 0
+    check = dict(qin=sets[0][0], kin=sets[0][1], vin=sets[0][2], o=o, lse=lse, SP=SP)
+    return check, (relay, pre, relay_back)
 
 
 def bench_chunked(torch, lcat, synth):
     B, S, C, Hq, Hkv = 4, 131072, 8192, 16, 2
     table, tags, n_blocks = synth.chunked_block_table(B, S, C, Hkv)
-    q = seeded_normal_bf16(torch, (B, S, Hq, D), 51)
-    k = seeded_normal_bf16(torch, (B, S, Hkv, D), 52)
-    v = seeded_normal_bf16(torch, (B, S, Hkv, D), 53)
+    q = seeded_normal_bf16(torch, (B, S, Hq, D), SEEDS["chunked_4x131072"][0])
+    k = seeded_normal_bf16(torch, (B, S, Hkv, D), SEEDS["chunked_4x131072"][1])
+    v = seeded_normal_bf16(torch, (B, S, Hkv, D), SEEDS["chunked_4x131072"][2])
     k_pool = torch.empty((n_blocks, 64, D), dtype=torch.bfloat16, device="cuda")
     v_pool = torch.empty((n_blocks, D, 64), dtype=torch.bfloat16, device="cuda")
     tags_d, table_d = dev_tensor(torch, tags), dev_tensor(torch, table)
@@ -403,14 +435,15 @@ def bench_chunked(torch, lcat, synth):
     ks = [k[:, c0:c0 + C].contiguous() for c0 in range(0, S, C)]
     vs = [v[:, c0:c0 + C].contiguous() for c0 in range(0, S, C)]
     cbs = [torch.full((B,), c0, dtype=torch.int32, device="cuda") for c0 in range(0, S, C)]
-    o = torch.empty((B, C, Hq, D), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((B, Hq, C), dtype=torch.float32, device="cuda")
+    # each chunk writes its own output, as a serving engine would
+    os_ = [torch.empty((B, C, Hq, D), dtype=torch.bfloat16, device="cuda") for _ in qs]
+    lses = [torch.empty((B, Hq, C), dtype=torch.float32, device="cuda") for _ in qs]
     timer = EventTimer(torch)
     for rep in range(2):
         with timer:
             for i in range(len(qs)):
                 lcat.attn_chunked_prefill(qs[i], ks[i], vs[i], k_pool, v_pool, tags_d, table_d,
-                                          cbs[i], o=o, lse=lse)
+                                          cbs[i], o=os_[i], lse=lses[i])
         if rep == 0:
             torch.cuda.synchronize()
             timer.pairs.clear()
@@ -418,9 +451,11 @@ def bench_chunked(torch, lcat, synth):
     ms = timer.mean_ms()
     flops = causal_flops(B, S, Hq)
     tf = flops / (ms * 1e-3) / 1e12
-    return dict(ms_per_pass=round(ms, 2), TFLOPs=round(tf, 1),
-                frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4), chunks=S // C,
-                workload="4 requests x 131072 tokens, 8192-token chunks, 16 Q / 2 KV heads")
+    del qs, ks, vs, k_pool, v_pool
+    check = dict(q=q, k=k, v=v, outs=os_, lses=lses, C=C)
+    return check, dict(ms_per_pass=round(ms, 2), TFLOPs=round(tf, 1),
+                       frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4), chunks=S // C,
+                       workload="4 requests x 131072 tokens, 8192-token chunks, 16 Q / 2 KV heads")
 
 
 def bench_cp(torch, lcat, iters=3):
@@ -429,9 +464,8 @@ def bench_cp(torch, lcat, iters=3):
     position-derived limits, the partials combined by the LSE rescale), all
     shards resident."""
     S, N, Hq, Hkv, mode = 65536, 4, 16, 2, "zigzag"
-    q = seeded_normal_bf16(torch, (S, Hq, D), 61)
-    k = seeded_normal_bf16(torch, (S, Hkv, D), 62)
-    v = seeded_normal_bf16(torch, (S, Hkv, D), 63)
+    q, k, v = (seeded_normal_bf16(torch, shape, sd) for shape, sd in
+               zip(((S, Hq, D), (S, Hkv, D), (S, Hkv, D)), SEEDS["cp_zigzag_64k"]))
     shards = [(lcat.cp_shard(k, N, s_, mode), lcat.cp_shard(v, N, s_, mode)[0]) for s_ in range(N)]
     res = {}
     for rank in (0, N - 1):
@@ -480,25 +514,242 @@ def bench_cp(torch, lcat, iters=3):
     return res
 
 
-def cpu_baseline(d, target_rows=1024):
-    """fp64 oracle on a seeded sample of query rows of the step workload
-    (RoPE of those rows and of all keys, then causal attention)."""
+def bench_fixed_cost(torch, lcat, reps=10):
+    """Per-workgroup fixed cost of the dense prefill kernel: non-causal launches
+    of 4096 workgroups (B x S/32 x Hkv at 16 Q / 2 KV heads) that see 8, 16, 32
+    or 64 key tiles each, and a least-squares fit of launch time against
+    tiles per workgroup (16 rounds of 256 workgroups per launch)."""
+    Hq, Hkv = 16, 2
+    pts = []
+    for S, B in ((512, 128), (1024, 64), (2048, 32), (4096, 16)):
+        q = seeded_normal_bf16(torch, (B, S, Hq, D), 71)
+        k = seeded_normal_bf16(torch, (B, S, Hkv, D), 72)
+        v = seeded_normal_bf16(torch, (B, S, Hkv, D), 73)
+        o, lse = torch.empty_like(q), torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+        run = lambda: lcat.attn_prefill(q, k, v, causal=False, o=o, lse=lse)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        ms = back_to_back_ms(torch, run, reps)
+        flops = 4.0 * D * Hq * B * S * S
+        pts.append(dict(tiles_per_wg=S // 64, workgroups=B * (S // 32) * Hkv, ms=round(ms, 4),
+                        TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1)))
+    t = np.array([p_["tiles_per_wg"] for p_ in pts], float)
+    m = np.array([p_["ms"] for p_ in pts]) * 1e3 / (4096 / 256)   # us per round of 256
+    (fixed, per_tile), *_ = np.linalg.lstsq(np.stack([np.ones_like(t), t], 1), m, rcond=None)
+    return dict(points=pts, fixed_us_per_workgroup=round(float(fixed), 2),
+                us_per_key_tile=round(float(per_tile), 3),
+                workload="non-causal prefill, 16 Q / 2 KV heads, 4096 workgroups per launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on every configuration, on this host's cores
+# ---------------------------------------------------------------------------
+BF16_TOL = 2e-2   # |gpu - oracle| <= 2e-2 + 2e-2 |oracle| on every sampled row
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def pick(t, rows, dim=1):
+    """Rows ``rows`` (numpy indices) of a GPU tensor along ``dim``."""
+    import torch
+    return t.index_select(dim, torch.as_tensor(rows, dtype=torch.long, device=t.device))
+
+
+def host(t):
+    """torch tensor -> numpy (bf16 as uint16 bit patterns)."""
+    import torch
+    t = t.detach().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def widen_bf16(a):
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def compare(got, ref, got_lse=None, ref_lse=None):
+    """Largest error of the GPU rows against the oracle rows, and whether every
+    element is within the bf16 bar (fp32 rows: max |err| <= 1e-3)."""
+    err = np.abs(got - ref)
+    out = dict(max_abs_err=float(err.max()),
+               within_tol=bool(np.all(err <= BF16_TOL + BF16_TOL * np.abs(ref))))
+    if got_lse is not None:
+        out["max_lse_err"] = float(np.max(np.abs(got_lse - ref_lse)))
+    return out
+
+
+def timed(fn):
+    t0 = time.perf_counter()
+    r = fn()
+    return r, time.perf_counter() - t0
+
+
+def rate(flops, sec, full_pairs, sample_pairs):
+    return dict(seconds=round(sec, 3), TFLOPs=round(flops / sec / 1e12, 6),
+                full_config_seconds_extrapolated=round(sec * full_pairs / sample_pairs, 1))
+
+
+def cpu_tiny(lcat, torch):
+    """Tiny fp32 case in full: 256 queries and keys, one head, non-causal."""
     import oracle
     import synth
+    d = synth.tiny_exact(seed=SEEDS["tiny_fp32"])
+    (ref, ref_lse), sec = timed(lambda: oracle.attention(d["q"], d["k"], d["v"], d["scale"]))
+    o, lse = lcat.attn_prefill(dev_tensor(torch, d["q"]), dev_tensor(torch, d["k"]),
+                               dev_tensor(torch, d["v"]), causal=False, scale=d["scale"])
+    got = o.cpu().numpy().astype(np.float64)
+    pairs = 256 * 256
+    r = rate(4.0 * 64 * pairs, sec, pairs, pairs)
+    err = float(np.abs(got - ref).max())
+    r.update(rows="all 256", max_abs_err=err, within_tol=err <= 1e-3,
+             max_lse_err=float(np.abs(lse.cpu().numpy() - ref_lse).max()))
+    return r
+
+
+def cpu_prefill_32k(chk, rows_n=512):
+    """Causal GQA prefill at 32768: RoPE of the sampled query rows and of all
+    keys, then causal attention of those rows."""
+    import oracle
+    import synth
+    d = chk["d"]
     S, Hq = d["q"].shape[1], d["q"].shape[2]
-    rows = synth.sample_rows(77, S, target_rows)
+    rows = synth.sample_rows(SEEDS["cpu_sample_rows"], S, rows_n, forced=(0, 1, 255, 256, S - 1))
     pos = d["positions"].astype(np.int64)
+
+    def run():
+        qr = oracle.rope(d["q"][0, rows], pos[rows])[None]
+        kr = oracle.rope(d["k"][0], pos)[None]
+        return oracle.attention_rows(qr, kr, oracle.widen(d["v"]), (rows + 1)[None], d["scale"])
+    (ref, ref_lse), sec = timed(run)
+    sample_pairs = float(np.sum(rows + 1))
+    r = rate(4.0 * D * Hq * sample_pairs, sec, S * (S + 1) / 2, sample_pairs)
+    r.update(rows=f"{rows.size} of the {S} query rows x {Hq} heads")
+    r.update(compare(widen_bf16(host(pick(chk["o"], rows))), ref,
+                     host(pick(chk["lse"], rows, 2)), ref_lse))
+    return r
+
+
+def cpu_pipeline_64k(chk, rows_n=512):
+    """64K pipeline, rank 0: relayout of the [4][16384][64|8][128] inputs,
+    RoPE at positions 0..65535, causal attention of the sampled rows."""
+    import oracle
+    import synth
+    qin, kin, vin = host(chk["qin"]), host(chk["kin"]), host(chk["vin"])
+    S = qin.shape[0] * qin.shape[1]
+    rows = synth.sample_rows(SEEDS["cpu_sample_rows"] + 1, S, rows_n,
+                             forced=(0, 1, 16383, 16384, 32767, 32768, 49151, 49152, S - 1))
+    pos = np.arange(S, dtype=np.int64)
+
+    def run():
+        q, k, v = (oracle.permute(x, 0) for x in (qin, kin, vin))
+        qr = oracle.rope(q[rows], pos[rows])[None]
+        kr = oracle.rope(k, pos)[None]
+        return oracle.attention_rows(qr, kr, v[None], (rows + 1)[None], 1.0 / np.sqrt(D))
+    (ref, ref_lse), sec = timed(run)
+    Hq = ref.shape[2]
+    sample_pairs = float(np.sum(rows + 1))
+    r = rate(4.0 * D * Hq * sample_pairs, sec, S * (S + 1) / 2, sample_pairs)
+    r.update(rows=f"{rows.size} of the {S} query rows x {Hq} heads")
+    r.update(compare(widen_bf16(host(pick(chk["o"], rows))), ref,
+                     host(pick(chk["lse"], rows, 2)), ref_lse))
+    return r
+
+
+def cpu_decode(chk):
+    """Paged decode, all 32 requests x 16 heads: gather of each request's
+    cache, then attention of its one query over all ctx_len keys."""
+    import oracle
+    c = chk["c"]
+    kp, vp, q = host(chk["k_pool"]), host(chk["v_pool"]), host(chk["q"])
+    ctx = c["ctx_len"]
+
+    def run():
+        ks, vs = oracle.paged_gather(kp, vp, c["block_table"], ctx)
+        return oracle.decode_attention(q, [ks[b] for b in range(len(ctx))],
+                                       [vs[b] for b in range(len(ctx))], ctx, c["scale"])
+    (ref, ref_lse), sec = timed(run)
+    pairs = float(np.sum(ctx))
+    Hq = q.shape[1]
+    r = rate(4.0 * D * Hq * pairs, sec, pairs, pairs)
+    r.update(rows=f"all {len(ctx)} requests x {Hq} heads")
+    r.update(compare(widen_bf16(host(chk["o"])), ref, host(chk["lse"]), ref_lse))
+    return r
+
+
+def cpu_chunked(chk, rows_per_req=64):
+    """Chunked prefill, 4 x 131072: causal attention of sampled rows of every
+    request over the full sequence (what the chunks compute, by definition)."""
+    import oracle
+    import synth
+    C = chk["C"]
+    B, S, Hq = chk["q"].shape[:3]
+    forced = [r for c0 in range(C, S, C) for r in (c0 - 1, c0)] + [0, S - 1]
+    rows = synth.sample_rows(SEEDS["cpu_sample_rows"] + 2, S, rows_per_req, forced=forced)
+    k, v = host(chk["k"]), host(chk["v"])
+    qs = host(pick(chk["q"], rows))
+
+    def run():
+        return oracle.attention_rows(qs, k, v, np.broadcast_to(rows + 1, (B, rows.size)),
+                                     1.0 / np.sqrt(D))
+    (ref, ref_lse), sec = timed(run)
+    got = np.stack([widen_bf16(host(chk["outs"][r // C][:, r % C])) for r in rows], axis=1)
+    got_lse = np.stack([host(chk["lses"][r // C][:, :, r % C]) for r in rows], axis=2)
+    sample_pairs = float(B * np.sum(rows + 1))
+    r = rate(4.0 * D * Hq * sample_pairs, sec, B * S * (S + 1) / 2, sample_pairs)
+    r.update(rows=f"{rows.size} of {S} per request x {B} requests x {Hq} heads, "
+                  f"incl. every chunk boundary")
+    r.update(compare(got, ref, got_lse, ref_lse))
+    return r
+
+
+def cpu_baseline(lcat, torch, checks):
+    """The fp64 oracle timed on a bounded sample of each configuration, on all
+    host cores in this process's affinity mask; each sample's GPU rows from
+    the legs above are checked against it."""
+    import oracle
+    cfg = {}
     t0 = time.perf_counter()
-    qr = oracle.rope(d["q"][0, rows], pos[rows])[None]
-    kr = oracle.rope(d["k"][0], pos)[None]
-    oracle.attention_rows(qr, kr, oracle.widen(d["v"]), (rows + 1)[None], d["scale"])
-    dt = time.perf_counter() - t0
-    flops = 4.0 * D * Hq * float(np.sum(rows + 1))
-    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=oracle.num_threads(),
-                kind="oracle", seconds=round(dt, 2),
-                sample=f"{rows.size} seeded query rows x {Hq} heads of the seq-32768 causal "
-                       f"workload ({flops:.3g} algorithmic FLOP), fp64, incl. RoPE of those rows "
-                       f"and all keys")
+    cfg["tiny_fp32"] = cpu_tiny(lcat, torch)
+    if "step" in checks:
+        cfg["causal_gqa_32k"] = cpu_prefill_32k(checks["step"])
+    if "relayout" in checks:
+        cfg["pipeline_64k"] = cpu_pipeline_64k(checks["relayout"])
+    if "decode" in checks:
+        cfg["decode_32req"] = cpu_decode(checks["decode"])
+    if "chunked" in checks:
+        cfg["chunked_4x131072"] = cpu_chunked(checks["chunked"])
+    total = time.perf_counter() - t0
+    head = cfg.get("causal_gqa_32k", cfg["tiny_fp32"])
+    return dict(value=head["TFLOPs"], unit="TFLOP/s", cores=oracle.num_threads(), kind="oracle",
+                cpu_model=cpu_model(), seconds_total=round(total, 1),
+                sample=(f"{head['rows']} of the seq-32768 causal GQA step workload, "
+                        "fp64, incl. RoPE of those rows and all keys; per-configuration samples, "
+                        "extrapolated full-configuration times and GPU-vs-oracle errors on the "
+                        "same rows under 'configs'"),
+                all_within_tol=all(c.get("within_tol", True) for c in cfg.values()),
+                configs=cfg)
+
+
+def git_sha():
+    """Commit of the working tree, when it is a git checkout (None otherwise)."""
+    import subprocess
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                           timeout=10)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return (r.stdout.strip() or None) if r.returncode == 0 else None
 
 
 def main():
@@ -508,7 +759,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="time only the step workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "decode", "relayout", "chunked", "cp", "mfma"],
+    ap.add_argument("--only", choices=["step", "decode", "relayout", "chunked", "cp", "mfma",
+                                       "fixed_cost"],
                     help="run a single leg (for profiling); prints its own JSON object")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -525,23 +777,27 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    lcat.load_library()
+    lib = lcat.load_library()
+    build_id = lib.attn_build_id().decode()
     if args.only and args.only != "step":
         log(f"bench: only {args.only}")
         if args.only == "decode":
-            res = bench_decode(torch, lcat, synth)
+            res = bench_decode(torch, lcat, synth)[1]
         elif args.only == "relayout":
-            res = bench_relayout_and_prefill_64k(torch, lcat)
+            res = bench_relayout_and_prefill_64k(torch, lcat)[1]
         elif args.only == "cp":
             res = bench_cp(torch, lcat)
         elif args.only == "mfma":
             res = bench_mfma_rate(torch, lcat)
+        elif args.only == "fixed_cost":
+            res = bench_fixed_cost(torch, lcat)
         else:
-            res = bench_chunked(torch, lcat, synth)
-        print(json.dumps({args.only: res}), flush=True)
+            res = bench_chunked(torch, lcat, synth)[1]
+        print(json.dumps({args.only: res, "build_id": build_id}), flush=True)
         return
     log("bench: causal GQA prefill step (seq 32768)")
-    d, step = bench_step(torch, lcat, synth, args.steps, args.warmup)
+    checks = {}
+    checks["step"], step = bench_step(torch, lcat, synth, args.steps, args.warmup)
     out = {
         "metric": METRIC, "value": round(step["value"], 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step["ms_per_step"], 4),
@@ -551,6 +807,7 @@ def main():
                                "seq 32768, 16 Q / 2 KV heads, head_dim 128",
                    "global_batch": 1, "seq_len": 32768, "parallelism": "single GPU"},
         "roofline": step["roofline"],
+        "seeds": SEEDS, "build_id": build_id, "git_sha": git_sha(),
     }
     if not args.no_extra and not args.only:
         log("bench: sustained MFMA rate")
@@ -560,17 +817,17 @@ def main():
         out["roofline"]["frac_of_sustained_lds"] = round(
             out["roofline"]["achieved"] / out["mfma_sustained"]["a_from_lds"]["tflops"], 4)
         log("bench: decode")
-        out["decode"] = bench_decode(torch, lcat, synth)
+        checks["decode"], out["decode"] = bench_decode(torch, lcat, synth)
         log("bench: relayout + prefill 64k")
-        out["relayout"], out["prefill_64k"], out["relayout_back"] = \
+        checks["relayout"], (out["relayout"], out["prefill_64k"], out["relayout_back"]) = \
             bench_relayout_and_prefill_64k(torch, lcat)
         log("bench: chunked prefill")
-        out["chunked_prefill"] = bench_chunked(torch, lcat, synth)
+        checks["chunked"], out["chunked_prefill"] = bench_chunked(torch, lcat, synth)
         log("bench: context parallelism (zigzag, 4 ranks, 64k)")
         out["cp_zigzag_64k"] = bench_cp(torch, lcat)
     if not args.no_cpu_baseline and not args.only:
-        log("bench: cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(d)
+        log("bench: cpu baseline (oracle) and GPU-vs-oracle check of the sampled rows")
+        out["cpu_baseline"] = cpu_baseline(lcat, torch, checks)
     print(json.dumps(out), flush=True)
 
 
