@@ -19,7 +19,8 @@
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
  *    never allocates or frees device memory and keeps no mutable state, so
- *    calls are thread-safe.  `stream` is a hipStream_t passed as void*
+ *    calls are thread-safe.  (attn_decode_noalloc is the one exception: it
+ *    uses a fixed device array of the library, see there.)  `stream` is a hipStream_t passed as void*
  *    (NULL = the default stream).  Every call only enqueues work on `stream`
  *    and returns without synchronising.  Grid sizes come from host arguments
  *    only; device arrays (ctx_before, ctx_len, tables) are read on the device.
@@ -61,7 +62,8 @@ enum attn_status {
   ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ATTN_ERR_UNSUPPORTED = 5, /* valid but not implemented (e.g. D != 128 on a bf16 path) */
   ATTN_ERR_WORKSPACE = 6,   /* decode workspace missing or too small */
-  ATTN_ERR_HIP = 7          /* the HIP runtime rejected a launch */
+  ATTN_ERR_HIP = 7,         /* the HIP runtime rejected a launch */
+  ATTN_ERR_SCRATCH = 8      /* attn_decode_noalloc: more than ATTN_NOALLOC_SCRATCH_BYTES needed */
 };
 
 enum attn_dtype { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 };
@@ -156,6 +158,31 @@ int attn_decode(const void *q, const void *k_pool, const void *v_pool, int n_blo
 
 /* Workspace bytes attn_decode needs (0 on invalid arguments). */
 size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_blocks, int split_tokens);
+
+/*
+ * attn_decode_noalloc — attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, and the same
+ * outputs (bit for bit: the same kernels run).  The split records go to a
+ * fixed device array of the library, one per GPU, of
+ * ATTN_NOALLOC_SCRATCH_BYTES bytes, which each GPU holds from the first call
+ * on it until the process ends.  A call whose records need more
+ * (attn_decode_workspace_bytes(B, Hq, D, max_blocks, split_tokens) above the
+ * maximum; with split_tokens = 0 that is (768 + B) * Hq * 528 bytes) returns
+ * ATTN_ERR_SCRATCH and enqueues nothing.  No part of the array needs to start
+ * at zero.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); the first call on a GPU looks up that GPU's copy of the
+ * array.  Every call on one GPU shares its array: calls that overlap on one
+ * GPU (on different streams, or from different threads without ordering)
+ * race on it and their outputs are undefined; calls ordered on one stream
+ * are safe.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16 << 20)
+int attn_decode_noalloc(const void *q, const void *k_pool, const void *v_pool, int n_blocks,
+                        const int32_t *block_head, const int32_t *block_table, int max_blocks,
+                        const int32_t *ctx_len, void *o, float *lse, int B, int Hq, int Hkv, int D,
+                        int kv_head_base, float scale, int split_tokens, int32_t *dev_status,
+                        void *stream);
 
 /*
  * FP8 KV cache ([ULY] §5.4 keeps the cache quantised in groups; FA3's FP8

@@ -211,6 +211,39 @@ def attn_decode(q, k_pool, v_pool, block_head, block_table, ctx_len, kv_head_bas
     return o, lse
 
 
+def attn_decode_noalloc(q, k_pool, v_pool, block_head, block_table, ctx_len, kv_head_base=0,
+                        scale=None, split_tokens=0, o=None, lse=None, dev_status=None,
+                        stream=None):
+    """:func:`attn_decode` with the split records in the library's fixed device
+    array instead of a workspace: the C call allocates nothing.  Pass ``o`` and
+    ``lse`` to allocate nothing here either.  Returns ``(o, lse)``."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    B, Hq, D = q.shape
+    n_blocks = k_pool.shape[0]
+    _need(k_pool, "k_pool", torch.bfloat16, (n_blocks, BLOCK_TOKENS, D))
+    _need(v_pool, "v_pool", torch.bfloat16, (n_blocks, D, BLOCK_TOKENS))
+    _need(block_head, "block_head", torch.int32, (n_blocks,))
+    _need(block_table, "block_table", torch.int32)
+    Hkv, max_blocks = block_table.shape[1], block_table.shape[2]
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][Hkv][max_blocks]")
+    _need(ctx_len, "ctx_len", torch.int32, (B,))
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, q.shape)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, (B, Hq))
+    scale = float(D ** -0.5) if scale is None else float(scale)
+    st = _lib.load().attn_decode_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), n_blocks, _ptr(block_head), _ptr(block_table),
+        max_blocks, _ptr(ctx_len), _ptr(o), _ptr(lse), B, Hq, Hkv, D, int(kv_head_base), scale,
+        int(split_tokens), _ptr(dev_status), _stream(stream))
+    _lib.check("attn_decode_noalloc", st)
+    return o, lse
+
+
 def attn_kv_quantize_fp8(k_pool, v_pool, k8_pool=None, v8_pool=None, k_scale=None, v_scale=None,
                          stream=None):
     """bf16 pools -> (k8_pool, v8_pool, k_scale, v_scale): e4m3 bytes (uint8)

@@ -10,6 +10,8 @@ LIB_PATH = os.path.join(PKG, "libattn.so")
 
 # enum attn_status / attn_dtype / attn_dev_status
 ATTN_OK = 0
+ATTN_ERR_SCRATCH = 8
+ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20
 ATTN_DTYPE_F32 = 0
 ATTN_DTYPE_BF16 = 1
 ATTN_DEV_OK = 0
@@ -34,6 +36,8 @@ SIGNATURES = {
     "attn_decode": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                          _i, _vp, _sz, _vp, _vp]),
     "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "attn_decode_noalloc": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i,
+                                 _i, _f, _i, _vp, _vp]),
     "attn_decode_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i,
                              _i, _i, _f, _i, _vp, _sz, _vp, _vp]),
     "attn_kv_quantize_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp]),

@@ -4,6 +4,8 @@
 // in include/attn.h.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "kernels.h"
 
@@ -24,6 +26,47 @@ constexpr int kDecodeRecord = 132;          // floats per decode split record
 constexpr int kStreamWaves = 768;
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- fixed device scratch of attn_decode_noalloc ---------------------------
+// The split records of the decode live in `scratch` (below); its device
+// address is resolved once per device, with that device current, and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];   // address of each device's copy, once resolved
+
+}  // namespace
+
+// One copy per GPU the library runs on, held until the process ends.  In host
+// code this name is only a handle for hipGetSymbolAddress: kernels receive
+// the address that call returns.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the device that runs `stream`.
+int scratch_address(hipStream_t stream, void **out) {
+  int dev = 0, cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_HIP;
+  if (stream) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return ATTN_ERR_HIP;
+    dev = d;
+  } else {
+    dev = cur;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_HIP;
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr) return ATTN_ERR_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return ATTN_OK;
+}
 
 // No relayout output may overlap any input or another output.
 bool qkv_disjoint(const void *const in[3], void *const out[3], const int H[3], int SP, int S_loc,
@@ -157,6 +200,8 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_UNSUPPORTED: return "configuration not supported";
     case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP runtime error";
+    case ATTN_ERR_SCRATCH:
+      return "call needs more decode scratch than the fixed device array of attn_decode_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -254,6 +299,22 @@ int attn_decode(const void *q, const void *k_pool, const void *v_pool, int n_blo
                        max_blocks, ctx_len, o, lse, B, Hq, Hkv, D, kv_head_base, scale,
                        split_tokens, CallerWorkspace{workspace, workspace_bytes}, dev_status,
                        stream);
+}
+
+int attn_decode_noalloc(const void *q, const void *k_pool, const void *v_pool, int n_blocks,
+                        const int32_t *block_head, const int32_t *block_table, int max_blocks,
+                        const int32_t *ctx_len, void *o, float *lse, int B, int Hq, int Hkv, int D,
+                        int kv_head_base, float scale, int split_tokens, int32_t *dev_status,
+                        void *stream) {
+  // The records go to this device's `scratch`: no allocation, and nothing
+  // in it needs clearing (the merge reads only records this call writes).
+  auto fixed_scratch = [stream](size_t need, void **out) -> int {
+    if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+    return scratch_address(static_cast<hipStream_t>(stream), out);
+  };
+  return decode_common(q, k_pool, v_pool, nullptr, nullptr, 0, n_blocks, block_head, block_table,
+                       max_blocks, ctx_len, o, lse, B, Hq, Hkv, D, kv_head_base, scale,
+                       split_tokens, fixed_scratch, dev_status, stream);
 }
 
 int attn_decode_fp8(const void *q, const void *k8_pool, const void *v8_pool, const float *k_scale,

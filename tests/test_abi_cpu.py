@@ -49,7 +49,7 @@ def test_header_declares_the_boundary():
               "head_to_seq_permute", "seq_to_head_permute_qkv_rope", "cp_shard_tokens",
               "cp_shard", "cp_unshard", "attn_key_limits", "attn_prefill_limited", "attn_merge",
               "attn_decode_fp8", "attn_kv_quantize_fp8", "attn_kv_append_fp8",
-              "attn_status_string", "attn_build_id", "attn_measure_mfma_rate"]:
+              "attn_status_string", "attn_build_id", "attn_decode_noalloc", "attn_measure_mfma_rate"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
 
@@ -133,6 +133,30 @@ def test_decode_validation(lib):
     assert call(ws=NUL) == WS
     assert call(wsb=need - 1) == WS
     assert call(ws=MIS) == ALIGN
+
+
+def test_decode_noalloc_validation(lib):
+    """The entry point without a workspace checks its arguments like
+    attn_decode, and rejects a call whose split records exceed the fixed
+    device array (ATTN_ERR_SCRATCH) before any HIP call."""
+    f = lib.attn_decode_noalloc
+    SCRATCH = 8
+
+    def call(B=32, Hq=16, Hkv=2, D=128, split=0, max_blocks=2048, q=A16):
+        return f(q, A16, A16, 100, A16, A16, max_blocks, A16, A16, NUL, B, Hq, Hkv, D, 0, 0.1,
+                 split, NUL, S0)
+
+    assert call(split=100) == SHAPE
+    assert call(Hq=15) == SHAPE
+    assert call(D=64) == UNSUP
+    assert call(q=NUL) == NULL
+    assert _lib.ATTN_NOALLOC_SCRATCH_BYTES == 16 << 20
+    # automatic splits: (768 + B) * Hq * 528 bytes; 16 heads fit up to B = 1217
+    assert lib.attn_decode_workspace_bytes(1218, 16, 128, 2048, 0) > 16 << 20
+    assert call(B=1218) == SCRATCH
+    # fixed splits of 64 keys over 2048 blocks: 32 * 16 * 2048 records, far too many
+    assert call(split=64) == SCRATCH
+    assert lcat.attn_status_string(SCRATCH).startswith("call needs more decode scratch")
 
 
 def test_rope_and_permute_validation(lib):
