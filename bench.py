@@ -29,6 +29,8 @@ The same JSON line also carries, each measured in this run:
                   RoPE on Q and K;
   relayout_back   the reverse exchange: that rank's attention output
                   [65536][16][128] back to its head slice of the shards;
+  rope            rope_apply on the step's Q and K with cold buffers, against
+                  an in-place copy of the same bytes;
   prefill_64k     the relayout + RoPE + causal prefill pipeline at 65536,
                   with separate and with fused relayout + RoPE;
   chunked_prefill 4 requests x 131072 tokens in 8192-token chunks;
@@ -422,6 +424,49 @@ def bench_relayout_and_prefill_64k(torch, lcat, iters=20, n_sets=4):
     return check, (relay, pre, relay_back)
 
 
+def bench_rope(torch, lcat, iters=30, n_sets=6):
+    """rope_apply on the 32K step's Q [32768][16][128] and K [32768][2][128]
+    bf16, in place, cycling through ``n_sets`` buffers (768 MB of Q, so no
+    call finds its data in the last-level cache); against an in-place copy of
+    the same bytes (the yardstick for a pass that rewrites its input) and a
+    copy into a separate buffer."""
+    S = 32768
+    pos = torch.arange(S, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, H in (("q", 16), ("k", 2)):
+        xs = [seeded_normal_bf16(torch, (S, H, D), 81 + i) for i in range(n_sets)]
+        run = rotating([lambda x=x: lcat.rope_apply(x, pos) for x in xs])
+        for _ in range(n_sets):
+            run()
+        torch.cuda.synchronize()
+        ms = back_to_back_ms(torch, run, iters)
+        nb = 2 * S * H * D * 2
+        gbs = nb / (ms * 1e-3) / 1e9
+        res[name] = dict(us=round(ms * 1e3, 2), GBps=round(gbs, 1),
+                         frac_hbm=round(gbs / PEAK_HBM_GBS, 4), bytes=nb,
+                         shape=f"[{S}][{H}][{D}] bf16, positions 0..{S - 1}")
+        if name == "q":
+            flat = [x.view(-1) for x in xs]
+            cp_in = rotating([lambda f=f: lcat.measure_hbm_copy(f, f) for f in flat])
+            for _ in range(n_sets):
+                cp_in()
+            torch.cuda.synchronize()
+            ms_in = back_to_back_ms(torch, cp_in, iters)
+            dst = torch.empty_like(flat[0])
+            cp_out = rotating([lambda f=f: lcat.measure_hbm_copy(f, dst) for f in flat])
+            ms_out = back_to_back_ms(torch, cp_out, iters)
+            in_gbs, out_gbs = nb / (ms_in * 1e-3) / 1e9, nb / (ms_out * 1e-3) / 1e9
+            res["copy_in_place"] = dict(GBps=round(in_gbs, 1),
+                                        frac_hbm=round(in_gbs / PEAK_HBM_GBS, 4),
+                                        kernel="hbm_copy_kernel with dst == src")
+            res["copy_separate"] = dict(GBps=round(out_gbs, 1),
+                                        frac_hbm=round(out_gbs / PEAK_HBM_GBS, 4))
+            res["q"]["frac_of_in_place_copy"] = round(gbs / in_gbs, 4)
+        del xs
+    res["buffer_sets"] = n_sets
+    return res
+
+
 def bench_chunked(torch, lcat, synth):
     B, S, C, Hq, Hkv = 4, 131072, 8192, 16, 2
     table, tags, n_blocks = synth.chunked_block_table(B, S, C, Hkv)
@@ -760,7 +805,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="time only the step workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["step", "decode", "relayout", "chunked", "cp", "mfma",
-                                       "fixed_cost"],
+                                       "fixed_cost", "rope"],
                     help="run a single leg (for profiling); prints its own JSON object")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -791,6 +836,8 @@ def main():
             res = bench_mfma_rate(torch, lcat)
         elif args.only == "fixed_cost":
             res = bench_fixed_cost(torch, lcat)
+        elif args.only == "rope":
+            res = bench_rope(torch, lcat)
         else:
             res = bench_chunked(torch, lcat, synth)[1]
         print(json.dumps({args.only: res, "build_id": build_id}), flush=True)
@@ -816,6 +863,8 @@ def main():
             out["roofline"]["achieved"] / out["mfma_sustained"]["tflops"], 4)
         out["roofline"]["frac_of_sustained_lds"] = round(
             out["roofline"]["achieved"] / out["mfma_sustained"]["a_from_lds"]["tflops"], 4)
+        log("bench: rope_apply")
+        out["rope"] = bench_rope(torch, lcat)
         log("bench: decode")
         checks["decode"], out["decode"] = bench_decode(torch, lcat, synth)
         log("bench: relayout + prefill 64k")

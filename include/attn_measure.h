@@ -62,7 +62,9 @@ long long attn_measure_hbm_read_bytes(long long bytes, int waves);
 /*
  * attn_measure_hbm_copy — dst[0, bytes) = src[0, bytes) with 16-byte loads
  * and non-temporal 16-byte stores, 4 per thread; bytes a positive multiple
- * of 16, both pointers 16-byte aligned, no overlap (ATTN_MEASURE_ERR_SHAPE).
+ * of 16, both pointers 16-byte aligned.  dst == src is allowed (an in-place
+ * pass: the yardstick for kernels that rewrite their input, such as
+ * rope_apply); any other overlap is ATTN_MEASURE_ERR_SHAPE.
  */
 int attn_measure_hbm_copy(const void *src, void *dst, long long bytes, void *stream);
 

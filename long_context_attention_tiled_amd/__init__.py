@@ -595,7 +595,8 @@ def measure_hbm_read(buf, waves=4096, out=None, stream=None):
 
 def measure_hbm_copy(src, dst, stream=None):
     """Enqueue a streaming copy of ``src`` into ``dst`` (same byte size,
-    16-byte aligned, not overlapping); returns the bytes copied."""
+    16-byte aligned; ``dst`` may be ``src`` itself, any other overlap is
+    refused); returns the bytes copied."""
     _need(src, "src")
     _need(dst, "dst")
     nbytes = src.numel() * src.element_size()

@@ -140,8 +140,8 @@ __global__ __launch_bounds__(64) void hbm_read_kernel(const u32x4 *__restrict__ 
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
 
-__global__ __launch_bounds__(kCopyThreads) void hbm_copy_kernel(const u32x4 *__restrict__ in,
-                                                               u32x4 *__restrict__ out,
+// in == out is allowed: each thread reads its units before it writes them.
+__global__ __launch_bounds__(kCopyThreads) void hbm_copy_kernel(const u32x4 *in, u32x4 *out,
                                                                long long n_units) {
   const long long base = (long long)blockIdx.x * (kCopyThreads * kCopyUnroll) + threadIdx.x;
   u32x4 v[kCopyUnroll];
@@ -184,7 +184,7 @@ extern "C" int attn_measure_hbm_copy(const void *src, void *dst, long long bytes
     return ATTN_MEASURE_ERR_ALIGN;
   const char *s = static_cast<const char *>(src);
   const char *d = static_cast<const char *>(dst);
-  if (s < d + bytes && d < s + bytes) return ATTN_MEASURE_ERR_SHAPE;   // overlap
+  if (s != d && s < d + bytes && d < s + bytes) return ATTN_MEASURE_ERR_SHAPE;   // overlap
   const long long n_units = bytes / 16;
   const long long per_wg = lcat::kCopyThreads * lcat::kCopyUnroll;
   const long long n_wg = (n_units + per_wg - 1) / per_wg;

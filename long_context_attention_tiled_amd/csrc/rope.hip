@@ -4,7 +4,9 @@
 //
 // A workgroup handles a few consecutive tokens: it builds theta once and the
 // (cos, sin) table of those tokens in LDS (each angle once, shared by all
-// heads), then streams the heads with 16-byte loads and stores.
+// heads), then streams the heads with 16-byte loads and non-temporal 16-byte
+// stores.  Many small workgroups stream HBM faster here than fewer ones that
+// each walk several token groups with their next loads issued ahead.
 #include "device.h"
 #include "kernels.h"
 #include "rope_math.h"
@@ -12,7 +14,7 @@
 namespace lcat {
 namespace {
 
-constexpr int NT = 256;
+constexpr int NT = 128;
 constexpr int UPT = 2;            // items per thread and batch
 constexpr int MAX_TABLE = 4096;   // (token, frequency) pairs per workgroup
 
@@ -71,8 +73,8 @@ __global__ __launch_bounds__(NT) void rope_kernel(bf16 *__restrict__ x,
         bf16 *row = row_of(it, c, t);
         bf16x8 nlo, nhi;
         rope_rotate8(lo[u], hi[u], &cs[t * half + 8 * c], nlo, nhi);
-        st_global_16(row + 8 * c, as_u32x4(nlo));
-        st_global_16(row + half + 8 * c, as_u32x4(nhi));
+        __builtin_nontemporal_store(as_u32x4(nlo), reinterpret_cast<u32x4 *>(row + 8 * c));
+        __builtin_nontemporal_store(as_u32x4(nhi), reinterpret_cast<u32x4 *>(row + half + 8 * c));
       }
     }
   }

@@ -253,8 +253,8 @@ def test_decode_fp8_32_requests():
     """FP8-cache decode at the 32-request shape, in the launch configuration
     the benchmark times (equal-share split): seeded e4m3 codes (exponent
     fields 3..10, random signs) and per-token scales for every cached token,
-    the NaN code and NaN scales in unused slots; four sampled requests (all
-    16 heads, whole contexts) against the oracle over the dequantised cache."""
+    the NaN code and NaN scales in unused slots; every request (all 16
+    heads, whole contexts) against the oracle over the dequantised cache."""
     from oracle import fp8 as ofp8
     log("C4 fp8: generating cache")
     c = synth.decode_cache(seed=4, B=32, with_content=False)
@@ -289,14 +289,17 @@ def test_decode_fp8_32_requests():
                                   dev_status=st)
     torch.cuda.synchronize()
     assert st.item() == 0
-    sel = sorted(set(np.random.default_rng(931).choice(32, 3, replace=False).tolist())
-                 | {int(np.argmax(c["ctx_len"]))})
-    log(f"C4 fp8: oracle on requests {sel}")
-    kq, vq = ofp8.gather_dequantized(k8, v8, ks, vs, table, c["ctx_len"], requests=sel)
-    ref, ref_lse = oracle.decode_attention(c["q"][sel], kq, vq, c["ctx_len"][sel], c["scale"])
-    e, r = assert_attention_close(to_np64(o)[sel], ref, lse.cpu().numpy()[sel], ref_lse,
-                                  what="C4 fp8")
-    log(f"C4 fp8: max abs {e:.3g} rel-L2 {r:.3g}")
+    got, got_lse = to_np64(o), lse.cpu().numpy()
+    log("C4 fp8: oracle on all 32 requests, one at a time")
+    worst = (0.0, 0.0)
+    for b in range(32):
+        kq, vq = ofp8.gather_dequantized(k8, v8, ks, vs, table, c["ctx_len"], requests=[b])
+        ref, ref_lse = oracle.decode_attention(c["q"][b:b + 1], kq, vq, c["ctx_len"][b:b + 1],
+                                               c["scale"])
+        e, r = assert_attention_close(got[b:b + 1], ref, got_lse[b:b + 1], ref_lse,
+                                      what=f"C4 fp8 request {b}")
+        worst = (max(worst[0], e), max(worst[1], r))
+    log(f"C4 fp8: max abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}")
 
 
 def test_chunked_prefill_4x131072():
@@ -321,11 +324,11 @@ def test_chunked_prefill_4x131072():
         lse[:, :, c0:c0 + C] = lc
     torch.cuda.synchronize()
     assert st.item() == 0
-    # >= 512 sampled rows per head across the 4 requests (128 seeded rows per
-    # request), plus every chunk boundary 8192c-1 / 8192c spread over requests
+    # 512 seeded rows per request and head, plus every chunk boundary
+    # 8192c-1 / 8192c in every request
     boundaries = [C * i + j for i in range(1, S // C) for j in (-1, 0)]
     for b in range(B):
-        rows = synth.sample_rows(55 + b, S, 128, forced_rows(S, boundaries[b::B]))
+        rows = synth.sample_rows(55 + b, S, N_SAMPLE, forced_rows(S, boundaries))
         idx = torch.from_numpy(rows).cuda()
         log(f"C5: oracle request {b}: {rows.size} rows x 16 heads")
         ref, ref_lse = oracle.attention(d["q"][b:b + 1], d["k"][b:b + 1], d["v"][b:b + 1],

@@ -807,3 +807,7 @@ def test_measure_hbm_read_and_copy():
     assert lcat.measure_hbm_copy(src, dst) == (1 << 20) + 48
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+    keep = src.clone()
+    lcat.measure_hbm_copy(src, src)     # in place: the data is unchanged
+    torch.cuda.synchronize()
+    assert torch.equal(src, keep)
