@@ -119,3 +119,88 @@ def gather_dequantized(k8, v8, k_scale, v_scale, block_table, ctx_len, requests=
         ks.append(kb)
         vs.append(vb)
     return ks, vs
+
+
+# ---------------------------------------------------------------------------
+# FP8 scores for prefill: power-of-two block scales
+# ---------------------------------------------------------------------------
+# FA3's FP8 path ("Flash Attention and distributed inference", §18.5) runs the
+# attention matmuls on FP8 operands with block quantisation; the pages give no
+# format or scale rule.  Reading taken here: QK^T in OCP e4m3, each block of 32
+# consecutive head dimensions of one token (one query row, or one key row)
+# with its own scale 2^e, e the smallest integer with amax <= 448 * 2^e (so the
+# block's largest magnitude lands in (224, 448] and nothing saturates); codes
+# are x / 2^e rounded to the nearest e4m3 value, ties to even.  A block of
+# zeros gets e = -127 and zero codes.  The query row is multiplied by
+# c = scale * log2(e) in fp32 before it is quantised, so the scores come out in
+# log2 units and the softmax is taken in base 2; P V stays in bf16.
+E8M0_BIAS = 127
+BLOCK = 32
+
+
+def block_exponents(x, block=BLOCK):
+    """e per block of ``block`` values along the last axis: the smallest
+    integer with max|x| <= 448 * 2^e (fp32 inputs, so the test is exact in
+    fp64); -127 for an all-zero block."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.max(np.abs(x.reshape(*x.shape[:-1], -1, block)), axis=-1)
+    e = np.full(amax.shape, -E8M0_BIAS, dtype=np.int64)
+    nz = amax > 0
+    # frexp: amax = m * 2^E with m in [0.5, 1); the candidate 2^(E-9) times 448
+    # is 0.875 * 2^E, so e = E - 9 exactly when amax <= 0.875 * 2^E
+    m, E = np.frexp(amax[nz])
+    e[nz] = np.maximum(np.where(m <= 0.875, E - 9, E - 8), -E8M0_BIAS)   # E8M0 floor 2^-127
+    return e
+
+
+def quantize_blocks(x, block=BLOCK):
+    """(codes uint8 [...][D], exponents int [...][D/block]) of fp32 values."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    e = block_exponents(x, block)
+    scaled = x.reshape(*x.shape[:-1], -1, block) / np.exp2(e)[..., None]   # exact: powers of two
+    codes = fp8_e4m3_encode(scaled).reshape(x.shape)
+    return codes.astype(np.uint8), e
+
+
+def dequantize_blocks(codes, e, block=BLOCK):
+    c = fp8_e4m3_decode(codes)
+    v = c.reshape(*c.shape[:-1], -1, block) * np.exp2(np.asarray(e, dtype=np.float64))[..., None]
+    return v.reshape(c.shape)
+
+
+def e8m0_bytes(e):
+    """Scale exponents as E8M0 bytes (2^(byte - 127))."""
+    return (np.asarray(e, dtype=np.int64) + E8M0_BIAS).astype(np.uint8)
+
+
+def query_multiplier(scale):
+    """The fp32 factor the query rows are multiplied by: fp32(scale) * fp32(log2 e),
+    rounded to fp32."""
+    return np.float32(np.float32(scale) * np.float32(1.4426950408889634))
+
+
+def prefill_fp8_operands(q_bits, k_bits, scale):
+    """Dequantised fp64 Q'' [..][D] (of q * c, log2 units) and K'' [..][D] from
+    bf16 bit patterns, following the reading above."""
+    qf = (np.asarray(q_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    kf = (np.asarray(k_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    qs = (qf * query_multiplier(scale)).astype(np.float32)      # fp32 product, as the kernel
+    qc, qe = quantize_blocks(qs)
+    kc, ke = quantize_blocks(kf)
+    return dequantize_blocks(qc, qe), dequantize_blocks(kc, ke)
+
+
+def attention_fp8(q_bits, k_bits, v_bits, scale, causal=False, rows=None):
+    """What the FP8-score prefill computes, in fp64: attention over the
+    dequantised Q'' (already in log2 units) and K'' with base-2 softmax,
+    i.e. weights 2^(q''.k''), and V as given (bf16).  q [B][S][Hq][D],
+    k/v [B][S][Hkv][D] bf16 bits.  Returns (out [B][R][Hq][D], lse [B][Hq][R])
+    with lse in natural-log units.  Causal row i sees keys 0..i."""
+    import oracle
+    B, S = q_bits.shape[:2]
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    qd, kd = prefill_fp8_operands(np.ascontiguousarray(np.asarray(q_bits)[:, rows]), k_bits, scale)
+    lim = (np.broadcast_to(rows[None, :] + 1, (B, rows.size)) if causal
+           else np.full((B, rows.size), np.asarray(k_bits).shape[1], dtype=np.int64))
+    # exp(ln 2 * s) = 2^s: the natural-log softmax of ln2-scaled scores
+    return oracle.attention_rows(qd, kd, v_bits, lim, float(np.log(2.0)))

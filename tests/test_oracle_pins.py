@@ -673,3 +673,106 @@ def test_gather_dequantized_equals_paged_gather_then_dequantize():
     for b, T in enumerate(c["ctx_len"]):
         x = synth.bf16_bits_to_f32(c["k_seq"][b]).astype(np.float64)
         assert np.all(np.abs(kq[b] - x) <= 2.0 ** -4 * np.abs(x).max(axis=-1, keepdims=True))
+
+
+# ---------------------------------------------------------------------------
+# FP8 scores for prefill: power-of-two block scales (reading in oracle/fp8.py)
+# ---------------------------------------------------------------------------
+def _block(v, *rest):
+    b = np.zeros(32)
+    b[0] = v
+    b[1:1 + len(rest)] = rest
+    return b
+
+
+def test_fp8_block_exponent_closed_forms():
+    """e is the smallest integer with amax <= 448 * 2^e: 448 -> 0, 449 -> 1,
+    224 -> -1, 224.5 -> 0, 1 -> -8 (1.75 >= 1 > 0.875), 2^-130 -> clamped to
+    -127, zeros -> -127."""
+    x = np.stack([_block(448.0), _block(449.0), _block(-224.0), _block(224.5), _block(1.0, -0.5),
+                  _block(2.0 ** -130), np.zeros(32)])
+    assert fp8.block_exponents(x).ravel().tolist() == [0, 1, -1, 0, -8, -127, -127]
+    assert fp8.e8m0_bytes([0, -8, -127, 127]).tolist() == [127, 119, 0, 254]
+
+
+def test_fp8_block_quantisation_values():
+    """Codes of a block follow x / 2^e through the e4m3 table: with amax 1,
+    e = -8 and 1 -> 256 (0x78), -0.5 -> -128 (0xF0), 2^-8 -> 1 (0x38),
+    3 * 2^-10 -> 0.75 = 1.5 * 2^-1 (0x34); a 448 block keeps 448 -> 0x7E."""
+    codes, e = fp8.quantize_blocks(np.stack([_block(1.0, -0.5, 2.0 ** -8, 3 * 2.0 ** -10),
+                                             _block(448.0, 1.0)]))
+    assert e.tolist() == [[-8], [0]]
+    assert codes[0, :4].tolist() == [0x78, 0xF0, 0x38, 0x34]
+    assert codes[1, :2].tolist() == [0x7E, 0x38]
+    assert not codes[0, 4:].any()
+
+
+def test_fp8_block_quantisation_invariance_and_error_bound():
+    """Scaling a block by 2^j keeps its codes and moves e by j; every value is
+    within half an e4m3 step: 2^-4 |x| in the normal range, 2^-10 * 2^e below."""
+    rng = np.random.default_rng(95)
+    x = (rng.standard_normal((40, 128)) * np.exp(rng.uniform(-20, 20, (40, 1)))).astype(np.float32)
+    c, e = fp8.quantize_blocks(x)
+    for j in (-5, 3, 17):
+        c2, e2 = fp8.quantize_blocks((x * np.float32(2.0 ** j)).astype(np.float32))
+        assert np.array_equal(c2, c) and np.array_equal(e2, e + j)
+    y = fp8.dequantize_blocks(c, e)
+    step = np.repeat(np.exp2(e.astype(np.float64)), 32, axis=-1)
+    xd = x.astype(np.float64)
+    normal = np.abs(xd) >= 2.0 ** -6 * step
+    assert np.all(np.abs(y - xd)[normal] <= 2.0 ** -4 * np.abs(xd)[normal])
+    assert np.all(np.abs(y - xd)[~normal] <= 2.0 ** -10 * step[~normal])
+    # the block maximum keeps full range: it lands in (224, 448] before rounding
+    blk = np.abs(xd).reshape(40, 4, 32).max(-1) / np.exp2(e)
+    assert np.all((blk > 224) & (blk <= 448))
+
+
+def test_attention_fp8_closed_forms():
+    """Base-2 softmax of the dequantised scores: one key gives O = V_0 and
+    LSE = ln2 * (q''.k''); two keys give weights 1 / (1 + 2^(s1 - s0))."""
+    rng = np.random.default_rng(96)
+    q = synth.normal_bf16(97, (1, 1, 1, 64))
+    k = synth.normal_bf16(98, (1, 2, 1, 64))
+    v = synth.normal_bf16(99, (1, 2, 1, 64))
+    qd, kd = fp8.prefill_fp8_operands(q, k, 0.125)
+    s = kd[0, :, 0] @ qd[0, 0, 0]                                     # log2 units
+    o1, l1 = fp8.attention_fp8(q, k[:, :1], v[:, :1], 0.125)
+    np.testing.assert_allclose(o1[0, 0, 0], oracle.widen(v)[0, 0, 0], rtol=0, atol=1e-15)
+    assert abs(l1[0, 0, 0] - np.log(2) * s[0]) <= 1e-12
+    o2, l2 = fp8.attention_fp8(q, k, v, 0.125)
+    w0 = 1.0 / (1.0 + 2.0 ** (s[1] - s[0]))
+    vv = oracle.widen(v)[0, :, 0]
+    np.testing.assert_allclose(o2[0, 0, 0], w0 * vv[0] + (1 - w0) * vv[1], rtol=1e-12, atol=1e-13)
+    assert rng is not None
+
+
+def test_fp8_operands_are_the_scaled_query_and_the_key():
+    """Q'' is q * scale * log2(e) and K'' is k, each within half an e4m3 step
+    of its block (2^-4 relative in the normal range)."""
+    d = synth.dense_bf16(seed=101, B=1, S=64, Hq=2, Hkv=1, D=128)
+    qd, kd = fp8.prefill_fp8_operands(d["q"], d["k"], d["scale"])
+    q = oracle.widen(d["q"]) * d["scale"] * np.log2(np.e)
+    k = oracle.widen(d["k"])
+    for got, want in ((qd, q), (kd, k)):
+        blk = np.abs(want).reshape(*want.shape[:-1], 4, 32).max(-1, keepdims=True)
+        tol = np.maximum(2.0 ** -4 * np.abs(want), 2.0 ** -10 * blk.repeat(32, -1).reshape(want.shape) / 224)
+        assert np.all(np.abs(got - want) <= tol * (1 + 1e-6))
+
+
+def test_attention_fp8_close_to_exact_attention():
+    """With the dequantised operands fixed (pinned above), each row's weights
+    differ from the exact softmax weights by at most a factor e^(2 Delta),
+    Delta = ln2 * max_j |s''_j - s_j| (log2-unit scores), so
+    |O_fp8 - O| <= (e^(2 Delta) - 1) max|v|; checked on 128 causal rows."""
+    d = synth.dense_bf16(seed=100, B=1, S=128, Hq=2, Hkv=1, D=128)
+    o8, _ = fp8.attention_fp8(d["q"], d["k"], d["v"], d["scale"], causal=True)
+    o, _ = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=True)
+    qd, kd = fp8.prefill_fp8_operands(d["q"], d["k"], d["scale"])
+    s8 = np.einsum("ihd,jd->ihj", qd[0], kd[0, :, 0])
+    s = np.einsum("ihd,jd->ihj", oracle.widen(d["q"])[0], oracle.widen(d["k"])[0, :, 0]) \
+        * d["scale"] * np.log2(np.e)
+    vmax = np.abs(oracle.widen(d["v"])).max()
+    for i in range(128):
+        delta = np.log(2) * np.abs(s8[i, :, :i + 1] - s[i, :, :i + 1]).max()
+        assert np.abs(o8[0, i] - o[0, i]).max() <= (np.exp(2 * delta) - 1) * vmax + 1e-12
+    assert np.abs(o8 - o).max() > 0          # the quantisation is not a no-op
