@@ -31,6 +31,9 @@ The same JSON line also carries, each measured in this run:
                   [65536][16][128] back to its head slice of the shards;
   rope            rope_apply on the step's Q and K with cold buffers, against
                   an in-place copy of the same bytes;
+  prefill_fp8     the step with FP8 scores (K block-quantised, QK^T on the
+                  scaled FP8 matrix cores, P V in bf16), against the fp8 peak
+                  and next to the bf16 kernel on the same inputs;
   prefill_64k     the relayout + RoPE + causal prefill pipeline at 65536,
                   with separate and with fused relayout + RoPE;
   chunked_prefill 4 requests x 131072 tokens in 8192-token chunks;
@@ -424,6 +427,66 @@ def bench_relayout_and_prefill_64k(torch, lcat, iters=20, n_sets=4):
     return check, (relay, pre, relay_back)
 
 
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 (e4m3) MFMA
+
+
+def bench_fp8_prefill(torch, lcat, synth, reps=10, warmup=5):
+    """The step workload with FP8 scores: RoPE on Q and K, block quantisation
+    of K (attn_quantize_fp8_blocks), then attn_prefill_fp8 (Q quantised in the
+    kernel, S = QK^T on the scaled FP8 matrix cores, P V in bf16).  The kernel
+    is also timed next to the bf16 prefill on the same inputs, and the two
+    outputs are compared (rel-L2 of the FP8 result against the bf16 one)."""
+    S, Hq, Hkv = 32768, 16, 2
+    d = synth.causal_gqa(seed=SEEDS["causal_gqa_32k"], S=S, Hq=Hq, Hkv=Hkv)
+    q0, k0, v = dev_tensor(torch, d["q"]), dev_tensor(torch, d["k"]), dev_tensor(torch, d["v"])
+    pos = dev_tensor(torch, d["positions"])
+    n = warmup + reps
+    qs = [q0.clone() for _ in range(n)]
+    ks = [k0.clone() for _ in range(n)]
+    k8 = torch.empty(k0.shape, dtype=torch.uint8, device="cuda")
+    ksc = torch.empty((*k0.shape[:-1], D // 32), dtype=torch.uint8, device="cuda")
+    o, lse = torch.empty_like(q0), torch.empty((1, Hq, S), dtype=torch.float32, device="cuda")
+    step_t, kern_t, quant_t = EventTimer(torch), EventTimer(torch), EventTimer(torch)
+    for i in range(n):   # the first `warmup` steps let the clock settle
+        with step_t:
+            lcat.rope_apply(qs[i][0], pos)
+            lcat.rope_apply(ks[i][0], pos)
+            with quant_t:
+                lcat.attn_quantize_fp8_blocks(ks[i], k8, ksc)
+            with kern_t:
+                lcat.attn_prefill_fp8(qs[i], k8, ksc, v, causal=True, o=o, lse=lse)
+        if i == warmup - 1:
+            torch.cuda.synchronize()
+            for t in (step_t, kern_t, quant_t):
+                t.pairs.clear()
+    torch.cuda.synchronize()
+    flops = causal_flops(1, S, Hq)
+    kms = kern_t.mean_ms()
+    tf = flops / (kms * 1e-3) / 1e12
+    # the same rotated inputs through the bf16 prefill, timed the same way
+    ob = torch.empty_like(o)
+    bf_t = EventTimer(torch)
+    for i in range(n):
+        with bf_t:
+            lcat.attn_prefill(qs[-1], ks[-1], v, causal=True, o=ob)
+        if i == warmup - 1:
+            torch.cuda.synchronize()
+            bf_t.pairs.clear()
+    torch.cuda.synchronize()
+    bms = bf_t.mean_ms()
+    diff = (o.float() - ob.float()).norm().item() / ob.float().norm().item()
+    # QK^T at the fp8 peak plus P V at the bf16 peak
+    mixed_peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+    return dict(kernel_ms=round(kms, 4), TFLOPs=round(tf, 1),
+                frac_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4),
+                frac_mixed_peak=round(tf / mixed_peak, 4), mixed_peak_TFLOPs=round(mixed_peak, 1),
+                step_ms=round(step_t.mean_ms(), 4), quantize_k_us=round(quant_t.mean_ms() * 1e3, 2),
+                bf16_kernel_ms=round(bms, 4), speedup_vs_bf16_kernel=round(bms / kms, 3),
+                rel_l2_vs_bf16_kernel=round(diff, 5),
+                workload="causal GQA prefill, seq 32768, 16 Q / 2 KV heads: RoPE, K block "
+                         "quantisation, FP8 scores with bf16 P V")
+
+
 def bench_rope(torch, lcat, iters=30, n_sets=6):
     """rope_apply on the 32K step's Q [32768][16][128] and K [32768][2][128]
     bf16, in place, cycling through ``n_sets`` buffers (768 MB of Q, so no
@@ -805,7 +868,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="time only the step workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["step", "decode", "relayout", "chunked", "cp", "mfma",
-                                       "fixed_cost", "rope"],
+                                       "fixed_cost", "rope", "fp8"],
                     help="run a single leg (for profiling); prints its own JSON object")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -838,6 +901,8 @@ def main():
             res = bench_fixed_cost(torch, lcat)
         elif args.only == "rope":
             res = bench_rope(torch, lcat)
+        elif args.only == "fp8":
+            res = bench_fp8_prefill(torch, lcat, synth)
         else:
             res = bench_chunked(torch, lcat, synth)[1]
         print(json.dumps({args.only: res, "build_id": build_id}), flush=True)
@@ -865,6 +930,8 @@ def main():
             out["roofline"]["achieved"] / out["mfma_sustained"]["a_from_lds"]["tflops"], 4)
         log("bench: rope_apply")
         out["rope"] = bench_rope(torch, lcat)
+        log("bench: prefill with FP8 scores")
+        out["prefill_fp8"] = bench_fp8_prefill(torch, lcat, synth)
         log("bench: decode")
         checks["decode"], out["decode"] = bench_decode(torch, lcat, synth)
         log("bench: relayout + prefill 64k")

@@ -228,6 +228,39 @@ int attn_decode_fp8(const void *q, const void *k8_pool, const void *v8_pool, con
                     int32_t *dev_status, void *stream);
 
 /*
+ * FP8 scores for prefill ([FA18] §18.5: FA3's FP8 path runs the attention
+ * matmuls on 8-bit operands with block quantisation).  Reading taken (the
+ * pages fix no format or rule): OCP e4m3 codes, one power-of-two scale per
+ * block of 32 consecutive head dims of one token, 2^e with e the smallest
+ * integer such that max|x| <= 448 * 2^e (floored at -127), codes = x / 2^e
+ * rounded to the nearest e4m3 value, ties to even; the scale is stored as the
+ * E8M0 byte e + 127.  Only S = Q K^T uses FP8; P V stays bf16.
+ *
+ * attn_quantize_fp8_blocks — x [rows][D] bf16 -> codes [rows][D] e4m3 and
+ *   scales [rows][D/32] E8M0 bytes (block i of a row covers elements
+ *   32i .. 32i+31).  D % 32 == 0 (ATTN_ERR_UNSUPPORTED otherwise); x and
+ *   codes 16-byte aligned; no buffer may overlap another (ATTN_ERR_SHAPE).
+ *   Codes and scales are fixed by the rule above (bit-exact).
+ */
+int attn_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scales, long long rows, int D,
+                             void *stream);
+
+/*
+ * attn_prefill_fp8 — attn_prefill (dense, causal or not) with the scores on
+ * the FP8 matrix cores.  q, v bf16 as in attn_prefill; k8 [B][S][Hkv][128]
+ * e4m3 codes and k_scale [B][S][Hkv][4] E8M0 bytes from
+ * attn_quantize_fp8_blocks on K (k_scale 4-byte aligned).  Each query row is
+ * multiplied by scale * log2(e) in fp32 and block-quantised by the same rule,
+ * so the result is exact attention over the dequantised query (in log2 units,
+ * base-2 softmax) and key, with P rounded to bf16 before P V (fp32
+ * accumulation) and o bf16; lse [B][Hq][S] fp32 natural log, or NULL.
+ * D must be 128, Hq/Hkv must divide 8 or be a multiple of 8.
+ */
+int attn_prefill_fp8(const void *q, const void *k8, const uint8_t *k_scale, const void *v, void *o,
+                     float *lse, int B, int S, int Hq, int Hkv, int D, int causal, float scale,
+                     void *stream);
+
+/*
  * rope_apply — rotary position embedding at absolute token positions, in
  * place ([ULY] §3.2 global token index table, §5.3).
  *   x [S][H][D] bf16, positions [S] int32 (device).

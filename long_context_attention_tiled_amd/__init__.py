@@ -335,6 +335,49 @@ def attn_decode_fp8(q, k8_pool, v8_pool, k_scale, v_scale, block_head, block_tab
     return o, lse
 
 
+def attn_quantize_fp8_blocks(x, codes=None, scales=None, stream=None):
+    """bf16 ``x [..][D]`` -> (e4m3 codes uint8 ``[..][D]``, E8M0 scales uint8
+    ``[..][D/32]``): one power-of-two scale per 32 consecutive elements."""
+    torch = _torch()
+    _need(x, "x", torch.bfloat16)
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((*x.shape[:-1], D // 32), dtype=torch.uint8, device=x.device)
+    _need(codes, "codes", torch.uint8, tuple(x.shape))
+    _need(scales, "scales", torch.uint8, (*x.shape[:-1], D // 32))
+    st = _lib.load().attn_quantize_fp8_blocks(_ptr(x), _ptr(codes), _ptr(scales), rows, D,
+                                              _stream(stream))
+    _lib.check("attn_quantize_fp8_blocks", st)
+    return codes, scales
+
+
+def attn_prefill_fp8(q, k8, k_scale, v, causal=True, scale=None, o=None, lse=None, stream=None):
+    """Prefill with FP8 scores: q, v bf16 ``[B][S][H][128]``, k8 / k_scale from
+    :func:`attn_quantize_fp8_blocks` on K; returns ``(o, lse)``."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    B, S, Hq, D = q.shape
+    Hkv = v.shape[2]
+    _need(k8, "k8", torch.uint8, (B, S, Hkv, D))
+    _need(k_scale, "k_scale", torch.uint8, (B, S, Hkv, D // 32))
+    _need(v, "v", torch.bfloat16, (B, S, Hkv, D))
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, q.shape)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, (B, Hq, S))
+    scale = float(D ** -0.5) if scale is None else float(scale)
+    st = _lib.load().attn_prefill_fp8(_ptr(q), _ptr(k8), _ptr(k_scale), _ptr(v), _ptr(o),
+                                      _ptr(lse), B, S, Hq, Hkv, D, int(bool(causal)), scale,
+                                      _stream(stream))
+    _lib.check("attn_prefill_fp8", st)
+    return o, lse
+
+
 def rope_apply(x, positions, base=10000.0, stream=None):
     """Rotate ``x [S][H][D]`` (bf16) in place at absolute ``positions [S]`` (int32)."""
     torch = _torch()

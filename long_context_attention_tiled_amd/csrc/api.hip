@@ -233,6 +233,43 @@ int attn_prefill(const void *q, const void *k, const void *v, void *o, float *ls
   return hip_status(lcat::launch_prefill_bf16(p, false, st));
 }
 
+int attn_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scales, long long rows, int D,
+                             void *stream) {
+  if (rows < 0 || D <= 0) return ATTN_ERR_SHAPE;
+  if (D % 32) return ATTN_ERR_UNSUPPORTED;
+  if (rows == 0) return ATTN_OK;
+  if (!x || !codes || !scales) return ATTN_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes)) return ATTN_ERR_ALIGN;
+  const long long n = rows * D;
+  auto overlap = [](const void *a, long long na, const void *b, long long nb) {
+    const char *x0 = static_cast<const char *>(a), *y0 = static_cast<const char *>(b);
+    return x0 < y0 + nb && y0 < x0 + na;
+  };
+  if (overlap(x, 2 * n, codes, n) || overlap(x, 2 * n, scales, n / 32) ||
+      overlap(codes, n, scales, n / 32))
+    return ATTN_ERR_SHAPE;
+  return hip_status(lcat::launch_quantize_fp8_blocks(x, codes, scales, n / 32,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+int attn_prefill_fp8(const void *q, const void *k8, const uint8_t *k_scale, const void *v, void *o,
+                     float *lse, int B, int S, int Hq, int Hkv, int D, int causal, float scale,
+                     void *stream) {
+  if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return ATTN_ERR_SHAPE;
+  if (D != kHeadDim || !group_ok(Hq, Hkv)) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || S == 0) return ATTN_OK;
+  if (!q || !k8 || !k_scale || !v || !o) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k8) || !aligned16(v) || !aligned16(o) ||
+      reinterpret_cast<uintptr_t>(k_scale) % 4)
+    return ATTN_ERR_ALIGN;
+  lcat::PrefillFp8Params p{};
+  p.q = q; p.k8 = k8; p.k_scale = k_scale; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.S = S; p.Hq = Hq; p.Hkv = Hkv;
+  p.causal = causal != 0;
+  p.scale = scale;
+  return hip_status(lcat::launch_prefill_fp8(p, static_cast<hipStream_t>(stream)));
+}
+
 int attn_kv_append(const void *k_new, const void *v_new, void *k_pool, void *v_pool, int n_blocks,
                    const int32_t *block_head, const int32_t *block_table, int max_blocks,
                    const int32_t *start_pos, int T, int B, int Hkv, int D, int kv_head_base,

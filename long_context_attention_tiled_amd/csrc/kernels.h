@@ -31,6 +31,27 @@ struct PrefillParams {
 
 hipError_t launch_prefill_bf16(const PrefillParams &p, bool paged, hipStream_t stream);
 
+// Dense prefill with FP8 (e4m3) scores: q and v bf16, k as e4m3 codes with
+// one E8M0 scale per 32 head dims (attn_quantize_fp8_blocks), head_dim 128.
+struct PrefillFp8Params {
+  const void *q;            // [B][S][Hq][128] bf16
+  const void *k8;           // [B][S][Hkv][128] e4m3
+  const uint8_t *k_scale;   // [B][S][Hkv][4] E8M0
+  const void *v;            // [B][S][Hkv][128] bf16
+  void *o;                  // [B][S][Hq][128] bf16
+  float *lse;               // [B][Hq][S] or null
+  int B, S, Hq, Hkv;
+  int causal;
+  float scale;
+};
+
+hipError_t launch_prefill_fp8(const PrefillFp8Params &p, hipStream_t stream);
+
+// Block quantisation: x [n_blocks * 32] bf16 -> e4m3 codes (same count) and
+// one E8M0 scale byte per block of 32 consecutive values.
+hipError_t launch_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scales,
+                                      long long n_blocks, hipStream_t stream);
+
 hipError_t launch_attn_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                            int B, int S, int Hq, int Hkv, int D, int causal, float scale,
                            hipStream_t stream);

@@ -49,7 +49,8 @@ def test_header_declares_the_boundary():
               "head_to_seq_permute", "seq_to_head_permute_qkv_rope", "cp_shard_tokens",
               "cp_shard", "cp_unshard", "attn_key_limits", "attn_prefill_limited", "attn_merge",
               "attn_decode_fp8", "attn_kv_quantize_fp8", "attn_kv_append_fp8",
-              "attn_status_string", "attn_build_id", "attn_decode_noalloc", "attn_measure_mfma_rate"]:
+              "attn_status_string", "attn_build_id", "attn_decode_noalloc", "attn_quantize_fp8_blocks",
+              "attn_prefill_fp8", "attn_measure_mfma_rate"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
 
@@ -157,6 +158,27 @@ def test_decode_noalloc_validation(lib):
     # fixed splits of 64 keys over 2048 blocks: 32 * 16 * 2048 records, far too many
     assert call(split=64) == SCRATCH
     assert lcat.attn_status_string(SCRATCH).startswith("call needs more decode scratch")
+
+
+def test_fp8_prefill_validation(lib):
+    qz, pf = lib.attn_quantize_fp8_blocks, lib.attn_prefill_fp8
+    codes, sc = P(0x200000), P(0x300000)
+    assert qz(A16, codes, sc, -1, 128, S0) == SHAPE
+    assert qz(A16, codes, sc, 4, 48, S0) == UNSUP          # D % 32 != 0
+    assert qz(A16, codes, sc, 0, 128, S0) == OK
+    assert qz(NUL, codes, sc, 4, 128, S0) == NULL
+    assert qz(MIS, codes, sc, 4, 128, S0) == ALIGN
+    assert qz(A16, P(0x10000 + 512), sc, 4, 128, S0) == SHAPE   # codes overlap x
+    args = lambda **kw: [kw.get(n, d) for n, d in (("q", A16), ("k8", A16), ("ks", A16), ("v", A16), ("o", A16))]
+    def call(B=1, S=64, Hq=16, Hkv=2, D=128, **kw):
+        return pf(*args(**kw), NUL, B, S, Hq, Hkv, D, 1, 0.1, S0)
+    assert call(Hq=15) == SHAPE
+    assert call(D=64) == UNSUP
+    assert call(Hq=6, Hkv=2) == UNSUP                        # group 3
+    assert call(S=0) == OK
+    assert call(k8=NUL) == NULL
+    assert call(ks=P(0x10002)) == ALIGN                     # scales 4-byte aligned
+    assert call(v=MIS) == ALIGN
 
 
 def test_rope_and_permute_validation(lib):
