@@ -643,9 +643,19 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
     fused(j + 2, Int<1>{}, Int<3>{});
     fused(j + 3, Int<0>{}, Int<0>{});
   }
+  // up to three more interleaved iterations (ring positions 1, 2, 3), so the
+  // plain path runs only where it must (first tile, mask, last tiles)
+  if (j < fused_end) {
+    fused(j++, Int<1>{}, Int<1>{});
+    if (j < fused_end) {
+      fused(j++, Int<0>{}, Int<2>{});
+      if (j < fused_end) fused(j++, Int<1>{}, Int<3>{});
+    }
+  }
   // back to run-time ring positions for the remaining iterations
   kc = (j % NKS) * TILE;
   vc = (NKS + (j + NVS - 2) % NVS) * TILE;
+  if (!(j & 1) && j <= n_tiles) plain(j++, Int<0>{});
 #pragma clang loop unroll(disable)
   for (; j <= n_tiles; j += 2) {
     plain(j, Int<1>{});
