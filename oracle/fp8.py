@@ -204,3 +204,33 @@ def attention_fp8(q_bits, k_bits, v_bits, scale, causal=False, rows=None):
            else np.full((B, rows.size), np.asarray(k_bits).shape[1], dtype=np.int64))
     # exp(ln 2 * s) = 2^s: the natural-log softmax of ln2-scaled scores
     return oracle.attention_rows(qd, kd, v_bits, lim, float(np.log(2.0)))
+
+
+def dequantized_v_keys(v_bits):
+    """V [B][S][Hkv][D] bf16 bits -> fp64 V'' with each (dim, block of 32
+    consecutive keys) quantised by the power-of-two rule above (the FP8 P V
+    reading: the key axis is the contraction axis of P V, so V's blocks run
+    along keys).  Keys past the last multiple of 32 form a shorter block as if
+    padded with zeros."""
+    v = (np.asarray(v_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    B, S, H, D = v.shape
+    Sp = -(-S // BLOCK) * BLOCK
+    vt = np.zeros((B, H, D, Sp), np.float32)
+    vt[..., :S] = np.transpose(v, (0, 2, 3, 1))
+    c, e = quantize_blocks(vt)
+    return np.ascontiguousarray(np.transpose(dequantize_blocks(c, e)[..., :S], (0, 3, 1, 2)))
+
+
+def attention_fp8_pv(q_bits, k_bits, v_bits, scale, causal=False, rows=None):
+    """What the FP8-score, FP8-P.V prefill computes before P is rounded:
+    attention_fp8 with V replaced by V'' (dequantised along keys).  The
+    kernel also rounds the weights P to e4m3 before P V, which depends on its
+    running reference maximum; that rounding is bounded in the tests, not
+    modelled here."""
+    import oracle
+    B, S = q_bits.shape[:2]
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    qd, kd = prefill_fp8_operands(np.ascontiguousarray(np.asarray(q_bits)[:, rows]), k_bits, scale)
+    lim = (np.broadcast_to(rows[None, :] + 1, (B, rows.size)) if causal
+           else np.full((B, rows.size), np.asarray(k_bits).shape[1], dtype=np.int64))
+    return oracle.attention_rows(qd, kd, dequantized_v_keys(v_bits), lim, float(np.log(2.0)))

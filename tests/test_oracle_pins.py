@@ -776,3 +776,43 @@ def test_attention_fp8_close_to_exact_attention():
         delta = np.log(2) * np.abs(s8[i, :, :i + 1] - s[i, :, :i + 1]).max()
         assert np.abs(o8[0, i] - o[0, i]).max() <= (np.exp(2 * delta) - 1) * vmax + 1e-12
     assert np.abs(o8 - o).max() > 0          # the quantisation is not a no-op
+
+
+def test_fp8_v_blocks_run_along_keys():
+    """V'' quantises each (dim, 32-key block): scaling one dimension of the keys
+    of one block by 2^j scales exactly those values by 2^j; a block of keys
+    is quantised independently of its neighbours (a huge value in keys 0..31
+    leaves keys 32..63 untouched); a ragged tail is a block of its own."""
+    rng = np.random.default_rng(102)
+    v = rng.standard_normal((1, 70, 1, 64)).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(v)
+    base = fp8.dequantized_v_keys(bits)
+    w = synth.bf16_bits_to_f32(bits).copy()
+    w[0, 32:64, 0, 5] *= np.float32(8.0)
+    got = fp8.dequantized_v_keys(synth.f32_to_bf16_bits(w))
+    np.testing.assert_array_equal(got[0, 32:64, 0, 5], 8 * base[0, 32:64, 0, 5])
+    mask = np.ones_like(got, bool)
+    mask[0, 32:64, 0, 5] = False
+    np.testing.assert_array_equal(got[mask], base[mask])
+    w2 = synth.bf16_bits_to_f32(bits).copy()
+    w2[0, 3, 0, :] = 1e6
+    got2 = fp8.dequantized_v_keys(synth.f32_to_bf16_bits(w2))
+    np.testing.assert_array_equal(got2[0, 32:], base[0, 32:])
+    assert not np.array_equal(got2[0, :32], base[0, :32])
+    # keys 64..69 form their own block: quantised with their own maximum
+    tail = synth.bf16_bits_to_f32(bits)[0, 64:, 0, :].astype(np.float64)
+    c, e = fp8.quantize_blocks(np.concatenate([tail, np.zeros((26, 64))]).T.astype(np.float32))
+    np.testing.assert_array_equal(base[0, 64:, 0, :], fp8.dequantize_blocks(c, e).T[:6])
+    v2 = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    assert np.all(np.abs(base - v2) <= 2.0 ** -4 * np.abs(v2) + 2.0 ** -10 * np.abs(v2).max())
+
+
+def test_attention_fp8_pv_uses_the_key_blocked_v():
+    """attention_fp8_pv = attention_fp8 with V'' in place of V (one-key row:
+    O = V''_0)."""
+    d = synth.dense_bf16(seed=103, B=1, S=40, Hq=2, Hkv=1, D=64)
+    o, _ = fp8.attention_fp8_pv(d["q"], d["k"], d["v"], d["scale"], causal=True)
+    vdd = fp8.dequantized_v_keys(d["v"])
+    np.testing.assert_allclose(o[0, 0, :, :], np.broadcast_to(vdd[0, 0, 0], (2, 64)), atol=1e-15)
+    o8, _ = fp8.attention_fp8(d["q"], d["k"], d["v"], d["scale"], causal=True)
+    assert 0 < np.abs(o - o8).max() < 0.2
