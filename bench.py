@@ -33,7 +33,9 @@ The same JSON line also carries, each measured in this run:
                   an in-place copy of the same bytes;
   prefill_fp8     the step with FP8 scores (K block-quantised, QK^T on the
                   scaled FP8 matrix cores, P V in bf16), against the fp8 peak
-                  and next to the bf16 kernel on the same inputs;
+                  and next to the bf16 kernel on the same inputs, and
+                  (fp8_pv) with P V on FP8 as well (V block-quantised along
+                  keys);
   prefill_64k     the relayout + RoPE + causal prefill pipeline at 65536,
                   with separate and with fused relayout + RoPE;
   chunked_prefill 4 requests x 131072 tokens in 8192-token chunks;
@@ -435,7 +437,9 @@ def bench_fp8_prefill(torch, lcat, synth, reps=10, warmup=5):
     of K (attn_quantize_fp8_blocks), then attn_prefill_fp8 (Q quantised in the
     kernel, S = QK^T on the scaled FP8 matrix cores, P V in bf16).  The kernel
     is also timed next to the bf16 prefill on the same inputs, and the two
-    outputs are compared (rel-L2 of the FP8 result against the bf16 one)."""
+    outputs are compared (rel-L2 of the FP8 result against the bf16 one).
+    ``fp8_pv``: the same rotated inputs with V block-quantised along keys
+    (attn_quantize_fp8_v) through attn_prefill_fp8_pv (both products on FP8)."""
     S, Hq, Hkv = 32768, 16, 2
     d = synth.causal_gqa(seed=SEEDS["causal_gqa_32k"], S=S, Hq=Hq, Hkv=Hkv)
     q0, k0, v = dev_tensor(torch, d["q"]), dev_tensor(torch, d["k"]), dev_tensor(torch, d["v"])
@@ -475,9 +479,35 @@ def bench_fp8_prefill(torch, lcat, synth, reps=10, warmup=5):
     torch.cuda.synchronize()
     bms = bf_t.mean_ms()
     diff = (o.float() - ob.float()).norm().item() / ob.float().norm().item()
+    # both products on FP8: V quantised along keys, then attn_prefill_fp8_pv
+    s64 = (S + 63) // 64 * 64
+    v8t = torch.empty((1, Hkv, D, s64), dtype=torch.uint8, device="cuda")
+    vsc = torch.empty((1, Hkv, s64 // 64, 256), dtype=torch.uint8, device="cuda")
+    op = torch.empty_like(o)
+    pv_t, vq_t = EventTimer(torch), EventTimer(torch)
+    for i in range(n):
+        with vq_t:
+            lcat.attn_quantize_fp8_v(v, v8t, vsc)
+        with pv_t:
+            lcat.attn_prefill_fp8_pv(qs[-1], k8, ksc, v8t, vsc, causal=True, o=op, lse=lse)
+        if i == warmup - 1:
+            torch.cuda.synchronize()
+            pv_t.pairs.clear()
+            vq_t.pairs.clear()
+    torch.cuda.synchronize()
+    pms = pv_t.mean_ms()
+    ptf = flops / (pms * 1e-3) / 1e12
+    pdiff = (op.float() - ob.float()).norm().item() / ob.float().norm().item()
+    fp8_pv = dict(kernel_ms=round(pms, 4), TFLOPs=round(ptf, 1),
+                  frac_fp8_peak=round(ptf / PEAK_FP8_TFLOPS, 4),
+                  quantize_v_us=round(vq_t.mean_ms() * 1e3, 2),
+                  speedup_vs_bf16_kernel=round(bms / pms, 3),
+                  speedup_vs_fp8_scores_kernel=round(kms / pms, 3),
+                  rel_l2_vs_bf16_kernel=round(pdiff, 5),
+                  workload="the same inputs, V block-quantised along keys, both products on FP8")
     # QK^T at the fp8 peak plus P V at the bf16 peak
     mixed_peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
-    return dict(kernel_ms=round(kms, 4), TFLOPs=round(tf, 1),
+    return dict(fp8_pv=fp8_pv, kernel_ms=round(kms, 4), TFLOPs=round(tf, 1),
                 frac_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4),
                 frac_mixed_peak=round(tf / mixed_peak, 4), mixed_peak_TFLOPs=round(mixed_peak, 1),
                 step_ms=round(step_t.mean_ms(), 4), quantize_k_us=round(quant_t.mean_ms() * 1e3, 2),

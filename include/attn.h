@@ -261,6 +261,38 @@ int attn_prefill_fp8(const void *q, const void *k8, const uint8_t *k_scale, cons
                      void *stream);
 
 /*
+ * attn_quantize_fp8_v — V for attn_prefill_fp8_pv: v [B][S][Hkv][128] bf16 ->
+ *   v8t [B][Hkv][128][S64] e4m3 codes, dimension-major (V^T), S64 = S
+ *   rounded up to a multiple of 64, keys S .. S64-1 written as code 0;
+ *   v_scale [B][Hkv][S64/64][256] E8M0 bytes, one per (dim, 32 consecutive
+ *   keys) by the rule above: in the 256-byte block of key tile t, byte
+ *   4 * (32 * h + r) + db is the scale of dim 32 * db + r over keys
+ *   64 t + 32 h .. +31 (the layout the kernel loads as is).  Codes and scales
+ *   are fixed by the rule (bit-exact).  D must be 128; v, v8t 16-byte
+ *   aligned; D * S64 < 2^31; no buffer may overlap another (ATTN_ERR_SHAPE).
+ */
+int attn_quantize_fp8_v(const void *v, void *v8t, uint8_t *v_scale, int B, int S, int Hkv, int D,
+                        void *stream);
+
+/*
+ * attn_prefill_fp8_pv — attn_prefill_fp8 with P V on the FP8 matrix cores
+ * too ([FA18] §18.5: both attention products on 8-bit operands with block
+ * quantisation).  q, k8, k_scale as in attn_prefill_fp8; v8t, v_scale from
+ * attn_quantize_fp8_v (v_scale 4-byte aligned).  Arithmetic: the scores are
+ * those of attn_prefill_fp8 (log2 units); the weights P' = 2^(s - m + 3), m a
+ * running reference maximum, are rounded to e4m3 (nearest even) and never
+ * exceed 2^8.75 (a tile that would is first rescaled to its exact maximum);
+ * O = sum P' V'' / sum P' with V'' the dequantised V and both sums over the
+ * same rounded weights (fp32 accumulation); o bf16; lse [B][Hq][S] fp32
+ * natural log of the row's sum of exp(scores), from the same rounded
+ * weights, or NULL.  D must be 128, Hq/Hkv must divide 8 or be a multiple
+ * of 8, D * S64 < 2^31.
+ */
+int attn_prefill_fp8_pv(const void *q, const void *k8, const uint8_t *k_scale, const void *v8t,
+                        const uint8_t *v_scale, void *o, float *lse, int B, int S, int Hq, int Hkv,
+                        int D, int causal, float scale, void *stream);
+
+/*
  * rope_apply — rotary position embedding at absolute token positions, in
  * place ([ULY] §3.2 global token index table, §5.3).
  *   x [S][H][D] bf16, positions [S] int32 (device).

@@ -27,7 +27,8 @@ __all__ = [
     "attn_decode_workspace_bytes", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv", "head_to_seq_permute",
     "seq_to_head_permute_qkv_rope", "cp_shard_tokens", "cp_shard", "cp_unshard",
     "attn_key_limits", "attn_prefill_limited", "attn_merge", "CP_MODES", "attn_decode_fp8",
-    "attn_kv_quantize_fp8", "attn_kv_append_fp8",
+    "attn_kv_quantize_fp8", "attn_kv_append_fp8", "attn_quantize_fp8_blocks", "attn_prefill_fp8",
+    "attn_quantize_fp8_v", "attn_prefill_fp8_pv", "attn_decode_noalloc",
     "attn_status_string", "measure_mfma_rate", "mfma_rate_flops", "measure_hbm_read",
     "measure_hbm_copy",
     "AttnError", "ATTN_DEV_OK", "ATTN_DEV_BAD_TAG", "ATTN_DEV_BAD_BLOCK", "load_library",
@@ -375,6 +376,55 @@ def attn_prefill_fp8(q, k8, k_scale, v, causal=True, scale=None, o=None, lse=Non
                                       _ptr(lse), B, S, Hq, Hkv, D, int(bool(causal)), scale,
                                       _stream(stream))
     _lib.check("attn_prefill_fp8", st)
+    return o, lse
+
+
+def attn_quantize_fp8_v(v, v8t=None, v_scale=None, stream=None):
+    """bf16 ``v [B][S][Hkv][128]`` -> (e4m3 ``v8t [B][Hkv][128][S64]``, E8M0
+    ``v_scale [B][Hkv][S64/64][256]``), S64 = S rounded up to 64: one
+    power-of-two scale per (dim, 32 consecutive keys), the layout
+    :func:`attn_prefill_fp8_pv` reads."""
+    torch = _torch()
+    _need(v, "v", torch.bfloat16)
+    B, S, Hkv, D = v.shape
+    s64 = (S + 63) // 64 * 64
+    if v8t is None:
+        v8t = torch.empty((B, Hkv, D, s64), dtype=torch.uint8, device=v.device)
+    if v_scale is None:
+        v_scale = torch.empty((B, Hkv, s64 // 64, 256), dtype=torch.uint8, device=v.device)
+    _need(v8t, "v8t", torch.uint8, (B, Hkv, D, s64))
+    _need(v_scale, "v_scale", torch.uint8, (B, Hkv, s64 // 64, 256))
+    st = _lib.load().attn_quantize_fp8_v(_ptr(v), _ptr(v8t), _ptr(v_scale), B, S, Hkv, D,
+                                         _stream(stream))
+    _lib.check("attn_quantize_fp8_v", st)
+    return v8t, v_scale
+
+
+def attn_prefill_fp8_pv(q, k8, k_scale, v8t, v_scale, causal=True, scale=None, o=None, lse=None,
+                        stream=None):
+    """Prefill with both products on FP8: q bf16 ``[B][S][Hq][128]``, k8 /
+    k_scale from :func:`attn_quantize_fp8_blocks` on K, v8t / v_scale from
+    :func:`attn_quantize_fp8_v`; returns ``(o, lse)``."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    B, S, Hq, D = q.shape
+    Hkv = k8.shape[2]
+    s64 = (S + 63) // 64 * 64
+    _need(k8, "k8", torch.uint8, (B, S, Hkv, D))
+    _need(k_scale, "k_scale", torch.uint8, (B, S, Hkv, D // 32))
+    _need(v8t, "v8t", torch.uint8, (B, Hkv, D, s64))
+    _need(v_scale, "v_scale", torch.uint8, (B, Hkv, s64 // 64, 256))
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, q.shape)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, (B, Hq, S))
+    scale = float(D ** -0.5) if scale is None else float(scale)
+    st = _lib.load().attn_prefill_fp8_pv(_ptr(q), _ptr(k8), _ptr(k_scale), _ptr(v8t),
+                                         _ptr(v_scale), _ptr(o), _ptr(lse), B, S, Hq, Hkv, D,
+                                         int(bool(causal)), scale, _stream(stream))
+    _lib.check("attn_prefill_fp8_pv", st)
     return o, lse
 
 

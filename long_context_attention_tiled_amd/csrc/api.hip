@@ -270,6 +270,47 @@ int attn_prefill_fp8(const void *q, const void *k8, const uint8_t *k_scale, cons
   return hip_status(lcat::launch_prefill_fp8(p, static_cast<hipStream_t>(stream)));
 }
 
+int attn_quantize_fp8_v(const void *v, void *v8t, uint8_t *v_scale, int B, int S, int Hkv, int D,
+                        void *stream) {
+  if (B < 0 || S < 0 || Hkv <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+  if (D != kHeadDim) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || S == 0) return ATTN_OK;
+  if (!v || !v8t || !v_scale) return ATTN_ERR_NULL;
+  if (!aligned16(v) || !aligned16(v8t)) return ATTN_ERR_ALIGN;
+  const long long s64 = ((long long)S + 63) / 64 * 64;
+  const long long nv = (long long)B * S * Hkv * D * 2;
+  const long long n8 = (long long)B * Hkv * D * s64;
+  const long long ns = (long long)B * Hkv * (s64 / 64) * 256;
+  if (D * s64 > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
+  auto overlap = [](const void *a, long long na, const void *b, long long nb) {
+    const char *x0 = static_cast<const char *>(a), *y0 = static_cast<const char *>(b);
+    return x0 < y0 + nb && y0 < x0 + na;
+  };
+  if (overlap(v, nv, v8t, n8) || overlap(v, nv, v_scale, ns) || overlap(v8t, n8, v_scale, ns))
+    return ATTN_ERR_SHAPE;
+  return hip_status(lcat::launch_quantize_fp8_v(v, v8t, v_scale, B, S, Hkv,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int attn_prefill_fp8_pv(const void *q, const void *k8, const uint8_t *k_scale, const void *v8t,
+                        const uint8_t *v_scale, void *o, float *lse, int B, int S, int Hq, int Hkv,
+                        int D, int causal, float scale, void *stream) {
+  if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return ATTN_ERR_SHAPE;
+  if (D != kHeadDim || !group_ok(Hq, Hkv)) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || S == 0) return ATTN_OK;
+  if ((long long)D * (((long long)S + 63) / 64 * 64) > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
+  if (!q || !k8 || !k_scale || !v8t || !v_scale || !o) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o) ||
+      reinterpret_cast<uintptr_t>(k_scale) % 4 || reinterpret_cast<uintptr_t>(v_scale) % 4)
+    return ATTN_ERR_ALIGN;
+  lcat::PrefillFp8PvParams p{};
+  p.q = q; p.k8 = k8; p.k_scale = k_scale; p.v8t = v8t; p.v_scale = v_scale; p.o = o; p.lse = lse;
+  p.B = B; p.S = S; p.Hq = Hq; p.Hkv = Hkv;
+  p.causal = causal != 0;
+  p.scale = scale;
+  return hip_status(lcat::launch_prefill_fp8_pv(p, static_cast<hipStream_t>(stream)));
+}
+
 int attn_kv_append(const void *k_new, const void *v_new, void *k_pool, void *v_pool, int n_blocks,
                    const int32_t *block_head, const int32_t *block_table, int max_blocks,
                    const int32_t *start_pos, int T, int B, int Hkv, int D, int kv_head_base,

@@ -41,6 +41,55 @@ __global__ __launch_bounds__(256) void quantize_fp8_blocks_kernel(const bf16 *__
   scales[blk] = (uint8_t)(e + 127);
 }
 
+// V for FP8 P V: blocks run along keys (the contraction axis of P V), one
+// thread per (batch, KV head, 32-key block, dim) with the dim fastest, so a
+// wave's loads are contiguous 128-byte pieces of 64 dims of one key row.
+// Output: v8t [B][Hkv][128][S64] (dimension-major, S64 = S rounded up to 64,
+// keys >= S written as code 0) and per 64-key tile a 256-byte scale block
+// whose byte 4 (32 h + r) + db is the scale of dim 32 db + r over keys
+// 64 t + 32 h .. +31: the word lane r + 32 h of a wave loads is the A-operand
+// scale word of P V for that lane, one dim group db per byte.
+__global__ __launch_bounds__(256) void quantize_fp8_v_kernel(const bf16 *__restrict__ v,
+                                                             uint8_t *__restrict__ v8t,
+                                                             uint8_t *__restrict__ v_scale, int S,
+                                                             int Hkv, int S64, long long n_threads) {
+  const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= n_threads) return;
+  const int d = (int)(id % 128);
+  long long rest = id / 128;
+  const int nblk = S64 / 32;
+  const int blk = (int)(rest % nblk);
+  rest /= nblk;
+  const int g = (int)(rest % Hkv);
+  const long long b = rest / Hkv;
+  const int key0 = 32 * blk;
+  const int n = min(32, S - key0);   // keys of this block that exist (may be <= 0)
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    x[i] = 0.f;
+    if (i < n) {
+      const uint16_t bits = *reinterpret_cast<const uint16_t *>(
+          v + (((b * S + key0 + i) * Hkv + g) * 128 + d));
+      x[i] = bf16_to_f32(bits);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const int e = fp8_block_exponent(amax);
+  u32x4 out[2];
+#pragma unroll
+  for (int w = 0; w < 8; ++w)
+    out[w >> 2][w & 3] = fp8x4_rne(__builtin_amdgcn_ldexpf(x[4 * w], -e), __builtin_amdgcn_ldexpf(x[4 * w + 1], -e),
+                                   __builtin_amdgcn_ldexpf(x[4 * w + 2], -e), __builtin_amdgcn_ldexpf(x[4 * w + 3], -e));
+  uint8_t *dst = v8t + ((b * Hkv + g) * 128 + d) * (long long)S64 + key0;
+  st_global_16(dst, out[0]);
+  st_global_16(dst + 16, out[1]);
+  const long long tile = (b * Hkv + g) * (S64 / 64) + blk / 2;
+  v_scale[tile * 256 + 4 * (32 * (blk & 1) + (d & 31)) + (d >> 5)] = (uint8_t)(e + 127);
+}
+
 }  // namespace
 
 hipError_t launch_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scales,
@@ -51,6 +100,19 @@ hipError_t launch_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scale
   hipLaunchKernelGGL(quantize_fp8_blocks_kernel, dim3((unsigned)n_wg), dim3(256), 0, stream,
                      static_cast<const bf16 *>(x), static_cast<uint8_t *>(codes), scales,
                      n_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8_v(const void *v, void *v8t, uint8_t *v_scale, int B, int S, int Hkv,
+                                 hipStream_t stream) {
+  const int S64 = (S + 63) / 64 * 64;
+  const long long n_threads = (long long)B * Hkv * (S64 / 32) * 128;
+  if (n_threads <= 0) return hipSuccess;
+  const long long n_wg = (n_threads + 255) / 256;
+  if (n_wg > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quantize_fp8_v_kernel, dim3((unsigned)n_wg), dim3(256), 0, stream,
+                     static_cast<const bf16 *>(v), static_cast<uint8_t *>(v8t), v_scale, S, Hkv, S64,
+                     n_threads);
   return hipGetLastError();
 }
 

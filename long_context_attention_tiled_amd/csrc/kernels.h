@@ -47,6 +47,28 @@ struct PrefillFp8Params {
 
 hipError_t launch_prefill_fp8(const PrefillFp8Params &p, hipStream_t stream);
 
+// Dense prefill with both products on FP8: q bf16, k as above, v as e4m3
+// codes in the dimension-major layout of attn_quantize_fp8_v (S64 = S rounded
+// up to 64 keys) with one E8M0 scale per (dim, 32 keys), head_dim 128.
+struct PrefillFp8PvParams {
+  const void *q;            // [B][S][Hq][128] bf16
+  const void *k8;           // [B][S][Hkv][128] e4m3
+  const uint8_t *k_scale;   // [B][S][Hkv][4] E8M0
+  const void *v8t;          // [B][Hkv][128][S64] e4m3
+  const uint8_t *v_scale;   // [B][Hkv][S64 / 64][256] E8M0 (tile layout)
+  void *o;                  // [B][S][Hq][128] bf16
+  float *lse;               // [B][Hq][S] or null
+  int B, S, Hq, Hkv;
+  int causal;
+  float scale;
+};
+
+hipError_t launch_prefill_fp8_pv(const PrefillFp8PvParams &p, hipStream_t stream);
+
+// V [B][S][Hkv][128] bf16 -> v8t and v_scale as PrefillFp8PvParams reads them.
+hipError_t launch_quantize_fp8_v(const void *v, void *v8t, uint8_t *v_scale, int B, int S, int Hkv,
+                                 hipStream_t stream);
+
 // Block quantisation: x [n_blocks * 32] bf16 -> e4m3 codes (same count) and
 // one E8M0 scale byte per block of 32 consecutive values.
 hipError_t launch_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scales,

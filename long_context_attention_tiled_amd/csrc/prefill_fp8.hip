@@ -19,22 +19,14 @@
 // rule as it loads them, so the matrix core produces the softmax exponents
 // (log2 units) directly.
 //
-// Operand layout of the scaled FP8 MFMA (measured on the part): for row r of
-// A (or column r of B), lane r + 32h holds 32 bytes; bytes 0..15 of lanes r
-// and r+32 form the first 32-element K block and bytes 16..31 the second;
-// the scale of block b comes from lane r + 32b, and op_sel k picks byte k of
-// the scale register.  So lane (r, h) holds, for the MFMA over dims
-// 64c .. 64c+63, dims 64c + 16h .. +15 in bytes 0..15 and 64c + 32 + 16h .. +15
-// in bytes 16..31, and its scale register holds the scale of block 2c + h in
-// byte 2c (one op_sel per MFMA for all lanes).
+// The operand layout of the scaled FP8 MFMA is stated in prefill_fp8_common.h.
 #include "device.h"
 #include "fp8_block.h"
 #include "kernels.h"
+#include "prefill_fp8_common.h"
 
 namespace lcat {
 namespace {
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int HD = 128;                 // head dimension
 constexpr int BN = 64;                  // keys per tile
@@ -72,24 +64,6 @@ __device__ __forceinline__ int vd_pos(int row, int c) { return c ^ ((row & 3) <<
 
 constexpr float kRescaleLog2 = 8.0f;    // lazy rescale threshold of the edge iterations
 constexpr float kSumLimit = 65536.0f;   // row-sum bound of the interleaved iterations
-
-template <int SEL>
-__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, sa, SEL, sb);
-}
-
-// 4-byte global -> LDS copy per lane (lane l writes lds_dst + 4 l); see
-// dma_to_lds_16 for the ordering rules.
-__device__ __forceinline__ void dma_to_lds_4(u32x4 rsrc, char *lds_dst, int voffset) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void *)lds_dst;
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %0, %2, 0 offen lds"
-      :
-      : "v"(voffset), "s"(m0), "s"(rsrc)
-      : "m0");
-}
 
 // Schedule: as the bf16 prefill, iteration j interleaves
 //   O^T += V_{j-1}^T P_{j-1}^T      (16 bf16 MFMA, operands from the V ring)
@@ -143,49 +117,11 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillFp8Params p, int
   const float c2 = p.scale * kLog2e;
   const int qrow = row0 + lr;
   i32x8 qf[2];
-  int qsw;
-  {
-    const int qr = min(qrow, p.S - 1);
-    const bf16 *qp = static_cast<const bf16 *>(p.q) + (((size_t)b * p.S + qr) * p.Hq + h) * HD;
-    bf16x8 raw[2][2][2];   // [c][part][8 dims]
+  const int qsw = quantize_query_row(
+      static_cast<const bf16 *>(p.q) + (((size_t)b * p.S + min(qrow, p.S - 1)) * p.Hq + h) * HD, gq,
+      c2, qf);
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          raw[c][pt][i] = as_bf16x8(ld_global_16(qp + 64 * c + 32 * pt + 16 * gq + 8 * i));
-    float y[2][2][16];
-    int eb[2][2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        float am = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          y[c][pt][e] = (float)raw[c][pt][e >> 3][e & 7] * c2;
-          am = fmaxf(am, fabsf(y[c][pt][e]));
-        }
-        // the block's other 16 dims sit in lane l ^ 32
-        eb[c][pt] = fp8_block_exponent(pair_max32(am));
-      }
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int e = -eb[c][pt];
-          qf[c][4 * pt + w] = (int)fp8x4_rne(
-              __builtin_amdgcn_ldexpf(y[c][pt][4 * w], e), __builtin_amdgcn_ldexpf(y[c][pt][4 * w + 1], e),
-              __builtin_amdgcn_ldexpf(y[c][pt][4 * w + 2], e), __builtin_amdgcn_ldexpf(y[c][pt][4 * w + 3], e));
-        }
-    const int e0 = gq ? eb[0][1] : eb[0][0], e1 = gq ? eb[1][1] : eb[1][0];
-    qsw = (e0 + 127) | ((e1 + 127) << 16);
-#pragma unroll
-    for (int c = 0; c < 2; ++c) asm volatile("" ::"v"(qf[c]));
-  }
+  for (int c = 0; c < 2; ++c) asm volatile("" ::"v"(qf[c]));
 
   // ---- LDS operand addresses (within a slot) ------------------------------
   // K rows are read in a permuted order (bits 2 and 3 of the row swapped) so
@@ -277,9 +213,9 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillFp8Params p, int
     for (int t = 0; t < 4; ++t) {
       const i32x8 a = (t < NPK && use_pre) ? kpre[t < NPK ? t : 0] : read_k(ks, t);
       if (t < 2)
-        sn[t & 1] = mfma_fp8<0>(a, qf[0], negm, ksw[t & 1], qsw);
+        sn[t & 1] = mfma_fp8<0, 0>(a, qf[0], negm, ksw[t & 1], qsw);
       else
-        sn[t & 1] = mfma_fp8<2>(a, qf[1], sn[t & 1], ksw[t & 1], qsw);
+        sn[t & 1] = mfma_fp8<2, 2>(a, qf[1], sn[t & 1], ksw[t & 1], qsw);
     }
   };
   auto tile_max = [&](const f32x16 (&sc)[2]) __attribute__((always_inline)) -> float {
@@ -490,9 +426,9 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillFp8Params p, int
         constexpr int t = i - 16;
         const int sw = (t & 1) ? ksw1 : ksw0;
         if constexpr (t < 2)
-          sn[t & 1] = mfma_fp8<0>(kop[t], qf[0], negm, sw, qsw);
+          sn[t & 1] = mfma_fp8<0, 0>(kop[t], qf[0], negm, sw, qsw);
         else
-          sn[t & 1] = mfma_fp8<2>(kop[t], qf[1], sn[t & 1], sw, qsw);
+          sn[t & 1] = mfma_fp8<2, 2>(kop[t], qf[1], sn[t & 1], sw, qsw);
         valu(Int<16 + 4 * t>{});
         valu(Int<17 + 4 * t>{});
         valu(Int<18 + 4 * t>{});

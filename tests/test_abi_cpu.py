@@ -50,7 +50,8 @@ def test_header_declares_the_boundary():
               "cp_shard", "cp_unshard", "attn_key_limits", "attn_prefill_limited", "attn_merge",
               "attn_decode_fp8", "attn_kv_quantize_fp8", "attn_kv_append_fp8",
               "attn_status_string", "attn_build_id", "attn_decode_noalloc", "attn_quantize_fp8_blocks",
-              "attn_prefill_fp8", "attn_measure_mfma_rate"]:
+              "attn_prefill_fp8", "attn_quantize_fp8_v", "attn_prefill_fp8_pv",
+              "attn_measure_mfma_rate"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
 
@@ -179,6 +180,32 @@ def test_fp8_prefill_validation(lib):
     assert call(k8=NUL) == NULL
     assert call(ks=P(0x10002)) == ALIGN                     # scales 4-byte aligned
     assert call(v=MIS) == ALIGN
+
+
+def test_fp8_pv_prefill_validation(lib):
+    qv, pf = lib.attn_quantize_fp8_v, lib.attn_prefill_fp8_pv
+    v8, vs = P(0x200000), P(0x300000)
+    assert qv(A16, v8, vs, 1, -1, 2, 128, S0) == SHAPE
+    assert qv(A16, v8, vs, 1, 64, 0, 128, S0) == SHAPE
+    assert qv(A16, v8, vs, 1, 64, 2, 64, S0) == UNSUP          # D != 128
+    assert qv(A16, v8, vs, 0, 64, 2, 128, S0) == OK
+    assert qv(NUL, v8, vs, 1, 64, 2, 128, S0) == NULL
+    assert qv(A16, MIS, vs, 1, 64, 2, 128, S0) == ALIGN
+    assert qv(A16, P(0x10000 + 4096), vs, 1, 64, 2, 128, S0) == SHAPE   # codes overlap v
+    assert qv(A16, v8, vs, 1, 1 << 24, 2, 128, S0) == SHAPE      # 128 * S64 >= 2^31
+    names = ("q", "k8", "ks", "v8", "vs", "o")
+    def call(B=1, S=64, Hq=16, Hkv=2, D=128, **kw):
+        ptrs = [kw.get(n, A16) for n in names]
+        return pf(*ptrs, NUL, B, S, Hq, Hkv, D, 1, 0.1, S0)
+    assert call(Hq=15) == SHAPE
+    assert call(D=64) == UNSUP
+    assert call(Hq=6, Hkv=2) == UNSUP                          # group 3
+    assert call(S=0) == OK
+    assert call(S=1 << 24) == SHAPE
+    assert call(v8=NUL) == NULL
+    assert call(vs=NUL) == NULL
+    assert call(vs=P(0x10002)) == ALIGN                        # scales 4-byte aligned
+    assert call(v8=MIS) == ALIGN
 
 
 def test_rope_and_permute_validation(lib):
