@@ -21,7 +21,8 @@ The same JSON line also carries, each measured in this run:
                   uniform in [8192, 131072], KV bytes per second against 8 TB/s
                   and against a plain streaming read of as many bytes
                   (read_sustained); and (fp8_cache) the same decode over the
-                  FP8 copy of the cache;
+                  FP8 copy of the cache, against a streaming read of its own
+                  (smaller) byte count;
   relayout        sequence-shard -> head-shard relayout of one rank's share of
                   [4][16384][64|8][128] bf16 Q/K/V (one launch), bytes per second,
                   also against a plain streaming copy of as many bytes
@@ -301,12 +302,23 @@ def bench_decode(torch, lcat, synth, iters=20):
                           iters)
     nbytes8 = ctx_total * c["Hkv"] * (2 * D + 8) + 2 * B * Hq * D * 2 + B * Hq * 4
     gbs8 = nbytes8 / (ms8 * 1e-3) / 1e9
+    del k8, v8, ks, vs
+    # its own yardstick: a streaming read of the FP8 decode's byte count
+    buf = torch.empty(nbytes8 // 16 * 16, dtype=torch.uint8, device="cuda")
+    rd8_out, rd8_bytes = lcat.measure_hbm_read(buf)
+    torch.cuda.synchronize()
+    ms_rd8 = back_to_back_ms(torch, lambda: lcat.measure_hbm_read(buf, out=rd8_out), iters)
+    del buf
+    rd8_gbs = rd8_bytes / (ms_rd8 * 1e-3) / 1e9
     res["fp8_cache"] = dict(ms=round(ms8, 4), GBps=round(gbs8, 1),
                             frac_hbm=round(gbs8 / PEAK_HBM_GBS, 4), bytes=nbytes8,
                             traffic=load_traffic("decode_stream_kernel", "decode_32req_fp8"),
-                            frac_of_sustained_read=round(gbs8 / rd_gbs, 4),
+                            read_sustained=dict(GBps=round(rd8_gbs, 1),
+                                                frac_hbm=round(rd8_gbs / PEAK_HBM_GBS, 4),
+                                                bytes=rd8_bytes),
+                            frac_of_sustained_read=round(gbs8 / rd8_gbs, 4),
+                            frac_of_bf16_bytes_read=round(gbs8 / rd_gbs, 4),
                             speedup_vs_bf16=round(ms / ms8, 3))
-    del k8, v8, ks, vs
     check = dict(c=c, q=args[0], k_pool=k_pool, v_pool=v_pool, o=o, lse=lse)
     return check, res
 
@@ -485,12 +497,14 @@ def bench_fp8_prefill(torch, lcat, synth, reps=10, warmup=5):
     vsc = torch.empty((1, Hkv, s64 // 64, 256), dtype=torch.uint8, device="cuda")
     op = torch.empty_like(o)
     pv_t, vq_t = EventTimer(torch), EventTimer(torch)
-    for i in range(n):
+    # this kernel draws less power than the others and the clock keeps rising
+    # over its first ~12 launches: three times the warm-up before timing
+    for i in range(3 * warmup + reps):
         with vq_t:
             lcat.attn_quantize_fp8_v(v, v8t, vsc)
         with pv_t:
             lcat.attn_prefill_fp8_pv(qs[-1], k8, ksc, v8t, vsc, causal=True, o=op, lse=lse)
-        if i == warmup - 1:
+        if i == 3 * warmup - 1:
             torch.cuda.synchronize()
             pv_t.pairs.clear()
             vq_t.pairs.clear()
