@@ -916,7 +916,7 @@ def main():
                     help="run a single leg (for profiling); prints its own JSON object")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+        print(f"bench.py: this library runs on exactly one GPU; --gpus {args.gpus} is not "
               "supported (the sequence-parallel exchange across GPUs is not built)",
               file=sys.stderr)
         sys.exit(2)
