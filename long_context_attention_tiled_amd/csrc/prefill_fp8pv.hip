@@ -97,6 +97,14 @@ __device__ __forceinline__ int k8_pos(int row, int c) { return c ^ (((row >> 1) 
 // quarter-wave's read fall on 16 distinct bank groups.
 __device__ __forceinline__ int v8_pos(int d, int c) { return c ^ ((d >> 2) & 3); }
 
+// Four values into one word of e4m3 codes (value i in byte i, nearest even),
+// written over `old`: both half-words are replaced, and taking the register's
+// previous contents as the merge source of the first one saves clearing it.
+__device__ __forceinline__ int fp8x4_over(int old, float y0, float y1, float y2, float y3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, old, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, lo, true);
+}
+
 // Word w (0..3) of a key half of P'_j holds keys 16 h + 4 w .. +3, which
 // sit in registers word_reg(w) .. +3 of the S^T MFMA over that half.
 __device__ constexpr int word_reg(int w) { return w == 0 ? 0 : w == 1 ? 8 : w == 2 ? 4 : 12; }
@@ -228,8 +236,8 @@ __global__ __launch_bounds__(NT) void prefill_fp8pv_kernel(PrefillFp8PvParams p,
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int hf = w >> 2, r = word_reg(w & 3);
-      pc[w] = (int)fp8x4_rne(fast_exp2(sc[hf][r] - d), fast_exp2(sc[hf][r + 1] - d),
-                             fast_exp2(sc[hf][r + 2] - d), fast_exp2(sc[hf][r + 3] - d));
+      pc[w] = fp8x4_over(pc[w], fast_exp2(sc[hf][r] - d), fast_exp2(sc[hf][r + 1] - d),
+                         fast_exp2(sc[hf][r + 2] - d), fast_exp2(sc[hf][r + 3] - d));
     }
   };
 
@@ -318,6 +326,8 @@ __global__ __launch_bounds__(NT) void prefill_fp8pv_kernel(PrefillFp8PvParams p,
     vb = d * s64 + 16 * v8_pos(d, lane & 3);
   }
   const int sb = lane * p.Hkv * 4;     // K-scale word of key row `lane`
+  const int vb16 = vb + 16 * s64;      // second V^T code DMA: 16 dim rows further
+  const int vsb = 4 * lane;            // V-scale word `lane`
   const size_t first = ((size_t)b * p.S) * p.Hkv + g;   // row index of key 0, head g
   const char *kbase = static_cast<const char *>(p.k8) + first * HD;
   const char *ksbase = reinterpret_cast<const char *>(p.k_scale) + first * 4;
@@ -333,9 +343,9 @@ __global__ __launch_bounds__(NT) void prefill_fp8pv_kernel(PrefillFp8PvParams p,
     const u32x4 rk = rsrc_words(kbase, live ? rows * HD : 0);
     const u32x4 rsc = rsrc_words(ksbase, live ? rows * 4 : 0);
     char *dst = smem + slot + wave * 2048;
-    dma_to_lds_16(rk, dst, opaque(kb0));
-    dma_to_lds_16(rk, dst + 1024, opaque(kb1));
-    dma_to_lds_4(rsc, smem + KSBASE + (slot / KT) * ST + 256 * wave, opaque(sb));
+    dma_to_lds_16(rk, dst, kb0);
+    dma_to_lds_16(rk, dst + 1024, kb1);
+    dma_to_lds_4(rsc, smem + KSBASE + (slot / KT) * ST + 256 * wave, sb);
     kbase += (size_t)BN * krs;
     ksbase += (size_t)BN * p.Hkv * 4;
     k_rows_left -= BN;
@@ -344,11 +354,10 @@ __global__ __launch_bounds__(NT) void prefill_fp8pv_kernel(PrefillFp8PvParams p,
     const bool live = tile < n_tiles;
     const u32x4 rv = rsrc_words(vbase, live ? (HD - 1) * s64 + BN : 0);
     const u32x4 rvs = rsrc_words(vsbase, live ? 256 : 0);
-    const int base = opaque(vb);
     char *dst = smem + slot + wave * 2048;
-    dma_to_lds_16(rv, dst, base);
-    dma_to_lds_16(rv, dst + 1024, base + 16 * s64);
-    dma_to_lds_4(rvs, smem + VSBASE + ((slot - VBASE) / VT) * ST + 256 * wave, opaque(4 * lane));
+    dma_to_lds_16(rv, dst, vb);
+    dma_to_lds_16(rv, dst + 1024, vb16);
+    dma_to_lds_4(rvs, smem + VSBASE + ((slot - VBASE) / VT) * ST + 256 * wave, vsb);
     vbase += BN;
     vsbase += 256;
   };
@@ -453,7 +462,7 @@ __global__ __launch_bounds__(NT) void prefill_fp8pv_kernel(PrefillFp8PvParams p,
       }
       if constexpr (i >= 1) {
         constexpr int w = i - 1;
-        pc[w] = (int)fp8x4_rne(xs[w & 1][0], xs[w & 1][1], xs[w & 1][2], xs[w & 1][3]);
+        pc[w] = fp8x4_over(pc[w], xs[w & 1][0], xs[w & 1][1], xs[w & 1][2], xs[w & 1][3]);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
