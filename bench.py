@@ -95,19 +95,42 @@ def causal_flops(B, S, Hq, D=D, ctx_before=0):
     return 4.0 * D * Hq * B * pairs
 
 
-# Sources that build no attention-path kernel (the sustained-MFMA yardstick):
-# a change there leaves the recorded traffic of the path's kernels valid.
-NOT_PATH_SOURCES = {"measure.hip"}
+# The source file that defines each kernel whose traffic is recorded.
+KERNEL_SOURCES = {
+    "prefill_kernel": "prefill_bf16.hip",
+    "permute16_kernel": "permute.hip",
+    "permute_rope_kernel": "relayout_rope.hip",
+    "rope_kernel": "rope.hip",
+    "decode_stream_kernel": "decode.hip",
+}
 
 
-def kernel_source_hash():
-    """sha256 over the attention-path kernel sources (csrc/*.hip, *.h)."""
-    h = hashlib.sha256()
+def kernel_source_hash(kernel):
+    """sha256 (first 16 hex digits) over the source file that defines
+    `kernel`, every local header it includes (transitively) and the compile
+    flags: a change anywhere else leaves the kernel's recorded traffic valid."""
+    import re
+    from long_context_attention_tiled_amd import _build
     csrc = os.path.join(ROOT, "long_context_attention_tiled_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")) and name not in NOT_PATH_SOURCES:
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    inc = os.path.join(ROOT, "include")
+    seen, todo = set(), [os.path.join(csrc, KERNEL_SOURCES[kernel])]
+    while todo:
+        path = os.path.normpath(todo.pop())
+        if path in seen:
+            continue
+        seen.add(path)
+        with open(path) as f:
+            for name in re.findall(r'^#include "([^"]+)"', f.read(), re.M):
+                for d in (os.path.dirname(path), csrc, inc):
+                    cand = os.path.normpath(os.path.join(d, name))
+                    if os.path.exists(cand):
+                        todo.append(cand)
+                        break
+    h = hashlib.sha256()
+    for path in sorted(seen):
+        with open(path, "rb") as f:
+            h.update(os.path.relpath(path, ROOT).encode() + b"\0" + f.read() + b"\0")
+    h.update(" ".join(_build.HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
 
 
@@ -121,7 +144,7 @@ def load_traffic(kernel, workload):
     except (OSError, ValueError):
         return None
     ent = rec.get(kernel, {}).get(workload)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 
