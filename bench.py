@@ -167,8 +167,11 @@ class EventTimer:
         self.e.record()
         self.pairs.append((self.s, self.e))
 
+    def times_ms(self):
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
     def mean_ms(self):
-        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
+        return float(np.mean(self.times_ms()))
 
 
 def back_to_back_ms(torch, fn, iters):
@@ -247,7 +250,8 @@ def bench_step(torch, lcat, synth, steps, warmup):
         roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
                       unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
                       traffic=traffic, kernel="prefill_kernel<dense,causal>",
-                      kernel_ms=round(k_ms, 4), flop_per_launch=flops,
+                      kernel_ms=round(k_ms, 4), kernel_ms_median=round(float(np.median(timer.times_ms())), 4),
+                      kernel_ms_min=round(float(np.min(timer.times_ms())), 4), flop_per_launch=flops,
                       timed_launches=f"prefill launches {warmup + 1}..{n} of this process "
                                      f"(the first {warmup} are warm-up)"))
 
@@ -930,7 +934,7 @@ def git_sha():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="time only the step workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
