@@ -234,7 +234,8 @@ int attn_decode_fp8(const void *q, const void *k8_pool, const void *v8_pool, con
  * block of 32 consecutive head dims of one token, 2^e with e the smallest
  * integer such that max|x| <= 448 * 2^e (floored at -127), codes = x / 2^e
  * rounded to the nearest e4m3 value, ties to even; the scale is stored as the
- * E8M0 byte e + 127.  Only S = Q K^T uses FP8; P V stays bf16.
+ * E8M0 byte e + 127.  attn_prefill_fp8 runs S = Q K^T on FP8 (P V in bf16);
+ * attn_prefill_fp8_pv runs both products on FP8.
  *
  * attn_quantize_fp8_blocks — x [rows][D] bf16 -> codes [rows][D] e4m3 and
  *   scales [rows][D/32] E8M0 bytes (block i of a row covers elements
