@@ -78,6 +78,8 @@ constexpr int kFp8OneX4 = 0x38383838;   // four e4m3 ones
 // queries j (groups 0, 2) and j + 16 (groups 1, 3).  The A operand selects
 // groups 0, 2 for rows 0..3 and 8..11 and groups 1, 3 for rows 4..7 and
 // 12..15: lane l then receives the sum of query l % 32 in every register.
+// (That layout is the one of the 16x16 MFMA family; the uniform-V closed form
+// in the tests, whose result depends on l alone, confirms it on the part.)
 __device__ __forceinline__ i32x8 l_selector(int lane) {
   const int grp = lane >> 4, row = lane & 15;
   const int v = (grp & 1) == ((row >> 2) & 1) ? kFp8OneX4 : 0;
