@@ -88,14 +88,15 @@ def _stepped_scores(seed, B, S, Hq, Hkv, step_keys=128, step=13.0, D=128):
     return dict(q=q, k=k, v=v, scale=scale)
 
 
-@pytest.mark.parametrize("S,B,causal,stepped", [
-    (2048, 1, True, False), (1100, 2, False, False), (2048, 1, True, True), (1100, 2, False, True),
+@pytest.mark.parametrize("S,B,Hq,Hkv,causal,stepped", [
+    (2048, 1, 16, 2, True, False), (1100, 2, 16, 2, False, False), (2048, 1, 16, 2, True, True),
+    (1100, 2, 16, 2, False, True), (1500, 1, 8, 2, True, False), (1300, 1, 4, 4, True, True),
 ])
-def test_prefill_fp8_long_rows(S, B, causal, stepped):
+def test_prefill_fp8_long_rows(S, B, Hq, Hkv, causal, stepped):
     """Long enough for the interleaved key loop; every row against the oracle."""
-    log(f"prefill fp8 long S={S} B={B} causal={causal} stepped={stepped}")
-    d = (_stepped_scores(820 + S, B, S, 16, 2) if stepped
-         else synth.dense_bf16(seed=820 + S, B=B, S=S, Hq=16, Hkv=2))
+    log(f"prefill fp8 long S={S} B={B} Hq={Hq} Hkv={Hkv} causal={causal} stepped={stepped}")
+    d = (_stepped_scores(820 + S, B, S, Hq, Hkv) if stepped
+         else synth.dense_bf16(seed=820 + S, B=B, S=S, Hq=Hq, Hkv=Hkv))
     k, k8, ks = _quantize_k(d["k"])
     o, lse = lcat.attn_prefill_fp8(to_dev(d["q"]), k8, ks, to_dev(d["v"]), causal=causal,
                                    scale=d["scale"])

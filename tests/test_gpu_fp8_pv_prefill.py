@@ -191,14 +191,19 @@ def _stepped_scores(seed, B, S, Hq, Hkv, step_keys=128, step=13.0, D=128):
     return dict(q=q, k=k, v=v, scale=scale)
 
 
-@pytest.mark.parametrize("S,B,causal,stepped", [
-    (2048, 1, True, False), (1100, 2, False, False), (2048, 1, True, True), (1100, 2, False, True),
+@pytest.mark.parametrize("S,B,Hq,Hkv,causal,stepped", [
+    (2048, 1, 16, 2, True, False), (1100, 2, 16, 2, False, False), (2048, 1, 16, 2, True, True),
+    (1100, 2, 16, 2, False, True), (1500, 1, 8, 2, True, False), (1300, 1, 4, 4, True, False),
+    (1300, 1, 4, 4, True, True),
 ])
-def test_prefill_fp8_pv_long_rows(S, B, causal, stepped):
-    """Long enough for the interleaved key loop; every row against the oracle."""
-    log(f"prefill fp8 pv long S={S} B={B} causal={causal} stepped={stepped}")
-    d = (_stepped_scores(840 + S, B, S, 16, 2) if stepped
-         else synth.dense_bf16(seed=840 + S, B=B, S=S, Hq=16, Hkv=2))
+def test_prefill_fp8_pv_long_rows(S, B, Hq, Hkv, causal, stepped):
+    """Long enough for the interleaved key loop; every row against the oracle.
+    With a GQA group below 8 a workgroup holds several 32-row blocks whose
+    causal rows end in different key tiles, so its waves leave the
+    interleaved loop at different iterations while sharing its barriers."""
+    log(f"prefill fp8 pv long S={S} B={B} Hq={Hq} Hkv={Hkv} causal={causal} stepped={stepped}")
+    d = (_stepped_scores(840 + S, B, S, Hq, Hkv) if stepped
+         else synth.dense_bf16(seed=840 + S, B=B, S=S, Hq=Hq, Hkv=Hkv))
     o, lse = _run(d, causal)
     torch.cuda.synchronize()
     ref, ref_lse = ofp8.attention_fp8_pv(d["q"], d["k"], d["v"], d["scale"], causal=causal)

@@ -311,16 +311,17 @@ def _stepped_scores(seed, B, S, Hq, Hkv, step_keys, step=13.0, D=128):
     return dict(q=q, k=k, v=v, scale=scale)
 
 
-@pytest.mark.parametrize("S,B,causal,stepped", [
-    (2048, 1, True, False), (1100, 2, False, False), (2048, 1, True, True), (1100, 2, False, True),
+@pytest.mark.parametrize("S,B,Hq,Hkv,causal,stepped", [
+    (2048, 1, 16, 2, True, False), (1100, 2, 16, 2, False, False), (2048, 1, 16, 2, True, True),
+    (1100, 2, 16, 2, False, True), (1500, 1, 8, 2, True, False), (1300, 1, 4, 4, True, True),
 ])
-def test_prefill_bf16_long_rows(S, B, causal, stepped):
+def test_prefill_bf16_long_rows(S, B, Hq, Hkv, causal, stepped):
     """Sequences long enough for the interleaved key loop (five or more
     full tiles before the diagonal), every row against the oracle; the
     stepped inputs make that loop take its exact-maximum recovery path."""
-    log(f"prefill bf16 long S={S} B={B} causal={causal} stepped={stepped}")
-    d = (_stepped_scores(800 + S, B, S, 16, 2, step_keys=128) if stepped
-         else synth.dense_bf16(seed=800 + S, B=B, S=S, Hq=16, Hkv=2))
+    log(f"prefill bf16 long S={S} B={B} Hq={Hq} Hkv={Hkv} causal={causal} stepped={stepped}")
+    d = (_stepped_scores(800 + S, B, S, Hq, Hkv, step_keys=128) if stepped
+         else synth.dense_bf16(seed=800 + S, B=B, S=S, Hq=Hq, Hkv=Hkv))
     o, lse = lcat.attn_prefill(to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"]), causal=causal)
     torch.cuda.synchronize()
     ref, ref_lse = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=causal)
