@@ -178,6 +178,33 @@ __device__ __forceinline__ float pair_max32_raw(float x) {
   return max_raw(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 
+// Order of causal prefill work over the XCDs.  The dispatcher deals
+// workgroups to the 8 XCDs in turn, so workgroup b runs on XCD b % 8 as the
+// (b / 8)-th workgroup there, and each XCD has its own L2.  Work items are
+// ranked by query block, longest rows first, times `per_q` combinations
+// (batch, KV head, head slice): item = rank * per_q + combination.  The
+// plain order (item = b) spreads the ranks an XCD runs at one time over
+// 4 * 32 consecutive ranks (per_q = 2).  This order, when per_q divides 8,
+// still keeps one combination per XCD, so that XCD streams one KV head
+// through its L2, and hands the 8 / per_q XCDs of a combination their ranks
+// in generations of kXcdCus consecutive ranks (one per CU), the XCDs taking
+// the blocks of a generation in alternating directions so that their totals
+// balance.  The workgroups an XCD runs together then walk nearly the same
+// key prefix at the same time.  The result is a bijection of
+// [0, n_qblk * per_q) whatever the part's layout; ranks past the last whole
+// generation keep the plain order.
+__device__ __forceinline__ int xcd_item(int b, int per_q, int n_qblk) {
+  constexpr int kXcds = 8, kXcdCus = 32;
+  if (per_q <= 0 || kXcds % per_q != 0) return b;
+  const int m = kXcds / per_q;   // XCDs that share one combination
+  const int x = b % kXcds, i = b / kXcds;
+  const int gen = i / kXcdCus;
+  if (gen >= n_qblk / (kXcdCus * m)) return b;
+  const int xp = x / per_q, comb = x % per_q;
+  const int blk = (gen & 1) ? m - 1 - xp : xp;
+  return (kXcdCus * (m * gen + blk) + i % kXcdCus) * per_q + comb;
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // acc + a.x + a.y for a pair of bf16 packed in one register (fp32 accumulate).
 __device__ __forceinline__ float add_bf16_pair(uint32_t a, float acc) {

@@ -138,9 +138,10 @@ __global__ __launch_bounds__(NT) void prefill_fp8pv_kernel(PrefillFp8PvParams p,
 
   // ---- workgroup -> (query block, batch, KV head, head slice) -------------
   const int per_q = p.B * p.Hkv * head_slices;
-  int qblk = blockIdx.x / per_q;
+  const int item = CAUSAL ? xcd_item(blockIdx.x, per_q, n_qblk) : (int)blockIdx.x;
+  int qblk = item / per_q;
   if (CAUSAL) qblk = n_qblk - 1 - qblk;   // longest rows first
-  int rem = blockIdx.x % per_q;
+  int rem = item % per_q;
   const int slice = rem % head_slices;
   rem /= head_slices;
   const int g = rem % p.Hkv;

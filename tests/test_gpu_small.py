@@ -328,6 +328,54 @@ def test_prefill_bf16_long_rows(S, B, Hq, Hkv, causal, stepped):
     e, r = assert_attention_close(to_np64(o), ref, lse.cpu().numpy(), ref_lse, what="prefill")
     log(f"  max abs {e:.3g} rel-L2 {r:.3g}")
 
+@pytest.mark.parametrize("S,B,Hq,Hkv", [
+    (4096, 1, 16, 2), (4096, 2, 16, 2), (8192, 1, 8, 1), (5000, 1, 16, 2), (4096, 3, 16, 2),
+])
+def test_causal_work_order_covers_every_row(S, B, Hq, Hkv):
+    """Causal prefill hands its work items (query block x batch x KV head) to
+    workgroups in an XCD-aware order: generations of 32 consecutive query
+    blocks per XCD, the XCDs of one KV head alternating direction between
+    generations.  The shapes take 1 and 2 whole generations with 2, 4 and 8
+    XCDs per KV head, a partial last generation, and a batch x head count
+    that does not divide 8 (plain order).  The order must be a bijection:
+    with outputs pre-filled with NaN, all three prefill kernels write every
+    row of every head; bf16 rows are checked against the oracle, and the
+    FP8 outputs must stay close to the bf16 ones."""
+    log(f"work order S={S} B={B} Hq={Hq} Hkv={Hkv}")
+    d = synth.dense_bf16(seed=600 + S + B, B=B, S=S, Hq=Hq, Hkv=Hkv)
+    q, k, v = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
+    k8, ks = lcat.attn_quantize_fp8_blocks(k)
+    v8t, vs = lcat.attn_quantize_fp8_v(v)
+    runs = {
+        "bf16": lambda o, l: lcat.attn_prefill(q, k, v, causal=True, o=o, lse=l),
+        "fp8": lambda o, l: lcat.attn_prefill_fp8(q, k8, ks, v, causal=True, scale=d["scale"],
+                                                  o=o, lse=l),
+        "fp8_pv": lambda o, l: lcat.attn_prefill_fp8_pv(q, k8, ks, v8t, vs, causal=True,
+                                                        scale=d["scale"], o=o, lse=l),
+    }
+    outs = {}
+    for name, run in runs.items():
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((B, Hq, S), float("nan"), device=q.device)
+        run(o, lse)
+        torch.cuda.synchronize()
+        assert not torch.isnan(o).any().item(), f"{name}: output rows left unwritten"
+        assert not torch.isnan(lse).any().item(), f"{name}: LSE entries left unwritten"
+        outs[name] = o.float()
+    rows = synth.sample_rows(601, S, 96, [0, 31, 32, S // 2, S - 1])
+    ref, ref_lse = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=True, rows=rows)
+    sel = torch.from_numpy(rows).cuda()
+    o16, l16 = runs["bf16"](None, None)
+    torch.cuda.synchronize()
+    assert_attention_close(to_np64(o16[:, sel]), ref, l16[:, :, sel].cpu().numpy(), ref_lse,
+                           what="work order")
+    for name in ("fp8", "fp8_pv"):
+        rel = (torch.linalg.vector_norm(outs[name] - outs["bf16"]) /
+               torch.linalg.vector_norm(outs["bf16"])).item()
+        log(f"  {name}: rel-L2 against bf16 {rel:.3g}")
+        assert rel < 0.1, (name, rel)
+
+
 # ---------------------------------------------------------------------------
 # decode over the paged cache
 # ---------------------------------------------------------------------------
