@@ -471,9 +471,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 // partial sums are combined through LDS.
 constexpr int MERGE_WAVES = 4;
 
-// Merge of the records (pieces) of one (request, query head): the global
-// max M of the piece maxima, then O = sum w_i O_i / sum w_i l_i with
-// w_i = 2^(m_i - M).  `rec(i)` is the record of piece i (NULL: no record).
+// Merge of the records (pieces) of one (request, query head):
+// O = sum w_i O_i / sum w_i l_i with w_i = 2^(m_i - M), M the largest piece
+// maximum.  Each wave folds pieces wave, wave + 4, ... in one pass, loading
+// kMergeBatch pieces at a time and keeping its sums relative to the largest
+// maximum it has seen (rescaled when that grows); the four waves' sums are
+// then brought to the common M and added.  `rec(i)` is the record of piece i
+// (NULL: no record).
+constexpr int kMergeBatch = 4;
 template <class RecOf>
 __device__ __forceinline__ void merge_records(const DecodeParams &p, int b, int h, int n_pieces,
                                               RecOf rec) {
@@ -483,34 +488,47 @@ __device__ __forceinline__ void merge_records(const DecodeParams &p, int b, int 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   bf16 *o = static_cast<bf16 *>(p.o) + ((size_t)b * p.Hq + h) * HD;
 
-  float M = -INFINITY;
-  for (int s = tid; s < n_pieces; s += 64 * MERGE_WAVES) {
-    const float *r = rec(s);
-    if (r) M = fmaxf(M, r[HD]);
-  }
+  float M = -INFINITY, n0 = 0.f, n1 = 0.f, den = 0.f;
+  for (int s0 = wave; s0 < n_pieces; s0 += MERGE_WAVES * kMergeBatch) {
+    float ms[kMergeBatch], ls[kMergeBatch];
+    float2 ov[kMergeBatch];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, wave_shfl_xor(M, off));
+    for (int c = 0; c < kMergeBatch; ++c) {
+      const int s = s0 + c * MERGE_WAVES;
+      const float *r = s < n_pieces ? rec(s) : nullptr;
+      ms[c] = -INFINITY;
+      ls[c] = 0.f;
+      ov[c] = make_float2(0.f, 0.f);
+      if (r) {
+        ms[c] = r[HD];
+        ls[c] = r[HD + 1];
+        ov[c] = *reinterpret_cast<const float2 *>(r + 2 * lane);
+      }
+    }
+    float bm = M;
+#pragma unroll
+    for (int c = 0; c < kMergeBatch; ++c) bm = fmaxf(bm, ms[c]);
+    if (bm == -INFINITY) continue;
+    const float a = M == -INFINITY ? 0.f : fast_exp2(M - bm);
+    n0 *= a;
+    n1 *= a;
+    den *= a;
+#pragma unroll
+    for (int c = 0; c < kMergeBatch; ++c) {
+      const float w = ms[c] == -INFINITY ? 0.f : fast_exp2(ms[c] - bm);
+      n0 = fmaf(w, ov[c].x, n0);
+      n1 = fmaf(w, ov[c].y, n1);
+      den = fmaf(w, ls[c], den);
+    }
+    M = bm;
+  }
   if (lane == 0) wmax[wave] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-
-  float n0 = 0.f, n1 = 0.f, den = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int s = wave; s < n_pieces; s += MERGE_WAVES) {
-      const float *r = rec(s);
-      if (!r) continue;
-      const float ms = r[HD];
-      const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
-      const float2 ov = *reinterpret_cast<const float2 *>(r + 2 * lane);
-      n0 = fmaf(w, ov.x, n0);
-      n1 = fmaf(w, ov.y, n1);
-      den = fmaf(w, r[HD + 1], den);
-    }
-  }
-  part[wave][2 * lane] = n0;
-  part[wave][2 * lane + 1] = n1;
-  if (lane == 0) part[wave][HD] = den;
+  const float Mg = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float a = M == -INFINITY ? 0.f : fast_exp2(M - Mg);
+  part[wave][2 * lane] = n0 * a;
+  part[wave][2 * lane + 1] = n1 * a;
+  if (lane == 0) part[wave][HD] = den * a;
   __syncthreads();
   if (tid < HD) {
     float num = 0.f, dsum = 0.f;
@@ -521,7 +539,7 @@ __device__ __forceinline__ void merge_records(const DecodeParams &p, int b, int 
     }
     o[tid] = to_bf16(dsum > 0.f ? num / dsum : 0.f);
     if (p.lse && tid == 0)
-      p.lse[(size_t)b * p.Hq + h] = dsum > 0.f ? (M + __log2f(dsum)) * kLn2 : -INFINITY;
+      p.lse[(size_t)b * p.Hq + h] = dsum > 0.f ? (Mg + __log2f(dsum)) * kLn2 : -INFINITY;
   }
 }
 
