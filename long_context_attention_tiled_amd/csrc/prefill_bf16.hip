@@ -140,7 +140,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p, int heads_
   const int per_q = p.B * p.Hkv * head_slices;
   const int item = CAUSAL && !PAGED ? xcd_item(blockIdx.x, per_q, n_qblk) : (int)blockIdx.x;
   int qblk = item / per_q;
-  if (CAUSAL && !PAGED) qblk = n_qblk - 1 - qblk;   // longest rows first
+  if (CAUSAL) qblk = n_qblk - 1 - qblk;   // longest rows first
   int rem = item % per_q;
   const int slice = rem % head_slices;
   rem /= head_slices;
