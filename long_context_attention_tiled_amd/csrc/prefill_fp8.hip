@@ -35,11 +35,10 @@ constexpr int NT = NW * 64;             // threads per workgroup
 constexpr int KT = BN * HD;             // bytes of one e4m3 K tile [64][128]
 constexpr int VT = BN * HD * 2;         // bytes of one bf16 V tile [64][128]
 constexpr int ST = 1024;                // bytes of a K-scale slot (4 copies of 64 words)
-constexpr int WD = 1;                   // DMAs are waited for WD iterations after issue
-constexpr int KA = WD + 3;              // iteration j fetches K_{j+KA}
-constexpr int VA = WD + 1;              // iteration j fetches V_{j+VA}
-constexpr int NKS = KA;                 // K (and K-scale) ring slots
-constexpr int NVS = VA + 2;             // V ring slots
+constexpr int KA = 5;                   // iteration j fetches K_{j+KA}
+constexpr int VA = 3;                   // iteration j fetches V_{j+VA}
+constexpr int NKS = 6;                  // K (and K-scale) ring slots
+constexpr int NVS = 6;                  // V ring slots
 constexpr int VBASE = NKS * KT;         // LDS byte offset of the V ring
 constexpr int SBASE = VBASE + NVS * VT; // LDS byte offset of the K-scale ring
 constexpr int LDS_BYTES = SBASE + NKS * ST;
@@ -50,8 +49,17 @@ constexpr int NDW = 4;                  // waves that issue the tile DMAs
 constexpr int KDPW = KT / 1024 / NDW;   // code DMAs per DMA wave and K tile
 constexpr int VDPW = VT / 1024 / NDW;   // DMAs per DMA wave and V tile
 constexpr int DPI = KDPW + 1 + VDPW;    // DMAs per DMA wave and iteration
-static_assert(KA >= WD + 3 && VA >= WD + 1, "tiles are published before their first read");
-static_assert(NKS == 4 && NVS == 4, "the interleaved loop is unrolled over a 4-slot ring");
+// Barriers come in pairs of iterations: only even iterations end with a DMA
+// wait and a barrier.  A tile fetched in an odd iteration j is published at
+// the end of j + 1, one fetched in an even iteration at the end of j + 2.
+// K_i is first read at the end of iteration i - 2 (operands read ahead)
+// and last read in iteration i - 1; V_i is first read at the end of
+// iteration i and last read in iteration i + 1.  The fetch in iteration j
+// follows the barrier of iteration j - 1 (j odd) or j - 2 (j even), and the
+// slot it fills must have been read for the last time before that barrier.
+static_assert(KA >= 5 && VA >= 3, "tiles are published before their first read");
+static_assert(NKS >= KA + 1 && NVS >= VA + 3, "a slot is refilled after its last read");
+static_assert(NKS == 6 && NVS == 6, "the interleaved loop is unrolled over a 6-slot ring");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 static_assert(KDPW == 2 && VDPW == 4, "row mapping of the DMAs");
 
@@ -166,8 +174,9 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillFp8Params p, int
     const int w = *reinterpret_cast<const int *>(smem + saddr + (ks / KT) * ST + 128 * hf);
     return (int)((uint32_t)w >> (8 * gq));
   };
-  auto next_k = [](int x) { return x + KT == NKS * KT ? 0 : x + KT; };
-  auto next_v = [](int x) { return x + VT == VBASE + NVS * VT ? VBASE : x + VT; };
+  // ring slots of K_t and V_t
+  auto k_slot = [](int t) { return (int)((unsigned)t % NKS) * KT; };
+  auto v_slot = [](int t) { return VBASE + (int)((unsigned)t % NVS) * VT; };
 
   const int qlast = CAUSAL ? min(n_keys - 1, qrow) : n_keys - 1;
 
@@ -349,15 +358,17 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillFp8Params p, int
   wait_vmcnt<0>();
   barrier_no_wait();
 
-  int kc = 0, vc = VBASE + (NVS - 2) * VT;
   auto fetch = [&](int j, int kdst, int vdst) __attribute__((always_inline)) {
     if (dma_wave) {
       issue_k(j + KA, kdst);
       issue_v(j + VA, vdst);
     }
   };
-  auto finish = [&](int j, int v_next, int k_next2) __attribute__((always_inline)) {
-    wait_vmcnt<DPI * WD>();   // DMAs of iterations j-WD+1 .. j may still fly
+  // End of iteration j: read the first operands of iteration j + 1; an even
+  // j first waits for the DMAs of j - 1 (those of j may still fly) and ends
+  // with the barrier that publishes them.
+  auto finish = [&](int j, int v_next, int k_next2, bool pair_end) __attribute__((always_inline)) {
+    if (pair_end) wait_vmcnt<DPI>();
     if (j < wave_tiles) {
 #pragma unroll
       for (int i = 0; i < NPV; ++i) vpre[i] = read_v(v_next, i);
@@ -368,7 +379,7 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillFp8Params p, int
       kswpre[0] = read_ksw(k_next2, 0);
       kswpre[1] = read_ksw(k_next2, 1);
     }
-    barrier_no_wait();
+    if (pair_end) barrier_no_wait();
   };
 
   // Interleaved iteration j (j >= 1, j + 1 < wave_tiles, no mask).  Twenty
@@ -384,7 +395,8 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillFp8Params p, int
     f32x16 (&sn)[2] = S[PAR ^ 1];
     bf16x8 (&pc)[4] = P[PAR];
     const bf16x8 (&pp)[4] = P[PAR ^ 1];
-    constexpr int kdma = R * KT, ks = ((R + 1) % NKS) * KT, kpre_s = ((R + 2) % NKS) * KT;
+    constexpr int kdma = ((R + KA) % NKS) * KT, ks = ((R + 1) % NKS) * KT,
+                  kpre_s = ((R + 2) % NKS) * KT;
     constexpr int vdma = VBASE + ((R + VA) % NVS) * VT, vs = VBASE + ((R + NVS - 1) % NVS) * VT,
                   vpre_s = VBASE + R * VT;
     fetch(j, kdma, vdma);
@@ -460,21 +472,18 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillFp8Params p, int
       }
       set_shift();
     }
-    finish(j, vpre_s, kpre_s);
+    finish(j, vpre_s, kpre_s, R % 2 == 0);   // j = R (mod NKS), NKS even
   };
 
   // Plain iteration j: whatever of P_{j-1} V_{j-1}, softmax(S_j), S_{j+1}
   // this wave still has, one after the other (ring positions at run time).
   auto plain = [&](int j, auto par_tag) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
-    const int vs = next_v(vc), ks = next_k(kc);   // V_{j-1}, K_{j+1}
-    fetch(j, kc, vc);
-    if (j >= 1 && j - 1 < wave_tiles) pv_plain(vs, P[PAR ^ 1]);
+    fetch(j, k_slot(j + KA), v_slot(j + VA));
+    if (j >= 1 && j - 1 < wave_tiles) pv_plain(opaque(v_slot(j + NVS - 1)), P[PAR ^ 1]);   // V_{j-1}
     if (j < wave_tiles) softmax_plain(j, S[PAR], P[PAR]);
-    if (j + 1 < wave_tiles) s_plain(ks, S[PAR ^ 1], true);
-    finish(j, next_v(vs), next_k(ks));
-    kc = next_k(kc);
-    vc = next_v(vc);
+    if (j + 1 < wave_tiles) s_plain(opaque(k_slot(j + 1)), S[PAR ^ 1], true);
+    finish(j, opaque(v_slot(j)), opaque(k_slot(j + 2)), (j & 1) == 0);
   };
 
   int fused_end = min(n_keys / BN, wave_tiles - 1);
@@ -482,19 +491,22 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillFp8Params p, int
   plain(0, Int<0>{});
   int j = 1;
 #pragma clang loop unroll(disable)
-  for (; j + 3 < fused_end; j += 4) {
+  for (; j + 5 < fused_end; j += 6) {
     fused(j, Int<1>{}, Int<1>{});
     fused(j + 1, Int<0>{}, Int<2>{});
     fused(j + 2, Int<1>{}, Int<3>{});
-    fused(j + 3, Int<0>{}, Int<0>{});
+    fused(j + 3, Int<0>{}, Int<4>{});
+    fused(j + 4, Int<1>{}, Int<5>{});
+    fused(j + 5, Int<0>{}, Int<0>{});
   }
-  kc = (j % NKS) * KT;
-  vc = VBASE + ((j + NVS - 2) % NVS) * VT;
 #pragma clang loop unroll(disable)
   for (; j <= n_tiles; j += 2) {
     plain(j, Int<1>{});
     if (j + 1 <= n_tiles) plain(j + 1, Int<0>{});
   }
+  // an odd last iteration ends without a wait: let its DMAs land before the
+  // workgroup's LDS is released
+  wait_vmcnt<0>();
 
   // ---- epilogue: divide by l once, store O (bf16) and LSE ----------------
   const float l_tot = pair_sum32(l_run);
