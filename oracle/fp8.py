@@ -179,18 +179,78 @@ def query_multiplier(scale):
     return np.float32(np.float32(scale) * np.float32(1.4426950408889634))
 
 
-def prefill_fp8_operands(q_bits, k_bits, scale):
+# ---------------------------------------------------------------------------
+# Incoherent processing: Q and K rotated before they are quantised
+# ---------------------------------------------------------------------------
+# FA3's FP8 path (same section) pairs block quantisation with incoherent
+# processing: Q and K are multiplied by one random orthogonal matrix before
+# quantisation, which leaves Q K^T unchanged and spreads a few large channels
+# over all of them.  The pages name the step and give no matrix.  Reading
+# taken here: M = diag(s) H, H the 128 x 128 Sylvester-Hadamard matrix
+# (H[i][j] = (-1)^popcount(i & j), entries +-1) and s a vector of +-1 signs
+# the caller draws; x -> x M for each 128-dim row.  H H^T = 128 I, so
+# (q M)(k M)^T = 128 q.k, and the query multiplier becomes c / 128 (exact: a
+# power of two).  Arithmetic, fixed so that quantised codes are reproducible:
+# the signs are applied to the bf16 values (exact), x H is the fast
+# Walsh-Hadamard transform in fp32 taken in the usual butterfly order (span
+# 1, 2, 4, ..., 64; element i with bit `span` clear pairs with i + span and
+# the pair becomes (a + b, a - b)), and the query is then multiplied by
+# c / 128 in fp32 (one rounding) before it is block-quantised.  V is not
+# rotated.
+HADAMARD_D = 128
+
+
+def hadamard_matrix(n=HADAMARD_D):
+    """Sylvester-Hadamard matrix of order n (a power of two), by doubling:
+    H_2n = [[H, H], [H, -H]]."""
+    h = np.ones((1, 1), dtype=np.int64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard_rotate(x, signs):
+    """x [..][128] (fp32 values) -> (s * x) H in fp32 by butterflies, in the
+    order stated above."""
+    s = np.asarray(signs)
+    if s.shape != (HADAMARD_D,) or not np.all(np.abs(s) == 1):
+        raise ValueError("oracle: signs must be 128 values of +-1")
+    y = (np.asarray(x, dtype=np.float32) * s.astype(np.float32)).astype(np.float32)
+    lead = y.shape[:-1]
+    span = 1
+    while span < HADAMARD_D:
+        y = y.reshape(*lead, HADAMARD_D // (2 * span), 2, span)
+        a, b = y[..., 0, :], y[..., 1, :]
+        y = np.stack([(a + b).astype(np.float32), (a - b).astype(np.float32)], axis=-2)
+        span *= 2
+    return y.reshape(*lead, HADAMARD_D)
+
+
+def prefill_fp8_operands(q_bits, k_bits, scale, signs=None):
     """Dequantised fp64 Q'' [..][D] (of q * c, log2 units) and K'' [..][D] from
-    bf16 bit patterns, following the reading above."""
+    bf16 bit patterns, following the reading above; with ``signs`` (128 values
+    +-1), Q and K are first rotated as stated above (then Q'' approximates
+    (q M) c / 128 and K'' approximates k M, whose product is c q.k)."""
     qf = (np.asarray(q_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
     kf = (np.asarray(k_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
-    qs = (qf * query_multiplier(scale)).astype(np.float32)      # fp32 product, as the kernel
+    c = query_multiplier(scale)
+    if signs is not None:
+        qf, kf = hadamard_rotate(qf, signs), hadamard_rotate(kf, signs)
+        c = np.float32(c / np.float32(HADAMARD_D))
+    qs = (qf * c).astype(np.float32)                 # fp32 product, as the kernel
     qc, qe = quantize_blocks(qs)
     kc, ke = quantize_blocks(kf)
     return dequantize_blocks(qc, qe), dequantize_blocks(kc, ke)
 
 
-def attention_fp8(q_bits, k_bits, v_bits, scale, causal=False, rows=None):
+def quantize_rotated_rows(x_bits, signs):
+    """K rows [..][128] bf16 bits -> (codes, exponents) of x M: the rotated
+    rows block-quantised (what the K quantiser with signs stores)."""
+    xf = (np.asarray(x_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return quantize_blocks(hadamard_rotate(xf, signs))
+
+
+def attention_fp8(q_bits, k_bits, v_bits, scale, causal=False, rows=None, signs=None):
     """What the FP8-score prefill computes, in fp64: attention over the
     dequantised Q'' (already in log2 units) and K'' with base-2 softmax,
     i.e. weights 2^(q''.k''), and V as given (bf16).  q [B][S][Hq][D],
@@ -199,7 +259,8 @@ def attention_fp8(q_bits, k_bits, v_bits, scale, causal=False, rows=None):
     import oracle
     B, S = q_bits.shape[:2]
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
-    qd, kd = prefill_fp8_operands(np.ascontiguousarray(np.asarray(q_bits)[:, rows]), k_bits, scale)
+    qd, kd = prefill_fp8_operands(np.ascontiguousarray(np.asarray(q_bits)[:, rows]), k_bits, scale,
+                                  signs)
     lim = (np.broadcast_to(rows[None, :] + 1, (B, rows.size)) if causal
            else np.full((B, rows.size), np.asarray(k_bits).shape[1], dtype=np.int64))
     # exp(ln 2 * s) = 2^s: the natural-log softmax of ln2-scaled scores
@@ -221,7 +282,7 @@ def dequantized_v_keys(v_bits):
     return np.ascontiguousarray(np.transpose(dequantize_blocks(c, e)[..., :S], (0, 3, 1, 2)))
 
 
-def attention_fp8_pv(q_bits, k_bits, v_bits, scale, causal=False, rows=None):
+def attention_fp8_pv(q_bits, k_bits, v_bits, scale, causal=False, rows=None, signs=None):
     """What the FP8-score, FP8-P.V prefill computes before P is rounded:
     attention_fp8 with V replaced by V'' (dequantised along keys).  The
     kernel also rounds the weights P to e4m3 before P V, which depends on its
@@ -230,7 +291,8 @@ def attention_fp8_pv(q_bits, k_bits, v_bits, scale, causal=False, rows=None):
     import oracle
     B, S = q_bits.shape[:2]
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
-    qd, kd = prefill_fp8_operands(np.ascontiguousarray(np.asarray(q_bits)[:, rows]), k_bits, scale)
+    qd, kd = prefill_fp8_operands(np.ascontiguousarray(np.asarray(q_bits)[:, rows]), k_bits, scale,
+                                  signs)
     lim = (np.broadcast_to(rows[None, :] + 1, (B, rows.size)) if causal
            else np.full((B, rows.size), np.asarray(k_bits).shape[1], dtype=np.int64))
     return oracle.attention_rows(qd, kd, dequantized_v_keys(v_bits), lim, float(np.log(2.0)))

@@ -128,6 +128,31 @@ def dense_bf16(seed: int, B: int, S: int, Hq: int, Hkv: int, D: int = 128):
     return dict(q=q, k=k, v=v, positions=pos, scale=float(1.0 / np.sqrt(D)))
 
 
+def dense_bf16_outliers(seed: int, B: int, S: int, Hq: int, Hkv: int, D: int = 128,
+                        n_channels: int = 4, q_gain: float = 8.0, k_gain: float = 2.0):
+    """dense_bf16 with a few outlier channels, the way a handful of feature
+    dimensions dominate the queries and keys of trained models: the same
+    ``n_channels`` head dims (a seeded choice) of every Q row are multiplied
+    by ``q_gain`` and of every K row by ``k_gain`` before rounding to bf16.
+    With the defaults the scores have a standard deviation of about 3 (in
+    natural-log units, after 1/sqrt(D)).  V is N(0, 1)."""
+    sq, sk, sv, sc = _seq(seed).spawn(4)
+    ch = np.random.default_rng(sc).choice(D, size=n_channels, replace=False)
+    gq = np.ones(D, np.float32)
+    gk = np.ones(D, np.float32)
+    gq[ch], gk[ch] = q_gain, k_gain
+    q = f32_to_bf16_bits(normal_f32(sq, (B, S, Hq, D)) * gq)
+    k = f32_to_bf16_bits(normal_f32(sk, (B, S, Hkv, D)) * gk)
+    v = normal_bf16(sv, (B, S, Hkv, D))
+    pos = np.arange(S, dtype=np.int32)
+    return dict(q=q, k=k, v=v, positions=pos, scale=float(1.0 / np.sqrt(D)), channels=np.sort(ch))
+
+
+def hadamard_signs(seed: int, D: int = 128) -> np.ndarray:
+    """The random signs (+1 / -1, int8) of the incoherent-processing rotation."""
+    return np.random.default_rng(_seq(seed)).choice(np.array([-1, 1], np.int8), size=D)
+
+
 def causal_gqa(seed: int = 2, S: int = 32768, Hq: int = 16, Hkv: int = 2, D: int = 128):
     """One sequence-parallel shard's heads: batch 1, full sequence, causal GQA."""
     return dense_bf16(seed, 1, S, Hq, Hkv, D)
