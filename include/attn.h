@@ -237,14 +237,26 @@ int attn_decode_fp8(const void *q, const void *k8_pool, const void *v8_pool, con
  * E8M0 byte e + 127.  attn_prefill_fp8 runs S = Q K^T on FP8 (P V in bf16);
  * attn_prefill_fp8_pv runs both products on FP8.
  *
+ * Incoherent processing (the other half of FA3's FP8 path in [FA18] §18.5):
+ * `signs`, when not NULL, is a HOST array of 128 values, each +1 or -1
+ * (ATTN_ERR_SHAPE otherwise), that the caller draws once.  Q and K rows are
+ * then rotated before they are quantised: x -> (s * x) H, H the 128 x 128
+ * Sylvester-Hadamard matrix (H[i][j] = (-1)^popcount(i & j)), computed in
+ * fp32 as butterflies of span 1, 2, 4, ..., 64 (pairs (i, i + span) with bit
+ * `span` of i clear become (a + b, a - b)), so the codes are reproducible.
+ * Since H H^T = 128 I the scores keep their values: the query multiplier
+ * becomes scale * log2(e) / 128.  K must be quantised with the same signs
+ * that the prefill receives; V is not rotated.
+ *
  * attn_quantize_fp8_blocks — x [rows][D] bf16 -> codes [rows][D] e4m3 and
  *   scales [rows][D/32] E8M0 bytes (block i of a row covers elements
- *   32i .. 32i+31).  D % 32 == 0 (ATTN_ERR_UNSUPPORTED otherwise); x and
- *   codes 16-byte aligned; no buffer may overlap another (ATTN_ERR_SHAPE).
- *   Codes and scales are fixed by the rule above (bit-exact).
+ *   32i .. 32i+31).  D % 32 == 0 (ATTN_ERR_UNSUPPORTED otherwise); with
+ *   signs, each row is rotated first and D must be 128; x and codes
+ *   16-byte aligned; no buffer may overlap another (ATTN_ERR_SHAPE).  Codes
+ *   and scales are fixed by the rules above (bit-exact).
  */
 int attn_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scales, long long rows, int D,
-                             void *stream);
+                             const int8_t *signs, void *stream);
 
 /*
  * attn_prefill_fp8 — attn_prefill (dense, causal or not) with the scores on
@@ -255,11 +267,14 @@ int attn_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scales, long l
  * so the result is exact attention over the dequantised query (in log2 units,
  * base-2 softmax) and key, with P rounded to bf16 before P V (fp32
  * accumulation) and o bf16; lse [B][Hq][S] fp32 natural log, or NULL.
+ * With signs (NULL: none), each query row is rotated as stated above before
+ * it is multiplied (by scale * log2(e) / 128) and quantised, and k8 /
+ * k_scale must come from attn_quantize_fp8_blocks with the same signs.
  * D must be 128, Hq/Hkv must divide 8 or be a multiple of 8.
  */
 int attn_prefill_fp8(const void *q, const void *k8, const uint8_t *k_scale, const void *v, void *o,
                      float *lse, int B, int S, int Hq, int Hkv, int D, int causal, float scale,
-                     void *stream);
+                     const int8_t *signs, void *stream);
 
 /*
  * attn_quantize_fp8_v — V for attn_prefill_fp8_pv: v [B][S][Hkv][128] bf16 ->
@@ -286,12 +301,13 @@ int attn_quantize_fp8_v(const void *v, void *v8t, uint8_t *v_scale, int B, int S
  * O = sum P' V'' / sum P' with V'' the dequantised V and both sums over the
  * same rounded weights (fp32 accumulation); o bf16; lse [B][Hq][S] fp32
  * natural log of the row's sum of exp(scores), from the same rounded
- * weights, or NULL.  D must be 128, Hq/Hkv must divide 8 or be a multiple
- * of 8, D * S64 < 2^31.
+ * weights, or NULL.  signs as in attn_prefill_fp8 (Q and K rotated, V
+ * not).  D must be 128, Hq/Hkv must divide 8 or be a multiple of 8,
+ * D * S64 < 2^31.
  */
 int attn_prefill_fp8_pv(const void *q, const void *k8, const uint8_t *k_scale, const void *v8t,
                         const uint8_t *v_scale, void *o, float *lse, int B, int S, int Hq, int Hkv,
-                        int D, int causal, float scale, void *stream);
+                        int D, int causal, float scale, const int8_t *signs, void *stream);
 
 /*
  * rope_apply — rotary position embedding at absolute token positions, in

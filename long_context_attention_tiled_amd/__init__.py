@@ -336,9 +336,24 @@ def attn_decode_fp8(q, k8_pool, v8_pool, k_scale, v_scale, block_head, block_tab
     return o, lse
 
 
-def attn_quantize_fp8_blocks(x, codes=None, scales=None, stream=None):
+def _signs(signs):
+    """Host int8 array of the 128 rotation signs (or None) for the C ABI; the
+    library checks that every entry is +1 or -1."""
+    if signs is None:
+        return None, None
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(signs, dtype=np.int64).reshape(-1).astype(np.int8))
+    if a.size != 128:
+        raise ValueError("signs must hold 128 values of +1 or -1")
+    return a, a.ctypes.data
+
+
+def attn_quantize_fp8_blocks(x, codes=None, scales=None, signs=None, stream=None):
     """bf16 ``x [..][D]`` -> (e4m3 codes uint8 ``[..][D]``, E8M0 scales uint8
-    ``[..][D/32]``): one power-of-two scale per 32 consecutive elements."""
+    ``[..][D/32]``): one power-of-two scale per 32 consecutive elements.
+    With ``signs`` (128 values +-1), each row (D = 128) is first rotated by
+    the incoherent-processing transform that :func:`attn_prefill_fp8` and
+    :func:`attn_prefill_fp8_pv` apply to Q with the same signs."""
     torch = _torch()
     _need(x, "x", torch.bfloat16)
     D = x.shape[-1]
@@ -349,15 +364,19 @@ def attn_quantize_fp8_blocks(x, codes=None, scales=None, stream=None):
         scales = torch.empty((*x.shape[:-1], D // 32), dtype=torch.uint8, device=x.device)
     _need(codes, "codes", torch.uint8, tuple(x.shape))
     _need(scales, "scales", torch.uint8, (*x.shape[:-1], D // 32))
-    st = _lib.load().attn_quantize_fp8_blocks(_ptr(x), _ptr(codes), _ptr(scales), rows, D,
+    keep, sp = _signs(signs)
+    st = _lib.load().attn_quantize_fp8_blocks(_ptr(x), _ptr(codes), _ptr(scales), rows, D, sp,
                                               _stream(stream))
+    del keep
     _lib.check("attn_quantize_fp8_blocks", st)
     return codes, scales
 
 
-def attn_prefill_fp8(q, k8, k_scale, v, causal=True, scale=None, o=None, lse=None, stream=None):
+def attn_prefill_fp8(q, k8, k_scale, v, causal=True, scale=None, o=None, lse=None, signs=None,
+                     stream=None):
     """Prefill with FP8 scores: q, v bf16 ``[B][S][H][128]``, k8 / k_scale from
-    :func:`attn_quantize_fp8_blocks` on K; returns ``(o, lse)``."""
+    :func:`attn_quantize_fp8_blocks` on K (with the same ``signs``, when Q is
+    to be rotated); returns ``(o, lse)``."""
     torch = _torch()
     _need(q, "q", torch.bfloat16)
     B, S, Hq, D = q.shape
@@ -372,9 +391,11 @@ def attn_prefill_fp8(q, k8, k_scale, v, causal=True, scale=None, o=None, lse=Non
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     _need(lse, "lse", torch.float32, (B, Hq, S))
     scale = float(D ** -0.5) if scale is None else float(scale)
+    keep, sp = _signs(signs)
     st = _lib.load().attn_prefill_fp8(_ptr(q), _ptr(k8), _ptr(k_scale), _ptr(v), _ptr(o),
-                                      _ptr(lse), B, S, Hq, Hkv, D, int(bool(causal)), scale,
+                                      _ptr(lse), B, S, Hq, Hkv, D, int(bool(causal)), scale, sp,
                                       _stream(stream))
+    del keep
     _lib.check("attn_prefill_fp8", st)
     return o, lse
 
@@ -401,9 +422,10 @@ def attn_quantize_fp8_v(v, v8t=None, v_scale=None, stream=None):
 
 
 def attn_prefill_fp8_pv(q, k8, k_scale, v8t, v_scale, causal=True, scale=None, o=None, lse=None,
-                        stream=None):
+                        signs=None, stream=None):
     """Prefill with both products on FP8: q bf16 ``[B][S][Hq][128]``, k8 /
-    k_scale from :func:`attn_quantize_fp8_blocks` on K, v8t / v_scale from
+    k_scale from :func:`attn_quantize_fp8_blocks` on K (with the same
+    ``signs``, when Q is to be rotated), v8t / v_scale from
     :func:`attn_quantize_fp8_v`; returns ``(o, lse)``."""
     torch = _torch()
     _need(q, "q", torch.bfloat16)
@@ -421,9 +443,11 @@ def attn_prefill_fp8_pv(q, k8, k_scale, v8t, v_scale, causal=True, scale=None, o
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     _need(lse, "lse", torch.float32, (B, Hq, S))
     scale = float(D ** -0.5) if scale is None else float(scale)
+    keep, sp = _signs(signs)
     st = _lib.load().attn_prefill_fp8_pv(_ptr(q), _ptr(k8), _ptr(k_scale), _ptr(v8t),
                                          _ptr(v_scale), _ptr(o), _ptr(lse), B, S, Hq, Hkv, D,
-                                         int(bool(causal)), scale, _stream(stream))
+                                         int(bool(causal)), scale, sp, _stream(stream))
+    del keep
     _lib.check("attn_prefill_fp8_pv", st)
     return o, lse
 

@@ -43,11 +43,12 @@ SIGNATURES = {
     "attn_kv_quantize_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp]),
     "attn_kv_append_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i,
                                 _i, _i, _vp, _vp]),
-    "attn_quantize_fp8_blocks": (_i, [_vp, _vp, _vp, _ll, _i, _vp]),
-    "attn_prefill_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp]),
+    "attn_quantize_fp8_blocks": (_i, [_vp, _vp, _vp, _ll, _i, _vp, _vp]),
+    "attn_prefill_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp,
+                              _vp]),
     "attn_quantize_fp8_v": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_prefill_fp8_pv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
-                                 _vp]),
+                                 _vp, _vp]),
     "rope_apply": (_i, [_vp, _vp, _i, _i, _i, _f, _vp]),
     "seq_to_head_permute": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "head_to_seq_permute": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),

@@ -92,6 +92,19 @@ bool qkv_disjoint(const void *const in[3], void *const out[3], const int H[3], i
 inline int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
 // GQA group sizes the bf16 kernels handle: divisors of 8 or multiples of 8.
+// Host signs (128 values of +1 or -1, or NULL) -> the rotation's sign mask.
+// Returns false when an entry is neither +1 nor -1.
+inline bool hadamard_signs(const int8_t *signs, lcat::HadamardSigns &sg) {
+  sg = lcat::HadamardSigns{};
+  if (!signs) return true;
+  for (int i = 0; i < 128; ++i) {
+    if (signs[i] != 1 && signs[i] != -1) return false;
+    if (signs[i] < 0) sg.neg[i >> 5] |= 1u << (i & 31);
+  }
+  sg.on = 1;
+  return true;
+}
+
 inline bool group_ok(int Hq, int Hkv) {
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return false;
   const int g = Hq / Hkv;
@@ -234,9 +247,11 @@ int attn_prefill(const void *q, const void *k, const void *v, void *o, float *ls
 }
 
 int attn_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scales, long long rows, int D,
-                             void *stream) {
+                             const int8_t *signs, void *stream) {
   if (rows < 0 || D <= 0) return ATTN_ERR_SHAPE;
-  if (D % 32) return ATTN_ERR_UNSUPPORTED;
+  if (D % 32 || (signs && D != kHeadDim)) return ATTN_ERR_UNSUPPORTED;
+  lcat::HadamardSigns sg;
+  if (!hadamard_signs(signs, sg)) return ATTN_ERR_SHAPE;
   if (rows == 0) return ATTN_OK;
   if (!x || !codes || !scales) return ATTN_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes)) return ATTN_ERR_ALIGN;
@@ -248,15 +263,20 @@ int attn_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scales, long l
   if (overlap(x, 2 * n, codes, n) || overlap(x, 2 * n, scales, n / 32) ||
       overlap(codes, n, scales, n / 32))
     return ATTN_ERR_SHAPE;
+  if (sg.on)
+    return hip_status(lcat::launch_quantize_fp8_rotated(x, codes, scales, rows, sg,
+                                                        static_cast<hipStream_t>(stream)));
   return hip_status(lcat::launch_quantize_fp8_blocks(x, codes, scales, n / 32,
                                                      static_cast<hipStream_t>(stream)));
 }
 
 int attn_prefill_fp8(const void *q, const void *k8, const uint8_t *k_scale, const void *v, void *o,
                      float *lse, int B, int S, int Hq, int Hkv, int D, int causal, float scale,
-                     void *stream) {
+                     const int8_t *signs, void *stream) {
   if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return ATTN_ERR_SHAPE;
   if (D != kHeadDim || !group_ok(Hq, Hkv)) return ATTN_ERR_UNSUPPORTED;
+  lcat::HadamardSigns sg;
+  if (!hadamard_signs(signs, sg)) return ATTN_ERR_SHAPE;
   if (B == 0 || S == 0) return ATTN_OK;
   if (!q || !k8 || !k_scale || !v || !o) return ATTN_ERR_NULL;
   if (!aligned16(q) || !aligned16(k8) || !aligned16(v) || !aligned16(o) ||
@@ -267,6 +287,7 @@ int attn_prefill_fp8(const void *q, const void *k8, const uint8_t *k_scale, cons
   p.B = B; p.S = S; p.Hq = Hq; p.Hkv = Hkv;
   p.causal = causal != 0;
   p.scale = scale;
+  p.rot = sg;
   return hip_status(lcat::launch_prefill_fp8(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -294,9 +315,11 @@ int attn_quantize_fp8_v(const void *v, void *v8t, uint8_t *v_scale, int B, int S
 
 int attn_prefill_fp8_pv(const void *q, const void *k8, const uint8_t *k_scale, const void *v8t,
                         const uint8_t *v_scale, void *o, float *lse, int B, int S, int Hq, int Hkv,
-                        int D, int causal, float scale, void *stream) {
+                        int D, int causal, float scale, const int8_t *signs, void *stream) {
   if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return ATTN_ERR_SHAPE;
   if (D != kHeadDim || !group_ok(Hq, Hkv)) return ATTN_ERR_UNSUPPORTED;
+  lcat::HadamardSigns sg;
+  if (!hadamard_signs(signs, sg)) return ATTN_ERR_SHAPE;
   if (B == 0 || S == 0) return ATTN_OK;
   if ((long long)D * (((long long)S + 63) / 64 * 64) > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
   if (!q || !k8 || !k_scale || !v8t || !v_scale || !o) return ATTN_ERR_NULL;
@@ -308,6 +331,7 @@ int attn_prefill_fp8_pv(const void *q, const void *k8, const uint8_t *k_scale, c
   p.B = B; p.S = S; p.Hq = Hq; p.Hkv = Hkv;
   p.causal = causal != 0;
   p.scale = scale;
+  p.rot = sg;
   return hip_status(lcat::launch_prefill_fp8_pv(p, static_cast<hipStream_t>(stream)));
 }
 

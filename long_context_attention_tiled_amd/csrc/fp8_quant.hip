@@ -5,6 +5,7 @@
 // consecutive blocks, so loads and stores are contiguous per wave.
 #include "device.h"
 #include "fp8_block.h"
+#include "hadamard.h"
 #include "kernels.h"
 
 namespace lcat {
@@ -39,6 +40,46 @@ __global__ __launch_bounds__(256) void quantize_fp8_blocks_kernel(const bf16 *__
   st_global_16(dst, out[0]);
   st_global_16(dst + 16, out[1]);
   scales[blk] = (uint8_t)(e + 127);
+}
+
+// Rows of 128 rotated by (s * x) H (hadamard.h) and then block-quantised
+// as above: one thread per row (the transform needs the whole row), 256
+// bytes in, 128 code bytes and the row's 4 scale bytes out.
+__global__ __launch_bounds__(256) void quantize_fp8_rotated_kernel(const bf16 *__restrict__ x,
+                                                                   uint8_t *__restrict__ codes,
+                                                                   uint8_t *__restrict__ scales,
+                                                                   long long n_rows, HadamardSigns sg) {
+  const long long row = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (row >= n_rows) return;
+  const bf16 *src = x + row * 128;
+  float v[128];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bf16x8 raw = as_bf16x8(ld_global_16(src + 8 * i));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[8 * i + e] = (float)raw[e];
+  }
+  hadamard128(v, sg);
+  uint32_t sc = 0;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[32 * blk + i]));
+    const int e = fp8_block_exponent(amax);
+    sc |= (uint32_t)(e + 127) << (8 * blk);
+    u32x4 out[2];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const float *y = v + 32 * blk + 4 * w;
+      out[w >> 2][w & 3] = fp8x4_rne(__builtin_amdgcn_ldexpf(y[0], -e), __builtin_amdgcn_ldexpf(y[1], -e),
+                                     __builtin_amdgcn_ldexpf(y[2], -e), __builtin_amdgcn_ldexpf(y[3], -e));
+    }
+    uint8_t *dst = codes + row * 128 + 32 * blk;
+    st_global_16(dst, out[0]);
+    st_global_16(dst + 16, out[1]);
+  }
+  *reinterpret_cast<uint32_t *>(scales + row * 4) = sc;
 }
 
 // V for FP8 P V: blocks run along keys (the contraction axis of P V), one
@@ -100,6 +141,16 @@ hipError_t launch_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scale
   hipLaunchKernelGGL(quantize_fp8_blocks_kernel, dim3((unsigned)n_wg), dim3(256), 0, stream,
                      static_cast<const bf16 *>(x), static_cast<uint8_t *>(codes), scales,
                      n_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8_rotated(const void *x, void *codes, uint8_t *scales,
+                                       long long n_rows, HadamardSigns sg, hipStream_t stream) {
+  if (n_rows <= 0) return hipSuccess;
+  const long long n_wg = (n_rows + 255) / 256;
+  if (n_wg > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quantize_fp8_rotated_kernel, dim3((unsigned)n_wg), dim3(256), 0, stream,
+                     static_cast<const bf16 *>(x), static_cast<uint8_t *>(codes), scales, n_rows, sg);
   return hipGetLastError();
 }
 

@@ -31,8 +31,18 @@ struct PrefillParams {
 
 hipError_t launch_prefill_bf16(const PrefillParams &p, bool paged, hipStream_t stream);
 
+// Signs of the incoherent-processing rotation x -> (s * x) H of 128-element
+// rows (hadamard.h): bit i of neg is set when s_i = -1; on = 0 means no
+// rotation.
+struct HadamardSigns {
+  uint32_t neg[4];
+  int on;
+};
+
 // Dense prefill with FP8 (e4m3) scores: q and v bf16, k as e4m3 codes with
 // one E8M0 scale per 32 head dims (attn_quantize_fp8_blocks), head_dim 128.
+// With rot.on, each query row is rotated before it is quantised, and k8 must
+// hold the rows of K rotated with the same signs.
 struct PrefillFp8Params {
   const void *q;            // [B][S][Hq][128] bf16
   const void *k8;           // [B][S][Hkv][128] e4m3
@@ -43,6 +53,7 @@ struct PrefillFp8Params {
   int B, S, Hq, Hkv;
   int causal;
   float scale;
+  HadamardSigns rot;
 };
 
 hipError_t launch_prefill_fp8(const PrefillFp8Params &p, hipStream_t stream);
@@ -61,6 +72,7 @@ struct PrefillFp8PvParams {
   int B, S, Hq, Hkv;
   int causal;
   float scale;
+  HadamardSigns rot;
 };
 
 hipError_t launch_prefill_fp8_pv(const PrefillFp8PvParams &p, hipStream_t stream);
@@ -73,6 +85,11 @@ hipError_t launch_quantize_fp8_v(const void *v, void *v8t, uint8_t *v_scale, int
 // one E8M0 scale byte per block of 32 consecutive values.
 hipError_t launch_quantize_fp8_blocks(const void *x, void *codes, uint8_t *scales,
                                       long long n_blocks, hipStream_t stream);
+
+// Rows of 128 bf16 values rotated by (s * x) H (hadamard.h), then block
+// quantised as above: codes [n_rows][128], scales [n_rows][4].
+hipError_t launch_quantize_fp8_rotated(const void *x, void *codes, uint8_t *scales,
+                                       long long n_rows, HadamardSigns sg, hipStream_t stream);
 
 hipError_t launch_attn_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                            int B, int S, int Hq, int Hkv, int D, int causal, float scale,

@@ -126,9 +126,10 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillFp8Params p, int
   const float c2 = p.scale * kLog2e;
   const int qrow = row0 + lr;
   i32x8 qf[2];
-  const int qsw = quantize_query_row(
-      static_cast<const bf16 *>(p.q) + (((size_t)b * p.S + min(qrow, p.S - 1)) * p.Hq + h) * HD, gq,
-      c2, qf);
+  const bf16 *qrow_p =
+      static_cast<const bf16 *>(p.q) + (((size_t)b * p.S + min(qrow, p.S - 1)) * p.Hq + h) * HD;
+  const int qsw = p.rot.on ? quantize_query_row_rotated(qrow_p, gq, c2 * (1.0f / 128), p.rot, qf)
+                           : quantize_query_row(qrow_p, gq, c2, qf);
 #pragma unroll
   for (int c = 0; c < 2; ++c) asm volatile("" ::"v"(qf[c]));
 

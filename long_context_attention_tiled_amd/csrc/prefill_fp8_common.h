@@ -13,6 +13,7 @@
 
 #include "device.h"
 #include "fp8_block.h"
+#include "hadamard.h"
 
 namespace lcat {
 
@@ -41,23 +42,16 @@ __device__ __forceinline__ void dma_to_lds_4(u32x4 rsrc, char *lds_dst, int voff
       : "m0");
 }
 
-// One query row of head_dim 128 (qp: its first element) as the two B
-// operands of S^T = K Q^T on the scaled FP8 MFMA, for the lane in half gq of
-// the wave.  Every element is multiplied by c2 in fp32 and block-quantised
-// with the rule of fp8_block.h (blocks of 32 dims; the other 16 dims of each
-// block sit in lane l ^ 32).  qf[c] covers dims 64c .. 64c+63: bytes 0..15
-// hold dims 64c + 16 gq .. +15 and bytes 16..31 dims 64c + 32 + 16 gq .. +15.
-// The returned scale word holds the E8M0 scale of block 2c + gq in byte 2c.
-__device__ __forceinline__ int quantize_query_row(const bf16 *qp, int gq, float c2, i32x8 (&qf)[2]) {
-  bf16x8 raw[2][2][2];   // [c][part][8 dims]
-#pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        raw[c][pt][i] = as_bf16x8(ld_global_16(qp + 64 * c + 32 * pt + 16 * gq + 8 * i));
-  float y[2][2][16];
+// A lane's 64 values of one query row as the two B operands of S^T = K Q^T
+// on the scaled FP8 MFMA, for the lane in half gq of the wave: y[c][pt][e] is
+// dim 64c + 32pt + 16gq + e, already multiplied by the query multiplier.
+// Each block of 32 dims is quantised with the rule of fp8_block.h (the other
+// 16 dims of a block sit in lane l ^ 32).  qf[c] covers dims 64c .. 64c+63:
+// bytes 0..15 hold dims 64c + 16 gq .. +15 and bytes 16..31 dims
+// 64c + 32 + 16 gq .. +15.  The returned scale word holds the E8M0 scale of
+// block 2c + gq in byte 2c.
+__device__ __forceinline__ int quantize_query_values(const float (&y)[2][2][16], int gq,
+                                                     i32x8 (&qf)[2]) {
   int eb[2][2];
 #pragma unroll
   for (int c = 0; c < 2; ++c)
@@ -65,10 +59,7 @@ __device__ __forceinline__ int quantize_query_row(const bf16 *qp, int gq, float 
     for (int pt = 0; pt < 2; ++pt) {
       float am = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        y[c][pt][e] = (float)raw[c][pt][e >> 3][e & 7] * c2;
-        am = fmaxf(am, fabsf(y[c][pt][e]));
-      }
+      for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(y[c][pt][e]));
       eb[c][pt] = fp8_block_exponent(pair_max32(am));
     }
 #pragma unroll
@@ -84,6 +75,51 @@ __device__ __forceinline__ int quantize_query_row(const bf16 *qp, int gq, float 
       }
   const int e0 = gq ? eb[0][1] : eb[0][0], e1 = gq ? eb[1][1] : eb[1][0];
   return (e0 + 127) | ((e1 + 127) << 16);
+}
+
+// One query row of head_dim 128 (qp: its first element): every element is
+// multiplied by c2 in fp32, then quantised as above.
+__device__ __forceinline__ int quantize_query_row(const bf16 *qp, int gq, float c2, i32x8 (&qf)[2]) {
+  bf16x8 raw[2][2][2];   // [c][part][8 dims]
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        raw[c][pt][i] = as_bf16x8(ld_global_16(qp + 64 * c + 32 * pt + 16 * gq + 8 * i));
+  float y[2][2][16];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) y[c][pt][e] = (float)raw[c][pt][e >> 3][e & 7] * c2;
+  return quantize_query_values(y, gq, qf);
+}
+
+// The same row rotated first (hadamard.h): both lanes of a row take the
+// whole row through the transform, each keeps its 64 dims, multiplies them
+// by c2r (the query multiplier divided by 128) in fp32 and quantises them.
+__device__ __forceinline__ int quantize_query_row_rotated(const bf16 *qp, int gq, float c2r,
+                                                          const HadamardSigns &sg, i32x8 (&qf)[2]) {
+  float v[128];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bf16x8 raw = as_bf16x8(ld_global_16(qp + 8 * i));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[8 * i + e] = (float)raw[e];
+  }
+  hadamard128(v, sg);
+  float y[2][2][16];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        y[c][pt][e] = (gq ? v[64 * c + 32 * pt + 16 + e] : v[64 * c + 32 * pt + e]) * c2r;
+  return quantize_query_values(y, gq, qf);
 }
 
 }  // namespace lcat

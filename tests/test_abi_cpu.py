@@ -164,19 +164,28 @@ def test_decode_noalloc_validation(lib):
 def test_fp8_prefill_validation(lib):
     qz, pf = lib.attn_quantize_fp8_blocks, lib.attn_prefill_fp8
     codes, sc = P(0x200000), P(0x300000)
-    assert qz(A16, codes, sc, -1, 128, S0) == SHAPE
-    assert qz(A16, codes, sc, 4, 48, S0) == UNSUP          # D % 32 != 0
-    assert qz(A16, codes, sc, 0, 128, S0) == OK
-    assert qz(NUL, codes, sc, 4, 128, S0) == NULL
-    assert qz(MIS, codes, sc, 4, 128, S0) == ALIGN
-    assert qz(A16, P(0x10000 + 512), sc, 4, 128, S0) == SHAPE   # codes overlap x
+    assert qz(A16, codes, sc, -1, 128, NUL, S0) == SHAPE
+    assert qz(A16, codes, sc, 4, 48, NUL, S0) == UNSUP          # D % 32 != 0
+    assert qz(A16, codes, sc, 0, 128, NUL, S0) == OK
+    assert qz(NUL, codes, sc, 4, 128, NUL, S0) == NULL
+    assert qz(MIS, codes, sc, 4, 128, NUL, S0) == ALIGN
+    assert qz(A16, P(0x10000 + 512), sc, 4, 128, NUL, S0) == SHAPE   # codes overlap x
+    # rotation signs: a host array of 128 values, each +1 or -1, and D = 128
+    good = (ctypes.c_int8 * 128)(*([1, -1] * 64))
+    bad = (ctypes.c_int8 * 128)(*([1] * 127 + [0]))
+    sp = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    assert qz(A16, codes, sc, 0, 128, sp(good), S0) == OK
+    assert qz(A16, codes, sc, 0, 128, sp(bad), S0) == SHAPE
+    assert qz(A16, codes, sc, 4, 64, sp(good), S0) == UNSUP       # rotation needs D = 128
     args = lambda **kw: [kw.get(n, d) for n, d in (("q", A16), ("k8", A16), ("ks", A16), ("v", A16), ("o", A16))]
-    def call(B=1, S=64, Hq=16, Hkv=2, D=128, **kw):
-        return pf(*args(**kw), NUL, B, S, Hq, Hkv, D, 1, 0.1, S0)
+    def call(B=1, S=64, Hq=16, Hkv=2, D=128, signs=NUL, **kw):
+        return pf(*args(**kw), NUL, B, S, Hq, Hkv, D, 1, 0.1, signs, S0)
     assert call(Hq=15) == SHAPE
     assert call(D=64) == UNSUP
     assert call(Hq=6, Hkv=2) == UNSUP                        # group 3
     assert call(S=0) == OK
+    assert call(S=0, signs=sp(good)) == OK
+    assert call(S=0, signs=sp(bad)) == SHAPE
     assert call(k8=NUL) == NULL
     assert call(ks=P(0x10002)) == ALIGN                     # scales 4-byte aligned
     assert call(v=MIS) == ALIGN
@@ -194,9 +203,11 @@ def test_fp8_pv_prefill_validation(lib):
     assert qv(A16, P(0x10000 + 4096), vs, 1, 64, 2, 128, S0) == SHAPE   # codes overlap v
     assert qv(A16, v8, vs, 1, 1 << 24, 2, 128, S0) == SHAPE      # 128 * S64 >= 2^31
     names = ("q", "k8", "ks", "v8", "vs", "o")
-    def call(B=1, S=64, Hq=16, Hkv=2, D=128, **kw):
+    def call(B=1, S=64, Hq=16, Hkv=2, D=128, signs=NUL, **kw):
         ptrs = [kw.get(n, A16) for n in names]
-        return pf(*ptrs, NUL, B, S, Hq, Hkv, D, 1, 0.1, S0)
+        return pf(*ptrs, NUL, B, S, Hq, Hkv, D, 1, 0.1, signs, S0)
+    bad = (ctypes.c_int8 * 128)(*([-1] * 64 + [2] * 64))
+    assert call(S=0, signs=ctypes.cast(bad, ctypes.c_void_p)) == SHAPE
     assert call(Hq=15) == SHAPE
     assert call(D=64) == UNSUP
     assert call(Hq=6, Hkv=2) == UNSUP                          # group 3

@@ -107,6 +107,70 @@ def test_prefill_fp8_long_rows(S, B, Hq, Hkv, causal, stepped):
     log(f"  max abs {e:.3g} rel-L2 {r:.3g}")
 
 
+@pytest.mark.parametrize("rows,outliers", [(1, True), (37, False), (4096, True), (65536, True)])
+def test_quantize_fp8_rotated_bit_exact(rows, outliers):
+    """K rows rotated by diag(s) H (fp32 butterflies in the stated order) and
+    block-quantised: codes and scale bytes equal to the oracle's."""
+    gen = synth.dense_bf16_outliers if outliers else synth.dense_bf16
+    d = gen(seed=570 + rows, B=1, S=rows, Hq=1, Hkv=1)
+    signs = synth.hadamard_signs(571 + rows)
+    log(f"quantize fp8 rotated rows={rows} outliers={outliers}")
+    codes, scales = lcat.attn_quantize_fp8_blocks(to_dev(d["k"]), signs=signs)
+    torch.cuda.synchronize()
+    want_c, want_e = ofp8.quantize_rotated_rows(d["k"], signs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), want_c)
+    np.testing.assert_array_equal(scales.cpu().numpy(), ofp8.e8m0_bytes(want_e))
+
+
+@pytest.mark.parametrize("S,B,Hq,Hkv,causal,outliers", [
+    (300, 2, 16, 2, True, True), (640, 1, 16, 2, False, True), (200, 1, 8, 8, True, False),
+    (1100, 1, 16, 2, True, True), (1300, 1, 4, 4, True, True),
+])
+def test_prefill_fp8_rotated_vs_oracle(S, B, Hq, Hkv, causal, outliers):
+    """FP8 scores with incoherent processing: every row against the oracle
+    over the rotated, dequantised Q and K."""
+    log(f"prefill fp8 rotated S={S} B={B} Hq={Hq} Hkv={Hkv} causal={causal} outliers={outliers}")
+    gen = synth.dense_bf16_outliers if outliers else synth.dense_bf16
+    d = gen(seed=580 + S, B=B, S=S, Hq=Hq, Hkv=Hkv)
+    signs = synth.hadamard_signs(581 + S)
+    k8, ks = lcat.attn_quantize_fp8_blocks(to_dev(d["k"]), signs=signs)
+    o, lse = lcat.attn_prefill_fp8(to_dev(d["q"]), k8, ks, to_dev(d["v"]), causal=causal,
+                                   scale=d["scale"], signs=signs)
+    torch.cuda.synchronize()
+    ref, ref_lse = ofp8.attention_fp8(d["q"], d["k"], d["v"], d["scale"], causal=causal, signs=signs)
+    e, r = assert_attention_close(to_np64(o), ref, lse.cpu().numpy(), ref_lse,
+                                  what="prefill fp8 rotated")
+    log(f"  max abs {e:.3g} rel-L2 {r:.3g}")
+
+
+def test_rotation_lowers_gpu_fp8_error_on_outlier_channels():
+    """Both FP8 prefills on inputs with outlier channels in Q and K: with the
+    rotation their outputs are at least 1.6 times closer (relative L2) to
+    exact attention of the bf16 inputs than without it."""
+    S = 2048
+    d = synth.dense_bf16_outliers(seed=590, B=1, S=S, Hq=16, Hkv=2)
+    signs = synth.hadamard_signs(591)
+    q, k, v = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
+    rows = synth.sample_rows(592, S, 256, [0, S - 1])
+    ref, _ = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=True, rows=rows)
+    sel = torch.from_numpy(rows).cuda()
+    v8t, vs = lcat.attn_quantize_fp8_v(v)
+    errs = {}
+    for sg in (None, signs):
+        k8, ks = lcat.attn_quantize_fp8_blocks(k, signs=sg)
+        o8, _ = lcat.attn_prefill_fp8(q, k8, ks, v, causal=True, scale=d["scale"], signs=sg)
+        opv, _ = lcat.attn_prefill_fp8_pv(q, k8, ks, v8t, vs, causal=True, scale=d["scale"],
+                                          signs=sg)
+        torch.cuda.synchronize()
+        for name, o in (("fp8", o8), ("fp8_pv", opv)):
+            got = to_np64(o[:, sel])
+            errs[name, sg is not None] = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    for name in ("fp8", "fp8_pv"):
+        log(f"  {name}: rel-L2 against exact {errs[name, False]:.4f} plain, "
+            f"{errs[name, True]:.4f} rotated")
+        assert errs[name, False] > 1.6 * errs[name, True], (name, errs)
+
+
 def test_prefill_fp8_32k_causal_sampled():
     """The 32K causal GQA shape (16 Q / 2 KV heads) on the seeded N(0,1)
     inputs themselves (RoPE has its own tests; the FP8 codes depend on the

@@ -65,17 +65,18 @@ def _expected_v_layout(v_bits):
     return codes, scales
 
 
-def _run(d, causal):
+def _run(d, causal, signs=None):
     q, k, v = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
-    k8, ks = lcat.attn_quantize_fp8_blocks(k)
+    k8, ks = lcat.attn_quantize_fp8_blocks(k, signs=signs)
     v8t, vs = lcat.attn_quantize_fp8_v(v)
-    return lcat.attn_prefill_fp8_pv(q, k8, ks, v8t, vs, causal=causal, scale=d["scale"])
+    return lcat.attn_prefill_fp8_pv(q, k8, ks, v8t, vs, causal=causal, scale=d["scale"], signs=signs)
 
 
-def _bounds(d, causal, ref, rows):
+def _bounds(d, causal, ref, rows, signs=None):
     """Per-element bound on |O - O''| and per-row bound on |dLSE| from the
     rounding of P' to e4m3 (module docstring)."""
-    qd, kd = ofp8.prefill_fp8_operands(np.ascontiguousarray(d["q"][:, rows]), d["k"], d["scale"])
+    qd, kd = ofp8.prefill_fp8_operands(np.ascontiguousarray(d["q"][:, rows]), d["k"], d["scale"],
+                                       signs)
     vabs = np.abs(ofp8.dequantized_v_keys(d["v"]))
     B, R, Hq, D = qd.shape
     S, Hkv = kd.shape[1], kd.shape[2]
@@ -102,8 +103,8 @@ def _bounds(d, causal, ref, rows):
     return bo, bl
 
 
-def _assert_close(got, ref, got_lse, ref_lse, d, causal, rows, what):
-    bo, bl = _bounds(d, causal, ref, rows)
+def _assert_close(got, ref, got_lse, ref_lse, d, causal, rows, what, signs=None):
+    bo, bl = _bounds(d, causal, ref, rows, signs)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     err = np.abs(got - ref)
     lim = bo + 2.0 ** -8 * np.abs(ref) + 1e-3
@@ -174,6 +175,28 @@ def test_prefill_fp8_pv_uniform_v():
     got = to_np64(o)[0].reshape(S, 2, 8, 128)
     err = np.abs(got - want[None, :, None, :])
     assert (err <= 2.0 ** -8 * np.abs(want[None, :, None, :]) + 1e-6).all(), err.max()
+
+
+@pytest.mark.parametrize("S,B,Hq,Hkv,causal,outliers", [
+    (300, 2, 16, 2, True, True), (640, 1, 16, 2, False, True), (130, 2, 4, 1, True, False),
+    (1100, 1, 16, 2, True, True), (1300, 1, 4, 4, True, True),
+])
+def test_prefill_fp8_pv_rotated_vs_oracle(S, B, Hq, Hkv, causal, outliers):
+    """Incoherent processing: Q and K rotated by diag(s) H before they are
+    quantised (the K quantiser and the prefill get the same signs); every
+    row against the oracle over the rotated, dequantised operands, on
+    N(0, 1) inputs and on inputs with outlier channels."""
+    log(f"prefill fp8 pv rotated S={S} B={B} Hq={Hq} Hkv={Hkv} causal={causal} outliers={outliers}")
+    gen = synth.dense_bf16_outliers if outliers else synth.dense_bf16
+    d = gen(seed=560 + S, B=B, S=S, Hq=Hq, Hkv=Hkv)
+    signs = synth.hadamard_signs(561 + S)
+    o, lse = _run(d, causal, signs)
+    torch.cuda.synchronize()
+    ref, ref_lse = ofp8.attention_fp8_pv(d["q"], d["k"], d["v"], d["scale"], causal=causal,
+                                         signs=signs)
+    e, r, t, f = _assert_close(to_np64(o), ref, lse.cpu().numpy(), ref_lse, d, causal,
+                               np.arange(S), "prefill fp8 pv rotated", signs)
+    log(f"  max abs {e:.3g} row rel-L2 {r:.3g} rel-L2 {t:.3g} (bound used {f:.2f})")
 
 
 def _stepped_scores(seed, B, S, Hq, Hkv, step_keys=128, step=13.0, D=128):
