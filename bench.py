@@ -82,6 +82,8 @@ SEEDS = {
     "chunked_4x131072": [51, 52, 53],     # torch: Q, K, V
     "cp_zigzag_64k": [61, 62, 63],        # torch: Q, K, V
     "cpu_sample_rows": 77,                # synth.sample_rows
+    "hadamard_signs": 93,                 # synth.hadamard_signs (FP8 incoherent processing)
+    "fp8_outliers": 94,                   # synth.dense_bf16_outliers
 }
 
 
@@ -478,7 +480,12 @@ def bench_fp8_prefill(torch, lcat, synth, reps=10, warmup=5):
     is also timed next to the bf16 prefill on the same inputs, and the two
     outputs are compared (rel-L2 of the FP8 result against the bf16 one).
     ``fp8_pv``: the same rotated inputs with V block-quantised along keys
-    (attn_quantize_fp8_v) through attn_prefill_fp8_pv (both products on FP8)."""
+    (attn_quantize_fp8_v) through attn_prefill_fp8_pv (both products on FP8).
+    ``incoherent``: attn_prefill_fp8_pv with Q and K rotated by the
+    random-sign Hadamard matrix before quantisation, timed on the same
+    inputs; and, on a 4096-token input with outlier channels in Q and K,
+    each FP8 prefill's distance to the bf16 prefill with and without the
+    rotation."""
     S, Hq, Hkv = 32768, 16, 2
     d = synth.causal_gqa(seed=SEEDS["causal_gqa_32k"], S=S, Hq=Hq, Hkv=Hkv)
     q0, k0, v = dev_tensor(torch, d["q"]), dev_tensor(torch, d["k"]), dev_tensor(torch, d["v"])
@@ -546,9 +553,45 @@ def bench_fp8_prefill(torch, lcat, synth, reps=10, warmup=5):
                   speedup_vs_fp8_scores_kernel=round(kms / pms, 3),
                   rel_l2_vs_bf16_kernel=round(pdiff, 5),
                   workload="the same inputs, V block-quantised along keys, both products on FP8")
+    # incoherent processing: the same inputs with Q and K rotated
+    signs = synth.hadamard_signs(SEEDS["hadamard_signs"])
+    k8r, kscr = torch.empty_like(k8), torch.empty_like(ksc)
+    lcat.attn_quantize_fp8_blocks(ks[-1], k8r, kscr, signs=signs)
+    rot_t = EventTimer(torch)
+    for i in range(3 * warmup + reps):
+        with rot_t:
+            lcat.attn_prefill_fp8_pv(qs[-1], k8r, kscr, v8t, vsc, causal=True, o=op, lse=lse,
+                                     signs=signs)
+        if i == 3 * warmup - 1:
+            torch.cuda.synchronize()
+            rot_t.pairs.clear()
+    torch.cuda.synchronize()
+    rms = rot_t.mean_ms()
+    rdiff = (op.float() - ob.float()).norm().item() / ob.float().norm().item()
+    # accuracy on outlier channels, against the bf16 prefill of the same input
+    do = synth.dense_bf16_outliers(seed=SEEDS["fp8_outliers"], B=1, S=4096, Hq=Hq, Hkv=Hkv)
+    qo, ko, vo = (dev_tensor(torch, do[x]) for x in ("q", "k", "v"))
+    ref, _ = lcat.attn_prefill(qo, ko, vo, causal=True)
+    vo8, vosc = lcat.attn_quantize_fp8_v(vo)
+    acc = {}
+    for tag, sg in (("plain", None), ("rotated", signs)):
+        ko8, kosc = lcat.attn_quantize_fp8_blocks(ko, signs=sg)
+        o8, _ = lcat.attn_prefill_fp8(qo, ko8, kosc, vo, causal=True, scale=do["scale"], signs=sg)
+        opv, _ = lcat.attn_prefill_fp8_pv(qo, ko8, kosc, vo8, vosc, causal=True, scale=do["scale"],
+                                          signs=sg)
+        for name, out in (("fp8", o8), ("fp8_pv", opv)):
+            acc[f"{name}_{tag}"] = round((out.float() - ref.float()).norm().item()
+                                         / ref.float().norm().item(), 5)
+    incoherent = dict(fp8_pv_kernel_ms=round(rms, 4),
+                      fp8_pv_TFLOPs=round(flops / (rms * 1e-3) / 1e12, 1),
+                      slowdown_vs_plain=round(rms / pms, 4),
+                      fp8_pv_rel_l2_vs_bf16_kernel=round(rdiff, 5),
+                      outliers_rel_l2_vs_bf16_kernel=acc,
+                      outliers_workload="4096 tokens causal, 16 Q / 2 KV heads, 4 seeded head "
+                                        "dims of Q x8 and of K x2 (synth.dense_bf16_outliers)")
     # QK^T at the fp8 peak plus P V at the bf16 peak
     mixed_peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
-    return dict(fp8_pv=fp8_pv, kernel_ms=round(kms, 4), TFLOPs=round(tf, 1),
+    return dict(fp8_pv=fp8_pv, incoherent=incoherent, kernel_ms=round(kms, 4), TFLOPs=round(tf, 1),
                 frac_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4),
                 frac_mixed_peak=round(tf / mixed_peak, 4), mixed_peak_TFLOPs=round(mixed_peak, 1),
                 step_ms=round(step_t.mean_ms(), 4), quantize_k_us=round(quant_t.mean_ms() * 1e3, 2),
