@@ -235,23 +235,27 @@ def test_prefill_fp8_pv_long_rows(S, B, Hq, Hkv, causal, stepped):
     log(f"  max abs {e:.3g} row rel-L2 {r:.3g} rel-L2 {t:.3g} (bound used {f:.2f})")
 
 
-def test_prefill_fp8_pv_32k_causal_sampled():
+@pytest.mark.parametrize("rotated", [False, True])
+def test_prefill_fp8_pv_32k_causal_sampled(rotated):
     """The 32K causal GQA shape (16 Q / 2 KV heads) on the seeded N(0,1)
-    inputs themselves: 512 seeded rows plus the forced rows against the
-    oracle over the dequantised operands; the error against exact attention
-    is logged for the record."""
+    inputs themselves, plain and with Q and K rotated (the signs the bench
+    uses): 512 seeded rows plus the forced rows against the oracle over the
+    dequantised operands; the error against exact attention is logged for
+    the record."""
     S = 32768
-    log("fp8 pv 32K: generating inputs")
+    log(f"fp8 pv 32K rotated={rotated}: generating inputs")
     d = synth.causal_gqa(seed=2, S=S)
-    o, lse = _run(d, True)
+    signs = synth.hadamard_signs(93) if rotated else None
+    o, lse = _run(d, True, signs)
     torch.cuda.synchronize()
     rows = synth.sample_rows(23, S, 512, [0, 1, 31, 32, 63, 64, 65, 127, 128, S // 2, S - 2, S - 1])
     log(f"fp8 pv 32K: oracle on {rows.size} rows x 16 heads")
-    ref, ref_lse = ofp8.attention_fp8_pv(d["q"], d["k"], d["v"], d["scale"], causal=True, rows=rows)
+    ref, ref_lse = ofp8.attention_fp8_pv(d["q"], d["k"], d["v"], d["scale"], causal=True, rows=rows,
+                                         signs=signs)
     idx = torch.from_numpy(rows).cuda()
     got = to_np64(o[:, idx])
     e, r, t, f = _assert_close(got, ref, lse[:, :, idx].cpu().numpy(), ref_lse, d, True, rows,
-                               "fp8 pv 32K")
+                               "fp8 pv 32K", signs)
     log(f"fp8 pv 32K: max abs {e:.3g} row rel-L2 {r:.3g} rel-L2 {t:.3g} (bound used {f:.2f})")
     exact, _ = oracle.attention(d["q"], d["k"], d["v"], d["scale"], causal=True, rows=rows)
     dev = np.abs(got - exact)
