@@ -17,7 +17,8 @@
 // writes them; v bf16 [B][S][Hkv][128].  Each wave multiplies its query rows
 // by scale * log2(e) in fp32 and quantises them per 32 dims with the same
 // rule as it loads them, so the matrix core produces the softmax exponents
-// (log2 units) directly.
+// (log2 units) directly.  With rotation signs (incoherent processing,
+// hadamard.h) each query row is first rotated, and k8 holds the rotated K.
 //
 // The operand layout of the scaled FP8 MFMA is stated in prefill_fp8_common.h.
 #include "device.h"

@@ -5,17 +5,19 @@
 // S = Q K^T and O = P V on 8-bit operands with block quantisation.  S^T =
 // K Q^T runs as in the FP8-score kernel (prefill_fp8.hip): per-32-dim E8M0
 // scales on Q and K inside the scaled MFMA, the query multiplied by
-// scale * log2(e) and quantised in the kernel.  P V contracts over keys, so
-// V's blocks run along keys: attn_quantize_fp8_v stores V^T (dimension-major)
-// as e4m3 with one scale per (dim, 32 keys), and the weights are rounded to
-// e4m3 in registers.  The weights are formed as P' = 2^(s - m + 3) (s, m in
-// log2 units, m the running reference), which puts the weights near the row
-// maximum in e4m3's normal range, and every P' stays at most 2^8.75 < 448:
-// a tile whose weights would exceed it is rescaled to its exact maximum
-// first.  The denominator l is the sum of the rounded weights themselves,
-// formed by one more FP8 MFMA (16x16x128) against a 0/1 operand, so
-// O = sum P' V / sum P' normalises exactly the weights that P V used.  The rest is the
-// bf16 prefill: K/V tiles staged in LDS rings by DMA, S^T = K Q^T so that
+// scale * log2(e) and quantised in the kernel (rotated first when rotation
+// signs are given: incoherent processing, hadamard.h).  P V contracts over
+// keys, so V's blocks run along keys: attn_quantize_fp8_v stores V^T
+// (dimension-major) as e4m3 with one scale per (dim, 32 keys), and the
+// weights are rounded to e4m3 in registers.  The weights are formed as
+// P' = 2^(s - m + 3) (s, m in log2 units, m the running reference), which
+// puts the weights near the row maximum in e4m3's normal range, and every P'
+// stays at most 2^8.75 < 448: a tile whose weights would exceed it is
+// rescaled to its exact maximum first.  The denominator l is the sum of the
+// rounded weights themselves, formed by one more FP8 MFMA (16x16x128)
+// against a 0/1 operand, so O = sum P' V / sum P' normalises exactly the
+// weights that P V used.  The rest is the bf16 prefill: K/V tiles staged in
+// LDS rings by DMA, S^T = K Q^T so that
 // softmax statistics are lane-local, online softmax with a running maximum
 // and denominator (§18.3), one division by l at the end (§18.4); scores never
 // leave registers.
