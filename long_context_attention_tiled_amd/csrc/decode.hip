@@ -232,25 +232,28 @@ __device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g
     const int v8_voff = qi * BT + 16 * g4;
     const int sc_voff = 64 * g4;   // bytes: scales of keys 16*g4 ..
     BlockRegs8 R8;
+    // The FP8 blocks are read with the non-temporal hint: 0.215 -> 0.193 ms
+    // for the 32-request workload.  The bf16 path below keeps plain loads:
+    // the hint made its K loads, and the kernel, 4% slower.
     auto load_k8 = [&](int blk) __attribute__((always_inline)) {
       const __amdgpu_buffer_rsrc_t r = make_rsrc(kp8 + (size_t)blk * BLOCK_BYTES8, BLOCK_BYTES8);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) R8.k[t][u] = buf_load_16(r, k8_voff + 64 * u, 512 * t);
+        for (int u = 0; u < 2; ++u) R8.k[t][u] = buf_load_16_nt(r, k8_voff + 64 * u, 512 * t);
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.k_scale + (size_t)blk * BT, BT * 4);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        R8.ks[t] = __builtin_bit_cast(f32x4, buf_load_16(rs, sc_voff, 16 * t));
+        R8.ks[t] = __builtin_bit_cast(f32x4, buf_load_16_nt(rs, sc_voff, 16 * t));
     };
     auto load_v8 = [&](int blk) __attribute__((always_inline)) {
       const __amdgpu_buffer_rsrc_t r = make_rsrc(vp8 + (size_t)blk * BLOCK_BYTES8, BLOCK_BYTES8);
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) R8.v[dt] = buf_load_16(r, v8_voff, 1024 * dt);
+      for (int dt = 0; dt < 8; ++dt) R8.v[dt] = buf_load_16_nt(r, v8_voff, 1024 * dt);
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.v_scale + (size_t)blk * BT, BT * 4);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        R8.vs[t] = __builtin_bit_cast(f32x4, buf_load_16(rs, sc_voff, 16 * t));
+        R8.vs[t] = __builtin_bit_cast(f32x4, buf_load_16_nt(rs, sc_voff, 16 * t));
     };
     auto step8 = [&](auto masked_tag, int blk_next, bool has_next, int nv) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(masked_tag)::value != 0;

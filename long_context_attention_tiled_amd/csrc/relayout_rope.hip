@@ -76,8 +76,8 @@ __global__ __launch_bounds__(NT) void permute_rope_kernel(RopeJob j0, RopeJob j1
     dst[u] = (t * j.H_loc + h) * row_bytes + 16LL * c;
     tab[u] = (int)(t - t_first) * half + 8 * c;
     if (p < p_end) {
-      lo[u] = ld_global_16(j.in + src);
-      hi[u] = ld_global_16(j.in + src + 2 * half);
+      lo[u] = ld_global_16_nt(j.in + src);
+      hi[u] = ld_global_16_nt(j.in + src + 2 * half);
     }
   }
   if (rot) {

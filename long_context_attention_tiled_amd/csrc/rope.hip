@@ -4,7 +4,7 @@
 //
 // A workgroup handles a few consecutive tokens: it builds theta once and the
 // (cos, sin) table of those tokens in LDS (each angle once, shared by all
-// heads), then streams the heads with 16-byte loads and non-temporal 16-byte
+// heads), then streams the heads with non-temporal 16-byte loads and
 // stores.  Many small workgroups stream HBM faster here than fewer ones that
 // each walk several token groups with their next loads issued ahead.
 #include "device.h"
@@ -50,8 +50,8 @@ __global__ __launch_bounds__(NT) void rope_kernel(bf16 *__restrict__ x,
       if (it < items) {
         int c, t;
         const bf16 *row = row_of(it, c, t);
-        lo[u] = as_bf16x8(ld_global_16(row + 8 * c));
-        hi[u] = as_bf16x8(ld_global_16(row + half + 8 * c));
+        lo[u] = as_bf16x8(ld_global_16_nt(row + 8 * c));
+        hi[u] = as_bf16x8(ld_global_16_nt(row + half + 8 * c));
       }
     }
   };
