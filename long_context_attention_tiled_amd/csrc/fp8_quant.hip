@@ -82,38 +82,49 @@ __global__ __launch_bounds__(256) void quantize_fp8_rotated_kernel(const bf16 *_
   *reinterpret_cast<uint32_t *>(scales + row * 4) = sc;
 }
 
-// V for FP8 P V: blocks run along keys (the contraction axis of P V), one
-// thread per (batch, KV head, 32-key block, dim) with the dim fastest, so a
-// wave's loads are contiguous 128-byte pieces of 64 dims of one key row.
+// V for FP8 P V: blocks run along keys (the contraction axis of P V).  One
+// workgroup per (batch, KV head, 64-key tile): the 64 x 128 bf16 tile comes
+// in with 16-byte loads (16 threads per 256-byte key row) and is written to
+// LDS transposed, dimension-major; thread (d, h) then takes the 32 keys
+// 32 h .. +31 of dim d from LDS, quantises them as one block and writes
+// their 32 codes, so the two threads of a dim write its 64 contiguous codes.
 // Output: v8t [B][Hkv][128][S64] (dimension-major, S64 = S rounded up to 64,
 // keys >= S written as code 0) and per 64-key tile a 256-byte scale block
 // whose byte 4 (32 h + r) + db is the scale of dim 32 db + r over keys
 // 64 t + 32 h .. +31: the word lane r + 32 h of a wave loads is the A-operand
 // scale word of P V for that lane, one dim group db per byte.
+constexpr int kVqPitch = 64 + 8;   // LDS row (one dim) in bf16: 64 keys + pad
 __global__ __launch_bounds__(256) void quantize_fp8_v_kernel(const bf16 *__restrict__ v,
                                                              uint8_t *__restrict__ v8t,
                                                              uint8_t *__restrict__ v_scale, int S,
-                                                             int Hkv, int S64, long long n_threads) {
-  const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (id >= n_threads) return;
-  const int d = (int)(id % 128);
-  long long rest = id / 128;
-  const int nblk = S64 / 32;
-  const int blk = (int)(rest % nblk);
-  rest /= nblk;
-  const int g = (int)(rest % Hkv);
-  const long long b = rest / Hkv;
-  const int key0 = 32 * blk;
-  const int n = min(32, S - key0);   // keys of this block that exist (may be <= 0)
+                                                             int Hkv, int S64) {
+  __shared__ __attribute__((aligned(16))) bf16 tile_t[128 * kVqPitch];
+  const int tid = threadIdx.x;
+  const int n_tiles = S64 / 64;
+  const int t = blockIdx.x % n_tiles;
+  const long long bg = blockIdx.x / n_tiles;   // b * Hkv + g
+  const long long b = bg / Hkv;
+  const int g = (int)(bg % Hkv);
+  const int key0 = 64 * t;
+  // load: chunk c = tid + 256 u covers key c / 16, dims 8 (c % 16) .. +7
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = tid + 256 * u;
+    const int key = c >> 4, d0 = 8 * (c & 15);
+    bf16x8 x = {};
+    if (key0 + key < S)
+      x = as_bf16x8(ld_global_16_nt(v + (((b * S + key0 + key) * Hkv + g) * 128 + d0)));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile_t[(d0 + e) * kVqPitch + key] = x[e];
+  }
+  __syncthreads();
+  const int d = tid >> 1, h = tid & 1;
   float x[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    x[i] = 0.f;
-    if (i < n) {
-      const uint16_t bits = *reinterpret_cast<const uint16_t *>(
-          v + (((b * S + key0 + i) * Hkv + g) * 128 + d));
-      x[i] = bf16_to_f32(bits);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const bf16x8 w = *reinterpret_cast<const bf16x8 *>(&tile_t[d * kVqPitch + 32 * h + 8 * i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[8 * i + e] = (float)w[e];
   }
   float amax = 0.f;
 #pragma unroll
@@ -124,11 +135,10 @@ __global__ __launch_bounds__(256) void quantize_fp8_v_kernel(const bf16 *__restr
   for (int w = 0; w < 8; ++w)
     out[w >> 2][w & 3] = fp8x4_rne(__builtin_amdgcn_ldexpf(x[4 * w], -e), __builtin_amdgcn_ldexpf(x[4 * w + 1], -e),
                                    __builtin_amdgcn_ldexpf(x[4 * w + 2], -e), __builtin_amdgcn_ldexpf(x[4 * w + 3], -e));
-  uint8_t *dst = v8t + ((b * Hkv + g) * 128 + d) * (long long)S64 + key0;
+  uint8_t *dst = v8t + (bg * 128 + d) * (long long)S64 + key0 + 32 * h;
   st_global_16(dst, out[0]);
   st_global_16(dst + 16, out[1]);
-  const long long tile = (b * Hkv + g) * (S64 / 64) + blk / 2;
-  v_scale[tile * 256 + 4 * (32 * (blk & 1) + (d & 31)) + (d >> 5)] = (uint8_t)(e + 127);
+  v_scale[(bg * n_tiles + t) * 256 + 4 * (32 * h + (d & 31)) + (d >> 5)] = (uint8_t)(e + 127);
 }
 
 }  // namespace
@@ -157,13 +167,11 @@ hipError_t launch_quantize_fp8_rotated(const void *x, void *codes, uint8_t *scal
 hipError_t launch_quantize_fp8_v(const void *v, void *v8t, uint8_t *v_scale, int B, int S, int Hkv,
                                  hipStream_t stream) {
   const int S64 = (S + 63) / 64 * 64;
-  const long long n_threads = (long long)B * Hkv * (S64 / 32) * 128;
-  if (n_threads <= 0) return hipSuccess;
-  const long long n_wg = (n_threads + 255) / 256;
+  const long long n_wg = (long long)B * Hkv * (S64 / 64);
+  if (n_wg <= 0) return hipSuccess;
   if (n_wg > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(quantize_fp8_v_kernel, dim3((unsigned)n_wg), dim3(256), 0, stream,
-                     static_cast<const bf16 *>(v), static_cast<uint8_t *>(v8t), v_scale, S, Hkv, S64,
-                     n_threads);
+                     static_cast<const bf16 *>(v), static_cast<uint8_t *>(v8t), v_scale, S, Hkv, S64);
   return hipGetLastError();
 }
 
