@@ -124,7 +124,7 @@ def test_quantize_fp8_rotated_bit_exact(rows, outliers):
 
 @pytest.mark.parametrize("S,B,Hq,Hkv,causal,outliers", [
     (300, 2, 16, 2, True, True), (640, 1, 16, 2, False, True), (200, 1, 8, 8, True, False),
-    (1100, 1, 16, 2, True, True), (1300, 1, 4, 4, True, True),
+    (1100, 1, 16, 2, True, True), (1300, 1, 4, 4, True, True), (257, 1, 32, 2, False, True),
 ])
 def test_prefill_fp8_rotated_vs_oracle(S, B, Hq, Hkv, causal, outliers):
     """FP8 scores with incoherent processing: every row against the oracle

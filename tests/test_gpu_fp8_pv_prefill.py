@@ -179,7 +179,7 @@ def test_prefill_fp8_pv_uniform_v():
 
 @pytest.mark.parametrize("S,B,Hq,Hkv,causal,outliers", [
     (300, 2, 16, 2, True, True), (640, 1, 16, 2, False, True), (130, 2, 4, 1, True, False),
-    (1100, 1, 16, 2, True, True), (1300, 1, 4, 4, True, True),
+    (1100, 1, 16, 2, True, True), (1300, 1, 4, 4, True, True), (257, 1, 32, 2, False, True),
 ])
 def test_prefill_fp8_pv_rotated_vs_oracle(S, B, Hq, Hkv, causal, outliers):
     """Incoherent processing: Q and K rotated by diag(s) H before they are
