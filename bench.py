@@ -224,8 +224,7 @@ def bench_step(torch, lcat, synth, steps, warmup):
 
     def step(i, time_kernel):
         q, k = qs[i], ks[i]
-        lcat.rope_apply(q[0], pos)
-        lcat.rope_apply(k[0], pos)
+        lcat.rope_apply_qk(q[0], k[0], pos)
         if time_kernel:
             with timer:
                 lcat.attn_prefill(q, k, v, causal=True, o=o, lse=lse)
@@ -431,8 +430,7 @@ def bench_relayout_and_prefill_64k(torch, lcat, iters=20, n_sets=4):
     for it in range(4):
         with ptimer:   # relayout, then RoPE in place, then prefill
             relayout()
-            lcat.rope_apply(qo, pos)
-            lcat.rope_apply(ko, pos)
+            lcat.rope_apply_qk(qo, ko, pos)
             with ktimer:
                 lcat.attn_prefill(qo[None], ko[None], vo[None], causal=True, o=o, lse=lse)
         with ftimer:   # fused relayout + RoPE, then prefill
@@ -499,8 +497,7 @@ def bench_fp8_prefill(torch, lcat, synth, reps=10, warmup=5):
     step_t, kern_t, quant_t = EventTimer(torch), EventTimer(torch), EventTimer(torch)
     for i in range(n):   # the first `warmup` steps let the clock settle
         with step_t:
-            lcat.rope_apply(qs[i][0], pos)
-            lcat.rope_apply(ks[i][0], pos)
+            lcat.rope_apply_qk(qs[i][0], ks[i][0], pos)
             with quant_t:
                 lcat.attn_quantize_fp8_blocks(ks[i], k8, ksc)
             with kern_t:
@@ -603,7 +600,8 @@ def bench_fp8_prefill(torch, lcat, synth, reps=10, warmup=5):
 
 def bench_rope(torch, lcat, iters=30, n_sets=6):
     """rope_apply on the 32K step's Q [32768][16][128] and K [32768][2][128]
-    bf16, in place, cycling through ``n_sets`` buffers (768 MB of Q, so no
+    bf16, in place, each alone and both in one rope_apply_qk launch, cycling
+    through ``n_sets`` buffers (768 MB of Q, so no
     call finds its data in the last-level cache); against an in-place copy of
     the same bytes (the yardstick for a pass that rewrites its input) and a
     copy into a separate buffer."""
@@ -640,6 +638,22 @@ def bench_rope(torch, lcat, iters=30, n_sets=6):
                                         frac_hbm=round(out_gbs / PEAK_HBM_GBS, 4))
             res["q"]["frac_of_in_place_copy"] = round(gbs / in_gbs, 4)
         del xs
+    # Q and K of one step in a single launch (rope_apply_qk), the form the
+    # step uses: 144 MB moved per call.
+    qs = [seeded_normal_bf16(torch, (S, 16, D), 81 + i) for i in range(n_sets)]
+    ks = [seeded_normal_bf16(torch, (S, 2, D), 91 + i) for i in range(n_sets)]
+    run = rotating([lambda a=a, b=b: lcat.rope_apply_qk(a, b, pos) for a, b in zip(qs, ks)])
+    for _ in range(n_sets):
+        run()
+    torch.cuda.synchronize()
+    ms = back_to_back_ms(torch, run, iters)
+    nb = 2 * S * (16 + 2) * D * 2
+    gbs = nb / (ms * 1e-3) / 1e9
+    res["qk"] = dict(us=round(ms * 1e3, 2), GBps=round(gbs, 1),
+                     frac_hbm=round(gbs / PEAK_HBM_GBS, 4), bytes=nb,
+                     two_calls_us=round(res["q"]["us"] + res["k"]["us"], 2),
+                     shape=f"Q [{S}][16][{D}] and K [{S}][2][{D}] bf16, one launch")
+    del qs, ks
     res["buffer_sets"] = n_sets
     return res
 

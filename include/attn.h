@@ -324,6 +324,16 @@ int attn_prefill_fp8_pv(const void *q, const void *k8, const uint8_t *k_scale, c
 int rope_apply(void *x, const int32_t *positions, int S, int H, int D, float base, void *stream);
 
 /*
+ * rope_apply_qk — rope_apply on q [S][Hq][D] and k [S][Hkv][D] at the same
+ * positions, in one launch: each token's (cos, sin) table is formed once and
+ * serves its query and key heads.  Results are those of rope_apply on each
+ * tensor, bit for bit.  Same rules as rope_apply; q and k must not overlap
+ * (ATTN_ERR_SHAPE).
+ */
+int rope_apply_qk(void *q, void *k, const int32_t *positions, int S, int Hq, int Hkv, int D,
+                  float base, void *stream);
+
+/*
  * seq_to_head_permute — the local half of the Ulysses exchange ([ULY] §2.2):
  * gather this rank's heads from every sequence shard into global token order.
  *   in  [SP][S_loc][H_tot][D], out [SP*S_loc][H_tot/SP][D], elements of

@@ -24,7 +24,7 @@ from ._lib import (ATTN_CP_CONTIGUOUS, ATTN_CP_STRIPED, ATTN_CP_ZIGZAG, ATTN_DEV
 
 __all__ = [
     "attn_prefill", "attn_chunked_prefill", "attn_kv_append", "attn_decode",
-    "attn_decode_workspace_bytes", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv", "head_to_seq_permute",
+    "attn_decode_workspace_bytes", "rope_apply", "rope_apply_qk", "seq_to_head_permute", "seq_to_head_permute_qkv", "head_to_seq_permute",
     "seq_to_head_permute_qkv_rope", "cp_shard_tokens", "cp_shard", "cp_unshard",
     "attn_key_limits", "attn_prefill_limited", "attn_merge", "CP_MODES", "attn_decode_fp8",
     "attn_kv_quantize_fp8", "attn_kv_append_fp8", "attn_quantize_fp8_blocks", "attn_prefill_fp8",
@@ -461,6 +461,21 @@ def rope_apply(x, positions, base=10000.0, stream=None):
     st = _lib.load().rope_apply(_ptr(x), _ptr(positions), S, H, D, float(base), _stream(stream))
     _lib.check("rope_apply", st)
     return x
+
+
+def rope_apply_qk(q, k, positions, base=10000.0, stream=None):
+    """Rotate ``q [S][Hq][D]`` and ``k [S][Hkv][D]`` (bf16) in place at the same
+    absolute ``positions [S]`` (int32), in one launch."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    _need(k, "k", torch.bfloat16, (S, Hkv, D))
+    _need(positions, "positions", torch.int32, (S,))
+    st = _lib.load().rope_apply_qk(_ptr(q), _ptr(k), _ptr(positions), S, Hq, Hkv, D, float(base),
+                                   _stream(stream))
+    _lib.check("rope_apply_qk", st)
+    return q, k
 
 
 def seq_to_head_permute_qkv(q, k, v, rank, outs=None, stream=None):

@@ -50,6 +50,7 @@ SIGNATURES = {
     "attn_prefill_fp8_pv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
                                  _vp, _vp]),
     "rope_apply": (_i, [_vp, _vp, _i, _i, _i, _f, _vp]),
+    "rope_apply_qk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _vp]),
     "seq_to_head_permute": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "head_to_seq_permute": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "seq_to_head_permute_qkv_rope": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,

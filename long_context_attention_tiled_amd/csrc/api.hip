@@ -471,7 +471,23 @@ int rope_apply(void *x, const int32_t *positions, int S, int H, int D, float bas
   if (S == 0) return ATTN_OK;
   if (!x || !positions) return ATTN_ERR_NULL;
   if (!aligned16(x)) return ATTN_ERR_ALIGN;
-  return hip_status(lcat::launch_rope(x, positions, S, H, D, base, static_cast<hipStream_t>(stream)));
+  return hip_status(lcat::launch_rope(x, H, nullptr, 0, positions, S, D, base,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int rope_apply_qk(void *q, void *k, const int32_t *positions, int S, int Hq, int Hkv, int D,
+                  float base, void *stream) {
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+  if (D % 16 || D > 256) return ATTN_ERR_UNSUPPORTED;
+  if (!(base > 0.f)) return ATTN_ERR_SHAPE;
+  if (S == 0) return ATTN_OK;
+  if (!q || !k || !positions) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k)) return ATTN_ERR_ALIGN;
+  const long long nq = (long long)S * Hq * D * 2, nk = (long long)S * Hkv * D * 2;
+  const char *a = static_cast<const char *>(q), *c = static_cast<const char *>(k);
+  if (a < c + nk && c < a + nq) return ATTN_ERR_SHAPE;   // q and k overlap
+  return hip_status(lcat::launch_rope(q, Hq, k, Hkv, positions, S, D, base,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int seq_to_head_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,

@@ -135,8 +135,10 @@ hipError_t launch_kv_append_fp8(const void *k_new, const void *v_new, void *k8, 
                                 int max_blocks, const int32_t *start_pos, int T, int B, int Hkv,
                                 int kv_head_base, int32_t *dev_status, hipStream_t stream);
 
-hipError_t launch_rope(void *x, const int32_t *positions, int S, int H, int D, float base,
-                       hipStream_t stream);
+// RoPE in place on x [S][H][D] and, when H2 > 0, on x2 [S][H2][D] at the
+// same positions (one launch, one (cos, sin) table per token).
+hipError_t launch_rope(void *x, int H, void *x2, int H2, const int32_t *positions, int S, int D,
+                       float base, hipStream_t stream);
 
 hipError_t launch_permute(const void *in, void *out, int SP, int S_loc, int H_tot, int D, int rank,
                           int elem_bytes, hipStream_t stream);

@@ -21,9 +21,12 @@ constexpr int MAX_TABLE = 4096;   // (token, frequency) pairs per workgroup
 // Dynamic LDS: theta_i for i < D/2 (doubles), then the (cos, sin) table of
 // the workgroup's tokens.  The first batch of loads is issued before the
 // table is built, so its latency is hidden behind that arithmetic.
-__global__ __launch_bounds__(NT) void rope_kernel(bf16 *__restrict__ x,
-                                                  const int32_t *__restrict__ positions, int S,
-                                                  int H, int D, double log2_base, int tok_per_wg) {
+// Two tensors can be rotated in one launch (Q and K at the same positions):
+// head h < H of a token is row h of x, head H + h2 is row h2 of x2, and the
+// token's (cos, sin) table serves both.
+__global__ __launch_bounds__(NT) void rope_kernel(bf16 *__restrict__ x, int H, bf16 *__restrict__ x2,
+                                                  int H2, const int32_t *__restrict__ positions,
+                                                  int S, int D, double log2_base, int tok_per_wg) {
   extern __shared__ __attribute__((aligned(16))) char rope_lds[];
   const int half = D >> 1;
   double *theta = reinterpret_cast<double *>(rope_lds);
@@ -34,14 +37,15 @@ __global__ __launch_bounds__(NT) void rope_kernel(bf16 *__restrict__ x,
   if (nt <= 0) return;
 
   const int chunks = half >> 3;                      // 8-element chunks per half
-  const int items = nt * H * chunks;
+  const int Ht = H + H2;
+  const int items = nt * Ht * chunks;
   bf16x8 lo[UPT], hi[UPT];
   auto row_of = [&](int it, int &c, int &t) __attribute__((always_inline)) -> bf16 * {
     c = it % chunks;
     const int th = it / chunks;
-    const int h = th % H;
-    t = th / H;
-    return x + ((size_t)(t0 + t) * H + h) * D;
+    const int h = th % Ht;
+    t = th / Ht;
+    return h < H ? x + ((size_t)(t0 + t) * H + h) * D : x2 + ((size_t)(t0 + t) * H2 + (h - H)) * D;
   };
   auto load = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
@@ -82,18 +86,18 @@ __global__ __launch_bounds__(NT) void rope_kernel(bf16 *__restrict__ x,
 
 }  // namespace
 
-hipError_t launch_rope(void *x, const int32_t *positions, int S, int H, int D, float base,
-                       hipStream_t stream) {
-  if (S <= 0 || H <= 0) return hipSuccess;
+hipError_t launch_rope(void *x, int H, void *x2, int H2, const int32_t *positions, int S, int D,
+                       float base, hipStream_t stream) {
+  if (S <= 0 || H + H2 <= 0) return hipSuccess;
   const int chunks = D / 16;
-  int tok = NT * UPT / (H * chunks);
+  int tok = NT * UPT / ((H + H2) * chunks);
   if (tok < 1) tok = 1;
   if (tok > 64) tok = 64;
   while (tok > 1 && tok * (D / 2) > MAX_TABLE) --tok;
   const size_t lds = (size_t)(D / 2) * sizeof(double) + (size_t)tok * (D / 2) * sizeof(float2);
   dim3 grid((S + tok - 1) / tok), block(NT);
-  hipLaunchKernelGGL(rope_kernel, grid, block, lds, stream, static_cast<bf16 *>(x), positions, S,
-                     H, D, log2((double)base), tok);
+  hipLaunchKernelGGL(rope_kernel, grid, block, lds, stream, static_cast<bf16 *>(x), H,
+                     static_cast<bf16 *>(x2), H2, positions, S, D, log2((double)base), tok);
   return hipGetLastError();
 }
 

@@ -45,8 +45,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["attn_prefill", "attn_chunked_prefill", "attn_decode", "attn_decode_workspace_bytes",
-              "attn_kv_append", "rope_apply", "seq_to_head_permute", "seq_to_head_permute_qkv",
-              "head_to_seq_permute", "seq_to_head_permute_qkv_rope", "cp_shard_tokens",
+              "attn_kv_append", "rope_apply", "rope_apply_qk", "seq_to_head_permute",
+              "seq_to_head_permute_qkv", "head_to_seq_permute", "seq_to_head_permute_qkv_rope", "cp_shard_tokens",
               "cp_shard", "cp_unshard", "attn_key_limits", "attn_prefill_limited", "attn_merge",
               "attn_decode_fp8", "attn_kv_quantize_fp8", "attn_kv_append_fp8",
               "attn_status_string", "attn_build_id", "attn_decode_noalloc", "attn_quantize_fp8_blocks",
@@ -226,6 +226,15 @@ def test_rope_and_permute_validation(lib):
     assert r(NUL, NUL, 0, 2, 128, 10000.0, S0) == OK
     assert r(NUL, A16, 10, 2, 128, 10000.0, S0) == NULL
     assert r(MIS, A16, 10, 2, 128, 10000.0, S0) == ALIGN
+    r2 = lib.rope_apply_qk
+    K = P(0x40000000)
+    assert r2(A16, K, A16, 10, 16, 2, 100, 10000.0, S0) == UNSUP
+    assert r2(A16, K, A16, 10, 16, 0, 128, 10000.0, S0) == SHAPE
+    assert r2(A16, K, A16, 10, 16, 2, 128, 0.0, S0) == SHAPE
+    assert r2(NUL, NUL, NUL, 0, 16, 2, 128, 10000.0, S0) == OK
+    assert r2(A16, NUL, A16, 10, 16, 2, 128, 10000.0, S0) == NULL
+    assert r2(A16, MIS, A16, 10, 16, 2, 128, 10000.0, S0) == ALIGN
+    assert r2(A16, P(0x10000 + 1024), A16, 10, 16, 2, 128, 10000.0, S0) == SHAPE   # k inside q
     p = lib.seq_to_head_permute
     assert p(A16, P(0x90000000), 4, 16, 6, 128, 0, 2, S0) == SHAPE     # 6 % 4
     assert p(A16, P(0x90000000), 4, 16, 8, 128, 4, 2, S0) == SHAPE     # rank out of range

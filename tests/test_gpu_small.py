@@ -176,6 +176,26 @@ def test_rope_commutes_with_relayout():
         assert torch.equal(pa, pb)
 
 
+@pytest.mark.parametrize("S,Hq,Hkv,D", [(1, 16, 2, 128), (300, 16, 2, 128), (4099, 16, 2, 128),
+                                         (77, 8, 8, 64), (130, 32, 1, 256)])
+def test_rope_apply_qk_equals_two_calls(S, Hq, Hkv, D):
+    """Q and K rotated in one launch equal rope_apply on each tensor bit for
+    bit, and Q matches the oracle; positions reach 2^17 and are not
+    consecutive."""
+    q = synth.normal_bf16(230 + S, (S, Hq, D))
+    k = synth.normal_bf16(231 + S, (S, Hkv, D))
+    pos = np.random.default_rng(232 + S).integers(0, 1 << 17, S).astype(np.int32)
+    qa, ka, pd = to_dev(q), to_dev(k), to_dev(pos)
+    lcat.rope_apply_qk(qa, ka, pd)
+    qb, kb = to_dev(q), to_dev(k)
+    lcat.rope_apply(qb, pd)
+    lcat.rope_apply(kb, pd)
+    torch.cuda.synchronize()
+    assert torch.equal(qa, qb) and torch.equal(ka, kb)
+    _rope_ref_bits_close(bits(qa), oracle.rope(q, pos))
+    _rope_ref_bits_close(bits(ka), oracle.rope(k, pos))
+
+
 # ---------------------------------------------------------------------------
 # fp32 exact path
 # ---------------------------------------------------------------------------
