@@ -18,6 +18,12 @@
 //    is a 16-byte read straight from HBM; the score registers already sit in
 //    B-operand order because K rows are read in a fixed permuted order.
 //  * K and V of a 64-token block go straight from HBM to registers; no LDS.
+//  * Every 16-byte load instruction covers whole 128-byte lines: the lanes
+//    of query slot qi < 8 fetch the first 64 bytes of a line, those of
+//    qi + 8 the second 64 bytes of the same line, and one DPP move per word
+//    (lane l and l ^ 8 of each 16-lane row) hands each lane the operand
+//    the MFMA expects.  With that, the non-temporal hint pays: loads that
+//    touched only half of each line ran 4% slower with it.
 //  * Slots at or past ctx_len are excluded by index: scores are set to -inf
 //    and their V entries to zero before any multiply (they may hold NaN).
 //
@@ -38,16 +44,39 @@ constexpr int HD = 128;
 constexpr int BT = 64;
 constexpr int REC = 132;   // floats per workspace record: O[128], m (log2 units), l, pad
 
+// Loads that fill whole lines (see above) leave lane l of each 16-lane row
+// (l = qi) holding, in `a`, the first half of a line of row r(qi & 7) when
+// qi < 8 and its second half when qi >= 8, and in `b` the same halves of
+// row r((qi & 7) + 8).  The operand of the first half for row r(qi) is then
+// a (qi < 8) or b of lane qi - 8, and that of the second half a of lane
+// qi + 8 or b (qi >= 8).  A row rotation by 8 lanes (DPP row_ror:8) reads
+// lane qi ^ 8; the bank mask keeps the lanes that already hold their part.
+constexpr int kDppRowRor8 = 0x128;
+__device__ __forceinline__ u32x4 line_first_half(u32x4 a, u32x4 b) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)   // lanes 8..15 of each row (banks 2, 3) take b from lane ^ 8
+    r[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)a[i], (int)b[i], kDppRowRor8, 0xF, 0xC, false);
+  return r;
+}
+__device__ __forceinline__ u32x4 line_second_half(u32x4 a, u32x4 b) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)   // lanes 0..7 of each row (banks 0, 1) take a from lane ^ 8
+    r[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)b[i], (int)a[i], kDppRowRor8, 0xF, 0x3, false);
+  return r;
+}
+
 struct BlockRegs {
-  u32x4 k[4][4];   // K rows of the four 16-key sub-tiles, four 32-wide d slices
-  u32x4 v[2][8];   // V^T: two 32-key halves x eight 16-row d tiles
+  u32x4 k[4][4];   // K of the four 16-key sub-tiles as loaded: [t][2h + x] = line h, rows x
+  u32x4 v[2][8];   // V^T of eight 16-row d tiles as loaded: [x][dt] = rows x
 };
 
 constexpr int BLOCK_BYTES = BT * HD * 2;   // 16 KiB: one K block or one V block
 constexpr int BLOCK_BYTES8 = BT * HD;     // 8 KiB: one fp8 K or V block
 
 struct BlockRegs8 {
-  u32x4 k[4][2];   // K rows of the four 16-key sub-tiles, two 64-wide d halves (16 dims each)
+  u32x4 k[4][2];   // K of the four 16-key sub-tiles as loaded: [t][x] = rows x
   u32x4 v[8];      // V^T: eight 16-row d tiles, 16 keys each
   f32x4 ks[4];     // K scale of the keys whose scores land in s[t]
   f32x4 vs[4];     // V scale of the same keys
@@ -116,26 +145,32 @@ __device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g
     return __builtin_amdgcn_readlane(ids, i - ids_base);
   };
 
-  // K row (within a block) read by this lane for sub-tile t = 2w + e:
-  //   32w + 8*(qi>>2) + 4e + (qi&3); its score then lands in register r of
-  //   lane group g4 exactly where the B operand of P V expects key
-  //   32w + 8*g4 + 4e + r.
-  const int k_voff = (8 * (qi >> 2) + (qi & 3)) * (HD * 2) + 16 * g4;
-  const int v_voff = qi * (BT * 2) + 16 * g4;
+  // K row (within a block) whose MFMA operand lane qi holds for sub-tile
+  // t = 2w + e: r(qi) = 32w + 8*(qi>>2) + 4e + (qi&3); its score then lands
+  // in register r of lane group g4 exactly where the B operand of P V
+  // expects key 32w + 8*g4 + 4e + r.  d slice ds (dims 32 ds + 8 g4 ..) of
+  // that row is half (ds & 1) of its 128-byte line ds >> 1.  Loads fill
+  // whole lines: load x of line h brings rows r((qi & 7) + 8x), bytes
+  // 128h + 64 (qi >> 3) + 16 g4; r(q + 8) = r(q) + 16.  V^T rows are head
+  // dims, 128 bytes each: load x of d tile dt brings row 16 dt + (qi & 7) + 8x,
+  // bytes 64 (qi >> 3) + 16 g4 (keys 32 (qi >> 3) + 8 g4 ..).
+  const int k_voff = (8 * ((qi & 7) >> 2) + (qi & 3)) * (HD * 2) + 64 * (qi >> 3) + 16 * g4;
+  const int v_voff = (qi & 7) * (BT * 2) + 64 * (qi >> 3) + 16 * g4;
   auto load_k = [&](BlockRegs &R, int blk) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(kp + (size_t)blk * BT * HD, BLOCK_BYTES);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        R.k[t][s] = buf_load_16(r, k_voff + 64 * s + 1024 * (t & 1), 8192 * (t >> 1));
+      for (int hx = 0; hx < 4; ++hx)   // hx = 2h + x
+        R.k[t][hx] = buf_load_16_nt(r, k_voff + 128 * (hx >> 1) + 4096 * (hx & 1) + 1024 * (t & 1),
+                                    8192 * (t >> 1));
   };
   auto load_v = [&](BlockRegs &R, int blk) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(vp + (size_t)blk * HD * BT, BLOCK_BYTES);
 #pragma unroll
-    for (int w = 0; w < 2; ++w)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) R.v[w][dt] = buf_load_16(r, v_voff + 64 * w, 2048 * dt);
+      for (int dt = 0; dt < 8; ++dt) R.v[x][dt] = buf_load_16_nt(r, v_voff + 1024 * x, 2048 * dt);
   };
 
   const float c2 = p.scale * kLog2e;
@@ -156,7 +191,11 @@ __device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g
     for (int t = 0; t < 4; ++t) {
       s[t] = f32x4{};
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) s[t] = mfma_16x16x32(as_bf16x8(R.k[t][ds]), qf[ds], s[t]);
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 a = R.k[t][2 * h], b = R.k[t][2 * h + 1];
+        s[t] = mfma_16x16x32(as_bf16x8(line_first_half(a, b)), qf[2 * h], s[t]);
+        s[t] = mfma_16x16x32(as_bf16x8(line_second_half(a, b)), qf[2 * h + 1], s[t]);
+      }
     }
     if (has_next) load_k(R, blk_next);
     if constexpr (MASKED) {
@@ -165,16 +204,6 @@ __device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (32 * (t >> 1) + 8 * g4 + 4 * (t & 1) + r >= nv) s[t][r] = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k0 = 32 * w + 8 * g4 + 2 * e;
-          const uint32_t keep = (k0 >= nv ? 0u : 0xFFFFu) | (k0 + 1 >= nv ? 0u : 0xFFFF0000u);
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) R.v[w][dt][e] &= keep;
-        }
-      }
     }
 
     float mx = s[0][0];
@@ -200,6 +229,25 @@ __device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g
         pb[t >> 1][4 * (t & 1) + r] = to_bf16(pv);
       }
     l_run = l_run * alpha + psum;
+    // V^T operands: R.v[w][dt] = keys 32w + 8 g4 .. of head dim 16 dt + qi
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const u32x4 a = R.v[0][dt], b = R.v[1][dt];
+      R.v[0][dt] = line_first_half(a, b);
+      R.v[1][dt] = line_second_half(a, b);
+    }
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k0 = 32 * w + 8 * g4 + 2 * e;
+          const uint32_t keep = (k0 >= nv ? 0u : 0xFFFFu) | (k0 + 1 >= nv ? 0u : 0xFFFF0000u);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) R.v[w][dt][e] &= keep;
+        }
+      }
+    }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       acc[dt] *= alpha;
@@ -222,25 +270,25 @@ __device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g
     else
       step(Int<1>{}, 0, false, tail);
   } else {
-    // K row read by this lane for sub-tile t: 16*(qi>>2) + 4t + (qi&3); its
-    // score lands in register r of lane group g4 as key 16*g4 + 4t + r, which
-    // is where the B operand of P V expects it (V^T operand w of a lane holds
-    // keys 16*g4 + 8w .. +7).
+    // K row whose operand lane qi holds for sub-tile t: r(qi) =
+    // 16*(qi>>2) + 4t + (qi&3); its score lands in register r of lane group
+    // g4 as key 16*g4 + 4t + r, which is where the B operand of P V expects
+    // it (V^T operand w of a lane holds keys 16*g4 + 8w .. +7).  Rows are
+    // 128 bytes, one line: load x brings rows r((qi & 7) + 8x) = r(qi & 7) +
+    // 32x, bytes 64 (qi >> 3) + 16 g4, and the operand of dims 64u + 16 g4 ..
+    // is half u of the line.  V^T rows (64 bytes) are whole per 4 lanes.
     const uint8_t *kp8 = static_cast<const uint8_t *>(p.k_pool);
     const uint8_t *vp8 = static_cast<const uint8_t *>(p.v_pool);
-    const int k8_voff = (16 * (qi >> 2) + (qi & 3)) * HD + 16 * g4;
+    const int k8_voff = (16 * ((qi & 7) >> 2) + (qi & 3)) * HD + 64 * (qi >> 3) + 16 * g4;
     const int v8_voff = qi * BT + 16 * g4;
     const int sc_voff = 64 * g4;   // bytes: scales of keys 16*g4 ..
     BlockRegs8 R8;
-    // The FP8 blocks are read with the non-temporal hint: 0.215 -> 0.193 ms
-    // for the 32-request workload.  The bf16 path below keeps plain loads:
-    // the hint made its K loads, and the kernel, 4% slower.
     auto load_k8 = [&](int blk) __attribute__((always_inline)) {
       const __amdgpu_buffer_rsrc_t r = make_rsrc(kp8 + (size_t)blk * BLOCK_BYTES8, BLOCK_BYTES8);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) R8.k[t][u] = buf_load_16_nt(r, k8_voff + 64 * u, 512 * t);
+        for (int x = 0; x < 2; ++x) R8.k[t][x] = buf_load_16_nt(r, k8_voff + 4096 * x, 512 * t);
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.k_scale + (size_t)blk * BT, BT * 4);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -261,10 +309,12 @@ __device__ __forceinline__ void decode_range(const DecodeParams &p, int b, int g
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         s[t] = f32x4{};
+        const u32x4 kh[2] = {line_first_half(R8.k[t][0], R8.k[t][1]),
+                             line_second_half(R8.k[t][0], R8.k[t][1])};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          s[t] = mfma_16x16x32(fp8x8_to_bf16(R8.k[t][u][0], R8.k[t][u][1]), qf[2 * u], s[t]);
-          s[t] = mfma_16x16x32(fp8x8_to_bf16(R8.k[t][u][2], R8.k[t][u][3]), qf[2 * u + 1], s[t]);
+          s[t] = mfma_16x16x32(fp8x8_to_bf16(kh[u][0], kh[u][1]), qf[2 * u], s[t]);
+          s[t] = mfma_16x16x32(fp8x8_to_bf16(kh[u][2], kh[u][3]), qf[2 * u + 1], s[t]);
         }
         s[t] *= R8.ks[t];
       }
