@@ -9,12 +9,15 @@
 // all-zero group gets scale 0 and codes 0.  The divisions are IEEE fp32
 // divisions, so the codes are fixed by the definition.
 //
-// One workgroup (256 threads) per 64-token block.  K: four threads per token
-// row, 32 elements each; the row maximum is combined with two lane
-// exchanges.  V: two threads per dimension row, 32 keys each; the per-key
-// (column) maximum is combined in LDS with an integer max on the float bits
-// (magnitudes are non-negative, so their bit patterns order like their
-// values).
+// One workgroup (256 threads) per 64-token block; the K and V loads of a
+// thread are issued together at the start.  K: four threads per token row,
+// 32 elements each; the row maximum is combined with two lane exchanges.
+// V: two threads per dimension row, 32 keys each.  The per-key (column)
+// maximum goes through LDS: the magnitudes, as bf16 bit patterns (sign
+// cleared; non-negative patterns order like their values), are written as
+// a [128][64] tile, each thread takes the maximum of a pair of keys over 16
+// dimensions with packed 16-bit integer maxima, and 64 threads fold the 8
+// partial maxima of their key.
 #include "device.h"
 #include "kernels.h"
 
@@ -39,29 +42,47 @@ __device__ __forceinline__ u32x2 to_fp8x8(const float (&y)[8]) {
   return w;
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 __global__ __launch_bounds__(256) void kv_quantize_fp8_kernel(const bf16 *__restrict__ k_pool,
                                                               const bf16 *__restrict__ v_pool,
                                                               uint8_t *__restrict__ k8,
                                                               uint8_t *__restrict__ v8,
                                                               float *__restrict__ k_scale,
                                                               float *__restrict__ v_scale) {
-  __shared__ uint32_t colmax[BT];
+  constexpr int PITCH = BT / 2 + 1;            // dwords per dimension row of the tile
+  __shared__ uint32_t vmag[HD * PITCH];        // |V| as bf16 pairs: [d][key pair]
+  __shared__ uint32_t part[8][BT / 2];         // column maxima over 16 dims, key pairs
+  __shared__ float vsc[BT];
   const int tid = threadIdx.x;
   const size_t blk = blockIdx.x;
-  if (tid < BT) colmax[tid] = 0u;
 
-  // ---- K: token row j = tid / 4, elements 32 * (tid % 4) .. +31 ----------
-  {
-    const int j = tid >> 2, qd = tid & 3;
-    const bf16 *src = k_pool + (blk * BT + j) * HD + 32 * qd;
-    bf16x8 x[4];
+  // K: token row j = tid / 4, elements 32 * (tid % 4) .. +31;
+  // V: dimension row d = tid / 2, keys 32 * (tid % 2) .. +31
+  const int j = tid >> 2, qd = tid & 3;
+  const int d = tid >> 1, hh = tid & 1;
+  const bf16 *ksrc = k_pool + (blk * BT + j) * HD + 32 * qd;
+  const bf16 *vsrc = v_pool + (blk * HD + d) * BT + 32 * hh;
+  bf16x8 kx[4], vx[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = as_bf16x8(ld_global_16(src + 8 * i));
+  for (int i = 0; i < 4; ++i) kx[i] = as_bf16x8(ld_global_16(ksrc + 8 * i));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vx[i] = as_bf16x8(ld_global_16(vsrc + 8 * i));
+
+  // ---- V magnitudes into the tile (read back after the K part) ----------
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      vmag[d * PITCH + 16 * hh + 4 * i + w] = as_u32x4(vx[i])[w] & 0x7FFF7FFFu;
+
+  // ---- K ------------------------------------------------------------------
+  {
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)x[i][e]));
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)kx[i][e]));
     amax = fmaxf(amax, wave_shfl_xor(amax, 1));
     amax = fmaxf(amax, wave_shfl_xor(amax, 2));
     const float scale = amax / kE4M3Max;
@@ -70,7 +91,7 @@ __global__ __launch_bounds__(256) void kv_quantize_fp8_kernel(const bf16 *__rest
     for (int i = 0; i < 4; ++i) {
       float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = scale > 0.f ? (float)x[i][e] / scale : 0.f;
+      for (int e = 0; e < 8; ++e) y[e] = scale > 0.f ? (float)kx[i][e] / scale : 0.f;
       const u32x2 w = to_fp8x8(y);
       out[i >> 1][2 * (i & 1)] = w[0];
       out[i >> 1][2 * (i & 1) + 1] = w[1];
@@ -81,27 +102,36 @@ __global__ __launch_bounds__(256) void kv_quantize_fp8_kernel(const bf16 *__rest
     if (qd == 0) k_scale[blk * BT + j] = scale;
   }
 
-  // ---- V: dimension row d = tid / 2, keys 32 * (tid % 2) .. +31 ----------
-  __syncthreads();   // colmax cleared
-  const int d = tid >> 1, hh = tid & 1;
-  const bf16 *src = v_pool + (blk * HD + d) * BT + 32 * hh;
-  bf16x8 x[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = as_bf16x8(ld_global_16(src + 8 * i));
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      atomicMax(&colmax[32 * hh + 8 * i + e], __builtin_bit_cast(uint32_t, fabsf((float)x[i][e])));
+  // ---- V column maxima: thread (dims 16 g .., key pair kp) ----------------
   __syncthreads();
+  {
+    const int kp = tid & 31, g = tid >> 5;
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, vmag[(16 * g + r) * PITCH + kp]));
+    part[g][kp] = __builtin_bit_cast(uint32_t, m);
+  }
+  __syncthreads();
+  if (tid < BT) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) m = max(m, (part[g][tid >> 1] >> (16 * (tid & 1))) & 0xFFFFu);
+    const float scale = __builtin_bit_cast(float, m << 16) / kE4M3Max;
+    vsc[tid] = scale;
+    v_scale[blk * BT + tid] = scale;
+  }
+  __syncthreads();
+
+  // ---- V codes ------------------------------------------------------------
   u32x4 out[2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float scale = __builtin_bit_cast(float, colmax[32 * hh + 8 * i + e]) / kE4M3Max;
-      y[e] = scale > 0.f ? (float)x[i][e] / scale : 0.f;
+      const float scale = vsc[32 * hh + 8 * i + e];
+      y[e] = scale > 0.f ? (float)vx[i][e] / scale : 0.f;
     }
     const u32x2 w = to_fp8x8(y);
     out[i >> 1][2 * (i & 1)] = w[0];
@@ -110,7 +140,6 @@ __global__ __launch_bounds__(256) void kv_quantize_fp8_kernel(const bf16 *__rest
   uint8_t *dst = v8 + (blk * HD + d) * BT + 32 * hh;
   st_global_16(dst, out[0]);
   st_global_16(dst + 16, out[1]);
-  if (tid < BT) v_scale[blk * BT + tid] = __builtin_bit_cast(float, colmax[tid]) / kE4M3Max;
 }
 
 // Append T new tokens per request straight into the fp8 pools (the token ->
