@@ -84,6 +84,7 @@ SEEDS = {
     "cpu_sample_rows": 77,                # synth.sample_rows
     "hadamard_signs": 93,                 # synth.hadamard_signs (FP8 incoherent processing)
     "fp8_outliers": 94,                   # synth.dense_bf16_outliers
+    "decode_graph": 95,                   # synth.decode_cache (q); torch pools 200 + 2 l, 201 + 2 l
 }
 
 
@@ -598,6 +599,63 @@ def bench_fp8_prefill(torch, lcat, synth, reps=10, warmup=5):
                          "quantisation, FP8 scores with bf16 P V")
 
 
+def bench_decode_graph(torch, lcat, synth, layers=32, iters=20):
+    """A launch-bound decode step: 4 requests of 8192 cached tokens (16 Q /
+    2 KV heads) through ``layers`` layers, each with its own paged cache
+    (33.5 MB per layer), as ``layers`` attn_decode calls made from Python
+    one after the other, against the same calls captured once in a HIP graph
+    and replayed.  Wall time per step between synchronisations."""
+    c = synth.decode_cache(seed=SEEDS["decode_graph"], B=4, ctx_lens=[8192] * 4,
+                           with_content=False)
+    n_blocks, B, Hq = c["n_blocks"], 4, 16
+    q = dev_tensor(torch, c["q"])
+    meta = [dev_tensor(torch, c[k]) for k in ("block_head", "block_table", "ctx_len")]
+    pools = [(seeded_normal_bf16(torch, (n_blocks, 64, D), 200 + 2 * l_),
+              seeded_normal_bf16(torch, (n_blocks, D, 64), 201 + 2 * l_)) for l_ in range(layers)]
+    wsb = lcat.attn_decode_workspace_bytes(B, Hq, c["max_blocks"])
+    ws = [torch.empty(wsb, dtype=torch.uint8, device="cuda") for _ in range(layers)]
+    outs = [(torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda"),
+             torch.empty((B, Hq), dtype=torch.float32, device="cuda")) for _ in range(layers)]
+
+    def step():
+        for l_, (kp, vp) in enumerate(pools):
+            lcat.attn_decode(q, kp, vp, *meta, workspace=ws[l_], o=outs[l_][0], lse=outs[l_][1])
+
+    def wall_us(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / iters
+
+    for _ in range(3):
+        step()
+    eager_us = wall_us(step)
+    eager_last = [o.clone() for o, _ in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    graph_us = wall_us(g.replay)
+    same = all(torch.equal(o.view(torch.int16), e.view(torch.int16))
+               for (o, _), e in zip(outs, eager_last))
+    nbytes = layers * (int(c["ctx_len"].sum()) * 2 * D * 2 * 2 + 2 * B * Hq * D * 2 + B * Hq * 4)
+    del pools, ws
+    return dict(layers=layers, eager_us_per_step=round(eager_us, 1),
+                graph_us_per_step=round(graph_us, 1), speedup=round(eager_us / graph_us, 2),
+                graph_us_per_layer=round(graph_us / layers, 2),
+                graph_GBps=round(nbytes / (graph_us * 1e-6) / 1e9, 1),
+                graph_equals_eager=bool(same),
+                workload=f"{layers} layers x 4 requests x 8192 cached tokens, 16 Q / 2 KV heads")
+
+
 def bench_rope(torch, lcat, iters=30, n_sets=6):
     """rope_apply on the 32K step's Q [32768][16][128] and K [32768][2][128]
     bf16, in place, each alone and both in one rope_apply_qk launch, cycling
@@ -996,7 +1054,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="time only the step workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["step", "decode", "relayout", "chunked", "cp", "mfma",
-                                       "fixed_cost", "rope", "fp8"],
+                                       "fixed_cost", "rope", "fp8", "decode_graph"],
                     help="run a single leg (for profiling); prints its own JSON object")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -1031,6 +1089,8 @@ def main():
             res = bench_rope(torch, lcat)
         elif args.only == "fp8":
             res = bench_fp8_prefill(torch, lcat, synth)
+        elif args.only == "decode_graph":
+            res = bench_decode_graph(torch, lcat, synth)
         else:
             res = bench_chunked(torch, lcat, synth)[1]
         print(json.dumps({args.only: res, "build_id": build_id}), flush=True)
@@ -1062,6 +1122,8 @@ def main():
         out["prefill_fp8"] = bench_fp8_prefill(torch, lcat, synth)
         log("bench: decode")
         checks["decode"], out["decode"] = bench_decode(torch, lcat, synth)
+        log("bench: decode step in a HIP graph")
+        out["decode_graph"] = bench_decode_graph(torch, lcat, synth)
         log("bench: relayout + prefill 64k")
         checks["relayout"], (out["relayout"], out["prefill_64k"], out["relayout_back"]) = \
             bench_relayout_and_prefill_64k(torch, lcat)

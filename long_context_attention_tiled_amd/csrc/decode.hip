@@ -459,6 +459,17 @@ __device__ __forceinline__ void unit_prefix(const DecodeParams &p, int target, l
   if (target >= p.B) before = total;
 }
 
+// Number of pieces the W units are cut into: about four blocks per wave at
+// the least (whole multiples of 256 waves, so every XCD gets the same number),
+// and at most `max_waves` (the launch).  Small steps (a few requests of a
+// few thousand tokens) then have fewer, longer pieces and fewer records to
+// merge: 4 requests x 8192 tokens ran 20.6 -> 16.4 us per call with 256
+// waves instead of 768, while long mixes keep 768.
+__device__ __forceinline__ long long stream_pieces(long long W, int max_waves) {
+  const long long by_work = (W / (4 * 256)) * 256;
+  return min((long long)max_waves, max(256LL, by_work));
+}
+
 // Request containing unit `pos` (< total) and the first unit of that request.
 __device__ __forceinline__ void locate_unit(const DecodeParams &p, long long pos, int &req,
                                             long long &req_start) {
@@ -485,13 +496,14 @@ template <bool FP8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_stream_kernel(
     DecodeParams p) {
   const int w = blockIdx.x, lane = threadIdx.x;
-  const int P = p.stream_waves;
   if (w == 0 && p.dev_status) {   // contexts longer than the block table are flagged and clamped
     for (int r = lane; r < p.B; r += 64)
       if (p.ctx_len[r] > p.max_blocks * BT) p.dev_status[0] = 2;
   }
   long long before, W;
   unit_prefix(p, p.B, before, W);
+  const long long P = stream_pieces(W, p.stream_waves);
+  if (w >= P) return;
   const long long st = W * w / P, en = W * (w + 1) / P;
   if (st >= en) return;
   int b;
@@ -519,19 +531,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   }
 }
 
-// One workgroup (4 waves) per (request, query head).  Wave w folds splits
-// w, w+4, ... with lane l owning output channels 2l and 2l+1, then the four
-// partial sums are combined through LDS.
-constexpr int MERGE_WAVES = 4;
+// One workgroup (MERGE_WAVES waves) per (request, query head).  Wave w folds
+// splits w, w + MERGE_WAVES, ... with lane l owning output channels 2l and
+// 2l+1, then the waves' partial sums are combined through LDS.  Eight waves
+// of eight pieces each take up to 64 pieces in one round of loads: short
+// steps, whose (request, head) rows have tens of pieces, are bound by these
+// rounds of dependent loads.
+constexpr int MERGE_WAVES = 8;
 
 // Merge of the records (pieces) of one (request, query head):
 // O = sum w_i O_i / sum w_i l_i with w_i = 2^(m_i - M), M the largest piece
-// maximum.  Each wave folds pieces wave, wave + 4, ... in one pass, loading
-// kMergeBatch pieces at a time and keeping its sums relative to the largest
-// maximum it has seen (rescaled when that grows); the four waves' sums are
-// then brought to the common M and added.  `rec(i)` is the record of piece i
+// maximum.  Each wave folds pieces wave, wave + MERGE_WAVES, ... in one
+// pass, loading kMergeBatch pieces at a time and keeping its sums relative to
+// the largest maximum it has seen (rescaled when that grows); the waves' sums
+// are then brought to the common M and added.  `rec(i)` is the record of piece i
 // (NULL: no record).
-constexpr int kMergeBatch = 4;
+constexpr int kMergeBatch = 8;
 template <class RecOf>
 __device__ __forceinline__ void merge_records(const DecodeParams &p, int b, int h, int n_pieces,
                                               RecOf rec) {
@@ -577,7 +592,9 @@ __device__ __forceinline__ void merge_records(const DecodeParams &p, int b, int 
   }
   if (lane == 0) wmax[wave] = M;
   __syncthreads();
-  const float Mg = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  float Mg = wmax[0];
+#pragma unroll
+  for (int w = 1; w < MERGE_WAVES; ++w) Mg = fmaxf(Mg, wmax[w]);
   const float a = M == -INFINITY ? 0.f : fast_exp2(M - Mg);
   part[wave][2 * lane] = n0 * a;
   part[wave][2 * lane + 1] = n1 * a;
@@ -625,9 +642,9 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void decode_merge_stream_kernel(D
     write_empty(p, b, h);
     return;
   }
-  const long long P = p.stream_waves;
   long long before, W;
   unit_prefix(p, b, before, W);
+  const long long P = stream_pieces(W, p.stream_waves);
   const long long s0 = before + (long long)g * nb, s1 = s0 + nb;
   const long long w_first = ((s0 + 1) * P - 1) / W, w_last = (s1 * P - 1) / W;
   const long long seg = (long long)b * p.Hkv + g;
