@@ -417,6 +417,37 @@ def test_decode_all_rows(split):
     log(f"  max abs {e:.3g} rel-L2 {r:.3g}")
 
 
+@pytest.mark.parametrize("ctx,pieces", [
+    ([8192] * 4, 256),                      # W = 1024 units: 256 waves, 4 units each
+    ([8192] * 8 + [4096], 512),             # W = 2176: 512 waves
+    ([8192] * 12 + [1000], 768),            # W = 3104: 768 waves (the launch)
+    ([8192] * 7 + [65, 1, 0, 9000], 512),   # ragged tails and an empty request in the mix
+])
+def test_decode_piece_count_regimes(ctx, pieces):
+    """The equal-share split cuts the W = sum(Hkv * blocks) units into
+    256 * floor(W / 1024) pieces, clamped to [256, 768]; each regime
+    against the oracle (every row) and against fixed 256-key splits."""
+    W = sum(2 * ((c + 63) // 64) for c in ctx)
+    assert min(768, max(256, (W // 1024) * 256)) == pieces
+    log(f"decode pieces={pieces} W={W} ctx={ctx}")
+    c = synth.decode_cache(seed=605, B=len(ctx), ctx_lens=ctx, Hq=16, Hkv=2, extra_blocks=1)
+    args = [to_dev(c[k]) for k in ("q", "k_pool", "v_pool", "block_head", "block_table", "ctx_len")]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o, lse = lcat.attn_decode(*args, dev_status=st)
+    of, lf = lcat.attn_decode(*args, split_tokens=256)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    nz = [i for i, n in enumerate(ctx) if n > 0]
+    ref, ref_lse = oracle.decode_attention(c["q"][nz], [c["k_seq"][i] for i in nz],
+                                           [c["v_seq"][i] for i in nz], c["ctx_len"][nz],
+                                           c["scale"])
+    for got_o, got_l, what in ((o, lse, "equal-share"), (of, lf, "fixed splits")):
+        go, gl = to_np64(got_o), got_l.cpu().numpy()
+        assert_attention_close(go[nz], ref, gl[nz], ref_lse, what=what)
+        for i in set(range(len(ctx))) - set(nz):   # empty request: o = 0, lse = -inf
+            assert not go[i].any() and np.isneginf(gl[i]).all()
+
+
 @pytest.mark.parametrize("group", [1, 4, 16])
 def test_decode_group_sizes(group):
     Hkv = 2
