@@ -143,8 +143,9 @@ int attn_chunked_prefill(const void *q, const void *k_new, const void *v_new, vo
  *   key 0 .. ctx_len-1 is visible.  Slots past ctx_len are never used in
  *   arithmetic (they may hold NaN).
  *   split_tokens: keys per split, a positive multiple of 64, or 0 = automatic
- *   (the blocks of all requests and KV heads are shared out equally among a
- *   fixed number of waves, so long and short contexts load the GPU evenly).
+ *   (the blocks of all requests and KV heads are shared out equally among
+ *   256 to 768 waves, about four blocks per wave at the least, so long and
+ *   short contexts load the GPU evenly).
  *   workspace: caller-owned device scratch of at least
  *   attn_decode_workspace_bytes(B, Hq, D, max_blocks, split_tokens) bytes.
  * D must be 128 and Hq/Hkv at most 16.  ctx_len[b] = 0 gives o = 0 and
