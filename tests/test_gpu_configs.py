@@ -73,6 +73,30 @@ def test_causal_gqa_prefill_32k():
     log(f"C2: max abs {e:.3g} rel-L2 {r:.3g}")
 
 
+def test_causal_prefill_131072_sampled():
+    """The longest sequence the bench runs (a 131072-token request, as in the
+    chunked workload) as one dense causal prefill with RoPE of Q and K in one
+    launch: sampled rows against the oracle, including the first and last
+    rows and rows at tile edges."""
+    S = 131072
+    log("S=131072: generating inputs")
+    d = synth.causal_gqa(seed=8, S=S)
+    q, k, v = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
+    pos = to_dev(d["positions"])
+    log("S=131072: rope + prefill")
+    lcat.rope_apply_qk(q[0], k[0], pos)
+    o, lse = lcat.attn_prefill(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(23, S, 32, forced_rows(S, (S - 64, S - 65)))
+    log(f"S=131072: oracle on {rows.size} rows x 16 heads")
+    ref, ref_lse = prefill_reference(d["q"], d["k"], d["v"], d["positions"].astype(np.int64),
+                                     rows, d["scale"])
+    got = to_np64(o[:, torch.from_numpy(rows).cuda()])
+    got_lse = lse[:, :, torch.from_numpy(rows).cuda()].cpu().numpy()
+    e, r = assert_attention_close(got, ref, got_lse, ref_lse, what="S=131072")
+    log(f"S=131072: max abs {e:.3g} rel-L2 {r:.3g}")
+
+
 def test_ulysses_relayout_rope_prefill_64k():
     SP, S_loc = 4, 16384
     S = SP * S_loc
