@@ -173,7 +173,9 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_blocks, int spl
  * ATTN_ERR_SCRATCH and enqueues nothing.  No part of the array needs to start
  * at zero.  The call allocates nothing (no hipMalloc, hipFree or allocating
  * library routine); the first call on a GPU looks up that GPU's copy of the
- * array.  Every call on one GPU shares its array: calls that overlap on one
+ * array, so a caller that captures a graph makes one call on that GPU
+ * before capturing (later calls enqueue kernels only).  Every call on one
+ * GPU shares its array: calls that overlap on one
  * GPU (on different streams, or from different threads without ordering)
  * race on it and their outputs are undefined; calls ordered on one stream
  * are safe.

@@ -49,8 +49,10 @@ def _same_f32(a, b):
 
 
 def test_decode_graph_replays_match_eager():
-    """Two decode calls in one graph, the bf16 cache and its FP8 copy (two
-    layers of a decode step), replayed with a new query each time."""
+    """Three decode calls in one graph (three layers of a decode step): the
+    bf16 cache with a workspace, its FP8 copy, and the bf16 cache again
+    through attn_decode_noalloc (the entry point for callers that capture
+    graphs and cannot allocate), replayed with a new query each time."""
     ctx = [1, 65, 1000, 4097, 20000]
     c = synth.decode_cache(seed=710, B=len(ctx), ctx_lens=ctx, Hq=16, Hkv=2, extra_blocks=2)
     q, k_pool, v_pool, head, table, ctx_len = (
@@ -60,14 +62,15 @@ def test_decode_graph_replays_match_eager():
     ws = torch.empty(lcat.attn_decode_workspace_bytes(B, Hq, c["max_blocks"]), dtype=torch.uint8,
                      device="cuda")
     ws8 = torch.empty_like(ws)
-    o, o8 = torch.empty_like(q), torch.empty_like(q)
+    o, o8, on = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-    lse8 = torch.empty_like(lse)
+    lse8, lsen = torch.empty_like(lse), torch.empty_like(lse)
 
     def step():
         lcat.attn_decode(q, k_pool, v_pool, head, table, ctx_len, workspace=ws, o=o, lse=lse)
         lcat.attn_decode_fp8(q, k8, v8, ks, vs, head, table, ctx_len, workspace=ws8, o=o8,
                              lse=lse8)
+        lcat.attn_decode_noalloc(q, k_pool, v_pool, head, table, ctx_len, o=on, lse=lsen)
 
     g = _capture(step)
     for rep in range(4):
@@ -77,12 +80,13 @@ def test_decode_graph_replays_match_eager():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = [t.clone() for t in (o, lse, o8, lse8)]
+        got = [t.clone() for t in (o, lse, o8, lse8, on, lsen)]
         eo, el = lcat.attn_decode(q, k_pool, v_pool, head, table, ctx_len)
         eo8, el8 = lcat.attn_decode_fp8(q, k8, v8, ks, vs, head, table, ctx_len)
         torch.cuda.synchronize()
         assert np.array_equal(bits(got[0]), bits(eo)) and _same_f32(got[1], el)
         assert np.array_equal(bits(got[2]), bits(eo8)) and _same_f32(got[3], el8)
+        assert np.array_equal(bits(got[4]), bits(eo)) and _same_f32(got[5], el)
     ref, ref_lse = oracle.decode_attention(qn, c["k_seq"], c["v_seq"], c["ctx_len"],
                                            c["scale"])
     assert_attention_close(to_np64(got[0]), ref, got[1].cpu().numpy(), ref_lse)
