@@ -9,7 +9,14 @@
 // splits with the same rescale identity: M = max m_s, w_s = 2^(m_s - M),
 // O = sum w_s O_s / sum w_s l_s.
 //
-// Split kernel, one wave per (split, KV head, request):
+// Pieces: by default the blocks of all requests and KV heads are laid end to
+// end and shared out equally among 256 to 768 waves (stream_pieces), so a
+// wave's share may span several (request, KV head) segments and a long and
+// a short context load the GPU alike; with a fixed split size, one wave per
+// (split, KV head, request).  Each piece writes one record per query head,
+// and the merge kernel finds a segment's pieces arithmetically.
+//
+// Per block of a piece (decode_range):
 //  * The GQA group of the KV head (up to 16 query heads) is the N axis of
 //    v_mfma_f32_16x16x32_bf16; K rows are the M axis (S^T = K Q^T), so each
 //    lane owns one query and its softmax statistics need only lane-local
