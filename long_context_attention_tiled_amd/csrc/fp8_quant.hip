@@ -77,20 +77,23 @@ __global__ __launch_bounds__(256) void quantize_fp8_rotated_kernel(const bf16 *_
 // V for FP8 P V: blocks run along keys (the contraction axis of P V).  One
 // workgroup per (batch, KV head, 64-key tile): the 64 x 128 bf16 tile comes
 // in with 16-byte loads (16 threads per 256-byte key row) and is written to
-// LDS transposed, dimension-major; thread (d, h) then takes the 32 keys
-// 32 h .. +31 of dim d from LDS, quantises them as one block and writes
-// their 32 codes, so the two threads of a dim write its 64 contiguous codes.
+// LDS key-major as 4-byte words, rows 65 words apart; thread (d, h) then
+// reads the 32 keys 32 h .. +31 of dim d down a column (the pitch puts the
+// rows of the two key halves 32 banks apart, and the lanes of a wave on
+// distinct words, so neither side has bank conflicts), quantises them as one
+// block and writes their 32 codes, so the two threads of a dim write its 64
+// contiguous codes.
 // Output: v8t [B][Hkv][128][S64] (dimension-major, S64 = S rounded up to 64,
 // keys >= S written as code 0) and per 64-key tile a 256-byte scale block
 // whose byte 4 (32 h + r) + db is the scale of dim 32 db + r over keys
 // 64 t + 32 h .. +31: the word lane r + 32 h of a wave loads is the A-operand
 // scale word of P V for that lane, one dim group db per byte.
-constexpr int kVqPitch = 64 + 8;   // LDS row (one dim) in bf16: 64 keys + pad
+constexpr int kVqPitch = 65;   // LDS row (one key) in 4-byte words: 64 words of dims + pad
 __global__ __launch_bounds__(256) void quantize_fp8_v_kernel(const bf16 *__restrict__ v,
                                                              uint8_t *__restrict__ v8t,
                                                              uint8_t *__restrict__ v_scale, int S,
                                                              int Hkv, int S64) {
-  __shared__ __attribute__((aligned(16))) bf16 tile_t[128 * kVqPitch];
+  __shared__ uint32_t tile[64 * kVqPitch];
   const int tid = threadIdx.x;
   const int n_tiles = S64 / 64;
   const int t = blockIdx.x % n_tiles;
@@ -102,21 +105,21 @@ __global__ __launch_bounds__(256) void quantize_fp8_v_kernel(const bf16 *__restr
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int c = tid + 256 * u;
-    const int key = c >> 4, d0 = 8 * (c & 15);
-    bf16x8 x = {};
+    const int key = c >> 4, w0 = 4 * (c & 15);
+    u32x4 x = {};
     if (key0 + key < S)
-      x = as_bf16x8(ld_global_16_nt(v + (((b * S + key0 + key) * Hkv + g) * 128 + d0)));
+      x = ld_global_16_nt(v + (((b * S + key0 + key) * Hkv + g) * 128 + 2 * w0));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tile_t[(d0 + e) * kVqPitch + key] = x[e];
+    for (int w = 0; w < 4; ++w) tile[key * kVqPitch + w0 + w] = x[w];
   }
   __syncthreads();
   const int d = tid >> 1, h = tid & 1;
+  const int half_sel = 16 * (d & 1);   // dim d is the low (even d) or high half of word d / 2
   float x[32];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x8 w = *reinterpret_cast<const bf16x8 *>(&tile_t[d * kVqPitch + 32 * h + 8 * i]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[8 * i + e] = (float)w[e];
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t wd = tile[(32 * h + i) * kVqPitch + (d >> 1)];
+    x[i] = __builtin_bit_cast(float, (wd >> half_sel) << 16);
   }
   float amax = 0.f;
 #pragma unroll
