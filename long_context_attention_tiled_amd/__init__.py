@@ -468,6 +468,9 @@ def rope_apply_qk(q, k, positions, base=10000.0, stream=None):
     absolute ``positions [S]`` (int32), in one launch."""
     torch = _torch()
     _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q and k must be [S][H][D]")
     S, Hq, D = q.shape
     Hkv = k.shape[1]
     _need(k, "k", torch.bfloat16, (S, Hkv, D))
